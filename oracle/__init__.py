@@ -1,0 +1,12 @@
+"""fp64 CPU oracle for Sketch Attention compression (test infrastructure).
+
+Only the tests, the smoke check and the bench's CPU-baseline leg use this
+package.  The GPU library never imports it, and it imports nothing from the
+GPU library; the two share only the seeded inputs of ``synth``.
+"""
+from .sa_oracle import (  # noqa: F401
+    allocations,
+    logits,
+    sketch_batch,
+    sketch_one,
+)

@@ -1,0 +1,274 @@
+"""Seeded input generator for the Sketch Attention (SA) workloads.
+
+The shapes and distributions follow the workloads of the SequenceO1 pages
+(page "100,000 videos in your pocket", section "How it works" item 1: k from
+several hundred to several thousand prototypes; review page "Summary": the
+deployed sketch is 1K x 128, training batches R=40 users, serving R=300
+requests).  The pages measure on proprietary Douyin histories only; these
+seeded Gaussian inputs stand in for them.
+
+Recipe.  ``numpy.random.SeedSequence(seed).spawn(R + 1)`` gives one PCG64
+stream for the shared draws and one per user, so users can be drawn in
+parallel threads and the result does not depend on the thread count.
+
+Shared stream, in this order:
+1. lengths (integers)
+2. Wk  [d, d]  ~ N(0, 1/d)
+3. Wv  [d, d]  ~ N(0, 1/d)
+4. P   [k, d]  ~ N(0, 1/d)        (optionally scaled, "sharp" config)
+User u's own stream:
+5. H_u [n_u, d] ~ N(0, 1)  (or, clustered: centres, picks, noise)
+Deterministic:
+6. token mask (only the masked config): the last floor(frac * n_u) slots.
+
+Values are drawn as float32 normals, scaled in float32, then rounded to
+bfloat16 with round-to-nearest-even for the bf16 configs.  The oracle consumes
+the rounded values exactly (upcast to fp64).  Nothing here computes logits,
+allocations or sketches.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, List, Optional
+
+import numpy as np
+
+__all__ = [
+    "CONFIGS",
+    "Inputs",
+    "bf16_bits_to_f32",
+    "f32_to_bf16_bits",
+    "make_config",
+    "make_inputs",
+]
+
+
+_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+_CHUNK = 1 << 20
+
+
+def _round_chunk(src: np.ndarray, dst: np.ndarray) -> None:
+    u = src.view(np.uint32)
+    # finite inputs only: the largest finite pattern plus 0x8000 fits in 32 bits
+    dst[...] = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+                >> np.uint32(16)).astype(np.uint16)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even).
+
+    Returns the 16-bit patterns as uint16.  Inputs must be finite.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    spans = [(i, min(i + _CHUNK, flat.size)) for i in range(0, flat.size, _CHUNK)]
+    if len(spans) <= 1:
+        _round_chunk(flat, out)
+    else:
+        with ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(lambda s: _round_chunk(flat[s[0]:s[1]], out[s[0]:s[1]]), spans))
+    return out.reshape(x.shape)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns (uint16) to float32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclasses.dataclass
+class Inputs:
+    """One synthetic batch, stored host-side.
+
+    Floating arrays are float32 holding exactly the values the GPU sees: for
+    ``dtype == "bf16"`` every value is a bfloat16 value widened to float32, and
+    ``*_bits`` hold the matching uint16 patterns that are uploaded.
+    """
+
+    name: str
+    dtype: str                      # "bf16" or "f32"
+    d: int
+    k: int
+    lengths: np.ndarray             # [R] int64 (slots, masked tokens included)
+    offsets: np.ndarray             # [R+1] int64, packed ragged layout
+    H: np.ndarray                   # [N, d] float32
+    Wk: np.ndarray                  # [d, d] float32
+    Wv: np.ndarray                  # [d, d] float32
+    P: np.ndarray                   # [k, d] float32
+    mask: Optional[np.ndarray]      # [N] uint8 (1 = keep) or None
+    seed: int
+    H_bits: Optional[np.ndarray] = None
+    Wk_bits: Optional[np.ndarray] = None
+    Wv_bits: Optional[np.ndarray] = None
+    P_bits: Optional[np.ndarray] = None
+
+    @property
+    def R(self) -> int:
+        return int(self.lengths.shape[0])
+
+    @property
+    def N(self) -> int:
+        return int(self.offsets[-1])
+
+    def valid_tokens(self) -> int:
+        if self.mask is None:
+            return self.N
+        return int(self.mask.sum())
+
+    def user_slice(self, u: int) -> slice:
+        return slice(int(self.offsets[u]), int(self.offsets[u + 1]))
+
+
+def _round_store(x32: np.ndarray, dtype: str):
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(x32)
+        return bf16_bits_to_f32(bits), bits
+    if dtype == "f32":
+        return np.ascontiguousarray(x32, dtype=np.float32), None
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def make_inputs(
+    lengths,
+    d: int,
+    k: int,
+    seed: int,
+    dtype: str = "bf16",
+    name: str = "custom",
+    p_scale: float = 1.0,
+    clustered: int = 0,
+    cluster_noise: float = 0.1,
+    mask_tail_frac: float = 0.0,
+) -> Inputs:
+    """Draw one batch with the fixed draw order of the module docstring.
+
+    ``lengths`` is either a sequence of ints or a callable ``rng -> array`` so
+    that drawing the lengths is the first use of the generator.
+    ``p_scale`` multiplies P after the N(0, 1/d) draw.  ``clustered > 0`` draws
+    that many N(0,1) centres per user and sets every token to a random centre
+    plus ``cluster_noise`` times N(0,1) noise.  ``mask_tail_frac`` masks the
+    last ``floor(frac * n_u)`` slots of every user.
+    """
+    ss = np.random.SeedSequence(seed)
+    rng = np.random.default_rng(ss.spawn(1)[0])
+    if callable(lengths):
+        lens = np.asarray(lengths(rng), dtype=np.int64)
+    else:
+        lens = np.asarray(list(lengths), dtype=np.int64)
+    if lens.ndim != 1 or (lens < 0).any():
+        raise ValueError("lengths must be a 1-D array of non-negative ints")
+    offsets = np.zeros(lens.shape[0] + 1, dtype=np.int64)
+    np.cumsum(lens, out=offsets[1:])
+    N = int(offsets[-1])
+    std_w = np.float32(1.0 / math.sqrt(d))
+
+    Wk32 = rng.standard_normal((d, d), dtype=np.float32) * std_w
+    Wv32 = rng.standard_normal((d, d), dtype=np.float32) * std_w
+    P32 = rng.standard_normal((k, d), dtype=np.float32) * std_w
+    if p_scale != 1.0:
+        P32 = P32 * np.float32(p_scale)
+
+    H32 = np.empty((N, d), dtype=np.float32)
+    user_ss = np.random.SeedSequence(seed).spawn(1 + lens.shape[0])[1:]
+
+    def draw_user(u: int) -> None:
+        lo, hi = int(offsets[u]), int(offsets[u + 1])
+        n = hi - lo
+        g = np.random.default_rng(user_ss[u])
+        if clustered:
+            centres = g.standard_normal((clustered, d), dtype=np.float32)
+            pick = g.integers(0, clustered, size=n)
+            noise = g.standard_normal((n, d), dtype=np.float32)
+            H32[lo:hi] = centres[pick] + np.float32(cluster_noise) * noise
+        elif n:
+            g.standard_normal(out=H32[lo:hi], dtype=np.float32)
+
+    with ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(draw_user, range(lens.shape[0])))
+
+    mask = None
+    if mask_tail_frac > 0.0:
+        mask = np.ones(N, dtype=np.uint8)
+        for u in range(lens.shape[0]):
+            lo, hi = int(offsets[u]), int(offsets[u + 1])
+            cut = int(math.floor(mask_tail_frac * (hi - lo)))
+            if cut:
+                mask[hi - cut:hi] = 0
+
+    H, H_bits = _round_store(H32, dtype)
+    del H32
+    Wk, Wk_bits = _round_store(Wk32, dtype)
+    Wv, Wv_bits = _round_store(Wv32, dtype)
+    P, P_bits = _round_store(P32, dtype)
+    return Inputs(name=name, dtype=dtype, d=d, k=k, lengths=lens,
+                  offsets=offsets, H=H, Wk=Wk, Wv=Wv, P=P, mask=mask,
+                  seed=seed, H_bits=H_bits, Wk_bits=Wk_bits,
+                  Wv_bits=Wv_bits, P_bits=P_bits)
+
+
+def _uniform_lengths(lo, hi, R):
+    return lambda rng: rng.integers(lo, hi + 1, size=R)
+
+
+def _lognormal_lengths(mu, sigma, lo, hi, R):
+    def draw(rng):
+        x = rng.lognormal(mean=mu, sigma=sigma, size=R)
+        return np.clip(np.rint(x), lo, hi).astype(np.int64)
+    return draw
+
+
+# Named workloads.  Each entry: kwargs for make_inputs.  The workload shapes
+# are the pages' (n up to 100K, k = 1K, d = 128, R = 40 train / 120 misses of
+# 300 serving requests); the seeds are fixed here.
+CONFIGS: Dict[str, dict] = {
+    # single user, fp32, the small case the oracle finishes in well under a second
+    "c1_fp32_n4096_d64_k64": dict(lengths=[4096], d=64, k=64, seed=0, dtype="f32"),
+    # single user, deployed 1K x 128 sketch
+    "c2_n100k_d128_k1024": dict(lengths=[100_000], d=128, k=1024, seed=1),
+    # training-style ragged batch: R=40, n ~ U[20000, 100000]
+    "c3_r40_ragged_d128_k1024": dict(
+        lengths=_uniform_lengths(20_000, 100_000, 40), d=128, k=1024, seed=2),
+    # literal reading of the training batch: 40 x 100000
+    "c3lit_r40_n100k_d128_k1024": dict(lengths=[100_000] * 40, d=128, k=1024, seed=2),
+    # serving cache-miss batch: 300 requests x miss 0.4 -> 120 users
+    "c4_r120_lognormal_d128_k1024": dict(
+        lengths=_lognormal_lengths(math.log(30_000), 0.8, 1_000, 100_000, 120),
+        d=128, k=1024, seed=3),
+    # sketch-size sweep, 8 users x 100000
+    "c5_r8_n100k_d128_k256": dict(lengths=[100_000] * 8, d=128, k=256, seed=4),
+    "c5_r8_n100k_d128_k512": dict(lengths=[100_000] * 8, d=128, k=512, seed=4),
+    "c5_r8_n100k_d128_k2048": dict(lengths=[100_000] * 8, d=128, k=2048, seed=4),
+    "c5mask_r8_n100k_d128_k1024": dict(lengths=[100_000] * 8, d=128, k=1024,
+                                       seed=4, mask_tail_frac=0.1),
+    # parity-only: peaked softmax (logit std ~ 4) and clustered histories
+    "sharp_n100k_d128_k1024": dict(lengths=[100_000], d=128, k=1024, seed=5,
+                                   p_scale=4.0 * math.sqrt(128)),
+    "clustered_r4_n100k_d128_k1024": dict(lengths=[100_000] * 4, d=128, k=1024,
+                                          seed=6, clustered=64),
+    # small ragged cases spanning several tiles and a ragged tail
+    "small_ragged_d128_k256": dict(lengths=[0, 1, 77, 1000, 3333, 4096],
+                                   d=128, k=256, seed=11),
+    "small_ragged_d128_k1024": dict(lengths=[5, 513, 2047, 0, 6000],
+                                    d=128, k=1024, seed=12),
+    "small_ragged_d64_k128": dict(lengths=[31, 1, 2500, 640], d=64, k=128, seed=13),
+    "small_mask_d128_k512": dict(lengths=[1000, 1777, 64], d=128, k=512, seed=14,
+                                 mask_tail_frac=0.1),
+    "small_fp32_ragged_d128_k192": dict(lengths=[3, 700, 2049], d=128, k=192,
+                                        seed=15, dtype="f32"),
+}
+
+
+def make_config(name: str, **overrides) -> Inputs:
+    if name not in CONFIGS:
+        raise KeyError(f"unknown config {name!r}; known: {sorted(CONFIGS)}")
+    kw = dict(CONFIGS[name])
+    kw.update(overrides)
+    return make_inputs(name=name, **kw)
+
+
+def config_names() -> List[str]:
+    return list(CONFIGS)
