@@ -1,0 +1,140 @@
+/*
+ * sa.h — C ABI of the Sketch Attention (SA) compression library (libsa.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  SequenceO1's Sketch Attention compresses one
+ * user's behaviour history H_u (n_u tokens of width d) into a fixed k x d
+ * sketch using k learnable prototypes P and prototype-wise normalisation:
+ *   - arXiv abstract (mlsanity paper page, "Abstract"): learnable prototypes
+ *     and prototype-wise normalisation compress the raw history into a
+ *     fixed-size, target-agnostic user representation; a fused FlashSA kernel
+ *     keeps the computation practical;
+ *   - blog "100,000 videos in your pocket", "How it works" item 1: every
+ *     history item is softly assigned across the k prototypes and distributes
+ *     its mass over them; the output is a k x d sketch; item 3: the fused
+ *     kernel runs under ragged batches without materialising the huge
+ *     intermediates;
+ *   - review page (evolve.pub), FAQ on how SA differs from standard
+ *     attention: normalisation runs across prototypes, not the sequence.
+ * With K = H_u Wk, V = H_u Wv (row vectors), for every token t and prototype j
+ *     L[j,t] = p_j . k_t / sqrt(d)
+ *     A[j,t] = exp(L[j,t]) / sum_j' exp(L[j',t])          (softmax over j)
+ *     m_j    = sum_t A[j,t]                                (prototype mass)
+ *     S_u[j] = (sum_t A[j,t] v_t) / m_j                    (0 where m_j = 0)
+ * An empty user (n_u = 0, or every token masked) gives S_u = 0 and m = 0.
+ *
+ * Ownership and threading.  The caller owns every buffer.  All pointers
+ * except `problem` and `bytes` are DEVICE pointers on the current HIP device.
+ * The library allocates nothing and keeps no mutable global state; calls on
+ * different streams with different workspaces may run concurrently.
+ * sa_compress is asynchronous and stream-ordered: on SA_OK the work is queued
+ * on `stream` (a hipStream_t; NULL = the default stream) and S / mass are
+ * valid once the stream reaches that point.  No C++ exception crosses this
+ * ABI.
+ */
+#ifndef SA_H_
+#define SA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Argument errors are detected on the host before any launch. */
+typedef enum {
+  SA_OK = 0,
+  SA_E_INVALID = 1,      /* NULL pointer, negative size, inconsistent sizes   */
+  SA_E_UNSUPPORTED = 2,  /* valid problem outside the built kernels' shapes   */
+  SA_E_WORKSPACE = 3,    /* workspace NULL or smaller than sa_workspace_size   */
+  SA_E_HIP = 4           /* a HIP runtime call or kernel launch failed         */
+} sa_status;
+
+/* Element type of H, Wk, Wv and P.  Outputs are always float32. */
+typedef enum {
+  SA_BF16 = 0,           /* bfloat16 inputs; MFMA on fp16 operands, fp32 sums */
+  SA_F32 = 1             /* float32 inputs; fp32 arithmetic throughout         */
+} sa_dtype;
+
+/*
+ * One batch of users.
+ *   num_users    R >= 0.
+ *   total_tokens N >= 0, equal to offsets[R] (a host copy, so that no
+ *                device-to-host read is needed).
+ *   d            history / key / value width.  Built: 64 or 128.
+ *   k            number of prototypes.  Built: a multiple of 64, 64..4096.
+ *   dtype        an sa_dtype value.
+ */
+typedef struct {
+  int64_t num_users;
+  int64_t total_tokens;
+  int32_t d;
+  int32_t k;
+  int32_t dtype;
+  int32_t reserved;      /* must be 0 */
+} sa_problem;
+
+/*
+ * Workspace size for `problem`.  Writes the byte count to *bytes.  Returns
+ * SA_E_INVALID / SA_E_UNSUPPORTED for a problem sa_compress would reject.
+ * Pure host code; needs no GPU.  The size grows linearly in N, R and k.
+ */
+sa_status sa_workspace_size(const sa_problem* problem, size_t* bytes);
+
+/*
+ * Compress a ragged batch of R user histories into R sketches.
+ *
+ *   H           [N, d] row-major, dtype `problem->dtype`.  User u owns rows
+ *               offsets[u] .. offsets[u+1]-1.  For SA_BF16, magnitudes of
+ *               unmasked entries must be below 65504: they are widened
+ *               exactly to fp16 MFMA operands, larger ones saturate.
+ *   offsets     [R+1] int64, 0 = offsets[0] <= offsets[1] <= ... <= offsets[R]
+ *               = N.  Device memory.  If the sequence breaks this contract
+ *               the kernels treat every user as empty (S = 0, mass = 0) and
+ *               raise the device error flag read by sa_read_device_error.
+ *   token_mask  [N] uint8, 1 = keep the token, 0 = drop it entirely (it takes
+ *               no part in allocation, mass or sums; NaN in a dropped row
+ *               does not propagate).  NULL keeps every token.
+ *   Wk, Wv      [d, d] row-major, K = H Wk and V = H Wv.
+ *   P           [k, d] row-major prototypes.
+ *   S           [R, k, d] float32 output, fully overwritten.
+ *   mass        [R, k] float32 output m_j (fully overwritten), or NULL.
+ *   workspace   device scratch of at least sa_workspace_size bytes, 256-byte
+ *               aligned.  Its contents on entry are ignored.  One workspace
+ *               must not be shared by calls that may run concurrently.
+ *   stream      hipStream_t to queue the kernels on (NULL = default stream).
+ *
+ * R = 0 is a no-op.  N = 0 writes zero sketches.
+ */
+sa_status sa_compress(const sa_problem* problem,
+                      const void* H,
+                      const int64_t* offsets,
+                      const uint8_t* token_mask,
+                      const void* Wk,
+                      const void* Wv,
+                      const void* P,
+                      float* S,
+                      float* mass,
+                      void* workspace,
+                      size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * Synchronously read the device error flag that the last sa_compress on
+ * `workspace` set (0 = none, 1 = offsets broke their contract).  Waits for
+ * `stream`.  Returns SA_E_HIP if the copy fails.
+ */
+sa_status sa_read_device_error(const void* workspace, void* stream, int32_t* flag);
+
+/* Static text for a status code.  Never NULL. */
+const char* sa_status_string(sa_status status);
+
+/* Library version as "major.minor.patch". */
+const char* sa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H_ */

@@ -1,0 +1,27 @@
+"""MI355X-native Sketch Attention (SequenceO1) compression.
+
+The computation lives in libsa.so (hand-written HIP for gfx950, C ABI in
+include/sa.h); this package is its thin Python binding.
+"""
+from ._lib import (  # noqa: F401
+    SA_BF16,
+    SA_E_HIP,
+    SA_E_INVALID,
+    SA_E_UNSUPPORTED,
+    SA_E_WORKSPACE,
+    SA_F32,
+    SA_OK,
+    SaError,
+    compress,
+    load,
+    read_device_error,
+    status_string,
+    version,
+    workspace_size,
+)
+
+__all__ = [
+    "compress", "load", "read_device_error", "status_string", "version", "workspace_size",
+    "SaError", "SA_OK", "SA_E_INVALID", "SA_E_UNSUPPORTED", "SA_E_WORKSPACE", "SA_E_HIP",
+    "SA_BF16", "SA_F32",
+]

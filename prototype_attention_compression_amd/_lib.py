@@ -1,0 +1,172 @@
+"""ctypes binding of libsa.so (the C ABI in include/sa.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libsa.  PyTorch provides device memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsa.so")
+
+SA_OK, SA_E_INVALID, SA_E_UNSUPPORTED, SA_E_WORKSPACE, SA_E_HIP = range(5)
+SA_BF16, SA_F32 = 0, 1
+
+# functions declared in include/sa.h
+EXPORTS = ("sa_workspace_size", "sa_compress", "sa_read_device_error",
+           "sa_status_string", "sa_version")
+
+
+class SaProblem(ctypes.Structure):
+    _fields_ = [
+        ("num_users", ctypes.c_int64),
+        ("total_tokens", ctypes.c_int64),
+        ("d", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class SaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libsa.so (built in-tree).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(
+            f"{p} not found: build it with `python -m prototype_attention_compression_amd.build`")
+    lib = ctypes.CDLL(p)
+    P = ctypes.POINTER(SaProblem)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.sa_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
+    lib.sa_workspace_size.restype = ctypes.c_int
+    lib.sa_compress.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sa_compress.restype = ctypes.c_int
+    lib.sa_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
+    lib.sa_read_device_error.restype = ctypes.c_int
+    lib.sa_status_string.argtypes = [ctypes.c_int]
+    lib.sa_status_string.restype = ctypes.c_char_p
+    lib.sa_version.argtypes = []
+    lib.sa_version.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().sa_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return load().sa_version().decode()
+
+
+def problem(num_users: int, total_tokens: int, d: int, k: int, dtype: int) -> SaProblem:
+    return SaProblem(int(num_users), int(total_tokens), int(d), int(k), int(dtype), 0)
+
+
+def workspace_size(num_users: int, total_tokens: int, d: int, k: int, dtype: int = SA_BF16) -> int:
+    """Bytes of device workspace sa_compress needs (pure host call)."""
+    pb = problem(num_users, total_tokens, d, k, dtype)
+    out = ctypes.c_size_t(0)
+    st = load().sa_workspace_size(ctypes.byref(pb), ctypes.byref(out))
+    if st != SA_OK:
+        raise SaError(st, "sa_workspace_size")
+    return int(out.value)
+
+
+def raw_compress(pb: SaProblem, H, offsets, mask, Wk, Wv, P, S, mass, workspace,
+                 workspace_bytes: int, stream) -> int:
+    """Direct call with integer device addresses (or None); returns the status."""
+    return int(load().sa_compress(ctypes.byref(pb), H, offsets, mask, Wk, Wv, P, S, mass,
+                                  workspace, ctypes.c_size_t(workspace_bytes), stream))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def compress(H, offsets, Wk, Wv, P, mask=None, return_mass: bool = False,
+             out=None, mass_out=None, workspace=None):
+    """Sketches of a packed ragged batch, computed by libsa on the GPU.
+
+    H [N, d], Wk/Wv [d, d], P [k, d]: torch tensors on the current ROCm device,
+    all bfloat16 or all float32, contiguous.  offsets [R+1] int64 (device).
+    mask [N] uint8/bool or None.  Returns S [R, k, d] float32 (and the masses
+    [R, k] if ``return_mass``).  Runs on torch's current stream.
+    """
+    import torch
+
+    if not (H.is_cuda and offsets.is_cuda and Wk.is_cuda and Wv.is_cuda and P.is_cuda):
+        raise ValueError("all tensors must be on the GPU")
+    if H.dtype == torch.bfloat16:
+        dt = SA_BF16
+    elif H.dtype == torch.float32:
+        dt = SA_F32
+    else:
+        raise ValueError(f"unsupported dtype {H.dtype}")
+    for name, t in (("Wk", Wk), ("Wv", Wv), ("P", P)):
+        if t.dtype != H.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from H dtype {H.dtype}")
+    if offsets.dtype != torch.int64 or offsets.dim() != 1:
+        raise ValueError("offsets must be a 1-D int64 tensor")
+    if H.dim() != 2:
+        raise ValueError("H must be [N, d]")
+    N, d = H.shape
+    k = P.shape[0]
+    if Wk.shape != (d, d) or Wv.shape != (d, d) or P.shape != (k, d):
+        raise ValueError("shape mismatch: need Wk, Wv [d, d] and P [k, d]")
+    for name, t in (("H", H), ("Wk", Wk), ("Wv", Wv), ("P", P), ("offsets", offsets)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    R = offsets.shape[0] - 1
+    if R < 0:
+        raise ValueError("offsets must have at least one element")
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        if mask.dtype != torch.uint8 or mask.shape != (N,) or not mask.is_cuda or not mask.is_contiguous():
+            raise ValueError("mask must be a contiguous [N] uint8/bool GPU tensor")
+    dev = H.device
+    pb = problem(R, N, d, k, dt)
+    wbytes = workspace_size(R, N, d, k, dt)
+    if workspace is None or workspace.numel() * workspace.element_size() < wbytes:
+        workspace = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
+    S = out if out is not None else torch.empty((R, k, d), dtype=torch.float32, device=dev)
+    if S.shape != (R, k, d) or S.dtype != torch.float32 or not S.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [R, k, d] tensor")
+    m = None
+    if return_mass:
+        m = mass_out if mass_out is not None else torch.empty((R, k), dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = raw_compress(pb, _ptr(H) if N > 0 else None, _ptr(offsets), _ptr(mask), _ptr(Wk), _ptr(Wv),
+                      _ptr(P), _ptr(S), _ptr(m), _ptr(workspace), wbytes, stream)
+    if st != SA_OK:
+        raise SaError(st, "sa_compress")
+    return (S, m) if return_mass else S
+
+
+def read_device_error(workspace) -> int:
+    """Device error flag of the last sa_compress on ``workspace`` (syncs)."""
+    import torch
+
+    flag = ctypes.c_int32(0)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(workspace.device).cuda_stream)
+    st = load().sa_read_device_error(_ptr(workspace), stream, ctypes.byref(flag))
+    if st != SA_OK:
+        raise SaError(st, "sa_read_device_error")
+    return int(flag.value)

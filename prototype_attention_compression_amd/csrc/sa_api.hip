@@ -1,0 +1,158 @@
+// sa_api.hip — the C ABI of libsa (declared in include/sa.h): argument
+// validation (pure host code, before any HIP call), workspace layout, and
+// the stream-ordered launch sequence.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/sa.h"
+#include "sa_launch.h"
+#include "sa_layout.h"
+
+namespace sa {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxTokens = (int64_t)1 << 31;
+constexpr int64_t kMaxUsers = (int64_t)1 << 28;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+sa_status check_problem(const sa_problem* p) {
+  if (p == nullptr) return SA_E_INVALID;
+  if (p->num_users < 0 || p->total_tokens < 0 || p->d <= 0 || p->k <= 0 || p->reserved != 0)
+    return SA_E_INVALID;
+  if (p->dtype != SA_BF16 && p->dtype != SA_F32) return SA_E_INVALID;
+  if (p->d != 64 && p->d != 128) return SA_E_UNSUPPORTED;
+  if (p->k % 64 != 0 || p->k > 4096) return SA_E_UNSUPPORTED;
+  if (p->total_tokens >= kMaxTokens || p->num_users >= kMaxUsers) return SA_E_UNSUPPORTED;
+  return SA_OK;
+}
+
+int pick_waves(int k) {
+  const int blocks64 = k / kProtoPerWave;
+  for (int w = 4; w > 1; --w)
+    if (blocks64 % w == 0) return w;
+  return 1;
+}
+
+// Tiles per pass-2 chunk: enough chunks that chunks x prototype blocks fill
+// the 256 compute units at least once, and no longer than 256 tiles (8192
+// tokens) so per-chunk partial sums stay a small fraction of the traffic.
+int pick_tiles_per_chunk(int64_t tiles_est, int n_pblocks, bool f32) {
+  const int64_t want = (tiles_est * n_pblocks + 255) / 256;
+  const int64_t lo = f32 ? 2 : 16, hi = f32 ? 64 : 256;
+  return (int)(want < lo ? lo : (want > hi ? hi : want));
+}
+
+Layout make_layout(const sa_problem& p) {
+  Layout L;
+  memset(&L, 0, sizeof(L));
+  L.N = p.total_tokens;
+  L.R = (int32_t)p.num_users;
+  L.d = p.d;
+  L.k = p.k;
+  L.dtype = p.dtype;
+  L.row = p.d + kFeat;
+  const bool f32 = p.dtype == SA_F32;
+  L.waves = f32 ? 1 : pick_waves(p.k);
+  L.n_pblocks = f32 ? p.k / 64 : p.k / (L.waves * kProtoPerWave);
+  // sum_u ceil(n_u / 32) <= (N + 31 R) / 32
+  const int64_t tiles_max = (p.total_tokens + (int64_t)(kTile - 1) * p.num_users) / kTile;
+  L.tiles_max = (int32_t)tiles_max;
+  L.tiles_per_chunk = pick_tiles_per_chunk(tiles_max, L.n_pblocks, f32);
+  // sum_u ceil(t_u / CT) <= (tiles + (CT - 1) R) / CT
+  L.chunks_max = (int32_t)((tiles_max + (int64_t)(L.tiles_per_chunk - 1) * p.num_users) / L.tiles_per_chunk);
+  const size_t R1 = (size_t)p.num_users + 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.off_hdr = take(64 * sizeof(int32_t));
+  L.off_tile_base = take(R1 * sizeof(int32_t));
+  L.off_chunk_base = take(R1 * sizeof(int32_t));
+  if (!f32) {
+    L.off_q16 = take((size_t)p.k * L.row * 2);
+    L.off_qnorm = take((size_t)p.k * sizeof(float));
+    L.off_h16 = take((size_t)tiles_max * kTile * L.row * 2);
+    L.off_h16t = take((size_t)tiles_max * p.d * kTile * 2);
+  } else {
+    L.off_q32 = take((size_t)p.k * p.d * sizeof(float));
+    L.off_lse32 = take((size_t)tiles_max * kTile * sizeof(float));
+  }
+  L.off_part_u = take((size_t)L.chunks_max * p.k * p.d * sizeof(float));
+  L.off_part_m = take((size_t)L.chunks_max * p.k * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+}  // namespace sa
+
+extern "C" {
+
+sa_status sa_workspace_size(const sa_problem* problem, size_t* bytes) {
+  if (bytes == nullptr) return SA_E_INVALID;
+  sa_status st = sa::check_problem(problem);
+  if (st != SA_OK) return st;
+  *bytes = sa::make_layout(*problem).total;
+  return SA_OK;
+}
+
+sa_status sa_compress(const sa_problem* problem, const void* H, const int64_t* offsets, const uint8_t* token_mask,
+                      const void* Wk, const void* Wv, const void* P, float* S, float* mass, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  try {
+    sa_status st = sa::check_problem(problem);
+    if (st != SA_OK) return st;
+    const sa_problem& p = *problem;
+    if (p.num_users == 0) return SA_OK;
+    if (offsets == nullptr || Wk == nullptr || Wv == nullptr || P == nullptr || S == nullptr)
+      return SA_E_INVALID;
+    if (p.total_tokens > 0 && H == nullptr) return SA_E_INVALID;
+    const sa::Layout L = sa::make_layout(p);
+    if (workspace == nullptr || workspace_bytes < L.total) return SA_E_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % sa::kAlign != 0) return SA_E_INVALID;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (sa::launch_prep(L, P, Wk, offsets, workspace, s) != hipSuccess) return SA_E_HIP;
+    if (p.total_tokens > 0) {
+      if (p.dtype == SA_BF16) {
+        if (sa::launch_pass1(L, H, offsets, token_mask, workspace, s) != hipSuccess) return SA_E_HIP;
+        if (sa::launch_pass2(L, workspace, s) != hipSuccess) return SA_E_HIP;
+      } else {
+        if (sa::launch_f32(L, H, offsets, token_mask, workspace, s) != hipSuccess) return SA_E_HIP;
+      }
+    }
+    if (sa::launch_finalize(L, Wv, workspace, S, mass, s) != hipSuccess) return SA_E_HIP;
+    return SA_OK;
+  } catch (...) {
+    return SA_E_HIP;
+  }
+}
+
+sa_status sa_read_device_error(const void* workspace, void* stream, int32_t* flag) {
+  if (workspace == nullptr || flag == nullptr) return SA_E_INVALID;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess) return SA_E_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return SA_E_HIP;
+  *flag = v;
+  return SA_OK;
+}
+
+const char* sa_status_string(sa_status status) {
+  switch (status) {
+    case SA_OK: return "SA_OK: success";
+    case SA_E_INVALID: return "SA_E_INVALID: invalid argument";
+    case SA_E_UNSUPPORTED: return "SA_E_UNSUPPORTED: problem shape or dtype not built (d in {64,128}, k % 64 == 0, k <= 4096)";
+    case SA_E_WORKSPACE: return "SA_E_WORKSPACE: workspace missing or smaller than sa_workspace_size";
+    case SA_E_HIP: return "SA_E_HIP: HIP runtime or launch error";
+  }
+  return "unknown sa_status";
+}
+
+const char* sa_version(void) { return "0.1.0"; }
+
+}  // extern "C"

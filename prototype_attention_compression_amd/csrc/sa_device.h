@@ -1,0 +1,86 @@
+// sa_device.h — device-side helpers for the gfx950 Sketch Attention kernels:
+// vector types, MFMA wrappers and the ragged tile/chunk lookups.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sa_layout.h"
+
+namespace sa {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// D = A(32x16) * B(16x32) + C on the matrix cores, fp16 operands, fp32 sums.
+// Lane l holds row (l % 32) of A and column (l % 32) of B, 8 contraction
+// elements each from half (l / 32) of the 16; the same element slot pairs up
+// in A and B, so any consistent assignment of contraction indices to slots is
+// valid.  Result: lane l, register r holds C[8*(r/4) + 4*(l/32) + r%4][l % 32].
+__device__ __forceinline__ float16v mfma32x32x16(half8 a, half8 b, float16v c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Row of the 32x32 accumulator held in register r by lane half g.
+__device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+// Exact widening of 8 packed bf16 values (one 16-byte load) to fp16.  bf16
+// values whose magnitude lies in [2^-17, 65504] are exactly representable in
+// fp16; the conversion truncates toward zero so larger values saturate.
+__device__ __forceinline__ half8 bf16x8_to_f16x8(u32x4 v) {
+  half8 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo = __uint_as_float(v[i] << 16);
+    float hi = __uint_as_float(v[i] & 0xffff0000u);
+    half2v p = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    out[2 * i] = p[0];
+    out[2 * i + 1] = p[1];
+  }
+  return out;
+}
+
+// Largest u with base[u] <= x, for a non-decreasing base[0..R] with base[0] = 0
+// and x < base[R].  Users with no tiles (base[u] == base[u+1]) are skipped.
+__device__ __forceinline__ int find_user(const int32_t* base, int R, int32_t x) {
+  int lo = 0, hi = R;  // invariant: base[lo] <= x < base[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (base[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int32_t* ws_i32(void* ws, size_t off) {
+  return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + off);
+}
+__device__ __forceinline__ float* ws_f32(void* ws, size_t off) {
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + off);
+}
+__device__ __forceinline__ _Float16* ws_f16(void* ws, size_t off) {
+  return reinterpret_cast<_Float16*>(reinterpret_cast<char*>(ws) + off);
+}
+
+// Where a tile lives: user, first token (packed index) and valid row count.
+struct TileInfo {
+  int user;
+  int64_t tok0;
+  int count;
+};
+
+__device__ __forceinline__ TileInfo tile_info(const int32_t* tile_base, const int64_t* offsets,
+                                              int R, int32_t tile) {
+  TileInfo t;
+  t.user = find_user(tile_base, R, tile);
+  int32_t i = tile - tile_base[t.user];
+  int64_t lo = offsets[t.user], hi = offsets[t.user + 1];
+  t.tok0 = lo + (int64_t)i * kTile;
+  int64_t rem = hi - t.tok0;
+  t.count = rem < kTile ? (int)rem : kTile;
+  return t;
+}
+
+}  // namespace sa

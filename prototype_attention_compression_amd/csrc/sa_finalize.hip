@@ -1,0 +1,107 @@
+// sa_finalize.hip — chunk reduction and prototype-wise normalisation.
+//
+// For user u and a block of 32 prototypes, sums the per-chunk partials
+// U_c[j, :] = sum_t A[j,t] h_t and m_c[j] over the user's chunks in chunk
+// order (a fixed order: the result is bitwise repeatable), then writes
+//     S_u[j, :] = (U[j, :] / m_j) Wv,   mass[u, j] = m_j
+// i.e. the mass-normalised allocation-weighted mean of the value rows
+// v_t = h_t Wv (SequenceO1 blog "How it works" item 1: the k x d sketch of
+// softly assigned items; the division by the prototype's total mass is the
+// prototype-wise normalisation read as a weighted mean).  Applying Wv after
+// the reduction equals summing A v_t because the projection is linear.  A
+// prototype with zero mass (every allocation underflowed, or an empty user)
+// gets a zero row.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sa_device.h"
+#include "sa_launch.h"
+
+namespace sa {
+
+template <typename T>
+__device__ __forceinline__ float wv_load(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float wv_load<uint16_t>(const uint16_t* p, int64_t i) {
+  return __uint_as_float(((uint32_t)p[i]) << 16);
+}
+template <>
+__device__ __forceinline__ float wv_load<float>(const float* p, int64_t i) {
+  return p[i];
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout L, void* ws, float* __restrict__ S,
+                                                float* __restrict__ mass, float mass_scale) {
+  constexpr int PER = kFinRows * D / 256;   // elements per thread
+  constexpr int RPI = 256 / D;              // rows per output pass
+  __shared__ float sh[kFinRows][D + 1];
+  __shared__ float ms[kFinRows];
+  const int nrb = L.k / kFinRows;
+  const int u = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+  const int j0 = rb * kFinRows;
+  const int tid = threadIdx.x;
+  const int32_t* chunk_base = ws_i32(ws, L.off_chunk_base);
+  const int c0 = chunk_base[u], c1 = chunk_base[u + 1];
+  const float* part_u = ws_f32(ws, L.off_part_u);
+  const float* part_m = ws_f32(ws, L.off_part_m);
+
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  for (int c = c0; c < c1; ++c) {
+    const float* base = part_u + ((int64_t)c * L.k + j0) * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
+  }
+  if (tid < kFinRows) {
+    float m = 0.f;
+    for (int c = c0; c < c1; ++c) m += part_m[(int64_t)c * L.k + j0 + tid];
+    ms[tid] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid + 256 * i, j = e / D, a = e % D;
+    const float m = ms[j];
+    sh[j][a] = m > 0.f ? acc[i] / m : 0.f;
+  }
+  __syncthreads();
+  const int c = tid % D, jr = tid / D;
+  float out[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) out[i] = 0.f;
+  for (int a = 0; a < D; ++a) {
+    const float w = wv_load<T>(Wv, (int64_t)a * D + c);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) out[i] = fmaf(sh[jr + RPI * i][a], w, out[i]);
+  }
+  float* dst = S + ((int64_t)u * L.k + j0) * D;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) dst[(int64_t)(jr + RPI * i) * D + c] = out[i];
+  if (mass != nullptr && tid < kFinRows) mass[(int64_t)u * L.k + j0 + tid] = ms[tid] * mass_scale;
+}
+
+hipError_t launch_finalize(const Layout& L, const void* Wv, void* ws, float* S, float* mass, hipStream_t stream) {
+  const int64_t grid = (int64_t)L.R * (L.k / kFinRows);
+  if (grid == 0) return hipSuccess;
+  if (L.dtype == 0) {
+    const float scale = 1.0f / 16384.0f;  // allocations were scaled by 2^14
+    if (L.d == 128)
+      hipLaunchKernelGGL((finalize<128, uint16_t>), dim3((unsigned)grid), dim3(256), 0, stream,
+                         (const uint16_t*)Wv, L, ws, S, mass, scale);
+    else
+      hipLaunchKernelGGL((finalize<64, uint16_t>), dim3((unsigned)grid), dim3(256), 0, stream,
+                         (const uint16_t*)Wv, L, ws, S, mass, scale);
+  } else {
+    if (L.d == 128)
+      hipLaunchKernelGGL((finalize<128, float>), dim3((unsigned)grid), dim3(256), 0, stream, (const float*)Wv, L,
+                         ws, S, mass, 1.0f);
+    else
+      hipLaunchKernelGGL((finalize<64, float>), dim3((unsigned)grid), dim3(256), 0, stream, (const float*)Wv, L,
+                         ws, S, mass, 1.0f);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,27 @@
+// sa_launch.h — host-side launchers of the libsa kernels (one per kernel
+// file), called in stream order by sa_compress.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sa_layout.h"
+
+namespace sa {
+
+// queries + ragged schedule
+hipError_t launch_prep(const Layout& L, const void* P, const void* Wk, const int64_t* offsets, void* ws,
+                       hipStream_t stream);
+// bf16 path, pass 1: per-token logsumexp, fp16 token rows and transposed tiles
+hipError_t launch_pass1(const Layout& L, const void* H, const int64_t* offsets, const uint8_t* mask,
+                        void* ws, hipStream_t stream);
+// bf16 path, pass 2: allocations, per-chunk sums of A h and masses
+hipError_t launch_pass2(const Layout& L, void* ws, hipStream_t stream);
+// fp32 path, both passes
+hipError_t launch_f32(const Layout& L, const void* H, const int64_t* offsets, const uint8_t* mask, void* ws,
+                      hipStream_t stream);
+// chunk reduction, prototype-wise normalisation and the value projection
+hipError_t launch_finalize(const Layout& L, const void* Wv, void* ws, float* S, float* mass,
+                           hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,255 @@
+// sa_pass1.hip — FlashSA pass 1 on gfx950 (bf16 inputs).
+//
+// Sketch Attention normalises each token's logits across the k prototypes
+// (SequenceO1 review page, FAQ on how SA differs from standard attention;
+// blog "How it works" item 1: every item spreads its mass over the
+// prototypes).  Pass 1 computes, for every token t, the base-2 logsumexp
+//     lse_t = log2 sum_j 2^(q_j . h_t)
+// over ALL k prototypes without materialising the k x n logit matrix (blog
+// "How it works" item 3: FlashSA avoids the huge intermediates), and emits
+// the token in the form pass 2 consumes:
+//   * an fp16 row [h_t (d values) | -l_hi, -l_lo, 0 x 14] with
+//     l = lse_t - 14 split into two fp16 parts, so the pass-2 logit MFMA
+//     against query rows [q_j | 1, 1, 0 x 14] yields q_j . h_t - l directly;
+//   * a transposed 32-token tile [d][32] whose token order matches the
+//     register order of the 32x32 MFMA accumulator (so pass 2 feeds its
+//     allocation registers straight into the second MFMA).
+// Masked tokens and tile padding get zero rows and l = 60000, i.e. A = 0.
+//
+// Layout: one workgroup = 4 waves = 8 tiles (256 tokens).  Each wave keeps the
+// fp16 history of its 2 tiles in registers as MFMA B operands (lane = token)
+// and streams the prototype queries through LDS in chunks of 64, computing
+// S[j, t] = Q H^T with v_mfma_f32_32x32x16_f16.  The accumulator layout puts
+// one token per lane, so the reduction over prototypes stays in the lane.
+//
+// Exponent range: every logit obeys |q_j . h_t| <= qmax |h_t| (Cauchy-Schwarz,
+// qmax = largest query norm).  When that bound is below 100 for every token of
+// the workgroup, 2^L can neither overflow nor leave the normal range, so the
+// sum is taken without a running maximum (one exp and one add per logit).
+// Otherwise the workgroup runs the exact two-sweep form (maximum, then the
+// shifted sum).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sa_device.h"
+#include "sa_launch.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kModeFast = 0;   // sum of 2^L
+constexpr int kModeMax = 1;    // running max of L
+constexpr int kModeShift = 2;  // sum of 2^(L - max)
+
+template <int D>
+struct P1 {
+  static constexpr int S = D / 16;           // MFMA K steps over the history
+  static constexpr int ROW = D + kFeat;      // fp16 token/query row width
+  static constexpr int QS = D + 8;           // LDS row stride (fp16), 16 B pad
+  static constexpr int PIECES = kQChunk * D / 8;   // 16-B pieces per query chunk
+  static constexpr int PPT = PIECES / 256;
+};
+
+template <int D, int MODE>
+__device__ __forceinline__ void sweep(const _Float16* __restrict__ q16, int nchunks, _Float16* qbuf,
+                                      const half8 (&hreg)[2][P1<D>::S], float (&acc_sum)[2],
+                                      float (&acc_max)[2], int tid, int col, int g) {
+  using C = P1<D>;
+  constexpr int BUF = kQChunk * C::QS;
+  // stage chunk 0
+  u32x4 pre[C::PPT];
+#pragma unroll
+  for (int i = 0; i < C::PPT; ++i) {
+    int p = tid + 256 * i, row = p / (D / 8), cp = p % (D / 8);
+    pre[i] = *reinterpret_cast<const u32x4*>(q16 + (int64_t)row * C::ROW + cp * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < C::PPT; ++i) {
+    int p = tid + 256 * i, row = p / (D / 8), cp = p % (D / 8);
+    *reinterpret_cast<u32x4*>(qbuf + row * C::QS + cp * 8) = pre[i];
+  }
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const _Float16* cur = qbuf + (c & 1) * BUF;
+    if (c + 1 < nchunks) {
+      const _Float16* src = q16 + (int64_t)(c + 1) * kQChunk * C::ROW;
+#pragma unroll
+      for (int i = 0; i < C::PPT; ++i) {
+        int p = tid + 256 * i, row = p / (D / 8), cp = p % (D / 8);
+        pre[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)row * C::ROW + cp * 8);
+      }
+    }
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      half8 af[C::S];
+#pragma unroll
+      for (int s = 0; s < C::S; ++s)
+        af[s] = *reinterpret_cast<const half8*>(cur + (pt * 32 + col) * C::QS + 16 * s + 8 * g);
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        float16v acc = {};
+#pragma unroll
+        for (int s = 0; s < C::S; ++s) acc = mfma32x32x16(af[s], hreg[tau][s], acc);
+        if (MODE == kModeFast) {
+          float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            s0 += __builtin_amdgcn_exp2f(acc[r]);
+            s1 += __builtin_amdgcn_exp2f(acc[r + 1]);
+          }
+          acc_sum[tau] += s0 + s1;
+        } else if (MODE == kModeMax) {
+          float m = acc_max[tau];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[r]);
+          acc_max[tau] = m;
+        } else {
+          float s0 = 0.f, s1 = 0.f;
+          const float mx = acc_max[tau];
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            s0 += __builtin_amdgcn_exp2f(acc[r] - mx);
+            s1 += __builtin_amdgcn_exp2f(acc[r + 1] - mx);
+          }
+          acc_sum[tau] += s0 + s1;
+        }
+      }
+    }
+    if (c + 1 < nchunks) {
+      _Float16* nxt = qbuf + ((c + 1) & 1) * BUF;
+#pragma unroll
+      for (int i = 0; i < C::PPT; ++i) {
+        int p = tid + 256 * i, row = p / (D / 8), cp = p % (D / 8);
+        *reinterpret_cast<u32x4*>(nxt + row * C::QS + cp * 8) = pre[i];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256) void pass1_lse(const uint16_t* __restrict__ H, const int64_t* __restrict__ offsets,
+                                                 const uint8_t* __restrict__ mask, Layout L, void* ws) {
+  using C = P1<D>;
+  __shared__ __attribute__((aligned(16))) _Float16 qbuf[2 * kQChunk * C::QS];
+  const int32_t* hdr = ws_i32(ws, L.off_hdr);
+  const int32_t total_tiles = hdr[kHdrTiles];
+  const int32_t tile0 = blockIdx.x * kPass1Tiles;
+  if (tile0 >= total_tiles) return;  // uniform over the workgroup
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, g = lane >> 5;
+  const int32_t* tile_base = ws_i32(ws, L.off_tile_base);
+  const float qmax = __int_as_float(hdr[kHdrQmax]);
+
+  half8 hreg[2][C::S];
+  bool valid[2];
+  int32_t tiles[2];
+  bool need_exact = false;
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    const int32_t tile = tile0 + 2 * wave + tau;
+    tiles[tau] = tile;
+    valid[tau] = false;
+#pragma unroll
+    for (int s = 0; s < C::S; ++s) hreg[tau][s] = half8{};
+    if (tile < total_tiles) {
+      TileInfo ti = tile_info(tile_base, offsets, L.R, tile);
+      if (col < ti.count) {
+        const int64_t tok = ti.tok0 + col;
+        valid[tau] = (mask == nullptr) || (mask[tok] != 0);
+        if (valid[tau]) {
+          const u32x4* src = reinterpret_cast<const u32x4*>(H + tok * D);
+#pragma unroll
+          for (int s = 0; s < C::S; ++s) hreg[tau][s] = bf16x8_to_f16x8(src[2 * s + g]);
+        }
+      }
+    }
+    float n2 = 0.f;
+#pragma unroll
+    for (int s = 0; s < C::S; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = (float)hreg[tau][s][e];
+        n2 = fmaf(v, v, n2);
+      }
+    n2 += __shfl_xor(n2, 32);
+    if (valid[tau] && qmax * sqrtf(n2) >= 100.0f) need_exact = true;
+  }
+  need_exact = __syncthreads_or(need_exact);
+
+  const _Float16* q16 = ws_f16(ws, L.off_q16);
+  const int nchunks = L.k / kQChunk;
+  float sum[2] = {0.f, 0.f};
+  float mx[2] = {-INFINITY, -INFINITY};
+  if (!need_exact) {
+    sweep<D, kModeFast>(q16, nchunks, qbuf, hreg, sum, mx, tid, col, g);
+  } else {
+    sweep<D, kModeMax>(q16, nchunks, qbuf, hreg, sum, mx, tid, col, g);
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) mx[tau] = fmaxf(mx[tau], __shfl_xor(mx[tau], 32));
+    sweep<D, kModeShift>(q16, nchunks, qbuf, hreg, sum, mx, tid, col, g);
+  }
+
+  _Float16* h16 = ws_f16(ws, L.off_h16);
+  _Float16* h16t = ws_f16(ws, L.off_h16t);
+  _Float16* scratch = qbuf + wave * (32 * C::QS);  // per-wave transpose area
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    float tot = sum[tau] + __shfl_xor(sum[tau], 32);
+    float lse = need_exact ? mx[tau] + log2f(tot) : log2f(tot);
+    float l = valid[tau] ? lse - kAllocShift : 60000.0f;
+    _Float16 lhi = (_Float16)l;
+    _Float16 llo = valid[tau] ? (_Float16)(l - (float)lhi) : (_Float16)0.0f;
+    const int32_t tile = tiles[tau];
+    const bool live = tile < total_tiles;
+    if (live) {
+      _Float16* dst = h16 + ((int64_t)tile * kTile + col) * C::ROW;
+#pragma unroll
+      for (int s = 0; s < C::S; ++s) *reinterpret_cast<half8*>(dst + 16 * s + 8 * g) = hreg[tau][s];
+      half8 f = {};
+      if (g == 0) {
+        f[0] = -lhi;
+        f[1] = -llo;
+      }
+      *reinterpret_cast<half8*>(dst + D + 8 * g) = f;
+    }
+    // transpose through LDS: rows of this tile, then [d][32] in accumulator order
+#pragma unroll
+    for (int s = 0; s < C::S; ++s)
+      *reinterpret_cast<half8*>(scratch + col * C::QS + 16 * s + 8 * g) = hreg[tau][s];
+    __syncthreads();
+    if (live) {
+#pragma unroll
+      for (int it = 0; it < D * 4 / 64; ++it) {
+        const int idx = it * 64 + lane;
+        const int dcol = idx >> 2, j = idx & 3;
+        const int kk = j >> 1, gg = j & 1;
+        half8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tk = 16 * kk + 8 * (e >> 2) + 4 * gg + (e & 3);
+          v[e] = scratch[tk * C::QS + dcol];
+        }
+        *reinterpret_cast<half8*>(h16t + ((int64_t)tile * D + dcol) * kTile + 8 * j) = v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_pass1(const Layout& L, const void* H, const int64_t* offsets, const uint8_t* mask, void* ws,
+                        hipStream_t stream) {
+  const int grid = (L.tiles_max + kPass1Tiles - 1) / kPass1Tiles;
+  if (grid == 0) return hipSuccess;
+  if (L.d == 128)
+    hipLaunchKernelGGL(pass1_lse<128>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)H, offsets, mask, L, ws);
+  else
+    hipLaunchKernelGGL(pass1_lse<64>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)H, offsets, mask, L, ws);
+  return hipGetLastError();
+}
+
+}  // namespace sa

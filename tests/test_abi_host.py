@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/sa.h declares, and rejects bad arguments before any
+HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import prototype_attention_compression_amd as sa
+from prototype_attention_compression_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "sa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declarations_are_exported():
+    names = _declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert re.fullmatch(r"\d+\.\d+\.\d+", sa.version())
+    for s in range(5):
+        assert sa.status_string(s).startswith("SA_")
+    assert sa.status_string(99) == "unknown sa_status"
+
+
+def _ws(R, N, d, k, dt, reserved=0):
+    pb = _lib.SaProblem(R, N, d, k, dt, reserved)
+    out = ctypes.c_size_t(0)
+    st = _lib.load().sa_workspace_size(ctypes.byref(pb), ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 10, 128, 1024, 0), sa.SA_E_INVALID),
+    ((1, -10, 128, 1024, 0), sa.SA_E_INVALID),
+    ((1, 10, 0, 1024, 0), sa.SA_E_INVALID),
+    ((1, 10, 128, 0, 0), sa.SA_E_INVALID),
+    ((1, 10, 128, 1024, 7), sa.SA_E_INVALID),
+    ((1, 10, 96, 1024, 0), sa.SA_E_UNSUPPORTED),
+    ((1, 10, 128, 1000, 0), sa.SA_E_UNSUPPORTED),
+    ((1, 10, 128, 8192, 0), sa.SA_E_UNSUPPORTED),
+    ((1, 1 << 31, 128, 1024, 0), sa.SA_E_UNSUPPORTED),
+])
+def test_workspace_size_rejects(args, code):
+    assert _ws(*args)[0] == code
+
+
+def test_workspace_size_reserved_and_null():
+    assert _ws(1, 10, 128, 1024, 0, reserved=1)[0] == sa.SA_E_INVALID
+    pb = _lib.problem(1, 10, 128, 1024, 0)
+    assert _lib.load().sa_workspace_size(ctypes.byref(pb), None) == sa.SA_E_INVALID
+    assert _lib.load().sa_workspace_size(None, ctypes.byref(ctypes.c_size_t())) == sa.SA_E_INVALID
+
+
+def test_workspace_size_grows():
+    base = sa.workspace_size(4, 10_000, 128, 1024)
+    assert sa.workspace_size(4, 20_000, 128, 1024) > base
+    assert sa.workspace_size(8, 10_000, 128, 1024) > base
+    assert sa.workspace_size(4, 10_000, 128, 2048) > base
+    assert sa.workspace_size(0, 0, 64, 64) > 0
+    for dt in (sa.SA_BF16, sa.SA_F32):
+        assert sa.workspace_size(3, 1000, 64, 128, dt) % 256 == 0
+
+
+FAKE = 0x100000  # never dereferenced: every case below fails before any HIP call
+
+
+def _call(pb, H=FAKE, off=FAKE, mask=None, Wk=FAKE, Wv=FAKE, P=FAKE, S=FAKE, mass=None,
+          ws=FAKE, wsb=1 << 40):
+    return _lib.raw_compress(pb, H, off, mask, Wk, Wv, P, S, mass, ws, wsb, None)
+
+
+def test_compress_argument_errors_before_launch():
+    lib = _lib.load()
+    vp = None
+    assert lib.sa_compress(None, vp, vp, vp, vp, vp, vp, vp, vp, vp, 0, vp) == sa.SA_E_INVALID
+    pb = _lib.problem(2, 100, 128, 256, 0)
+    assert _call(pb, off=None) == sa.SA_E_INVALID
+    assert _call(pb, H=None) == sa.SA_E_INVALID
+    assert _call(pb, Wk=None) == sa.SA_E_INVALID
+    assert _call(pb, Wv=None) == sa.SA_E_INVALID
+    assert _call(pb, P=None) == sa.SA_E_INVALID
+    assert _call(pb, S=None) == sa.SA_E_INVALID
+    assert _call(pb, ws=None) == sa.SA_E_WORKSPACE
+    need = sa.workspace_size(2, 100, 128, 256)
+    assert _call(pb, wsb=need - 1) == sa.SA_E_WORKSPACE
+    assert _call(pb, ws=FAKE + 16, wsb=need) == sa.SA_E_INVALID        # misaligned
+    assert _call(_lib.problem(2, 100, 96, 256, 0)) == sa.SA_E_UNSUPPORTED
+    assert _call(_lib.problem(-2, 100, 128, 256, 0)) == sa.SA_E_INVALID
+
+
+def test_zero_users_is_a_noop():
+    # R = 0 returns before touching any pointer or the GPU
+    pb = _lib.problem(0, 0, 128, 1024, 0)
+    assert _call(pb, H=None, off=None, Wk=None, Wv=None, P=None, S=None, ws=None, wsb=0) == sa.SA_OK
+
+
+def test_binding_validates_before_library():
+    import torch
+    H = torch.zeros(4, 128, dtype=torch.bfloat16)
+    off = torch.tensor([0, 4])
+    with pytest.raises(ValueError):
+        sa.compress(H, off, H[:0], H[:0], H[:0])   # CPU tensors are refused

@@ -1,0 +1,82 @@
+"""GPU parity: libsa (HIP, gfx950) against the fp64 oracle on the same seeded
+inputs.  Bar: bf16 inputs max_rel <= 2e-2 and mean_rel <= 2e-3, fp32 inputs
+<= 1e-4 (normwise over all compared sketch elements); masses to the same
+bar.  Full-size workloads compare a sample of users (the oracle computes one
+user at a time) in the very launch configuration the bench times."""
+import numpy as np
+import pytest
+
+from oracle import sketch_batch
+from synth import make_config
+from tests.gpu_util import TOL, rel_errors, run, upload
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["c1_fp32_n4096_d64_k64", "small_ragged_d128_k256", "small_ragged_d128_k1024",
+         "small_ragged_d64_k128", "small_mask_d128_k512", "small_fp32_ragged_d128_k192"]
+
+
+def _check(inp, users=None):
+    dev = upload(inp)
+    print(f"[case] {inp.name} R={inp.R} N={inp.N} k={inp.k} d={inp.d} dtype={inp.dtype} users={users}", flush=True)
+    S, m = run(dev)
+    S = S.cpu().numpy()
+    m = m.cpu().numpy()
+    Sref, mref = sketch_batch(inp.H, inp.offsets, inp.Wk, inp.Wv, inp.P, mask=inp.mask, users=users)
+    sel = list(range(inp.R)) if users is None else list(users)
+    mx, mean = rel_errors(S[sel], Sref[sel])
+    mmx, mmean = rel_errors(m[sel], mref[sel])
+    tmax, tmean = TOL[inp.dtype]
+    print(f"   S max_rel={mx:.3e} mean_rel={mean:.3e}  mass max_rel={mmx:.3e} mean_rel={mmean:.3e}", flush=True)
+    assert np.isfinite(S).all() and np.isfinite(m).all()
+    assert mx <= tmax and mean <= tmean, (mx, mean)
+    assert mmx <= tmax and mmean <= tmean, (mmx, mmean)
+    # users outside the sample must still be finite, and empty users exactly zero
+    for u in range(inp.R):
+        if inp.lengths[u] == 0:
+            assert not S[u].any() and not m[u].any()
+    return S, m
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_parity_small(name):
+    _check(make_config(name))
+
+
+def _sample(inp, n_random=2, seed=0):
+    lens = inp.lengths
+    pick = {int(np.argmin(lens)), int(np.argmax(lens))}
+    rng = np.random.default_rng(seed)
+    while len(pick) < min(inp.R, 2 + n_random):
+        pick.add(int(rng.integers(0, inp.R)))
+    return sorted(pick)
+
+
+def test_parity_c2_single_user_100k():
+    _check(make_config("c2_n100k_d128_k1024"))
+
+
+def test_parity_c3_training_batch_sampled():
+    inp = make_config("c3_r40_ragged_d128_k1024")
+    _check(inp, users=_sample(inp))
+
+
+def test_parity_c4_serving_batch_sampled():
+    inp = make_config("c4_r120_lognormal_d128_k1024")
+    _check(inp, users=_sample(inp, n_random=1))
+
+
+@pytest.mark.parametrize("name", ["c5_r8_n100k_d128_k256", "c5_r8_n100k_d128_k512",
+                                  "c5_r8_n100k_d128_k2048", "c5mask_r8_n100k_d128_k1024"])
+def test_parity_c5_sweep_sampled(name):
+    inp = make_config(name)
+    _check(inp, users=[0, inp.R - 1])
+
+
+def test_parity_sharp_softmax():
+    _check(make_config("sharp_n100k_d128_k1024"))
+
+
+def test_parity_clustered_history():
+    inp = make_config("clustered_r4_n100k_d128_k1024")
+    _check(inp, users=[1, 3])
