@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Throughput bench of Sketch Attention compression (libsa on one MI355X).
+
+One step = one sa_compress call over the whole synthetic batch (query prep,
+pass 1 per-token logsumexp, pass 2 allocations + sums, finalize), inputs
+already resident in HBM.  Prints ONE JSON line.
+
+Default workload: 40 users x 100,000 history tokens, k = 1024 prototypes,
+d = 128, bf16 inputs -- the n = 100K, k = 1K x 128 sketch batched over 40
+users.  ``--workload`` selects any named config of ``synth.CONFIGS``.
+
+Timing: W warm-up steps, then K steps bracketed by device synchronisation;
+each timed step also records HIP events at the library's phase boundaries on
+the same stream, giving the average duration of every kernel phase.  The
+roofline object reports the dominant kernel (pass 2) against the fp16/bf16
+dense MFMA peak.  The CPU baseline times the fp64 oracle on a bounded sample
+of the same workload on the host cores and checks the GPU sketches of that
+sample against it.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MFMA_F16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0
+METRIC = "history tokens/s + TFLOP/s (%bf16 MFMA peak), SA n=100K,k=1024,d=128"
+DEFAULT_WORKLOAD = "c3lit_r40_n100k_d128_k1024"
+
+# measured by rocprofv3 --pmc on the pass-2 kernel of the default workload, in
+# KiB per dispatch, each scaled by the factor a plain copy kernel of known
+# size reads for the same counter (see profiles/); None until measured
+PASS2_TRAFFIC_BYTES = None
+
+
+class _Hip:
+    """The few HIP runtime calls the bench needs for phase events."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def elapsed_ms(self, a, b):
+        out = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+def _upload(inp, torch, dev):
+    if inp.dtype == "bf16":
+        t = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+        H, Wk, Wv, P = t(inp.H_bits), t(inp.Wk_bits), t(inp.Wv_bits), t(inp.P_bits)
+    else:
+        t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        H, Wk, Wv, P = t(inp.H), t(inp.Wk), t(inp.Wv), t(inp.P)
+    off = torch.from_numpy(inp.offsets).to(dev)
+    mask = None if inp.mask is None else torch.from_numpy(inp.mask).to(dev)
+    return H, off, Wk, Wv, P, mask
+
+
+def cpu_baseline(inp, S_gpu, budget_s: float):
+    """fp64 oracle on the host cores over a bounded sample of users."""
+    import threadpoolctl
+
+    from oracle import sketch_one
+
+    cores = len(os.sched_getaffinity(0))
+    with threadpoolctl.threadpool_limits(cores):
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        users, tokens, t_total = [], 0, 0.0
+        errs = []
+        for u in range(inp.R):
+            sl = inp.user_slice(u)
+            Hu = inp.H[sl] if inp.mask is None else inp.H[sl][inp.mask[sl] != 0]
+            t0 = time.perf_counter()
+            S, _ = sketch_one(Hu, inp.Wk, inp.Wv, inp.P)
+            t_total += time.perf_counter() - t0
+            users.append(u)
+            tokens += Hu.shape[0]
+            ref = S
+            diff = np.abs(S_gpu[u].astype(np.float64) - ref)
+            errs.append((diff.max(), np.abs(ref).max(), diff.sum(), np.abs(ref).sum()))
+            if t_total >= budget_s:
+                break
+    max_rel = max(e[0] for e in errs) / max(max(e[1] for e in errs), 1e-300)
+    mean_rel = sum(e[2] for e in errs) / max(sum(e[3] for e in errs), 1e-300)
+    return {
+        "value": tokens / t_total,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"users {users[0]}..{users[-1]} ({len(users)} of {inp.R}, {tokens} tokens), "
+                  f"numpy fp64, {t_total:.1f} s",
+        "parity_on_sample": {"max_rel": max_rel, "mean_rel": mean_rel},
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the Sketch Attention path here runs on a single "
+              "MI355X (users shard across GPUs with no exchange; no multi-GPU run is built). "
+              "Use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import prototype_attention_compression_amd as sa
+    from synth import make_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_config(args.workload)
+    H, off, Wk, Wv, P, mask = _upload(inp, torch, dev)
+    R, N, d, k = inp.R, inp.N, inp.d, inp.k
+    n_valid = inp.valid_tokens()
+    ws = torch.empty(sa.workspace_size(R, N, d, k, sa.SA_BF16 if inp.dtype == "bf16" else sa.SA_F32),
+                     dtype=torch.uint8, device=dev)
+    S = torch.empty((R, k, d), dtype=torch.float32, device=dev)
+    m = torch.empty((R, k), dtype=torch.float32, device=dev)
+
+    hip = _Hip()
+    n_ev = sa._lib.NUM_PHASE_EVENTS
+    step_events = [[hip.event() for _ in range(n_ev)] for _ in range(args.steps)]
+    ev_arrays = [(ctypes.c_void_p * n_ev)(*evs) for evs in step_events]
+
+    def step(events=None):
+        sa.compress(H, off, Wk, Wv, P, mask=mask, return_mass=True, out=S, mass_out=m,
+                    workspace=ws, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(ev_arrays[i])
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+
+    phases = ["prep", "pass1_lse", "pass2_accum", "finalize"]
+    phase_ms = {p: 0.0 for p in phases}
+    for evs in step_events:
+        for i, p in enumerate(phases):
+            phase_ms[p] += hip.elapsed_ms(evs[i], evs[i + 1]) / args.steps
+    for evs in step_events:
+        for e in evs:
+            hip.destroy(e)
+
+    algo_flop = 4.0 * n_valid * k * d          # logits + A^T V contractions
+    tflops = algo_flop / (ms_step * 1e-3) / 1e12
+    tokens_per_s = n_valid / (ms_step * 1e-3)
+    p2_s = phase_ms["pass2_accum"] * 1e-3
+    p2_achieved = algo_flop / p2_s / 1e12 if p2_s > 0 else 0.0
+    roofline = {
+        "kernel": "pass2_accum",
+        "bound": "mfma",
+        "achieved": p2_achieved,
+        "peak": PEAK_MFMA_F16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": p2_achieved / PEAK_MFMA_F16_TFLOPS,
+        "traffic": PASS2_TRAFFIC_BYTES,
+        "per_launch_flop": algo_flop,
+        "avg_launch_ms": phase_ms["pass2_accum"],
+    }
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if inp.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": inp.name, "users": R, "tokens": n_valid, "k": k, "d": d,
+                   "input_dtype": inp.dtype, "parallelism": "single_gpu"},
+        "tflops": tflops,
+        "pct_peak": tflops / PEAK_MFMA_F16_TFLOPS,
+        "phase_ms": phase_ms,
+        "wall_s_timed": t_wall,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, S.cpu().numpy(), args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

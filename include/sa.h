@@ -120,6 +120,35 @@ sa_status sa_compress(const sa_problem* problem,
                       size_t workspace_bytes,
                       void* stream);
 
+/* Number of phase-boundary events sa_compress_with_events records. */
+#define SA_NUM_PHASE_EVENTS 5
+
+/*
+ * sa_compress, recording caller-created HIP events (hipEvent_t handles) on
+ * `stream` at the phase boundaries, for timing with hipEventElapsedTime:
+ *   events[0] before the query/schedule preparation,
+ *   events[1] after it (start of pass 1: per-token logsumexp),
+ *   events[2] after pass 1 (start of pass 2: allocations and sums),
+ *   events[3] after pass 2 (start of the normalise / value-projection step),
+ *   events[4] after the last kernel.
+ * `events` may be NULL (then this is sa_compress).  A phase with no work
+ * (e.g. N = 0) records its two events back to back.  Same arguments, errors
+ * and semantics as sa_compress otherwise.
+ */
+sa_status sa_compress_with_events(const sa_problem* problem,
+                                  const void* H,
+                                  const int64_t* offsets,
+                                  const uint8_t* token_mask,
+                                  const void* Wk,
+                                  const void* Wv,
+                                  const void* P,
+                                  float* S,
+                                  float* mass,
+                                  void* workspace,
+                                  size_t workspace_bytes,
+                                  void* stream,
+                                  void* const* events);
+
 /*
  * Synchronously read the device error flag that the last sa_compress on
  * `workspace` set (0 = none, 1 = offsets broke their contract).  Waits for

@@ -16,8 +16,9 @@ SA_OK, SA_E_INVALID, SA_E_UNSUPPORTED, SA_E_WORKSPACE, SA_E_HIP = range(5)
 SA_BF16, SA_F32 = 0, 1
 
 # functions declared in include/sa.h
-EXPORTS = ("sa_workspace_size", "sa_compress", "sa_read_device_error",
-           "sa_status_string", "sa_version")
+EXPORTS = ("sa_workspace_size", "sa_compress", "sa_compress_with_events",
+           "sa_read_device_error", "sa_status_string", "sa_version")
+NUM_PHASE_EVENTS = 5
 
 
 class SaProblem(ctypes.Structure):
@@ -56,6 +57,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sa_workspace_size.restype = ctypes.c_int
     lib.sa_compress.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sa_compress.restype = ctypes.c_int
+    lib.sa_compress_with_events.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    lib.sa_compress_with_events.restype = ctypes.c_int
     lib.sa_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
     lib.sa_read_device_error.restype = ctypes.c_int
     lib.sa_status_string.argtypes = [ctypes.c_int]
@@ -90,10 +93,17 @@ def workspace_size(num_users: int, total_tokens: int, d: int, k: int, dtype: int
 
 
 def raw_compress(pb: SaProblem, H, offsets, mask, Wk, Wv, P, S, mass, workspace,
-                 workspace_bytes: int, stream) -> int:
-    """Direct call with integer device addresses (or None); returns the status."""
-    return int(load().sa_compress(ctypes.byref(pb), H, offsets, mask, Wk, Wv, P, S, mass,
-                                  workspace, ctypes.c_size_t(workspace_bytes), stream))
+                 workspace_bytes: int, stream, events=None) -> int:
+    """Direct call with device addresses (or None); returns the status.
+
+    ``events``: optional ctypes array of NUM_PHASE_EVENTS hipEvent_t handles.
+    """
+    if events is None:
+        return int(load().sa_compress(ctypes.byref(pb), H, offsets, mask, Wk, Wv, P, S, mass,
+                                      workspace, ctypes.c_size_t(workspace_bytes), stream))
+    return int(load().sa_compress_with_events(ctypes.byref(pb), H, offsets, mask, Wk, Wv, P, S, mass,
+                                              workspace, ctypes.c_size_t(workspace_bytes), stream,
+                                              events))
 
 
 def _ptr(t):
@@ -101,7 +111,7 @@ def _ptr(t):
 
 
 def compress(H, offsets, Wk, Wv, P, mask=None, return_mass: bool = False,
-             out=None, mass_out=None, workspace=None):
+             out=None, mass_out=None, workspace=None, events=None):
     """Sketches of a packed ragged batch, computed by libsa on the GPU.
 
     H [N, d], Wk/Wv [d, d], P [k, d]: torch tensors on the current ROCm device,
@@ -154,7 +164,7 @@ def compress(H, offsets, Wk, Wv, P, mask=None, return_mass: bool = False,
         m = mass_out if mass_out is not None else torch.empty((R, k), dtype=torch.float32, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     st = raw_compress(pb, _ptr(H) if N > 0 else None, _ptr(offsets), _ptr(mask), _ptr(Wk), _ptr(Wv),
-                      _ptr(P), _ptr(S), _ptr(m), _ptr(workspace), wbytes, stream)
+                      _ptr(P), _ptr(S), _ptr(m), _ptr(workspace), wbytes, stream, events)
     if st != SA_OK:
         raise SaError(st, "sa_compress")
     return (S, m) if return_mass else S

@@ -104,6 +104,14 @@ sa_status sa_workspace_size(const sa_problem* problem, size_t* bytes) {
 sa_status sa_compress(const sa_problem* problem, const void* H, const int64_t* offsets, const uint8_t* token_mask,
                       const void* Wk, const void* Wv, const void* P, float* S, float* mass, void* workspace,
                       size_t workspace_bytes, void* stream) {
+  return sa_compress_with_events(problem, H, offsets, token_mask, Wk, Wv, P, S, mass, workspace, workspace_bytes,
+                                 stream, nullptr);
+}
+
+sa_status sa_compress_with_events(const sa_problem* problem, const void* H, const int64_t* offsets,
+                                  const uint8_t* token_mask, const void* Wk, const void* Wv, const void* P, float* S,
+                                  float* mass, void* workspace, size_t workspace_bytes, void* stream,
+                                  void* const* events) {
   try {
     sa_status st = sa::check_problem(problem);
     if (st != SA_OK) return st;
@@ -116,16 +124,26 @@ sa_status sa_compress(const sa_problem* problem, const void* H, const int64_t* o
     if (workspace == nullptr || workspace_bytes < L.total) return SA_E_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % sa::kAlign != 0) return SA_E_INVALID;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    auto mark = [&](int i) {
+      return events == nullptr || hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s) == hipSuccess;
+    };
+    if (!mark(0)) return SA_E_HIP;
     if (sa::launch_prep(L, P, Wk, offsets, workspace, s) != hipSuccess) return SA_E_HIP;
-    if (p.total_tokens > 0) {
-      if (p.dtype == SA_BF16) {
-        if (sa::launch_pass1(L, H, offsets, token_mask, workspace, s) != hipSuccess) return SA_E_HIP;
-        if (sa::launch_pass2(L, workspace, s) != hipSuccess) return SA_E_HIP;
-      } else {
-        if (sa::launch_f32(L, H, offsets, token_mask, workspace, s) != hipSuccess) return SA_E_HIP;
-      }
+    if (!mark(1)) return SA_E_HIP;
+    if (p.dtype == SA_BF16) {
+      if (p.total_tokens > 0 && sa::launch_pass1(L, H, offsets, token_mask, workspace, s) != hipSuccess)
+        return SA_E_HIP;
+      if (!mark(2)) return SA_E_HIP;
+      if (p.total_tokens > 0 && sa::launch_pass2(L, workspace, s) != hipSuccess) return SA_E_HIP;
+    } else {
+      // the fp32 path launches both passes from one launcher
+      if (p.total_tokens > 0 && sa::launch_f32(L, H, offsets, token_mask, workspace, s) != hipSuccess)
+        return SA_E_HIP;
+      if (!mark(2)) return SA_E_HIP;
     }
+    if (!mark(3)) return SA_E_HIP;
     if (sa::launch_finalize(L, Wv, workspace, S, mass, s) != hipSuccess) return SA_E_HIP;
+    if (!mark(4)) return SA_E_HIP;
     return SA_OK;
   } catch (...) {
     return SA_E_HIP;
