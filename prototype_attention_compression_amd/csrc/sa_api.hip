@@ -41,8 +41,9 @@ int pick_waves(int k) {
 // tokens) so per-chunk partial sums stay a small fraction of the traffic.
 int pick_tiles_per_chunk(int64_t tiles_est, int n_pblocks, bool f32) {
   const int64_t want = (tiles_est * n_pblocks + 255) / 256;
-  const int64_t lo = f32 ? 2 : 16, hi = f32 ? 64 : 256;
-  return (int)(want < lo ? lo : (want > hi ? hi : want));
+  const int64_t lo = f32 ? 4 : 16, hi = f32 ? 64 : 256;
+  const int64_t ct = want < lo ? lo : (want > hi ? hi : want);
+  return (int)((ct + kUserTileAlign - 1) / kUserTileAlign * kUserTileAlign);
 }
 
 Layout make_layout(const sa_problem& p) {
@@ -53,12 +54,12 @@ Layout make_layout(const sa_problem& p) {
   L.d = p.d;
   L.k = p.k;
   L.dtype = p.dtype;
-  L.row = p.d + kFeat;
   const bool f32 = p.dtype == SA_F32;
   L.waves = f32 ? 1 : pick_waves(p.k);
   L.n_pblocks = f32 ? p.k / 64 : p.k / (L.waves * kProtoPerWave);
-  // sum_u ceil(n_u / 32) <= (N + 31 R) / 32
-  const int64_t tiles_max = (p.total_tokens + (int64_t)(kTile - 1) * p.num_users) / kTile;
+  // sum_u A ceil(n_u / (32 A)) <= (N + (32 A - 1) R) / 32 for A = kUserTileAlign
+  const int64_t span = (int64_t)kTile * kUserTileAlign;
+  const int64_t tiles_max = (p.total_tokens + (span - 1) * p.num_users) / span * kUserTileAlign;
   L.tiles_max = (int32_t)tiles_max;
   L.tiles_per_chunk = pick_tiles_per_chunk(tiles_max, L.n_pblocks, f32);
   // sum_u ceil(t_u / CT) <= (tiles + (CT - 1) R) / CT
@@ -74,10 +75,11 @@ Layout make_layout(const sa_problem& p) {
   L.off_tile_base = take(R1 * sizeof(int32_t));
   L.off_chunk_base = take(R1 * sizeof(int32_t));
   if (!f32) {
-    L.off_q16 = take((size_t)p.k * L.row * 2);
+    L.off_q16 = take((size_t)p.k * p.d * 2);
     L.off_qnorm = take((size_t)p.k * sizeof(float));
-    L.off_h16 = take((size_t)tiles_max * kTile * L.row * 2);
+    L.off_h16 = take((size_t)tiles_max * kTile * p.d * 2);
     L.off_h16t = take((size_t)tiles_max * p.d * kTile * 2);
+    L.off_nl = take((size_t)tiles_max * kTile * sizeof(float));
   } else {
     L.off_q32 = take((size_t)p.k * p.d * sizeof(float));
     L.off_lse32 = take((size_t)tiles_max * kTile * sizeof(float));

@@ -8,19 +8,21 @@
 // over ALL k prototypes without materialising the k x n logit matrix (blog
 // "How it works" item 3: FlashSA avoids the huge intermediates), and emits
 // the token in the form pass 2 consumes:
-//   * an fp16 row [h_t (d values) | -l_hi, -l_lo, 0 x 14] with
-//     l = lse_t - 14 split into two fp16 parts, so the pass-2 logit MFMA
-//     against query rows [q_j | 1, 1, 0 x 14] yields q_j . h_t - l directly;
+//   * the fp16 row h_t (bf16 widened exactly),
 //   * a transposed 32-token tile [d][32] whose token order matches the
 //     register order of the 32x32 MFMA accumulator (so pass 2 feeds its
-//     allocation registers straight into the second MFMA).
-// Masked tokens and tile padding get zero rows and l = 60000, i.e. A = 0.
+//     allocation registers straight into the second MFMA),
+//   * -l_t = -(lse_t - 14) in fp32, the starting value of pass 2's logit
+//     accumulator (the 2^14 keeps fp16 allocations in the normal range).
+// Masked tokens and tile padding get zero rows and -l = -60000, i.e. A = 0.
 //
 // Layout: one workgroup = 4 waves = 8 tiles (256 tokens).  Each wave keeps the
 // fp16 history of its 2 tiles in registers as MFMA B operands (lane = token)
-// and streams the prototype queries through LDS in chunks of 64, computing
-// S[j, t] = Q H^T with v_mfma_f32_32x32x16_f16.  The accumulator layout puts
-// one token per lane, so the reduction over prototypes stays in the lane.
+// and streams the prototype queries through LDS in chunks of 128 (direct
+// global->LDS loads, double-buffered, rows XOR-swizzled for the 64-bank
+// LDS), computing S[j, t] = Q H^T with v_mfma_f32_32x32x16_f16.  The
+// accumulator layout puts one token per lane, so the reduction over
+// prototypes stays in the lane.
 //
 // Exponent range: every logit obeys |q_j . h_t| <= qmax |h_t| (Cauchy-Schwarz,
 // qmax = largest query norm).  When that bound is below 100 for every token of
@@ -42,51 +44,63 @@ namespace {
 constexpr int kModeFast = 0;   // sum of 2^L
 constexpr int kModeMax = 1;    // running max of L
 constexpr int kModeShift = 2;  // sum of 2^(L - max)
+constexpr int kQC = 128;       // prototypes per LDS chunk
 
 template <int D>
 struct P1 {
-  static constexpr int S = D / 16;           // MFMA K steps over the history
-  static constexpr int ROW = D + kFeat;      // fp16 token/query row width
-  static constexpr int QS = D + 8;           // LDS row stride (fp16), 16 B pad
-  static constexpr int PIECES = kQChunk * D / 8;   // 16-B pieces per query chunk
-  static constexpr int PPT = PIECES / 256;
+  static constexpr int S = D / 16;                   // MFMA K steps over d
+  static constexpr int CPR = D / 8;                  // 16-B chunks per query row
+  static constexpr int ROWSH = (CPR == 16) ? 0 : 1;
+  static constexpr int CHUNK_BYTES = kQC * D * 2;    // one LDS query chunk
+  static constexpr int LOADS = CHUNK_BYTES / 1024;   // 1-KB direct loads per chunk
+  static constexpr int TS = D + 8;                   // transpose scratch row stride (fp16)
 };
 
-template <int D, int MODE>
-__device__ __forceinline__ void sweep(const _Float16* __restrict__ q16, int nchunks, _Float16* qbuf,
-                                      const half8 (&hreg)[2][P1<D>::S], float (&acc_sum)[2],
-                                      float (&acc_max)[2], int tid, int col, int g) {
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return (row >> P1<D>::ROWSH) & (P1<D>::CPR - 1);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Direct loads of query chunk c (rows c*128 .. +127) into LDS buffer `dst`.
+template <int D>
+__device__ __forceinline__ void issue_chunk(const char* q16, int c, int nrows, char* dst, int wave, int lane) {
   using C = P1<D>;
-  constexpr int BUF = kQChunk * C::QS;
-  // stage chunk 0
-  u32x4 pre[C::PPT];
 #pragma unroll
-  for (int i = 0; i < C::PPT; ++i) {
-    int p = tid + 256 * i, row = p / (D / 8), cp = p % (D / 8);
-    pre[i] = *reinterpret_cast<const u32x4*>(q16 + (int64_t)row * C::ROW + cp * 8);
+  for (int i = wave; i < C::LOADS; i += 4) {
+    const int q = 64 * i + lane;
+    const int row = q / C::CPR, cs = q % C::CPR;
+    if (row >= nrows) break;   // uniform: a 64-prototype last chunk
+    const int cl = cs ^ swz<D>(row);
+    const char* src = q16 + ((int64_t)c * kQC + row) * (D * 2) + cl * 16;
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(dst + 1024 * i), 16, 0, 0);
   }
-#pragma unroll
-  for (int i = 0; i < C::PPT; ++i) {
-    int p = tid + 256 * i, row = p / (D / 8), cp = p % (D / 8);
-    *reinterpret_cast<u32x4*>(qbuf + row * C::QS + cp * 8) = pre[i];
-  }
-  __syncthreads();
+}
+
+template <int D, int MODE>
+__device__ __forceinline__ void sweep(const char* q16, int k, char* lds, const half8 (&hreg)[2][P1<D>::S],
+                                      float (&acc_sum)[2], float (&acc_max)[2], int wave, int lane, int col, int g) {
+  using C = P1<D>;
+  const int nchunks = (k + kQC - 1) / kQC;
+  issue_chunk<D>(q16, 0, min(kQC, k), lds, wave, lane);
   for (int c = 0; c < nchunks; ++c) {
-    const _Float16* cur = qbuf + (c & 1) * BUF;
-    if (c + 1 < nchunks) {
-      const _Float16* src = q16 + (int64_t)(c + 1) * kQChunk * C::ROW;
+    char* cur = lds + (c & 1) * C::CHUNK_BYTES;
+    const int npt = min(kQC, k - c * kQC) / 32;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of chunk c landed
+    __syncthreads();                     // ... and everyone's; chunk c-1's buffer is free
+    if (c + 1 < nchunks)
+      issue_chunk<D>(q16, c + 1, min(kQC, k - (c + 1) * kQC), lds + ((c + 1) & 1) * C::CHUNK_BYTES, wave, lane);
 #pragma unroll
-      for (int i = 0; i < C::PPT; ++i) {
-        int p = tid + 256 * i, row = p / (D / 8), cp = p % (D / 8);
-        pre[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)row * C::ROW + cp * 8);
-      }
-    }
-#pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
+    for (int pt = 0; pt < kQC / 32; ++pt) {
+      if (pt >= npt) break;   // uniform
+      const int row = pt * 32 + col;
       half8 af[C::S];
 #pragma unroll
-      for (int s = 0; s < C::S; ++s)
-        af[s] = *reinterpret_cast<const half8*>(cur + (pt * 32 + col) * C::QS + 16 * s + 8 * g);
+      for (int s = 0; s < C::S; ++s) {
+        const int cl = (2 * s + g) ^ swz<D>(row);
+        af[s] = *reinterpret_cast<const half8*>(cur + row * (D * 2) + cl * 16);
+      }
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
         float16v acc = {};
@@ -117,16 +131,8 @@ __device__ __forceinline__ void sweep(const _Float16* __restrict__ q16, int nchu
         }
       }
     }
-    if (c + 1 < nchunks) {
-      _Float16* nxt = qbuf + ((c + 1) & 1) * BUF;
-#pragma unroll
-      for (int i = 0; i < C::PPT; ++i) {
-        int p = tid + 256 * i, row = p / (D / 8), cp = p % (D / 8);
-        *reinterpret_cast<u32x4*>(nxt + row * C::QS + cp * 8) = pre[i];
-      }
-    }
-    __syncthreads();
   }
+  __syncthreads();  // all waves are done with the last chunk before LDS is reused
 }
 
 }  // namespace
@@ -135,7 +141,7 @@ template <int D>
 __global__ __launch_bounds__(256) void pass1_lse(const uint16_t* __restrict__ H, const int64_t* __restrict__ offsets,
                                                  const uint8_t* __restrict__ mask, Layout L, void* ws) {
   using C = P1<D>;
-  __shared__ __attribute__((aligned(16))) _Float16 qbuf[2 * kQChunk * C::QS];
+  __shared__ __attribute__((aligned(1024))) char lds[2 * C::CHUNK_BYTES];
   const int32_t* hdr = ws_i32(ws, L.off_hdr);
   const int32_t total_tiles = hdr[kHdrTiles];
   const int32_t tile0 = blockIdx.x * kPass1Tiles;
@@ -181,46 +187,38 @@ __global__ __launch_bounds__(256) void pass1_lse(const uint16_t* __restrict__ H,
   }
   need_exact = __syncthreads_or(need_exact);
 
-  const _Float16* q16 = ws_f16(ws, L.off_q16);
-  const int nchunks = L.k / kQChunk;
+  const char* q16 = reinterpret_cast<const char*>(ws_f16(ws, L.off_q16));
   float sum[2] = {0.f, 0.f};
   float mx[2] = {-INFINITY, -INFINITY};
   if (!need_exact) {
-    sweep<D, kModeFast>(q16, nchunks, qbuf, hreg, sum, mx, tid, col, g);
+    sweep<D, kModeFast>(q16, L.k, lds, hreg, sum, mx, wave, lane, col, g);
   } else {
-    sweep<D, kModeMax>(q16, nchunks, qbuf, hreg, sum, mx, tid, col, g);
+    sweep<D, kModeMax>(q16, L.k, lds, hreg, sum, mx, wave, lane, col, g);
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) mx[tau] = fmaxf(mx[tau], __shfl_xor(mx[tau], 32));
-    sweep<D, kModeShift>(q16, nchunks, qbuf, hreg, sum, mx, tid, col, g);
+    sweep<D, kModeShift>(q16, L.k, lds, hreg, sum, mx, wave, lane, col, g);
   }
 
   _Float16* h16 = ws_f16(ws, L.off_h16);
   _Float16* h16t = ws_f16(ws, L.off_h16t);
-  _Float16* scratch = qbuf + wave * (32 * C::QS);  // per-wave transpose area
+  float* nl = ws_f32(ws, L.off_nl);
+  _Float16* scratch = reinterpret_cast<_Float16*>(lds) + wave * (kTile * C::TS);  // per-wave transpose area
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
-    float tot = sum[tau] + __shfl_xor(sum[tau], 32);
-    float lse = need_exact ? mx[tau] + log2f(tot) : log2f(tot);
-    float l = valid[tau] ? lse - kAllocShift : 60000.0f;
-    _Float16 lhi = (_Float16)l;
-    _Float16 llo = valid[tau] ? (_Float16)(l - (float)lhi) : (_Float16)0.0f;
+    const float tot = sum[tau] + __shfl_xor(sum[tau], 32);
+    const float lse = need_exact ? mx[tau] + log2f(tot) : log2f(tot);
     const int32_t tile = tiles[tau];
     const bool live = tile < total_tiles;
     if (live) {
-      _Float16* dst = h16 + ((int64_t)tile * kTile + col) * C::ROW;
+      _Float16* dst = h16 + ((int64_t)tile * kTile + col) * D;
 #pragma unroll
       for (int s = 0; s < C::S; ++s) *reinterpret_cast<half8*>(dst + 16 * s + 8 * g) = hreg[tau][s];
-      half8 f = {};
-      if (g == 0) {
-        f[0] = -lhi;
-        f[1] = -llo;
-      }
-      *reinterpret_cast<half8*>(dst + D + 8 * g) = f;
+      if (g == 0) nl[(int64_t)tile * kTile + col] = valid[tau] ? kAllocShift - lse : -60000.0f;
     }
     // transpose through LDS: rows of this tile, then [d][32] in accumulator order
 #pragma unroll
     for (int s = 0; s < C::S; ++s)
-      *reinterpret_cast<half8*>(scratch + col * C::QS + 16 * s + 8 * g) = hreg[tau][s];
+      *reinterpret_cast<half8*>(scratch + col * C::TS + 16 * s + 8 * g) = hreg[tau][s];
     __syncthreads();
     if (live) {
 #pragma unroll
@@ -232,7 +230,7 @@ __global__ __launch_bounds__(256) void pass1_lse(const uint16_t* __restrict__ H,
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int tk = 16 * kk + 8 * (e >> 2) + 4 * gg + (e & 3);
-          v[e] = scratch[tk * C::QS + dcol];
+          v[e] = scratch[tk * C::TS + dcol];
         }
         *reinterpret_cast<half8*>(h16t + ((int64_t)tile * D + dcol) * kTile + 8 * j) = v;
       }

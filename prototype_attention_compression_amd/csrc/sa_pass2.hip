@@ -11,14 +11,25 @@
 // ever stored (blog "How it works" item 3).
 //
 // Per 32-token tile, each wave (64 prototypes = 2 blocks of 32) runs
-//   GEMM1  C[t, j] = [h_t | features] . [q_j | 1, 1, 0..]  = L - l   (fp16 MFMA)
-//   A'     = 2^C  (= 2^14 A, fits fp16), converted pairwise to fp16,
+//   GEMM1  C[t, j] = -l_t + h_t . q_j   (fp16 MFMA; the accumulator starts at
+//          -l_t, l_t = lse_t - 14, read from LDS, so no subtraction is needed)
+//   A'     = 2^C (= 2^14 A, inside fp16 range), converted pairwise to fp16;
 //          mass += A' pairs (v_dot2 on the rounded values)
-//   GEMM2  U[j, c] += sum_t A'[j,t] h_t[c]                           (fp16 MFMA)
+//   GEMM2  U[j, c] += sum_t A'[j,t] h_t[c]                            (fp16 MFMA)
 // The accumulator of GEMM1 holds prototype (lane % 32) and 16 tokens per lane;
-// those registers are exactly the A operand of GEMM2 once the transposed tile
-// stores tokens in the accumulator's row order (done by pass 1), so no data
-// moves between lanes.  The 2^14 scale cancels in U / m.
+// those registers are exactly the A operand of GEMM2 because the transposed
+// tile stores tokens in the accumulator's row order (pass 1 writes it so), so
+// no data moves between lanes.  The 2^14 scale cancels in U / m.
+//
+// Data movement: tiles reach LDS with direct global->LDS loads (16 B per
+// lane), 4 tiles (128 tokens) per stage, two stages in flight.  LDS rows are
+// XOR-swizzled by 16-byte chunk so each group of 16 lanes of a ds_read_b128
+// hits 16 different 16-byte bank slots (gfx950 LDS: 64 banks of 4 bytes).
+// Every user's tile count is a multiple of 4 (pass 1 fills the padding tiles
+// with zero rows and A = 0), so every stage is full and the stage body is one
+// straight-line block.  Within it the exponentials of tile t are interleaved
+// with the GEMM1 MFMAs of tile t+1, so the VALU work hides under the matrix
+// cores.
 //
 // Work item = (chunk of <= tiles_per_chunk tiles of one user, prototype block
 // of waves*64).  Workgroups are numbered so that the prototype blocks of one
@@ -32,21 +43,40 @@
 
 namespace sa {
 
+namespace {
+
+constexpr int kStageTiles = 4;
+
+template <int D>
+struct P2 {
+  static constexpr int S = D / 16;                 // MFMA K steps over d
+  static constexpr int DT = D / 32;                // 32-column output blocks
+  static constexpr int CPR = D / 8;                // 16-B chunks per token row
+  static constexpr int ROWSH = (CPR == 16) ? 0 : 1;  // rows sharing a 256-B bank line: 2^ROWSH
+  static constexpr int TILE_BYTES = kTile * D * 2;   // one tile, rows or transposed
+  static constexpr int ROWS_BYTES = kStageTiles * TILE_BYTES;
+  static constexpr int NL_OFF = 2 * ROWS_BYTES;      // -l values of the stage (fp32)
+  static constexpr int STAGE_BYTES = NL_OFF + kStageTiles * kTile * 4;
+  static constexpr int LOADS_ROWS = ROWS_BYTES / 1024;   // 1-KB direct loads per stage, rows
+  static constexpr int LOADS_TR = ROWS_BYTES / 1024;     // and transposed tiles
+};
+
+// chunk swizzle of a token row (row index within the stage) and of a
+// transposed-tile row (feature column)
+template <int D>
+__device__ __forceinline__ int swz_row(int tok) {
+  return (tok >> P2<D>::ROWSH) & (P2<D>::CPR - 1);
+}
+__device__ __forceinline__ int swz_tr(int dcol) { return (dcol >> 2) & 3; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+}  // namespace
+
 template <int D, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
-  constexpr int NT = WAVES * 64;
-  constexpr int S = D / 16;        // history K steps
-  constexpr int SF = S + 1;        // + the feature step
-  constexpr int ROW = D + kFeat;
-  constexpr int HS = ROW + 8;      // LDS row stride of token rows (fp16)
-  constexpr int TS = kTile + 8;    // LDS row stride of the transposed tile (fp16)
-  constexpr int DT = D / 32;       // 32-column blocks of the output
-  constexpr int P_ROWS = kTile * ROW / 8;   // 16-B pieces per tile, token rows
-  constexpr int P_TR = D * kTile / 8;       // 16-B pieces per tile, transposed
-  constexpr int PIECES = P_ROWS + P_TR;
-  constexpr int PPT = (PIECES + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) _Float16 hrow[2][kTile * HS];
-  __shared__ __attribute__((aligned(16))) _Float16 htr[2][D * TS];
+  using C = P2<D>;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * C::STAGE_BYTES];
 
   const int32_t* hdr = ws_i32(ws, L.off_hdr);
   const int x = blockIdx.x, xcd = x & 7, slot = x >> 3;
@@ -67,73 +97,101 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   const int col = lane & 31, g = lane >> 5;
   const int p0 = pb * (WAVES * kProtoPerWave) + wave * kProtoPerWave;
 
+  // B operands of GEMM1: the wave's 64 query rows, kept in registers
   const _Float16* q16 = ws_f16(ws, L.off_q16);
-  half8 qf[2][SF];
+  half8 qf[2][C::S];
 #pragma unroll
   for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-    for (int s = 0; s < SF; ++s)
-      qf[pt][s] = *reinterpret_cast<const half8*>(q16 + (int64_t)(p0 + 32 * pt + col) * ROW + 16 * s + 8 * g);
+    for (int s = 0; s < C::S; ++s)
+      qf[pt][s] = *reinterpret_cast<const half8*>(q16 + (int64_t)(p0 + 32 * pt + col) * D + 16 * s + 8 * g);
 
-  const _Float16* h16 = ws_f16(ws, L.off_h16);
-  const _Float16* h16t = ws_f16(ws, L.off_h16t);
-  auto load_tile = [&](int32_t tile, u32x4 (&pre)[PPT]) {
-    const _Float16* rows = h16 + (int64_t)tile * kTile * ROW;
-    const _Float16* tr = h16t + (int64_t)tile * D * kTile;
+  const char* h16 = reinterpret_cast<const char*>(ws_f16(ws, L.off_h16));
+  const char* h16t = reinterpret_cast<const char*>(ws_f16(ws, L.off_h16t));
+  const char* nlg = reinterpret_cast<const char*>(ws_f32(ws, L.off_nl));
+
+  // Direct loads of stage `ts` (tiles 4 ts .. 4 ts + 3 of the chunk) into
+  // buffer b.  Load i of the rows part fills LDS bytes [1024 i, 1024 i + 1024)
+  // of the stage: lane l writes chunk slot 64 i + l = (token, swizzled chunk).
+  // Every user's tile count is a multiple of 4, so stages are always full.
+  auto issue = [&](int ts, int b) {
+    char* base = lds + b * C::STAGE_BYTES;
+    const int64_t tile0 = (int64_t)t0 + (int64_t)ts * kStageTiles;
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + NT * i;
-      if (p < P_ROWS) {
-        pre[i] = *reinterpret_cast<const u32x4*>(rows + p * 8);
-      } else if (p < PIECES) {
-        pre[i] = *reinterpret_cast<const u32x4*>(tr + (p - P_ROWS) * 8);
-      }
+    for (int i = wave; i < C::LOADS_ROWS; i += WAVES) {
+      const int q = 64 * i + lane;
+      const int tok = q / C::CPR, cs = q % C::CPR;
+      const int c = cs ^ swz_row<D>(tok);
+      const char* src = h16 + (tile0 * kTile + tok) * (D * 2) + c * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(base + 1024 * i), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = wave; i < C::LOADS_TR; i += WAVES) {
+      const int q = 64 * i + lane;
+      const int tt = q / (C::TILE_BYTES / 16), qq = q % (C::TILE_BYTES / 16);
+      const int dcol = qq >> 2, c = (qq & 3) ^ swz_tr(dcol);
+      const char* src = h16t + (tile0 + tt) * C::TILE_BYTES + dcol * 64 + c * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(base + C::ROWS_BYTES + 1024 * i), 16, 0, 0);
+    }
+    if (wave == WAVES - 1 && lane < 8 * kStageTiles) {
+      const char* src = nlg + tile0 * (kTile * 4) + lane * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(base + C::NL_OFF), 16, 0, 0);
     }
   };
-  auto store_tile = [&](int buf, const u32x4 (&pre)[PPT]) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + NT * i;
-      if (p < P_ROWS) {
-        const int r = p / (ROW / 8), c = p % (ROW / 8);
-        *reinterpret_cast<u32x4*>(&hrow[buf][r * HS + c * 8]) = pre[i];
-      } else if (p < PIECES) {
-        const int q = p - P_ROWS, r = q / (kTile / 8), c = q % (kTile / 8);
-        *reinterpret_cast<u32x4*>(&htr[buf][r * TS + c * 8]) = pre[i];
-      }
-    }
-  };
 
-  float16v U[2][DT];
+  float16v U[2][C::DT];
 #pragma unroll
   for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) U[pt][dt] = float16v{};
+    for (int dt = 0; dt < C::DT; ++dt) U[pt][dt] = float16v{};
   float msum[2] = {0.f, 0.f};
   const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  {
-    u32x4 pre[PPT];
-    load_tile(t0, pre);
-    store_tile(0, pre);
-  }
-  __syncthreads();
-
-  for (int i = 0; i < nt; ++i) {
-    const int buf = i & 1;
-    u32x4 pre[PPT];
-    if (i + 1 < nt) load_tile(t0 + i + 1, pre);
-
-    // GEMM1: C[t, j] = L[j, t] - l_t for the wave's 2 x 32 prototypes
-    float16v Cm[2] = {float16v{}, float16v{}};
+  // Operand fragments of one tile, read from LDS ahead of their MFMAs.
+  struct Frag {
+    half8 h[C::S];        // GEMM1 A operands: token rows (lane = token)
+    float16v init;        // GEMM1 accumulator start: -l of the lane-half's tokens
+  };
+  auto read_rows = [&](const char* base, int t, Frag& f) {
+    const char* rows = base + t * C::TILE_BYTES;
+    const float* nl = reinterpret_cast<const float*>(base + C::NL_OFF) + t * kTile;
 #pragma unroll
-    for (int s = 0; s < SF; ++s) {
-      const half8 ha = *reinterpret_cast<const half8*>(&hrow[buf][col * HS + 16 * s + 8 * g]);
-#pragma unroll
-      for (int pt = 0; pt < 2; ++pt) Cm[pt] = mfma32x32x16(ha, qf[pt][s], Cm[pt]);
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(nl + 8 * q + 4 * g);
+      f.init[4 * q] = v.x;
+      f.init[4 * q + 1] = v.y;
+      f.init[4 * q + 2] = v.z;
+      f.init[4 * q + 3] = v.w;
     }
-    // allocations (scaled by 2^14) in fp16, and the masses of the rounded values
-    half8 ap[2][2];
+    const int tok = t * kTile + col;   // row within the stage
+#pragma unroll
+    for (int s = 0; s < C::S; ++s) {
+      const int c = (2 * s + g) ^ swz_row<D>(tok);
+      f.h[s] = *reinterpret_cast<const half8*>(rows + col * (D * 2) + c * 16);
+    }
+  };
+  // GEMM2 B operands: transposed tile (lane = feature column), token order of
+  // the GEMM1 accumulator
+  auto read_tr = [&](const char* base, int t, half8 (&hb)[2][C::DT]) {
+    const char* tr = base + C::ROWS_BYTES + t * C::TILE_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const int dcol = 32 * dt + col;
+        const int c = (2 * kk + g) ^ swz_tr(dcol);
+        hb[kk][dt] = *reinterpret_cast<const half8*>(tr + dcol * 64 + c * 16);
+      }
+  };
+  // GEMM1: C[tok, proto] = -l_tok + h_tok . q_proto
+  auto gemm1 = [&](const Frag& f, float16v (&Cm)[2]) {
+#pragma unroll
+    for (int s = 0; s < C::S; ++s)
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) Cm[pt] = mfma32x32x16(f.h[s], qf[pt][s], s == 0 ? f.init : Cm[pt]);
+  };
+  // allocations 2^C in fp16 and the masses of the rounded values
+  auto expo = [&](const float16v (&Cm)[2], half8 (&ap)[2][2]) {
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
@@ -146,17 +204,75 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
           ap[pt][kk][e] = h[0];
           ap[pt][kk][e + 1] = h[1];
         }
-    // GEMM2: U[j, c] += sum_t A'[j, t] h_t[c]
+  };
+  // GEMM2: U[proto, c] += sum_tok A'[proto, tok] h_tok[c]
+  auto gemm2 = [&](const half8 (&ap)[2][2], const half8 (&hb)[2][C::DT]) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const half8 hb = *reinterpret_cast<const half8*>(&htr[buf][(32 * dt + col) * TS + 16 * kk + 8 * g]);
+      for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt) U[pt][dt] = mfma32x32x16(ap[pt][kk], hb, U[pt][dt]);
+        for (int pt = 0; pt < 2; ++pt) U[pt][dt] = mfma32x32x16(ap[pt][kk], hb[kk][dt], U[pt][dt]);
+  };
+  // MFMA / VALU / LDS-read interleave for a phase that runs GEMM1 of the next
+  // tile beside the exponentials of the current one
+  auto interleave_g1_exp = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2 * C::S; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read (next operands)
+    }
+  };
+
+  // Software pipeline over the chunk's tiles (stage = 4 tiles, 2 LDS buffers):
+  //   phase t:  read operands of tile t+1;  GEMM1(t+1) || exp(t);  GEMM2(t)
+  // At the last tile of a stage the next stage must be resident: wait for the
+  // loads, barrier, then refill the buffer just finished with the stage after.
+  const int nstages = nt / kStageTiles;
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  if (nstages > 1) issue(1, 1);
+  Frag fr;
+  float16v Ca[2], Cb[2];
+  half8 ap[2][2];
+  half8 hb[2][C::DT];
+  read_rows(lds, 0, fr);
+  gemm1(fr, Ca);
+  for (int st = 0; st < nstages; ++st) {
+    const int b = st & 1;
+    const char* base = lds + b * C::STAGE_BYTES;
+    const char* nbase = lds + (b ^ 1) * C::STAGE_BYTES;
+    const bool more = st + 1 < nstages;
+#pragma unroll
+    for (int j = 0; j < kStageTiles; ++j) {
+      float16v (&Cx)[2] = (j & 1) ? Cb : Ca;
+      float16v (&Cy)[2] = (j & 1) ? Ca : Cb;
+      read_tr(base, j, hb);
+      if (j + 1 < kStageTiles) {
+        __builtin_amdgcn_sched_barrier(0);
+        read_rows(base, j + 1, fr);
+        gemm1(fr, Cy);
+        expo(Cx, ap);
+        interleave_g1_exp();
+        __builtin_amdgcn_sched_barrier(0);
+      } else if (more) {
+        // next stage: its loads landed, and every wave read this stage's data
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (st + 2 < nstages) issue(st + 2, b);
+        __builtin_amdgcn_sched_barrier(0);
+        read_rows(nbase, 0, fr);
+        gemm1(fr, Cy);
+        expo(Cx, ap);
+        interleave_g1_exp();
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        expo(Cx, ap);
       }
-    if (i + 1 < nt) store_tile(buf ^ 1, pre);
-    __syncthreads();
+      gemm2(ap, hb);
+    }
   }
 
   float* part_u = ws_f32(ws, L.off_part_u) + (int64_t)chunk * L.k * D;
@@ -164,7 +280,7 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
 #pragma unroll
   for (int pt = 0; pt < 2; ++pt) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         part_u[(int64_t)(p0 + 32 * pt + acc_row(r, g)) * D + 32 * dt + col] = U[pt][dt][r];

@@ -27,15 +27,13 @@ __device__ __forceinline__ float load_in<float>(const float* p, int64_t i) {
 }
 
 // One workgroup of 256 threads computes 256 / D query rows.  Thread (j, c)
-// forms q[j][c] = sum_a P[j][a] * Wk[c][a], scaled.  The bf16 path stores fp16
-// rows of width D + kFeat whose feature columns are (1, 1, 0, ...): they meet
-// the per-token features (-l_hi, -l_lo, 0, ...) of the token rows so that the
-// logit MFMA directly yields L - l.  The fp32 path stores fp32 rows.
+// forms q[j][c] = sum_a P[j][a] * Wk[c][a], scaled.  The bf16 path stores the
+// rows in fp16 (the MFMA operand type) with their norms; the fp32 path stores
+// fp32 rows.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void prep_queries(const T* __restrict__ P, const T* __restrict__ Wk,
                                                     Layout L, void* ws) {
   constexpr int PR = 256 / D;
-  constexpr int ROW = D + kFeat;
   __shared__ float prow[PR][D];
   __shared__ float red[256];
   const int tid = threadIdx.x;
@@ -53,10 +51,9 @@ __global__ __launch_bounds__(256) void prep_queries(const T* __restrict__ P, con
     ws_f32(ws, L.off_q32)[(int64_t)j * D + c] = q;
     return;
   }
-  _Float16* q16 = ws_f16(ws, L.off_q16) + (int64_t)j * ROW;
+  _Float16* q16 = ws_f16(ws, L.off_q16) + (int64_t)j * D;
   const _Float16 qh = (_Float16)q;
   q16[c] = qh;
-  if (c < kFeat) q16[D + c] = (_Float16)(c < 2 ? 1.0f : 0.0f);
   const float qf = (float)qh;
   red[tid] = qf * qf;
   __syncthreads();
@@ -69,8 +66,9 @@ __global__ __launch_bounds__(256) void prep_queries(const T* __restrict__ P, con
 
 // Single workgroup.  Checks 0 = offsets[0] <= ... <= offsets[R] = N; on a
 // violation every user is treated as empty and the error flag is raised.
-// Writes tile_base / chunk_base (exclusive prefix sums of ceil(n_u / 32) and
-// ceil(tiles_u / tiles_per_chunk)), the totals, and the largest query norm.
+// Writes tile_base / chunk_base (exclusive prefix sums of tiles_u = ceil(n_u /
+// 32) rounded up to a multiple of kUserTileAlign, and ceil(tiles_u /
+// tiles_per_chunk)), the totals, and the largest query norm.
 __global__ __launch_bounds__(1024) void prep_schedule(const int64_t* __restrict__ offsets, Layout L,
                                                       void* ws) {
   __shared__ int32_t sc_t[1024];
@@ -90,7 +88,7 @@ __global__ __launch_bounds__(1024) void prep_schedule(const int64_t* __restrict_
   int32_t nt = 0, nc = 0;
   for (int u = u0; u < u1; ++u) {
     int64_t n = bad ? 0 : offsets[u + 1] - offsets[u];
-    int32_t t = (int32_t)((n + kTile - 1) / kTile);
+    int32_t t = (int32_t)((n + kTile * kUserTileAlign - 1) / (kTile * kUserTileAlign)) * kUserTileAlign;
     nt += t;
     nc += (t + CT - 1) / CT;
   }
@@ -113,7 +111,7 @@ __global__ __launch_bounds__(1024) void prep_schedule(const int64_t* __restrict_
     tile_base[u] = bt;
     chunk_base[u] = bc;
     int64_t n = bad ? 0 : offsets[u + 1] - offsets[u];
-    int32_t t = (int32_t)((n + kTile - 1) / kTile);
+    int32_t t = (int32_t)((n + kTile * kUserTileAlign - 1) / (kTile * kUserTileAlign)) * kUserTileAlign;
     bt += t;
     bc += (t + CT - 1) / CT;
   }
