@@ -47,6 +47,14 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     if _lib is not None and path is None:
         return _lib
     p = path or LIB_PATH
+    # PyTorch-ROCm ships its own HIP runtime.  Load it first so that libsa's
+    # libamdhip64 dependency resolves to that same runtime: with two runtimes
+    # in one process, device pointers and streams of one are invalid in the
+    # other.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(p):
         raise ImportError(
             f"{p} not found: build it with `python -m prototype_attention_compression_amd.build`")

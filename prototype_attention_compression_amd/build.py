@@ -45,9 +45,17 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# per-file code generation options: keep MFMA accumulators in ordinary VGPRs
+# (the VALU reads them directly, no accumulator-register copies)
+FILE_FLAGS = {
+    "sa_pass1.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "sa_pass2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str, hipcc: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc, *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = (res.stdout + res.stderr).strip()
     # the host pass does not know the device-only feature flag: harmless

@@ -5,7 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/sa.h"
+#include "sa.h"
 #include "sa_launch.h"
 #include "sa_layout.h"
 
@@ -29,11 +29,10 @@ sa_status check_problem(const sa_problem* p) {
   return SA_OK;
 }
 
+// pass-2 waves per workgroup: 8, 4 or 2, dividing k / 32 (k is a multiple of 64)
 int pick_waves(int k) {
-  const int blocks64 = k / kProtoPerWave;
-  for (int w = 4; w > 1; --w)
-    if (blocks64 % w == 0) return w;
-  return 1;
+  const int blocks = k / kProtoPerWave;
+  return blocks % 8 == 0 ? 8 : (blocks % 4 == 0 ? 4 : 2);
 }
 
 // Tiles per pass-2 chunk: enough chunks that chunks x prototype blocks fill
@@ -79,7 +78,7 @@ Layout make_layout(const sa_problem& p) {
     L.off_qnorm = take((size_t)p.k * sizeof(float));
     L.off_h16 = take((size_t)tiles_max * kTile * p.d * 2);
     L.off_h16t = take((size_t)tiles_max * p.d * kTile * 2);
-    L.off_nl = take((size_t)tiles_max * kTile * sizeof(float));
+    L.off_nl = take((size_t)tiles_max * kTile * sizeof(uint32_t));
   } else {
     L.off_q32 = take((size_t)p.k * p.d * sizeof(float));
     L.off_lse32 = take((size_t)tiles_max * kTile * sizeof(float));

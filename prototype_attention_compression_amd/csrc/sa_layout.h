@@ -19,7 +19,7 @@ namespace sa {
 constexpr int kTile = 32;            // tokens per tile (one 32-wide MFMA block)
 constexpr int kUserTileAlign = 4;    // tiles per user: multiple of this (pass-2 stage)
 constexpr int kPass1Tiles = 8;       // tiles per pass-1 workgroup (4 waves x 2 tiles)
-constexpr int kProtoPerWave = 64;    // prototypes owned by one pass-2 wave
+constexpr int kProtoPerWave = 32;    // prototypes owned by one pass-2 wave
 constexpr int kQChunk = 64;          // prototypes per pass-1 LDS chunk
 constexpr int kFinRows = 32;         // prototypes per finalize workgroup
 constexpr float kAllocShift = 14.0f; // fp16 allocations carry a 2^14 scale
@@ -48,7 +48,8 @@ struct Layout {
   size_t off_qnorm;        // [k] float      |q_j| of the fp16 queries
   size_t off_h16;          // [tiles_max, 32, d] fp16    token rows
   size_t off_h16t;         // [tiles_max, d, 32] fp16    token-permuted transpose
-  size_t off_nl;           // [tiles_max, 32] float      -(lse_t - 14), -60000 if dropped
+  size_t off_nl;           // [tiles_max, 32] fp16 pairs (-l_hi, -l_lo), l = lse_t - 14;
+                           //   (-60000, 0) if the token is dropped
   size_t off_q32;          // [k, d] float   queries, fp32 path
   size_t off_lse32;        // [tiles_max*32] float, fp32 path
   size_t off_part_u;       // [chunks_max, k, d] float  per-chunk sums of A h

@@ -12,8 +12,9 @@
 //   * a transposed 32-token tile [d][32] whose token order matches the
 //     register order of the 32x32 MFMA accumulator (so pass 2 feeds its
 //     allocation registers straight into the second MFMA),
-//   * -l_t = -(lse_t - 14) in fp32, the starting value of pass 2's logit
-//     accumulator (the 2^14 keeps fp16 allocations in the normal range).
+//   * -l_t = -(lse_t - 14) as two fp16 parts (hi, lo), the token's entries of
+//     pass 2's extra MFMA K step, so that step subtracts l_t from every logit
+//     (the 2^14 keeps fp16 allocations in the normal range).
 // Masked tokens and tile padding get zero rows and -l = -60000, i.e. A = 0.
 //
 // Layout: one workgroup = 4 waves = 8 tiles (256 tokens).  Each wave keeps the
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(256) void pass1_lse(const uint16_t* __restrict__ H,
 
   _Float16* h16 = ws_f16(ws, L.off_h16);
   _Float16* h16t = ws_f16(ws, L.off_h16t);
-  float* nl = ws_f32(ws, L.off_nl);
+  uint32_t* nl = reinterpret_cast<uint32_t*>(ws_i32(ws, L.off_nl));
   _Float16* scratch = reinterpret_cast<_Float16*>(lds) + wave * (kTile * C::TS);  // per-wave transpose area
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
@@ -213,7 +214,14 @@ __global__ __launch_bounds__(256) void pass1_lse(const uint16_t* __restrict__ H,
       _Float16* dst = h16 + ((int64_t)tile * kTile + col) * D;
 #pragma unroll
       for (int s = 0; s < C::S; ++s) *reinterpret_cast<half8*>(dst + 16 * s + 8 * g) = hreg[tau][s];
-      if (g == 0) nl[(int64_t)tile * kTile + col] = valid[tau] ? kAllocShift - lse : -60000.0f;
+      if (g == 0) {
+        // -l = 14 - lse as an fp16 pair (hi, lo) with hi + lo = -l to ~2^-16
+        const float nlv = valid[tau] ? kAllocShift - lse : -60000.0f;
+        const _Float16 hi = (_Float16)nlv;
+        const _Float16 lo = valid[tau] ? (_Float16)(nlv - (float)hi) : (_Float16)0.0f;
+        half2v pr = {hi, lo};
+        nl[(int64_t)tile * kTile + col] = __builtin_bit_cast(uint32_t, pr);
+      }
     }
     // transpose through LDS: rows of this tile, then [d][32] in accumulator order
 #pragma unroll

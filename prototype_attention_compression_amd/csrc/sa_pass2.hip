@@ -10,12 +10,13 @@
 // (prototype-wise normalisation) and applies Wv.  Nothing of size k x n is
 // ever stored (blog "How it works" item 3).
 //
-// Per 32-token tile, each wave (64 prototypes = 2 blocks of 32) runs
-//   GEMM1  C[t, j] = -l_t + h_t . q_j   (fp16 MFMA; the accumulator starts at
-//          -l_t, l_t = lse_t - 14, read from LDS, so no subtraction is needed)
+// Per 32-token tile, each wave (32 prototypes) runs
+//   GEMM1  C[t, j] = h_t . q_j - l_t with fp16 MFMAs: 8 K steps over d plus
+//          one "feature" step in which the token supplies (-l_hi, -l_lo) and
+//          the prototype (1, 1), l_t = lse_t - 14 split into two fp16 parts;
 //   A'     = 2^C (= 2^14 A, inside fp16 range), converted pairwise to fp16;
-//          mass += A' pairs (v_dot2 on the rounded values)
-//   GEMM2  U[j, c] += sum_t A'[j,t] h_t[c]                            (fp16 MFMA)
+//          mass += A' pairs (v_dot2 on the rounded values);
+//   GEMM2  U[j, c] += sum_t A'[j,t] h_t[c]                           (fp16 MFMA)
 // The accumulator of GEMM1 holds prototype (lane % 32) and 16 tokens per lane;
 // those registers are exactly the A operand of GEMM2 because the transposed
 // tile stores tokens in the accumulator's row order (pass 1 writes it so), so
@@ -27,12 +28,14 @@
 // hits 16 different 16-byte bank slots (gfx950 LDS: 64 banks of 4 bytes).
 // Every user's tile count is a multiple of 4 (pass 1 fills the padding tiles
 // with zero rows and A = 0), so every stage is full and the stage body is one
-// straight-line block.  Within it the exponentials of tile t are interleaved
-// with the GEMM1 MFMAs of tile t+1, so the VALU work hides under the matrix
-// cores.
+// straight-line block.  A workgroup has up to 8 waves of 32 prototypes (two
+// waves per SIMD, every MFMA operand and result in VGPRs), so one wave's
+// exponentials and LDS reads run while the other wave's MFMAs execute.  LDS
+// read traffic is about 1 KB per MFMA, close to what the LDS sustains; the
+// feature step keeps the per-token -l down to 4 bytes per lane.
 //
 // Work item = (chunk of <= tiles_per_chunk tiles of one user, prototype block
-// of waves*64).  Workgroups are numbered so that the prototype blocks of one
+// of waves*32).  Workgroups are numbered so that the prototype blocks of one
 // chunk land on the same XCD back to back (dispatch goes round-robin over the
 // 8 XCDs), letting them share the chunk's tiles through that XCD's L2.
 #include <hip/hip_runtime.h>
@@ -49,13 +52,13 @@ constexpr int kStageTiles = 4;
 
 template <int D>
 struct P2 {
-  static constexpr int S = D / 16;                 // MFMA K steps over d
-  static constexpr int DT = D / 32;                // 32-column output blocks
-  static constexpr int CPR = D / 8;                // 16-B chunks per token row
+  static constexpr int S = D / 16;                   // MFMA K steps over d
+  static constexpr int DT = D / 32;                  // 32-column output blocks
+  static constexpr int CPR = D / 8;                  // 16-B chunks per token row
   static constexpr int ROWSH = (CPR == 16) ? 0 : 1;  // rows sharing a 256-B bank line: 2^ROWSH
   static constexpr int TILE_BYTES = kTile * D * 2;   // one tile, rows or transposed
   static constexpr int ROWS_BYTES = kStageTiles * TILE_BYTES;
-  static constexpr int NL_OFF = 2 * ROWS_BYTES;      // -l values of the stage (fp32)
+  static constexpr int NL_OFF = 2 * ROWS_BYTES;      // (-l_hi, -l_lo) pairs of the stage
   static constexpr int STAGE_BYTES = NL_OFF + kStageTiles * kTile * 4;
   static constexpr int LOADS_ROWS = ROWS_BYTES / 1024;   // 1-KB direct loads per stage, rows
   static constexpr int LOADS_TR = ROWS_BYTES / 1024;     // and transposed tiles
@@ -97,23 +100,23 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   const int col = lane & 31, g = lane >> 5;
   const int p0 = pb * (WAVES * kProtoPerWave) + wave * kProtoPerWave;
 
-  // B operands of GEMM1: the wave's 64 query rows, kept in registers
+  // B operands of GEMM1: the wave's 32 query rows (kept in registers), and the
+  // feature step's (1, 1, 0, ...) column pair
   const _Float16* q16 = ws_f16(ws, L.off_q16);
-  half8 qf[2][C::S];
+  half8 qf[C::S];
 #pragma unroll
-  for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-    for (int s = 0; s < C::S; ++s)
-      qf[pt][s] = *reinterpret_cast<const half8*>(q16 + (int64_t)(p0 + 32 * pt + col) * D + 16 * s + 8 * g);
+  for (int s = 0; s < C::S; ++s)
+    qf[s] = *reinterpret_cast<const half8*>(q16 + (int64_t)(p0 + col) * D + 16 * s + 8 * g);
+  const half8 qfeat = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)0.0f, (_Float16)0.0f,
+                       (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
 
   const char* h16 = reinterpret_cast<const char*>(ws_f16(ws, L.off_h16));
   const char* h16t = reinterpret_cast<const char*>(ws_f16(ws, L.off_h16t));
-  const char* nlg = reinterpret_cast<const char*>(ws_f32(ws, L.off_nl));
+  const char* nlg = reinterpret_cast<const char*>(ws_i32(ws, L.off_nl));
 
   // Direct loads of stage `ts` (tiles 4 ts .. 4 ts + 3 of the chunk) into
   // buffer b.  Load i of the rows part fills LDS bytes [1024 i, 1024 i + 1024)
   // of the stage: lane l writes chunk slot 64 i + l = (token, swizzled chunk).
-  // Every user's tile count is a multiple of 4, so stages are always full.
   auto issue = [&](int ts, int b) {
     char* base = lds + b * C::STAGE_BYTES;
     const int64_t tile0 = (int64_t)t0 + (int64_t)ts * kStageTiles;
@@ -139,154 +142,69 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
     }
   };
 
-  float16v U[2][C::DT];
+  float16v U[C::DT];
 #pragma unroll
-  for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) U[pt][dt] = float16v{};
-  float msum[2] = {0.f, 0.f};
+  for (int dt = 0; dt < C::DT; ++dt) U[dt] = float16v{};
+  float msum = 0.f;
   const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  // Operand fragments of one tile, read from LDS ahead of their MFMAs.
-  struct Frag {
-    half8 h[C::S];        // GEMM1 A operands: token rows (lane = token)
-    float16v init;        // GEMM1 accumulator start: -l of the lane-half's tokens
-  };
-  auto read_rows = [&](const char* base, int t, Frag& f) {
-    const char* rows = base + t * C::TILE_BYTES;
-    const float* nl = reinterpret_cast<const float*>(base + C::NL_OFF) + t * kTile;
+  const int nstages = nt / kStageTiles;
+  issue(0, 0);
+  for (int st = 0; st < nstages; ++st) {
+    const int b = st & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of stage st landed
+    __syncthreads();                     // ... every wave's; and stage st-1's buffer is free
+    if (st + 1 < nstages) issue(st + 1, b ^ 1);
+    const char* base = lds + b * C::STAGE_BYTES;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 v = *reinterpret_cast<const float4*>(nl + 8 * q + 4 * g);
-      f.init[4 * q] = v.x;
-      f.init[4 * q + 1] = v.y;
-      f.init[4 * q + 2] = v.z;
-      f.init[4 * q + 3] = v.w;
-    }
-    const int tok = t * kTile + col;   // row within the stage
+    for (int t = 0; t < kStageTiles; ++t) {
+      const char* rows = base + t * C::TILE_BYTES;
+      const char* tr = base + C::ROWS_BYTES + t * C::TILE_BYTES;
+      // GEMM1: C[tok, proto] = h_tok . q_proto - l_tok
+      const uint32_t nlp = reinterpret_cast<const uint32_t*>(base + C::NL_OFF)[t * kTile + col];
+      const u32x4 fv = {g == 0 ? nlp : 0u, 0u, 0u, 0u};
+      float16v Cm = mfma32x32x16(__builtin_bit_cast(half8, fv), qfeat, float16v{});
+      const int tok = t * kTile + col;   // row within the stage
 #pragma unroll
-    for (int s = 0; s < C::S; ++s) {
-      const int c = (2 * s + g) ^ swz_row<D>(tok);
-      f.h[s] = *reinterpret_cast<const half8*>(rows + col * (D * 2) + c * 16);
-    }
-  };
-  // GEMM2 B operands: transposed tile (lane = feature column), token order of
-  // the GEMM1 accumulator
-  auto read_tr = [&](const char* base, int t, half8 (&hb)[2][C::DT]) {
-    const char* tr = base + C::ROWS_BYTES + t * C::TILE_BYTES;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        const int dcol = 32 * dt + col;
-        const int c = (2 * kk + g) ^ swz_tr(dcol);
-        hb[kk][dt] = *reinterpret_cast<const half8*>(tr + dcol * 64 + c * 16);
+      for (int s = 0; s < C::S; ++s) {
+        const int c = (2 * s + g) ^ swz_row<D>(tok);
+        const half8 ha = *reinterpret_cast<const half8*>(rows + col * (D * 2) + c * 16);
+        Cm = mfma32x32x16(ha, qf[s], Cm);
       }
-  };
-  // GEMM1: C[tok, proto] = -l_tok + h_tok . q_proto
-  auto gemm1 = [&](const Frag& f, float16v (&Cm)[2]) {
-#pragma unroll
-    for (int s = 0; s < C::S; ++s)
-#pragma unroll
-      for (int pt = 0; pt < 2; ++pt) Cm[pt] = mfma32x32x16(f.h[s], qf[pt][s], s == 0 ? f.init : Cm[pt]);
-  };
-  // allocations 2^C in fp16 and the masses of the rounded values
-  auto expo = [&](const float16v (&Cm)[2], half8 (&ap)[2][2]) {
-#pragma unroll
-    for (int pt = 0; pt < 2; ++pt)
+      // allocations 2^C (= 2^14 A) in fp16, masses of the rounded values
+      half8 ap[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          float2v v = {__builtin_amdgcn_exp2f(Cm[pt][8 * kk + e]), __builtin_amdgcn_exp2f(Cm[pt][8 * kk + e + 1])};
+          float2v v = {__builtin_amdgcn_exp2f(Cm[8 * kk + e]), __builtin_amdgcn_exp2f(Cm[8 * kk + e + 1])};
           half2v h = __builtin_convertvector(v, half2v);
-          msum[pt] = __builtin_amdgcn_fdot2(h, ones, msum[pt], false);
-          ap[pt][kk][e] = h[0];
-          ap[pt][kk][e + 1] = h[1];
+          msum = __builtin_amdgcn_fdot2(h, ones, msum, false);
+          ap[kk][e] = h[0];
+          ap[kk][e + 1] = h[1];
         }
-  };
-  // GEMM2: U[proto, c] += sum_tok A'[proto, tok] h_tok[c]
-  auto gemm2 = [&](const half8 (&ap)[2][2], const half8 (&hb)[2][C::DT]) {
+      // GEMM2: U[proto, c] += sum_tok A'[proto, tok] h_tok[c]
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt) U[pt][dt] = mfma32x32x16(ap[pt][kk], hb[kk][dt], U[pt][dt]);
-  };
-  // MFMA / VALU / LDS-read interleave for a phase that runs GEMM1 of the next
-  // tile beside the exponentials of the current one
-  auto interleave_g1_exp = [&]() {
-#pragma unroll
-    for (int i = 0; i < 2 * C::S; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read (next operands)
-    }
-  };
-
-  // Software pipeline over the chunk's tiles (stage = 4 tiles, 2 LDS buffers):
-  //   phase t:  read operands of tile t+1;  GEMM1(t+1) || exp(t);  GEMM2(t)
-  // At the last tile of a stage the next stage must be resident: wait for the
-  // loads, barrier, then refill the buffer just finished with the stage after.
-  const int nstages = nt / kStageTiles;
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  if (nstages > 1) issue(1, 1);
-  Frag fr;
-  float16v Ca[2], Cb[2];
-  half8 ap[2][2];
-  half8 hb[2][C::DT];
-  read_rows(lds, 0, fr);
-  gemm1(fr, Ca);
-  for (int st = 0; st < nstages; ++st) {
-    const int b = st & 1;
-    const char* base = lds + b * C::STAGE_BYTES;
-    const char* nbase = lds + (b ^ 1) * C::STAGE_BYTES;
-    const bool more = st + 1 < nstages;
-#pragma unroll
-    for (int j = 0; j < kStageTiles; ++j) {
-      float16v (&Cx)[2] = (j & 1) ? Cb : Ca;
-      float16v (&Cy)[2] = (j & 1) ? Ca : Cb;
-      read_tr(base, j, hb);
-      if (j + 1 < kStageTiles) {
-        __builtin_amdgcn_sched_barrier(0);
-        read_rows(base, j + 1, fr);
-        gemm1(fr, Cy);
-        expo(Cx, ap);
-        interleave_g1_exp();
-        __builtin_amdgcn_sched_barrier(0);
-      } else if (more) {
-        // next stage: its loads landed, and every wave read this stage's data
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-        if (st + 2 < nstages) issue(st + 2, b);
-        __builtin_amdgcn_sched_barrier(0);
-        read_rows(nbase, 0, fr);
-        gemm1(fr, Cy);
-        expo(Cx, ap);
-        interleave_g1_exp();
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
-        expo(Cx, ap);
-      }
-      gemm2(ap, hb);
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const int dcol = 32 * dt + col;
+          const int c = (2 * kk + g) ^ swz_tr(dcol);
+          const half8 hb = *reinterpret_cast<const half8*>(tr + dcol * 64 + c * 16);
+          U[dt] = mfma32x32x16(ap[kk], hb, U[dt]);
+        }
     }
   }
 
   float* part_u = ws_f32(ws, L.off_part_u) + (int64_t)chunk * L.k * D;
   float* part_m = ws_f32(ws, L.off_part_m) + (int64_t)chunk * L.k;
 #pragma unroll
-  for (int pt = 0; pt < 2; ++pt) {
+  for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        part_u[(int64_t)(p0 + 32 * pt + acc_row(r, g)) * D + 32 * dt + col] = U[pt][dt][r];
-    const float m = msum[pt] + __shfl_xor(msum[pt], 32);
-    if (g == 0) part_m[p0 + 32 * pt + col] = m;
-  }
+    for (int r = 0; r < 16; ++r)
+      part_u[(int64_t)(p0 + acc_row(r, g)) * D + 32 * dt + col] = U[dt][r];
+  const float m = msum + __shfl_xor(msum, 32);
+  if (g == 0) part_m[p0 + col] = m;
 }
 
 hipError_t launch_pass2(const Layout& L, void* ws, hipStream_t stream) {
@@ -297,17 +215,15 @@ hipError_t launch_pass2(const Layout& L, void* ws, hipStream_t stream) {
   hipLaunchKernelGGL((pass2_accum<DD, WW>), dim3((unsigned)grid), dim3(WW * 64), 0, stream, L, ws)
   if (L.d == 128) {
     switch (L.waves) {
+      case 8: SA_P2(128, 8); break;
       case 4: SA_P2(128, 4); break;
-      case 3: SA_P2(128, 3); break;
-      case 2: SA_P2(128, 2); break;
-      default: SA_P2(128, 1); break;
+      default: SA_P2(128, 2); break;
     }
   } else {
     switch (L.waves) {
+      case 8: SA_P2(64, 8); break;
       case 4: SA_P2(64, 4); break;
-      case 3: SA_P2(64, 3); break;
-      case 2: SA_P2(64, 2); break;
-      default: SA_P2(64, 1); break;
+      default: SA_P2(64, 2); break;
     }
   }
 #undef SA_P2
