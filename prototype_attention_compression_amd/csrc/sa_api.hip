@@ -77,7 +77,6 @@ Layout make_layout(const sa_problem& p) {
     L.off_q16 = take((size_t)p.k * p.d * 2);
     L.off_qnorm = take((size_t)p.k * sizeof(float));
     L.off_h16 = take((size_t)tiles_max * kTile * p.d * 2);
-    L.off_h16t = take((size_t)tiles_max * p.d * kTile * 2);
     L.off_nl = take((size_t)tiles_max * kTile * sizeof(uint32_t));
   } else {
     L.off_q32 = take((size_t)p.k * p.d * sizeof(float));

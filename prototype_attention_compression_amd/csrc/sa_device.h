@@ -14,6 +14,8 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 // D = A(32x16) * B(16x32) + C on the matrix cores, fp16 operands, fp32 sums.
 // Lane l holds row (l % 32) of A and column (l % 32) of B, 8 contraction

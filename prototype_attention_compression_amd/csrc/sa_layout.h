@@ -47,7 +47,6 @@ struct Layout {
   size_t off_q16;          // [k, d] fp16    queries
   size_t off_qnorm;        // [k] float      |q_j| of the fp16 queries
   size_t off_h16;          // [tiles_max, 32, d] fp16    token rows
-  size_t off_h16t;         // [tiles_max, d, 32] fp16    token-permuted transpose
   size_t off_nl;           // [tiles_max, 32] fp16 pairs (-l_hi, -l_lo), l = lse_t - 14;
                            //   (-60000, 0) if the token is dropped
   size_t off_q32;          // [k, d] float   queries, fp32 path

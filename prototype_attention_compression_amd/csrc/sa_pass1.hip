@@ -9,9 +9,6 @@
 // "How it works" item 3: FlashSA avoids the huge intermediates), and emits
 // the token in the form pass 2 consumes:
 //   * the fp16 row h_t (bf16 widened exactly),
-//   * a transposed 32-token tile [d][32] whose token order matches the
-//     register order of the 32x32 MFMA accumulator (so pass 2 feeds its
-//     allocation registers straight into the second MFMA),
 //   * -l_t = -(lse_t - 14) as two fp16 parts (hi, lo), the token's entries of
 //     pass 2's extra MFMA K step, so that step subtracts l_t from every logit
 //     (the 2^14 keeps fp16 allocations in the normal range).
@@ -54,7 +51,6 @@ struct P1 {
   static constexpr int ROWSH = (CPR == 16) ? 0 : 1;
   static constexpr int CHUNK_BYTES = kQC * D * 2;    // one LDS query chunk
   static constexpr int LOADS = CHUNK_BYTES / 1024;   // 1-KB direct loads per chunk
-  static constexpr int TS = D + 8;                   // transpose scratch row stride (fp16)
 };
 
 template <int D>
@@ -79,11 +75,52 @@ __device__ __forceinline__ void issue_chunk(const char* q16, int c, int nrows, c
   }
 }
 
+// Reduce one 32-prototype group of logits (two 32-token tiles, 16 values per
+// lane each) into the per-lane running statistics.
+template <int MODE>
+__device__ __forceinline__ void reduce_group(const float16v (&acc)[2], float (&acc_sum)[2], float (&acc_max)[2]) {
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    if (MODE == kModeFast) {
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        s0 += __builtin_amdgcn_exp2f(acc[tau][r]);
+        s1 += __builtin_amdgcn_exp2f(acc[tau][r + 1]);
+      }
+      acc_sum[tau] += s0 + s1;
+    } else if (MODE == kModeMax) {
+      float m = acc_max[tau];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[tau][r]);
+      acc_max[tau] = m;
+    } else {
+      float s0 = 0.f, s1 = 0.f;
+      const float mx = acc_max[tau];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        s0 += __builtin_amdgcn_exp2f(acc[tau][r] - mx);
+        s1 += __builtin_amdgcn_exp2f(acc[tau][r + 1] - mx);
+      }
+      acc_sum[tau] += s0 + s1;
+    }
+  }
+}
+
+// One sweep over all k prototypes.  Software-pipelined over 32-prototype
+// groups: the MFMAs of group i are issued interleaved with the reduction of
+// group i-1 (independent work), so the exponentials run under the matrix
+// cores.  The pending group starts at -inf, which every reduction ignores.
 template <int D, int MODE>
 __device__ __forceinline__ void sweep(const char* q16, int k, char* lds, const half8 (&hreg)[2][P1<D>::S],
                                       float (&acc_sum)[2], float (&acc_max)[2], int wave, int lane, int col, int g) {
   using C = P1<D>;
   const int nchunks = (k + kQC - 1) / kQC;
+  float16v pend[2];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pend[tau][r] = -INFINITY;
   issue_chunk<D>(q16, 0, min(kQC, k), lds, wave, lane);
   for (int c = 0; c < nchunks; ++c) {
     char* cur = lds + (c & 1) * C::CHUNK_BYTES;
@@ -94,45 +131,31 @@ __device__ __forceinline__ void sweep(const char* q16, int k, char* lds, const h
       issue_chunk<D>(q16, c + 1, min(kQC, k - (c + 1) * kQC), lds + ((c + 1) & 1) * C::CHUNK_BYTES, wave, lane);
 #pragma unroll
     for (int pt = 0; pt < kQC / 32; ++pt) {
-      if (pt >= npt) break;   // uniform
-      const int row = pt * 32 + col;
-      half8 af[C::S];
+      if (pt < npt) {   // uniform; false only in a 64-prototype last chunk
+        const int row = pt * 32 + col;
+        half8 af[C::S];
 #pragma unroll
-      for (int s = 0; s < C::S; ++s) {
-        const int cl = (2 * s + g) ^ swz<D>(row);
-        af[s] = *reinterpret_cast<const half8*>(cur + row * (D * 2) + cl * 16);
-      }
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        float16v acc = {};
-#pragma unroll
-        for (int s = 0; s < C::S; ++s) acc = mfma32x32x16(af[s], hreg[tau][s], acc);
-        if (MODE == kModeFast) {
-          float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            s0 += __builtin_amdgcn_exp2f(acc[r]);
-            s1 += __builtin_amdgcn_exp2f(acc[r + 1]);
-          }
-          acc_sum[tau] += s0 + s1;
-        } else if (MODE == kModeMax) {
-          float m = acc_max[tau];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[r]);
-          acc_max[tau] = m;
-        } else {
-          float s0 = 0.f, s1 = 0.f;
-          const float mx = acc_max[tau];
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            s0 += __builtin_amdgcn_exp2f(acc[r] - mx);
-            s1 += __builtin_amdgcn_exp2f(acc[r + 1] - mx);
-          }
-          acc_sum[tau] += s0 + s1;
+        for (int s = 0; s < C::S; ++s) {
+          const int cl = (2 * s + g) ^ swz<D>(row);
+          af[s] = *reinterpret_cast<const half8*>(cur + row * (D * 2) + cl * 16);
         }
+        float16v acc[2] = {float16v{}, float16v{}};
+#pragma unroll
+        for (int s = 0; s < C::S; ++s)
+#pragma unroll
+          for (int tau = 0; tau < 2; ++tau) acc[tau] = mfma32x32x16(af[s], hreg[tau][s], acc[tau]);
+        reduce_group<MODE>(pend, acc_sum, acc_max);
+#pragma unroll
+        for (int i = 0; i < 2 * C::S; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // 4 VALU
+        }
+        pend[0] = acc[0];
+        pend[1] = acc[1];
       }
     }
   }
+  reduce_group<MODE>(pend, acc_sum, acc_max);
   __syncthreads();  // all waves are done with the last chunk before LDS is reused
 }
 
@@ -201,49 +224,24 @@ __global__ __launch_bounds__(256) void pass1_lse(const uint16_t* __restrict__ H,
   }
 
   _Float16* h16 = ws_f16(ws, L.off_h16);
-  _Float16* h16t = ws_f16(ws, L.off_h16t);
   uint32_t* nl = reinterpret_cast<uint32_t*>(ws_i32(ws, L.off_nl));
-  _Float16* scratch = reinterpret_cast<_Float16*>(lds) + wave * (kTile * C::TS);  // per-wave transpose area
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
+    const int32_t tile = tiles[tau];
+    if (tile >= total_tiles) continue;
     const float tot = sum[tau] + __shfl_xor(sum[tau], 32);
     const float lse = need_exact ? mx[tau] + log2f(tot) : log2f(tot);
-    const int32_t tile = tiles[tau];
-    const bool live = tile < total_tiles;
-    if (live) {
-      _Float16* dst = h16 + ((int64_t)tile * kTile + col) * D;
+    _Float16* dst = h16 + ((int64_t)tile * kTile + col) * D;
 #pragma unroll
-      for (int s = 0; s < C::S; ++s) *reinterpret_cast<half8*>(dst + 16 * s + 8 * g) = hreg[tau][s];
-      if (g == 0) {
-        // -l = 14 - lse as an fp16 pair (hi, lo) with hi + lo = -l to ~2^-16
-        const float nlv = valid[tau] ? kAllocShift - lse : -60000.0f;
-        const _Float16 hi = (_Float16)nlv;
-        const _Float16 lo = valid[tau] ? (_Float16)(nlv - (float)hi) : (_Float16)0.0f;
-        half2v pr = {hi, lo};
-        nl[(int64_t)tile * kTile + col] = __builtin_bit_cast(uint32_t, pr);
-      }
+    for (int s = 0; s < C::S; ++s) *reinterpret_cast<half8*>(dst + 16 * s + 8 * g) = hreg[tau][s];
+    if (g == 0) {
+      // -l = 14 - lse as an fp16 pair (hi, lo) with hi + lo = -l to ~2^-16
+      const float nlv = valid[tau] ? kAllocShift - lse : -60000.0f;
+      const _Float16 hi = (_Float16)nlv;
+      const _Float16 lo = valid[tau] ? (_Float16)(nlv - (float)hi) : (_Float16)0.0f;
+      half2v pr = {hi, lo};
+      nl[(int64_t)tile * kTile + col] = __builtin_bit_cast(uint32_t, pr);
     }
-    // transpose through LDS: rows of this tile, then [d][32] in accumulator order
-#pragma unroll
-    for (int s = 0; s < C::S; ++s)
-      *reinterpret_cast<half8*>(scratch + col * C::TS + 16 * s + 8 * g) = hreg[tau][s];
-    __syncthreads();
-    if (live) {
-#pragma unroll
-      for (int it = 0; it < D * 4 / 64; ++it) {
-        const int idx = it * 64 + lane;
-        const int dcol = idx >> 2, j = idx & 3;
-        const int kk = j >> 1, gg = j & 1;
-        half8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tk = 16 * kk + 8 * (e >> 2) + 4 * gg + (e & 3);
-          v[e] = scratch[tk * C::TS + dcol];
-        }
-        *reinterpret_cast<half8*>(h16t + ((int64_t)tile * D + dcol) * kTile + 8 * j) = v;
-      }
-    }
-    __syncthreads();
   }
 }
 

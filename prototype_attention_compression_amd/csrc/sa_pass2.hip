@@ -18,21 +18,28 @@
 //          mass += A' pairs (v_dot2 on the rounded values);
 //   GEMM2  U[j, c] += sum_t A'[j,t] h_t[c]                           (fp16 MFMA)
 // The accumulator of GEMM1 holds prototype (lane % 32) and 16 tokens per lane;
-// those registers are exactly the A operand of GEMM2 because the transposed
-// tile stores tokens in the accumulator's row order (pass 1 writes it so), so
-// no data moves between lanes.  The 2^14 scale cancels in U / m.
+// those registers are exactly the A operand of GEMM2, so no data moves
+// between lanes.  GEMM2's B operand (lane = feature column, 8 tokens in the
+// accumulator's row order) comes from the same token rows in LDS through the
+// gfx950 transposing read ds_read_b64_tr_b16: within each group of 16 lanes,
+// destination lane i receives element i % 4 of the 4-element vectors that
+// source lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12 address, so source lane s
+// addresses token (s / 4) of the group's 4 tokens at columns 4 (s % 4) ...
+// The 2^14 scale cancels in U / m.
 //
-// Data movement: tiles reach LDS with direct global->LDS loads (16 B per
-// lane), 4 tiles (128 tokens) per stage, two stages in flight.  LDS rows are
-// XOR-swizzled by 16-byte chunk so each group of 16 lanes of a ds_read_b128
-// hits 16 different 16-byte bank slots (gfx950 LDS: 64 banks of 4 bytes).
+// Data movement: token rows reach LDS with direct global->LDS loads (16 B per
+// lane), 4 tiles (128 tokens) per stage, three stage buffers (loads run two
+// stages ahead).  Rows are XOR-swizzled by 16-byte chunk so that both the
+// 16-byte GEMM1 reads (16 tokens per 16-lane group) and the transposing
+// 8-byte reads (4 tokens x 32 bytes per group) touch 64 distinct banks
+// (gfx950 LDS: 64 banks of 4 bytes).
 // Every user's tile count is a multiple of 4 (pass 1 fills the padding tiles
 // with zero rows and A = 0), so every stage is full and the stage body is one
 // straight-line block.  A workgroup has up to 8 waves of 32 prototypes (two
 // waves per SIMD, every MFMA operand and result in VGPRs), so one wave's
 // exponentials and LDS reads run while the other wave's MFMAs execute.  LDS
-// read traffic is about 1 KB per MFMA, close to what the LDS sustains; the
-// feature step keeps the per-token -l down to 4 bytes per lane.
+// read traffic is about 1 KB per MFMA; the feature step keeps the per-token -l
+// down to 4 bytes per lane.
 //
 // Work item = (chunk of <= tiles_per_chunk tiles of one user, prototype block
 // of waves*32).  Workgroups are numbered so that the prototype blocks of one
@@ -49,37 +56,42 @@ namespace sa {
 namespace {
 
 constexpr int kStageTiles = 4;
+constexpr int kBufs = 3;           // stage buffers: loads run two stages ahead
 
 template <int D>
 struct P2 {
   static constexpr int S = D / 16;                   // MFMA K steps over d
   static constexpr int DT = D / 32;                  // 32-column output blocks
   static constexpr int CPR = D / 8;                  // 16-B chunks per token row
-  static constexpr int ROWSH = (CPR == 16) ? 0 : 1;  // rows sharing a 256-B bank line: 2^ROWSH
-  static constexpr int TILE_BYTES = kTile * D * 2;   // one tile, rows or transposed
+  static constexpr int TILE_BYTES = kTile * D * 2;   // one tile of token rows
   static constexpr int ROWS_BYTES = kStageTiles * TILE_BYTES;
-  static constexpr int NL_OFF = 2 * ROWS_BYTES;      // (-l_hi, -l_lo) pairs of the stage
+  static constexpr int NL_OFF = ROWS_BYTES;          // (-l_hi, -l_lo) pairs of the stage
   static constexpr int STAGE_BYTES = NL_OFF + kStageTiles * kTile * 4;
-  static constexpr int LOADS_ROWS = ROWS_BYTES / 1024;   // 1-KB direct loads per stage, rows
-  static constexpr int LOADS_TR = ROWS_BYTES / 1024;     // and transposed tiles
+  static constexpr int LOADS_ROWS = ROWS_BYTES / 1024;   // 1-KB direct loads per stage
 };
 
-// chunk swizzle of a token row (row index within the stage) and of a
-// transposed-tile row (feature column)
+// 16-byte chunk swizzle of a token row (t = row within the stage): a bit
+// rotation of t mod 16 mixed with bit 1, reduced to the row's chunk count.
+// Conflict-free for both LDS read patterns at d = 64 and d = 128.
 template <int D>
-__device__ __forceinline__ int swz_row(int tok) {
-  return (tok >> P2<D>::ROWSH) & (P2<D>::CPR - 1);
+__device__ __forceinline__ int swz(int t) {
+  const int x = t & 15;
+  return (((x >> 1) | ((x & 1) << 3)) ^ (x & 2)) & (P2<D>::CPR - 1);
 }
-__device__ __forceinline__ int swz_tr(int dcol) { return (dcol >> 2) & 3; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt and lgkmcnt left at their no-wait maxima)
+constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 }  // namespace
 
 template <int D, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   using C = P2<D>;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[kBufs * C::STAGE_BYTES];
 
   const int32_t* hdr = ws_i32(ws, L.off_hdr);
   const int x = blockIdx.x, xcd = x & 7, slot = x >> 3;
@@ -111,12 +123,15 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
                        (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
 
   const char* h16 = reinterpret_cast<const char*>(ws_f16(ws, L.off_h16));
-  const char* h16t = reinterpret_cast<const char*>(ws_f16(ws, L.off_h16t));
   const char* nlg = reinterpret_cast<const char*>(ws_i32(ws, L.off_nl));
 
   // Direct loads of stage `ts` (tiles 4 ts .. 4 ts + 3 of the chunk) into
-  // buffer b.  Load i of the rows part fills LDS bytes [1024 i, 1024 i + 1024)
-  // of the stage: lane l writes chunk slot 64 i + l = (token, swizzled chunk).
+  // buffer b.  Load i fills LDS bytes [1024 i, 1024 i + 1024) of the stage:
+  // lane l writes chunk slot 64 i + l = (token, swizzled chunk).  Every wave
+  // issues the same number of loads per stage (LOADS_ROWS / WAVES rows plus
+  // one slice of the -l pairs), so a vmcnt wait can name a later stage.
+  constexpr int LPW = C::LOADS_ROWS / WAVES + 1;   // loads per wave per stage
+  static_assert(LPW < 64, "vmcnt range");
   auto issue = [&](int ts, int b) {
     char* base = lds + b * C::STAGE_BYTES;
     const int64_t tile0 = (int64_t)t0 + (int64_t)ts * kStageTiles;
@@ -124,23 +139,37 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
     for (int i = wave; i < C::LOADS_ROWS; i += WAVES) {
       const int q = 64 * i + lane;
       const int tok = q / C::CPR, cs = q % C::CPR;
-      const int c = cs ^ swz_row<D>(tok);
+      const int c = cs ^ swz<D>(tok);
       const char* src = h16 + (tile0 * kTile + tok) * (D * 2) + c * 16;
       __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(base + 1024 * i), 16, 0, 0);
     }
-#pragma unroll
-    for (int i = wave; i < C::LOADS_TR; i += WAVES) {
-      const int q = 64 * i + lane;
-      const int tt = q / (C::TILE_BYTES / 16), qq = q % (C::TILE_BYTES / 16);
-      const int dcol = qq >> 2, c = (qq & 3) ^ swz_tr(dcol);
-      const char* src = h16t + (tile0 + tt) * C::TILE_BYTES + dcol * 64 + c * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(base + C::ROWS_BYTES + 1024 * i), 16, 0, 0);
-    }
-    if (wave == WAVES - 1 && lane < 8 * kStageTiles) {
-      const char* src = nlg + tile0 * (kTile * 4) + lane * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(base + C::NL_OFF), 16, 0, 0);
+    constexpr int NL_LANES = kStageTiles * kTile * 4 / 16 / WAVES;   // 16-B pieces per wave
+    if (lane < NL_LANES) {
+      const char* src = nlg + tile0 * (kTile * 4) + (wave * NL_LANES + lane) * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(base + C::NL_OFF + wave * NL_LANES * 16), 16, 0, 0);
     }
   };
+  static_assert(C::LOADS_ROWS % WAVES == 0, "row loads split evenly over waves");
+
+  // per-lane byte offsets of the transposing reads (GEMM2 B operands): for
+  // K step kk, output block dt and token half h (tokens +0 / +8), source lane
+  // s = lane % 16 reads token 16 kk + 8 h + 4 g + s / 4 of the tile, columns
+  // 32 dt + 16 ((lane / 16) % 2) + 4 (s % 4) .. + 3
+  int tr_off[2][2][C::DT];
+  {
+    const int i16 = lane & 15, gh = (lane >> 4) & 1;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const int tok = 16 * kk + 8 * h + 4 * g + (i16 >> 2);
+          const int colm = 32 * dt + 16 * gh + 4 * (i16 & 3);
+          const int chunk = (colm >> 3) ^ swz<D>(tok);
+          tr_off[kk][h][dt] = tok * (D * 2) + chunk * 16 + 8 * (i16 & 1);
+        }
+  }
 
   float16v U[C::DT];
 #pragma unroll
@@ -150,24 +179,27 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
 
   const int nstages = nt / kStageTiles;
   issue(0, 0);
+  if (nstages > 1) issue(1, 1);
   for (int st = 0; st < nstages; ++st) {
-    const int b = st & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of stage st landed
-    __syncthreads();                     // ... every wave's; and stage st-1's buffer is free
-    if (st + 1 < nstages) issue(st + 1, b ^ 1);
+    const int b = st % kBufs;
+    // this wave's loads of stage st have landed (those of st+1 may still fly)
+    if (st + 1 < nstages)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();                             // ... every wave's; stage st-1's buffer is free
+    if (st + 2 < nstages) issue(st + 2, (st + 2) % kBufs);
     const char* base = lds + b * C::STAGE_BYTES;
 #pragma unroll
     for (int t = 0; t < kStageTiles; ++t) {
       const char* rows = base + t * C::TILE_BYTES;
-      const char* tr = base + C::ROWS_BYTES + t * C::TILE_BYTES;
       // GEMM1: C[tok, proto] = h_tok . q_proto - l_tok
       const uint32_t nlp = reinterpret_cast<const uint32_t*>(base + C::NL_OFF)[t * kTile + col];
       const u32x4 fv = {g == 0 ? nlp : 0u, 0u, 0u, 0u};
       float16v Cm = mfma32x32x16(__builtin_bit_cast(half8, fv), qfeat, float16v{});
-      const int tok = t * kTile + col;   // row within the stage
 #pragma unroll
       for (int s = 0; s < C::S; ++s) {
-        const int c = (2 * s + g) ^ swz_row<D>(tok);
+        const int c = (2 * s + g) ^ swz<D>(col);
         const half8 ha = *reinterpret_cast<const half8*>(rows + col * (D * 2) + c * 16);
         Cm = mfma32x32x16(ha, qf[s], Cm);
       }
@@ -188,10 +220,11 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          const int dcol = 32 * dt + col;
-          const int c = (2 * kk + g) ^ swz_tr(dcol);
-          const half8 hb = *reinterpret_cast<const half8*>(tr + dcol * 64 + c * 16);
-          U[dt] = mfma32x32x16(ap[kk], hb, U[dt]);
+          typedef __attribute__((address_space(3))) s16x4* tr_ptr;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(rows + tr_off[kk][0][dt]));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(rows + tr_off[kk][1][dt]));
+          const s16x8 hb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          U[dt] = mfma32x32x16(ap[kk], __builtin_bit_cast(half8, hb), U[dt]);
         }
     }
   }
