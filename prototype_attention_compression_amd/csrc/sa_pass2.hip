@@ -30,9 +30,8 @@
 // Data movement: token rows reach LDS with direct global->LDS loads (16 B per
 // lane), 4 tiles (128 tokens) per stage, three stage buffers (loads run two
 // stages ahead).  Rows are XOR-swizzled by 16-byte chunk so that both the
-// 16-byte GEMM1 reads (16 tokens per 16-lane group) and the transposing
-// 8-byte reads (4 tokens x 32 bytes per group) touch 64 distinct banks
-// (gfx950 LDS: 64 banks of 4 bytes).
+// 16-byte GEMM1 reads and the transposing 8-byte reads touch 64 distinct
+// banks per pass (gfx950 LDS: 64 banks of 4 bytes).
 // Every user's tile count is a multiple of 4 (pass 1 fills the padding tiles
 // with zero rows and A = 0), so every stage is full and the stage body is one
 // straight-line block.  A workgroup has up to 8 waves of 32 prototypes (two
@@ -47,6 +46,8 @@
 // 8 XCDs), letting them share the chunk's tiles through that XCD's L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "sa_device.h"
 #include "sa_launch.h"
@@ -71,12 +72,17 @@ struct P2 {
 };
 
 // 16-byte chunk swizzle of a token row (t = row within the stage): a bit
-// rotation of t mod 16 mixed with bit 1, reduced to the row's chunk count.
-// Conflict-free for both LDS read patterns at d = 64 and d = 128.
+// permutation of t mod 16 (output bits 0..3 take input bits 2, 3, 1, 0),
+// reduced to the row's chunk count.  The 16-byte GEMM1 reads are served 16
+// lanes (16 tokens, one logical chunk) per pass and need distinct swizzles
+// over 16 consecutive tokens; the 8-byte transposing reads are served 32
+// lanes (4 consecutive tokens x 64 bytes) per pass and need the 4 tokens'
+// swizzles to differ in bits 2-3.  This permutation meets both at d = 64 and
+// d = 128.
 template <int D>
 __device__ __forceinline__ int swz(int t) {
   const int x = t & 15;
-  return (((x >> 1) | ((x & 1) << 3)) ^ (x & 2)) & (P2<D>::CPR - 1);
+  return (((x >> 2) & 3) | ((x & 2) << 1) | ((x & 1) << 3)) & (P2<D>::CPR - 1);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -150,25 +156,25 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
     }
   };
   static_assert(C::LOADS_ROWS % WAVES == 0, "row loads split evenly over waves");
+  static_assert(kBufs == 3, "the stage loop below is unrolled over 3 buffers");
 
   // per-lane byte offsets of the transposing reads (GEMM2 B operands): for
-  // K step kk, output block dt and token half h (tokens +0 / +8), source lane
-  // s = lane % 16 reads token 16 kk + 8 h + 4 g + s / 4 of the tile, columns
-  // 32 dt + 16 ((lane / 16) % 2) + 4 (s % 4) .. + 3
-  int tr_off[2][2][C::DT];
+  // output block dt and token half h (tokens +0 / +8), source lane s = lane %
+  // 16 reads token 8 h + 4 g + s / 4 of the tile's first 16 tokens, columns
+  // 32 dt + 16 ((lane / 16) % 2) + 4 (s % 4) .. + 3; K step kk adds 16 tokens
+  // (same swizzle, a constant offset)
+  int tr_off[2][C::DT];
   {
     const int i16 = lane & 15, gh = (lane >> 4) & 1;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) {
-          const int tok = 16 * kk + 8 * h + 4 * g + (i16 >> 2);
-          const int colm = 32 * dt + 16 * gh + 4 * (i16 & 3);
-          const int chunk = (colm >> 3) ^ swz<D>(tok);
-          tr_off[kk][h][dt] = tok * (D * 2) + chunk * 16 + 8 * (i16 & 1);
-        }
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const int tok = 8 * h + 4 * g + (i16 >> 2);
+        const int colm = 32 * dt + 16 * gh + 4 * (i16 & 3);
+        const int chunk = (colm >> 3) ^ swz<D>(tok);
+        tr_off[h][dt] = tok * (D * 2) + chunk * 16 + 8 * (i16 & 1);
+      }
   }
 
   float16v U[C::DT];
@@ -177,34 +183,40 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   float msum = 0.f;
   const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
 
+  // per-lane byte offsets of the GEMM1 operand reads (token row `col`,
+  // swizzled chunk 2 s + g) within a tile
+  int ha_off[C::S];
+#pragma unroll
+  for (int s = 0; s < C::S; ++s) ha_off[s] = col * (D * 2) + (((2 * s + g) ^ swz<D>(col)) * 16);
+
+  // One stage held in buffer B (a compile-time constant, so every LDS read is
+  // a per-lane offset register plus an immediate).
   const int nstages = nt / kStageTiles;
-  issue(0, 0);
-  if (nstages > 1) issue(1, 1);
-  for (int st = 0; st < nstages; ++st) {
-    const int b = st % kBufs;
+  auto stage = [&](int st, auto Bc) {
+    constexpr int B = decltype(Bc)::value;
     // this wave's loads of stage st have landed (those of st+1 may still fly)
     if (st + 1 < nstages)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
     else
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();                             // ... every wave's; stage st-1's buffer is free
-    if (st + 2 < nstages) issue(st + 2, (st + 2) % kBufs);
-    const char* base = lds + b * C::STAGE_BYTES;
-#pragma unroll
-    for (int t = 0; t < kStageTiles; ++t) {
+    if (st + 2 < nstages) issue(st + 2, (B + 2) % kBufs);
+    const char* base = lds + B * C::STAGE_BYTES;
+    typedef __attribute__((address_space(3))) s16x4* tr_ptr;
+    // GEMM1 of tile t: C[tok, proto] = h_tok . q_proto - l_tok
+    auto gemm1 = [&](int t, float16v& Cm) {
       const char* rows = base + t * C::TILE_BYTES;
-      // GEMM1: C[tok, proto] = h_tok . q_proto - l_tok
       const uint32_t nlp = reinterpret_cast<const uint32_t*>(base + C::NL_OFF)[t * kTile + col];
-      const u32x4 fv = {g == 0 ? nlp : 0u, 0u, 0u, 0u};
-      float16v Cm = mfma32x32x16(__builtin_bit_cast(half8, fv), qfeat, float16v{});
+      half8 ha[C::S];
 #pragma unroll
-      for (int s = 0; s < C::S; ++s) {
-        const int c = (2 * s + g) ^ swz<D>(col);
-        const half8 ha = *reinterpret_cast<const half8*>(rows + col * (D * 2) + c * 16);
-        Cm = mfma32x32x16(ha, qf[s], Cm);
-      }
-      // allocations 2^C (= 2^14 A) in fp16, masses of the rounded values
-      half8 ap[2];
+      for (int s = 0; s < C::S; ++s) ha[s] = *reinterpret_cast<const half8*>(rows + ha_off[s]);
+      const u32x4 fv = {g == 0 ? nlp : 0u, 0u, 0u, 0u};
+      Cm = mfma32x32x16(__builtin_bit_cast(half8, fv), qfeat, float16v{});
+#pragma unroll
+      for (int s = 0; s < C::S; ++s) Cm = mfma32x32x16(ha[s], qf[s], Cm);
+    };
+    // allocations 2^C (= 2^14 A) in fp16, masses of the rounded values
+    auto expo = [&](const float16v& Cm, half8 (&ap)[2]) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -215,18 +227,53 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
           ap[kk][e] = h[0];
           ap[kk][e + 1] = h[1];
         }
-      // GEMM2: U[proto, c] += sum_tok A'[proto, tok] h_tok[c]
+    };
+    // GEMM2 of tile t: U[proto, c] += sum_tok A'[proto, tok] h_tok[c]
+    auto gemm2 = [&](int t, const half8 (&ap)[2]) {
+      const char* rows = base + t * C::TILE_BYTES;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          typedef __attribute__((address_space(3))) s16x4* tr_ptr;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(rows + tr_off[kk][0][dt]));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(rows + tr_off[kk][1][dt]));
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(rows + kk * 16 * (D * 2) + tr_off[0][dt]));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(rows + kk * 16 * (D * 2) + tr_off[1][dt]));
           const s16x8 hb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           U[dt] = mfma32x32x16(ap[kk], __builtin_bit_cast(half8, hb), U[dt]);
         }
+    };
+    // Pipeline within the stage: GEMM1 of tile t+1 is issued interleaved
+    // with the exponentials of tile t (independent work), then GEMM2 of t.
+    float16v Ca, Cb;
+    half8 ap[2];
+    __builtin_amdgcn_sched_barrier(0);
+    gemm1(0, Ca);
+#pragma unroll
+    for (int t = 0; t < kStageTiles; ++t) {
+      float16v& Cx = (t & 1) ? Cb : Ca;
+      float16v& Cy = (t & 1) ? Ca : Cb;
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < kStageTiles) {
+        gemm1(t + 1, Cy);
+        expo(Cx, ap);
+        __builtin_amdgcn_sched_group_barrier(0x100, C::S + 1, 0);   // GEMM1 LDS reads
+#pragma unroll
+        for (int i = 0; i < C::S + 1; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);        // 4 VALU
+        }
+      } else {
+        expo(Cx, ap);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      gemm2(t, ap);
     }
+  };
+  issue(0, 0);
+  if (nstages > 1) issue(1, 1);
+  for (int st = 0; st < nstages; st += kBufs) {
+    stage(st, std::integral_constant<int, 0>{});
+    if (st + 1 < nstages) stage(st + 1, std::integral_constant<int, 1>{});
+    if (st + 2 < nstages) stage(st + 2, std::integral_constant<int, 2>{});
   }
 
   float* part_u = ws_f32(ws, L.off_part_u) + (int64_t)chunk * L.k * D;
