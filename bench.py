@@ -37,10 +37,27 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "history tokens/s + TFLOP/s (%bf16 MFMA peak), SA n=100K,k=1024,d=128"
 DEFAULT_WORKLOAD = "c3lit_r40_n100k_d128_k1024"
 
-# measured by rocprofv3 --pmc on the pass-2 kernel of the default workload, in
-# KiB per dispatch, each scaled by the factor a plain copy kernel of known
-# size reads for the same counter (see profiles/); None until measured
-PASS2_TRAFFIC_BYTES = None
+# HBM bytes per pass-2 launch on the default workload: rocprofv3 --pmc
+# FETCH_SIZE + WRITE_SIZE (KiB per dispatch), each scaled by what the same
+# counter reads for a plain device copy of known size (--calibrate-copy).
+# Valid only for the kernel source it was measured on: the digest of the
+# pass-2 sources is recorded beside it and the figure is reported as null
+# once they differ.
+PASS2_TRAFFIC_BYTES = 1351407001      # 1.0766e9 fetched + 0.2748e9 written
+PASS2_TRAFFIC_SOURCES_SHA256 = "43df0bab28ce2e7ebf5c07263adafe70fce3d757a4114e91faa979c67d83a8fc"
+PASS2_SOURCES = ("sa_pass2.hip", "sa_layout.h", "sa_device.h")
+COPY_CALIBRATION_BYTES = 1 << 30
+
+
+def pass2_sources_digest() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "prototype_attention_compression_amd", "csrc")
+    for name in PASS2_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 class _Hip:
@@ -127,6 +144,8 @@ def main(argv=None):
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, copy 1 GiB device-to-device once (counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -197,7 +216,7 @@ def main(argv=None):
         "peak": PEAK_MFMA_F16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": p2_achieved / PEAK_MFMA_F16_TFLOPS,
-        "traffic": PASS2_TRAFFIC_BYTES,
+        "traffic": PASS2_TRAFFIC_BYTES if PASS2_TRAFFIC_SOURCES_SHA256 == pass2_sources_digest() else None,
         "per_launch_flop": algo_flop,
         "avg_launch_ms": phase_ms["pass2_accum"],
     }
@@ -222,6 +241,13 @@ def main(argv=None):
         "wall_s_timed": t_wall,
         "roofline": roofline,
     }
+    if args.calibrate_copy:
+        src = torch.ones(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, S.cpu().numpy(), args.cpu_budget)
     print(json.dumps(out), flush=True)
