@@ -144,6 +144,8 @@ def main(argv=None):
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=["auto", "one", "two"], default="auto",
+                    help="kernel path: the library's choice, the one-pass or the two-pass kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device once (counter calibration)")
     args = ap.parse_args(argv)
@@ -178,7 +180,7 @@ def main(argv=None):
 
     def step(events=None):
         sa.compress(H, off, Wk, Wv, P, mask=mask, return_mass=True, out=S, mass_out=m,
-                    workspace=ws, events=events)
+                    workspace=ws, events=events, path=args.path)
 
     for _ in range(args.warmup):
         step()

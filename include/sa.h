@@ -72,8 +72,24 @@ typedef struct {
   int32_t d;
   int32_t k;
   int32_t dtype;
-  int32_t reserved;      /* must be 0 */
+  int32_t flags;         /* 0, or one of the SA_FLAG_* path requests */
 } sa_problem;
+
+/*
+ * Path requests (sa_problem.flags; results agree within rounding either way).
+ * For bf16 inputs with k = 256 * 2^i (i = 0..4) the library can run the
+ * one-pass kernel: groups of k / 256 co-resident workgroups exchange
+ * per-token partial softmax denominators, so every logit is computed once.
+ * Otherwise, or when the batch is fragmented into many short users, it runs
+ * two passes (per-token logsumexp, then allocations and sums), computing every
+ * logit twice.  0 lets the library choose.  Setting both flags is
+ * SA_E_INVALID.
+ *   SA_FLAG_TWO_PASS  always run the two-pass kernels.
+ *   SA_FLAG_ONE_PASS  run the one-pass kernel whenever the shape and device
+ *                     allow it, whatever the batch looks like.
+ */
+#define SA_FLAG_TWO_PASS 1
+#define SA_FLAG_ONE_PASS 2
 
 /*
  * Workspace size for `problem`.  Writes the byte count to *bytes.  Returns
@@ -127,9 +143,12 @@ sa_status sa_compress(const sa_problem* problem,
  * sa_compress, recording caller-created HIP events (hipEvent_t handles) on
  * `stream` at the phase boundaries, for timing with hipEventElapsedTime:
  *   events[0] before the query/schedule preparation,
- *   events[1] after it (start of pass 1: per-token logsumexp),
- *   events[2] after pass 1 (start of pass 2: allocations and sums),
- *   events[3] after pass 2 (start of the normalise / value-projection step),
+ *   events[1] after it (start of the token pass: the per-token logsumexp of
+ *             the two-pass path, or the fp16 packing of the one-pass path),
+ *   events[2] after the token pass (start of the accumulation: allocations
+ *             and sums),
+ *   events[3] after the accumulation (start of the normalise /
+ *             value-projection step),
  *   events[4] after the last kernel.
  * `events` may be NULL (then this is sa_compress).  A phase with no work
  * (e.g. N = 0) records its two events back to back.  Same arguments, errors
@@ -149,10 +168,15 @@ sa_status sa_compress_with_events(const sa_problem* problem,
                                   void* stream,
                                   void* const* events);
 
+/* Device error flag bits. */
+#define SA_DEVICE_ERR_OFFSETS 1   /* offsets broke their contract: all users empty */
+#define SA_DEVICE_ERR_EXCHANGE 2  /* one-pass: a bounded wait between workgroups
+                                     expired; the sketches of that call are invalid */
+
 /*
- * Synchronously read the device error flag that the last sa_compress on
- * `workspace` set (0 = none, 1 = offsets broke their contract).  Waits for
- * `stream`.  Returns SA_E_HIP if the copy fails.
+ * Synchronously read the device error flags that the last sa_compress on
+ * `workspace` set (0 = none, else a combination of SA_DEVICE_ERR_*).  Waits
+ * for `stream`.  Returns SA_E_HIP if the copy fails.
  */
 sa_status sa_read_device_error(const void* workspace, void* stream, int32_t* flag);
 

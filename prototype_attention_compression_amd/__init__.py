@@ -5,11 +5,15 @@ include/sa.h); this package is its thin Python binding.
 """
 from ._lib import (  # noqa: F401
     SA_BF16,
+    SA_DEVICE_ERR_EXCHANGE,
+    SA_DEVICE_ERR_OFFSETS,
     SA_E_HIP,
     SA_E_INVALID,
     SA_E_UNSUPPORTED,
     SA_E_WORKSPACE,
     SA_F32,
+    SA_FLAG_ONE_PASS,
+    SA_FLAG_TWO_PASS,
     SA_OK,
     SaError,
     compress,
@@ -23,5 +27,6 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "compress", "load", "read_device_error", "status_string", "version", "workspace_size",
     "SaError", "SA_OK", "SA_E_INVALID", "SA_E_UNSUPPORTED", "SA_E_WORKSPACE", "SA_E_HIP",
-    "SA_BF16", "SA_F32",
+    "SA_BF16", "SA_F32", "SA_FLAG_ONE_PASS", "SA_FLAG_TWO_PASS", "SA_DEVICE_ERR_OFFSETS",
+    "SA_DEVICE_ERR_EXCHANGE",
 ]

@@ -14,6 +14,9 @@ LIB_PATH = os.path.join(_PKG, "libsa.so")
 
 SA_OK, SA_E_INVALID, SA_E_UNSUPPORTED, SA_E_WORKSPACE, SA_E_HIP = range(5)
 SA_BF16, SA_F32 = 0, 1
+SA_FLAG_TWO_PASS, SA_FLAG_ONE_PASS = 1, 2
+SA_DEVICE_ERR_OFFSETS, SA_DEVICE_ERR_EXCHANGE = 1, 2
+_PATH_FLAGS = {None: 0, "auto": 0, "two": SA_FLAG_TWO_PASS, "one": SA_FLAG_ONE_PASS}
 
 # functions declared in include/sa.h
 EXPORTS = ("sa_workspace_size", "sa_compress", "sa_compress_with_events",
@@ -28,7 +31,7 @@ class SaProblem(ctypes.Structure):
         ("d", ctypes.c_int32),
         ("k", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -86,8 +89,8 @@ def version() -> str:
     return load().sa_version().decode()
 
 
-def problem(num_users: int, total_tokens: int, d: int, k: int, dtype: int) -> SaProblem:
-    return SaProblem(int(num_users), int(total_tokens), int(d), int(k), int(dtype), 0)
+def problem(num_users: int, total_tokens: int, d: int, k: int, dtype: int, flags: int = 0) -> SaProblem:
+    return SaProblem(int(num_users), int(total_tokens), int(d), int(k), int(dtype), int(flags))
 
 
 def workspace_size(num_users: int, total_tokens: int, d: int, k: int, dtype: int = SA_BF16) -> int:
@@ -119,13 +122,15 @@ def _ptr(t):
 
 
 def compress(H, offsets, Wk, Wv, P, mask=None, return_mass: bool = False,
-             out=None, mass_out=None, workspace=None, events=None):
+             out=None, mass_out=None, workspace=None, events=None, path: Optional[str] = None):
     """Sketches of a packed ragged batch, computed by libsa on the GPU.
 
     H [N, d], Wk/Wv [d, d], P [k, d]: torch tensors on the current ROCm device,
     all bfloat16 or all float32, contiguous.  offsets [R+1] int64 (device).
     mask [N] uint8/bool or None.  Returns S [R, k, d] float32 (and the masses
-    [R, k] if ``return_mass``).  Runs on torch's current stream.
+    [R, k] if ``return_mass``).  Runs on torch's current stream.  ``path``:
+    None/"auto" (library's choice), "one" or "two" (SA_FLAG_ONE_PASS /
+    SA_FLAG_TWO_PASS).
     """
     import torch
 
@@ -159,8 +164,10 @@ def compress(H, offsets, Wk, Wv, P, mask=None, return_mass: bool = False,
             mask = mask.view(torch.uint8)
         if mask.dtype != torch.uint8 or mask.shape != (N,) or not mask.is_cuda or not mask.is_contiguous():
             raise ValueError("mask must be a contiguous [N] uint8/bool GPU tensor")
+    if path not in _PATH_FLAGS:
+        raise ValueError(f"path must be one of {sorted(k for k in _PATH_FLAGS if k)} or None")
     dev = H.device
-    pb = problem(R, N, d, k, dt)
+    pb = problem(R, N, d, k, dt, _PATH_FLAGS[path])
     wbytes = workspace_size(R, N, d, k, dt)
     if workspace is None or workspace.numel() * workspace.element_size() < wbytes:
         workspace = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)

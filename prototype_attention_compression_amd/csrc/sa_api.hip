@@ -5,6 +5,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "sa.h"
 #include "sa_launch.h"
 #include "sa_layout.h"
@@ -20,8 +23,9 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 sa_status check_problem(const sa_problem* p) {
   if (p == nullptr) return SA_E_INVALID;
-  if (p->num_users < 0 || p->total_tokens < 0 || p->d <= 0 || p->k <= 0 || p->reserved != 0)
-    return SA_E_INVALID;
+  if (p->num_users < 0 || p->total_tokens < 0 || p->d <= 0 || p->k <= 0) return SA_E_INVALID;
+  if ((p->flags & ~(SA_FLAG_TWO_PASS | SA_FLAG_ONE_PASS)) != 0) return SA_E_INVALID;
+  if ((p->flags & SA_FLAG_TWO_PASS) && (p->flags & SA_FLAG_ONE_PASS)) return SA_E_INVALID;
   if (p->dtype != SA_BF16 && p->dtype != SA_F32) return SA_E_INVALID;
   if (p->d != 64 && p->d != 128) return SA_E_UNSUPPORTED;
   if (p->k % 64 != 0 || p->k > 4096) return SA_E_UNSUPPORTED;
@@ -63,6 +67,15 @@ Layout make_layout(const sa_problem& p) {
   L.tiles_per_chunk = pick_tiles_per_chunk(tiles_max, L.n_pblocks, f32);
   // sum_u ceil(t_u / CT) <= (tiles + (CT - 1) R) / CT
   L.chunks_max = (int32_t)((tiles_max + (int64_t)(L.tiles_per_chunk - 1) * p.num_users) / L.tiles_per_chunk);
+  // the one-pass path: sized whenever its shape is built, used per call
+  L.fused = 0;
+  L.groups = 0;
+  int64_t parts = L.chunks_max;
+  if (fused_shape_ok(L)) {
+    L.groups = kFusedWGs / (p.k / kFusedProtos);
+    parts = std::max<int64_t>(parts, (int64_t)L.groups + p.num_users);
+  }
+  L.parts_max = (int32_t)parts;
   const size_t R1 = (size_t)p.num_users + 1;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -78,14 +91,42 @@ Layout make_layout(const sa_problem& p) {
     L.off_qnorm = take((size_t)p.k * sizeof(float));
     L.off_h16 = take((size_t)tiles_max * kTile * p.d * 2);
     L.off_nl = take((size_t)tiles_max * kTile * sizeof(uint32_t));
+    if (L.groups > 0) L.off_xbuf = take((size_t)L.groups * kXSlots * kTile * (p.k / kFusedProtos) * sizeof(uint64_t));
   } else {
     L.off_q32 = take((size_t)p.k * p.d * sizeof(float));
     L.off_lse32 = take((size_t)tiles_max * kTile * sizeof(float));
   }
-  L.off_part_u = take((size_t)L.chunks_max * p.k * p.d * sizeof(float));
-  L.off_part_m = take((size_t)L.chunks_max * p.k * sizeof(float));
+  L.off_part_u = take((size_t)L.parts_max * p.k * p.d * sizeof(float));
+  L.off_part_m = take((size_t)L.parts_max * p.k * sizeof(float));
   L.total = off;
   return L;
+}
+
+// Whether the one-pass cooperative grid fits `device`, asked once per device.
+bool device_fits_fused(const Layout& L) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev][5];   // per P index: 0 unknown, 1 no, 2 yes
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return false;
+  int pi = 0;
+  for (int P = L.k / kFusedProtos; P > 1; P >>= 1) ++pi;
+  if (pi > 4) return false;
+  int v = cache[dev][pi].load(std::memory_order_relaxed);
+  if (v == 0) {
+    v = fused_fits_device(L, dev) ? 2 : 1;
+    cache[dev][pi].store(v, std::memory_order_relaxed);
+  }
+  return v == 2;
+}
+
+// One-pass unless the shape or device rules it out, the caller asks for two
+// passes, or (no request either way) the batch is so fragmented that the
+// per-segment pipeline start of the one-pass kernel would dominate: fewer
+// than 8 tiles per (group, user) segment on average.
+bool use_fused(const sa_problem& p, const Layout& L) {
+  if (L.groups == 0 || (p.flags & SA_FLAG_TWO_PASS)) return false;
+  if (!(p.flags & SA_FLAG_ONE_PASS) && (int64_t)L.tiles_max < 8 * ((int64_t)L.groups + p.num_users)) return false;
+  return device_fits_fused(L);
 }
 
 }  // namespace
@@ -120,17 +161,22 @@ sa_status sa_compress_with_events(const sa_problem* problem, const void* H, cons
     if (offsets == nullptr || Wk == nullptr || Wv == nullptr || P == nullptr || S == nullptr)
       return SA_E_INVALID;
     if (p.total_tokens > 0 && H == nullptr) return SA_E_INVALID;
-    const sa::Layout L = sa::make_layout(p);
+    sa::Layout L = sa::make_layout(p);
     if (workspace == nullptr || workspace_bytes < L.total) return SA_E_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % sa::kAlign != 0) return SA_E_INVALID;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     auto mark = [&](int i) {
       return events == nullptr || hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s) == hipSuccess;
     };
+    if (p.dtype == SA_BF16 && p.total_tokens > 0) L.fused = sa::use_fused(p, L) ? 1 : 0;
     if (!mark(0)) return SA_E_HIP;
     if (sa::launch_prep(L, P, Wk, offsets, workspace, s) != hipSuccess) return SA_E_HIP;
     if (!mark(1)) return SA_E_HIP;
-    if (p.dtype == SA_BF16) {
+    if (L.fused) {
+      if (sa::launch_pack(L, H, offsets, token_mask, workspace, s) != hipSuccess) return SA_E_HIP;
+      if (!mark(2)) return SA_E_HIP;
+      if (sa::launch_fused(L, workspace, s) != hipSuccess) return SA_E_HIP;
+    } else if (p.dtype == SA_BF16) {
       if (p.total_tokens > 0 && sa::launch_pass1(L, H, offsets, token_mask, workspace, s) != hipSuccess)
         return SA_E_HIP;
       if (!mark(2)) return SA_E_HIP;

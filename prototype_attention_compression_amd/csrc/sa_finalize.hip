@@ -1,8 +1,8 @@
 // sa_finalize.hip — chunk reduction and prototype-wise normalisation.
 //
-// For user u and a block of 32 prototypes, sums the per-chunk partials
-// U_c[j, :] = sum_t A[j,t] h_t and m_c[j] over the user's chunks in chunk
-// order (a fixed order: the result is bitwise repeatable), then writes
+// For user u and a block of 32 prototypes, sums the partials
+// U_c[j, :] = sum_t A[j,t] h_t and m_c[j] over the user's partial slots in
+// slot order (a fixed order: the result is bitwise repeatable), then writes
 //     S_u[j, :] = (U[j, :] / m_j) Wv,   mass[u, j] = m_j
 // i.e. the mass-normalised allocation-weighted mean of the value rows
 // v_t = h_t Wv (SequenceO1 blog "How it works" item 1: the k x d sketch of
@@ -41,8 +41,25 @@ __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout
   const int u = blockIdx.x / nrb, rb = blockIdx.x % nrb;
   const int j0 = rb * kFinRows;
   const int tid = threadIdx.x;
-  const int32_t* chunk_base = ws_i32(ws, L.off_chunk_base);
-  const int c0 = chunk_base[u], c1 = chunk_base[u + 1];
+  // the user's partial-sum slots: chunks c0 .. c1-1 (two-pass path), or
+  // group + u for the groups g0 .. g1-1 whose tile ranges meet the user's
+  // (one-pass path)
+  int c0, c1;
+  if (!L.fused) {
+    const int32_t* chunk_base = ws_i32(ws, L.off_chunk_base);
+    c0 = chunk_base[u];
+    c1 = chunk_base[u + 1];
+  } else {
+    const int32_t* tile_base = ws_i32(ws, L.off_tile_base);
+    const int32_t nt = ws_i32(ws, L.off_hdr)[kHdrTiles];
+    const int32_t Tg = (nt + 4 * L.groups - 1) / (4 * L.groups) * 4;
+    const int32_t t0 = tile_base[u], t1 = tile_base[u + 1];
+    c0 = c1 = 0;
+    if (t1 > t0) {
+      c0 = t0 / Tg + u;
+      c1 = (t1 - 1) / Tg + 1 + u;
+    }
+  }
   const float* part_u = ws_f32(ws, L.off_part_u);
   const float* part_m = ws_f32(ws, L.off_part_m);
 

@@ -20,7 +20,15 @@ hipError_t launch_pass2(const Layout& L, void* ws, hipStream_t stream);
 // fp32 path, both passes
 hipError_t launch_f32(const Layout& L, const void* H, const int64_t* offsets, const uint8_t* mask, void* ws,
                       hipStream_t stream);
-// chunk reduction, prototype-wise normalisation and the value projection
+// one-pass path: fp16 token rows, keep words and the largest row norm
+hipError_t launch_pack(const Layout& L, const void* H, const int64_t* offsets, const uint8_t* mask, void* ws,
+                       hipStream_t stream);
+// one-pass path: shapes it is built for; whether the device holds its
+// cooperative grid; the cooperative launch itself
+bool fused_shape_ok(const Layout& L);
+bool fused_fits_device(const Layout& L, int device);
+hipError_t launch_fused(const Layout& L, void* ws, hipStream_t stream);
+// partial-sum reduction, prototype-wise normalisation and the value projection
 hipError_t launch_finalize(const Layout& L, const void* Wv, void* ws, float* S, float* mass,
                            hipStream_t stream);
 

@@ -3,12 +3,21 @@
 //
 // Work units.  Every user's history is cut into TILEs of 32 tokens; the tile
 // count of a user is rounded up to a multiple of kUserTileAlign (the trailing
-// tiles hold padding rows, which carry zero allocation).  Pass 1 (per-token logsumexp over prototypes)
-// runs over tiles; pass 2 (allocation + accumulation) runs over CHUNKs of up
-// to `tiles_per_chunk` consecutive tiles of one user, times prototype blocks.
-// Tiles and chunks are numbered user by user; tile_base[u] / chunk_base[u]
-// (exclusive prefix sums, written on the device from `offsets`) map a global
-// tile or chunk index back to its user by binary search.
+// tiles hold padding rows, which carry zero allocation).  Tiles are numbered
+// user by user; tile_base[u] (exclusive prefix sums, written on the device
+// from `offsets`) maps a global tile index back to its user by binary search.
+//
+// Two paths share the workspace:
+//   * two-pass: pass 1 (per-token logsumexp over prototypes) runs over tiles;
+//     pass 2 (allocation + accumulation) runs over CHUNKs of up to
+//     `tiles_per_chunk` consecutive tiles of one user, times prototype blocks
+//     (chunk_base[u] numbers them user by user); partial sums per chunk.
+//   * one-pass: a packing kernel writes the fp16 token rows; then GROUPS of
+//     n_pblocks co-resident workgroups (one per 256-prototype block) each walk
+//     an equal contiguous range of tiles, exchanging per-token partial
+//     softmax denominators; partial sums per (group, user) pair, stored at
+//     index group + user (unique for overlapping pairs: both ranges are
+//     contiguous and increasing, so along the overlaps group + user rises).
 #pragma once
 
 #include <stddef.h>
@@ -24,9 +33,13 @@ constexpr int kQChunk = 64;          // prototypes per pass-1 LDS chunk
 constexpr int kFinRows = 32;         // prototypes per finalize workgroup
 constexpr float kAllocShift = 14.0f; // fp16 allocations carry a 2^14 scale
 constexpr int kF32ChunkTiles = 8;    // tiles per chunk on the fp32 path
+constexpr int kFusedProtos = 256;    // prototypes per one-pass workgroup (8 waves x 32)
+constexpr int kFusedWGs = 256;       // one-pass grid: groups x n_pblocks workgroups
+constexpr int kXSlots = 8;           // ring slots of the one-pass exchange
 
-// Device error flags (workspace header word 0).
+// Device error flags (workspace header word 0, bitwise or).
 constexpr int32_t kErrBadOffsets = 1;
+constexpr int32_t kErrExchange = 2;  // a bounded wait between workgroups expired
 
 struct Layout {
   // problem
@@ -40,6 +53,10 @@ struct Layout {
   int32_t tiles_per_chunk;
   int32_t tiles_max;       // bound on sum_u tiles_u
   int32_t chunks_max;      // bound on sum_u ceil(tiles_u / tiles_per_chunk)
+  int32_t fused;           // 1: the one-pass path is built for this shape
+  int32_t groups;          // one-pass groups (kFusedWGs / n_pblocks)
+  int32_t parts_max;       // partial-sum slots: max(chunks_max, groups + R)
+  int32_t pad_;
   // byte offsets into the workspace (all 256-aligned)
   size_t off_hdr;          // [64] int32: error flag, qmax (float), totals
   size_t off_tile_base;    // [R+1] int32
@@ -47,12 +64,14 @@ struct Layout {
   size_t off_q16;          // [k, d] fp16    queries
   size_t off_qnorm;        // [k] float      |q_j| of the fp16 queries
   size_t off_h16;          // [tiles_max, 32, d] fp16    token rows
-  size_t off_nl;           // [tiles_max, 32] fp16 pairs (-l_hi, -l_lo), l = lse_t - 14;
-                           //   (-60000, 0) if the token is dropped
+  size_t off_nl;           // [tiles_max, 32] uint32 per token.  Two-pass: fp16 pairs
+                           //   (-l_hi, -l_lo), l = lse_t - 14, (-60000, 0) if dropped.
+                           //   One-pass: 1 if the token takes part, else 0.
+  size_t off_xbuf;         // [groups, kXSlots, 32, n_pblocks] uint64 exchange words
   size_t off_q32;          // [k, d] float   queries, fp32 path
   size_t off_lse32;        // [tiles_max*32] float, fp32 path
-  size_t off_part_u;       // [chunks_max, k, d] float  per-chunk sums of A h
-  size_t off_part_m;       // [chunks_max, k] float     per-chunk masses
+  size_t off_part_u;       // [parts_max, k, d] float  partial sums of A h
+  size_t off_part_m;       // [parts_max, k] float     partial masses
   size_t total;
 };
 
@@ -61,5 +80,6 @@ constexpr int kHdrErr = 0;
 constexpr int kHdrQmax = 1;      // float bits
 constexpr int kHdrTiles = 2;     // total tiles
 constexpr int kHdrChunks = 3;    // total chunks
+constexpr int kHdrHmax = 4;      // float bits: largest |h_t| of a kept token (one-pass)
 
 }  // namespace sa

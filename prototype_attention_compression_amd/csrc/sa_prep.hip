@@ -122,6 +122,7 @@ __global__ __launch_bounds__(1024) void prep_schedule(const int64_t* __restrict_
     hdr[kHdrErr] = bad ? kErrBadOffsets : 0;
     hdr[kHdrTiles] = sc_t[1023];
     hdr[kHdrChunks] = sc_c[1023];
+    hdr[kHdrHmax] = 0;
   }
   if (L.dtype == 0) {
     float m = 0.f;
@@ -137,6 +138,13 @@ __global__ __launch_bounds__(1024) void prep_schedule(const int64_t* __restrict_
   } else if (tid == 0) {
     hdr[kHdrQmax] = 0;
   }
+}
+
+// Zero fill of the one-pass exchange ring (its tags must not match a tile of
+// this call).  A kernel rather than a memset so that the sequence can be
+// captured in a graph.
+__global__ __launch_bounds__(256) void clear_words(uint64_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0ull;
 }
 
 hipError_t launch_prep(const Layout& L, const void* P, const void* Wk, const int64_t* offsets, void* ws,
@@ -159,6 +167,11 @@ hipError_t launch_prep(const Layout& L, const void* P, const void* Wk, const int
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(prep_schedule, dim3(1), dim3(1024), 0, stream, offsets, L, ws);
+  e = hipGetLastError();
+  if (e != hipSuccess || !L.fused) return e;
+  const int64_t words = (int64_t)L.groups * kXSlots * kTile * (L.k / kFusedProtos);
+  hipLaunchKernelGGL(clear_words, dim3(64), dim3(256), 0, stream,
+                     reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + L.off_xbuf), words);
   return hipGetLastError();
 }
 

@@ -34,8 +34,8 @@ def test_version_and_status_strings():
     assert sa.status_string(99) == "unknown sa_status"
 
 
-def _ws(R, N, d, k, dt, reserved=0):
-    pb = _lib.SaProblem(R, N, d, k, dt, reserved)
+def _ws(R, N, d, k, dt, flags=0):
+    pb = _lib.SaProblem(R, N, d, k, dt, flags)
     out = ctypes.c_size_t(0)
     st = _lib.load().sa_workspace_size(ctypes.byref(pb), ctypes.byref(out))
     return st, out.value
@@ -56,8 +56,13 @@ def test_workspace_size_rejects(args, code):
     assert _ws(*args)[0] == code
 
 
-def test_workspace_size_reserved_and_null():
-    assert _ws(1, 10, 128, 1024, 0, reserved=1)[0] == sa.SA_E_INVALID
+def test_workspace_size_flags_and_null():
+    assert _ws(1, 10, 128, 1024, 0, flags=4)[0] == sa.SA_E_INVALID
+    assert _ws(1, 10, 128, 1024, 0, flags=sa.SA_FLAG_ONE_PASS | sa.SA_FLAG_TWO_PASS)[0] == sa.SA_E_INVALID
+    base = _ws(1, 10, 128, 1024, 0)
+    assert base[0] == sa.SA_OK
+    for f in (sa.SA_FLAG_ONE_PASS, sa.SA_FLAG_TWO_PASS):
+        assert _ws(1, 10, 128, 1024, 0, flags=f) == base   # one workspace serves both paths
     pb = _lib.problem(1, 10, 128, 1024, 0)
     assert _lib.load().sa_workspace_size(ctypes.byref(pb), None) == sa.SA_E_INVALID
     assert _lib.load().sa_workspace_size(None, ctypes.byref(ctypes.c_size_t())) == sa.SA_E_INVALID

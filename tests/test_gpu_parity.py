@@ -2,7 +2,10 @@
 inputs.  Bar: bf16 inputs max_rel <= 2e-2 and mean_rel <= 2e-3, fp32 inputs
 <= 1e-4 (normwise over all compared sketch elements); masses to the same
 bar.  Full-size workloads compare a sample of users (the oracle computes one
-user at a time) in the very launch configuration the bench times."""
+user at a time) in the very launch configuration the bench times (the
+library's own path choice), and again with each path forced: "one" (the
+one-pass kernel with the cross-workgroup exchange; for shapes it is not built
+for the library runs two passes) and "two" (two passes)."""
 import numpy as np
 import pytest
 
@@ -16,10 +19,11 @@ SMALL = ["c1_fp32_n4096_d64_k64", "small_ragged_d128_k256", "small_ragged_d128_k
          "small_ragged_d64_k128", "small_mask_d128_k512", "small_fp32_ragged_d128_k192"]
 
 
-def _check(inp, users=None):
+def _check(inp, users=None, path=None):
     dev = upload(inp)
-    print(f"[case] {inp.name} R={inp.R} N={inp.N} k={inp.k} d={inp.d} dtype={inp.dtype} users={users}", flush=True)
-    S, m = run(dev)
+    print(f"[case] {inp.name} R={inp.R} N={inp.N} k={inp.k} d={inp.d} dtype={inp.dtype} users={users} "
+          f"path={path}", flush=True)
+    S, m = run(dev, path=path)
     S = S.cpu().numpy()
     m = m.cpu().numpy()
     Sref, mref = sketch_batch(inp.H, inp.offsets, inp.Wk, inp.Wv, inp.P, mask=inp.mask, users=users)
@@ -38,9 +42,20 @@ def _check(inp, users=None):
     return S, m
 
 
+@pytest.mark.parametrize("path", ["one", "two"])
 @pytest.mark.parametrize("name", SMALL)
-def test_parity_small(name):
-    _check(make_config(name))
+def test_parity_small(name, path):
+    _check(make_config(name), path=path)
+
+
+@pytest.mark.parametrize("k", [256, 512, 1024, 2048, 4096])
+@pytest.mark.parametrize("d", [64, 128])
+def test_parity_one_pass_every_block_count(k, d):
+    """Every built prototype-block count (k / 256 = 1 .. 16 workgroups per
+    group), ragged users with empty, one-token and tile-straddling lengths."""
+    from synth import make_inputs
+    inp = make_inputs([2049, 0, 1, 5000, 31, 700], d=d, k=k, seed=1000 + k + d)
+    _check(inp, path="one")
 
 
 def _sample(inp, n_random=2, seed=0):
@@ -52,8 +67,16 @@ def _sample(inp, n_random=2, seed=0):
     return sorted(pick)
 
 
-def test_parity_c2_single_user_100k():
-    _check(make_config("c2_n100k_d128_k1024"))
+@pytest.mark.parametrize("path", [None, "two"])
+def test_parity_c2_single_user_100k(path):
+    _check(make_config("c2_n100k_d128_k1024"), path=path)
+
+
+def test_parity_bench_workload_sampled():
+    """40 users x 100,000 tokens, k = 1024, d = 128: the bench's workload and
+    launch configuration."""
+    inp = make_config("c3lit_r40_n100k_d128_k1024")
+    _check(inp, users=[0, 17, 39])
 
 
 def test_parity_c3_training_batch_sampled():
@@ -73,8 +96,11 @@ def test_parity_c5_sweep_sampled(name):
     _check(inp, users=[0, inp.R - 1])
 
 
-def test_parity_sharp_softmax():
-    _check(make_config("sharp_n100k_d128_k1024"))
+@pytest.mark.parametrize("path", [None, "two"])
+def test_parity_sharp_softmax(path):
+    """Peaked softmax (logit std about 4): both paths take their exact,
+    max-shifted exponent mode here."""
+    _check(make_config("sharp_n100k_d128_k1024"), path=path)
 
 
 def test_parity_clustered_history():
