@@ -80,13 +80,12 @@ typedef struct {
  * For bf16 inputs with k = 256 * 2^i (i = 0..4) the library can run the
  * one-pass kernel: groups of k / 256 co-resident workgroups exchange
  * per-token partial softmax denominators, so every logit is computed once.
- * Otherwise, or when the batch is fragmented into many short users, it runs
- * two passes (per-token logsumexp, then allocations and sums), computing every
- * logit twice.  0 lets the library choose.  Setting both flags is
- * SA_E_INVALID.
+ * Otherwise it runs two passes (per-token logsumexp, then allocations and
+ * sums), computing every logit twice.  0 lets the library choose (currently
+ * two passes, the faster on MI355X).  Setting both flags is SA_E_INVALID.
  *   SA_FLAG_TWO_PASS  always run the two-pass kernels.
  *   SA_FLAG_ONE_PASS  run the one-pass kernel whenever the shape and device
- *                     allow it, whatever the batch looks like.
+ *                     allow it.
  */
 #define SA_FLAG_TWO_PASS 1
 #define SA_FLAG_ONE_PASS 2

@@ -119,13 +119,11 @@ bool device_fits_fused(const Layout& L) {
   return v == 2;
 }
 
-// One-pass unless the shape or device rules it out, the caller asks for two
-// passes, or (no request either way) the batch is so fragmented that the
-// per-segment pipeline start of the one-pass kernel would dominate: fewer
-// than 8 tiles per (group, user) segment on average.
+// The one-pass kernel when the caller asks for it and the shape and device
+// allow it; otherwise (and by default: it does not yet beat the two-pass
+// kernels on MI355X) two passes.
 bool use_fused(const sa_problem& p, const Layout& L) {
-  if (L.groups == 0 || (p.flags & SA_FLAG_TWO_PASS)) return false;
-  if (!(p.flags & SA_FLAG_ONE_PASS) && (int64_t)L.tiles_max < 8 * ((int64_t)L.groups + p.num_users)) return false;
+  if (L.groups == 0 || !(p.flags & SA_FLAG_ONE_PASS)) return false;
   return device_fits_fused(L);
 }
 
