@@ -50,7 +50,6 @@ def sources():
 FILE_FLAGS = {
     "sa_pass1.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "sa_pass2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    "sa_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

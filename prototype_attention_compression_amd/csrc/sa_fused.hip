@@ -18,22 +18,24 @@
 // exchange their per-token partial denominators through device-coherent
 // memory: every logit is computed once.
 //
-// Per 32-token tile, each of the 8 waves (32 prototypes; lane = token) runs
-//   GEMM1  C[j, t] = q_j . h_t                       (8 fp16 MFMAs, K = d)
-//   E      = 2^C,  p = sum of the lane's 16 values,  e = E / p in fp16
-//          (kept in registers while the denominator is exchanged)
+// A workgroup has 4 waves (one per SIMD, up to 512 registers each); each
+// wave owns 64 prototypes as two 32-prototype blocks, so every operand
+// fragment read from LDS feeds two MFMAs.  Per 32-token tile a wave runs
+//   GEMM1  C[j, t] = q_j . h_t                  (2 x 8 fp16 MFMAs, K = d)
+//   E      = 2^C,  p = sum of a lane's 16 values of a block,  e = E / p in
+//          fp16 (kept in registers while the denominator is exchanged)
 //   partial denominator of the wave, then of the workgroup (LDS), published
 //          to the group's exchange ring as a (tag, value) word
 // and, three tiles later, when Z_t of that tile is known,
 //   A'     = e * (p 2^14 / Z_t)  (= 2^14 A, packed fp16), staged through LDS
 //          and read back transposed (ds_read_b64_tr_b16: lane = prototype)
-//   mass  += A' (v_dot2 of the rounded values),  U += A' H  (8 fp16 MFMAs)
+//   mass  += A' (v_dot2 of the rounded values),  U += A' H  (2 x 8 fp16 MFMAs)
 // The 2^14 scale keeps fp16 allocations in the normal range; it cancels in
 // U / m.  If some token could overflow 2^C (largest |q| x largest |h| >= 100)
 // the exact variant keeps per-lane maxima and exchanges partial
 // log-sum-exps instead of sums.
 //
-// Exchange.  Wave 7 of every workgroup is the exchange wave: it publishes the
+// Exchange.  Wave 3 of every workgroup is the exchange wave: it publishes the
 // workgroup partial of tile i at the start of iteration i + 1, polls the P
 // words of tile i at the end of iteration i + 1, and at the end of iteration
 // i + 2 writes 2^14 / Z_t to an LDS ring from which all waves read it in
@@ -54,7 +56,8 @@
 // element e of read h in lane half g).  Every read is then a single per-lane
 // base register plus an immediate offset.
 //
-// The allocation staging buffer (per wave, 32 tokens x 32 prototypes fp16)
+// The allocation staging buffers (per wave and block, 32 tokens x 32
+// prototypes fp16)
 // stores token t in row 8 (t % 4) + t / 4 with its 16-byte chunks XOR'ed by
 // t % 4: conflict-free for the 16-byte writes (lane = token) and for the
 // transposing reads (lane = prototype, tokens as above).
@@ -76,8 +79,9 @@ namespace sa {
 
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kXWave = kWaves - 1;
+constexpr int kNB = 2;            // 32-prototype blocks per wave
 constexpr int kStageTiles = 4;
 constexpr int kBufs = 4;
 constexpr int kLag = 3;           // GEMM2 of tile i runs in iteration i + kLag
@@ -104,9 +108,9 @@ struct F {
   // ... and, in a separate array (so that accesses to it provably do not
   // alias the direct loads in flight), the per-wave staging buffers and the
   // exchange state
-  static constexpr int EBUF_OFF = 0;                                 // [8 waves][32 tok][32 proto] fp16
-  static constexpr int PART_OFF = EBUF_OFF + kWaves * 2048;          // [kPSlots][32 tok][8 waves] float
-  static constexpr int CNT_OFF = PART_OFF + kPSlots * kTile * kWaves * 4;   // [kPSlots][8 waves] uint32 progress
+  static constexpr int EBUF_OFF = 0;                                 // [waves][blocks][32 tok][32 proto] fp16
+  static constexpr int PART_OFF = EBUF_OFF + kWaves * kNB * 2048;    // [kPSlots][32 tok][waves] float
+  static constexpr int CNT_OFF = PART_OFF + kPSlots * kTile * kWaves * 4;   // [kPSlots][waves] uint32 progress
   static constexpr int ABORT_OFF = CNT_OFF + kPSlots * kWaves * 4;   // uint32
   static constexpr int ZR_OFF = CNT_OFF + 256;                       // [kXSlots][32] float
   static constexpr int ZTAG_OFF = ZR_OFF + kXSlots * kTile * 4;      // [kXSlots] uint32
@@ -171,7 +175,7 @@ __device__ __forceinline__ void fused_body(const Layout& L, void* ws, char* lds,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, g = lane >> 5;
   const bool xw = (wave == kXWave);
-  const int p0 = pb * kFusedProtos + wave * kProtoPerWave;
+  const int p0 = pb * kFusedProtos + wave * (kNB * kProtoPerWave);   // the wave's first prototype
 
   // zero the progress words, abort word and ring tags (used across
   // segments; the first stage barrier orders these stores before any use)
@@ -190,17 +194,19 @@ __device__ __forceinline__ void fused_body(const Layout& L, void* ws, char* lds,
   float* zring = reinterpret_cast<float*>(ctl + C::ZR_OFF);
   float* part = reinterpret_cast<float*>(ctl + C::PART_OFF);
 
-  // A operands of GEMM1: the wave's 32 query rows, row m holding prototype
-  // p0 + pi(m) with pi(8 (r/4) + 4 h + r % 4) = 16 h + r, so that accumulator
-  // register r of lane half h is prototype p0 + 16 h + r (16 contiguous
-  // prototypes per lane)
+  // A operands of GEMM1: per block b the 32 query rows, row m holding
+  // prototype p0 + 32 b + pi(m) with pi(8 (r/4) + 4 h + r % 4) = 16 h + r, so
+  // that accumulator register r of lane half h is prototype p0 + 32 b + 16 h
+  // + r (16 contiguous prototypes per lane and block)
   const _Float16* q16 = ws_f16(ws, L.off_q16);
-  half8 qf[C::S];
+  half8 qf[kNB][C::S];
   {
     const int pm = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
 #pragma unroll
-    for (int s = 0; s < C::S; ++s)
-      qf[s] = *reinterpret_cast<const half8*>(q16 + (int64_t)(p0 + pm) * D + 16 * s + 8 * g);
+    for (int b = 0; b < kNB; ++b)
+#pragma unroll
+      for (int s = 0; s < C::S; ++s)
+        qf[b][s] = *reinterpret_cast<const half8*>(q16 + (int64_t)(p0 + 32 * b + pm) * D + 16 * s + 8 * g);
   }
 
   const char* h16 = reinterpret_cast<const char*>(ws_f16(ws, L.off_h16));
@@ -225,8 +231,8 @@ __device__ __forceinline__ void fused_body(const Layout& L, void* ws, char* lds,
   // reads token 4 (i16 / 4) + 2 g (+ 16 kk + h) at columns 16 gh + 4 (i16 % 4)
   // (+ 32 dt) .. + 3
   const int tr_base = (4 * (i16 >> 2) + 2 * g) * C::PITCH + 32 * gh + 8 * (i16 & 3);
-  // the wave's allocation staging buffer
-  char* ebuf = ctl + C::EBUF_OFF + wave * 2048;
+  // the wave's allocation staging buffers (block b at + 2048 b)
+  char* ebuf = ctl + C::EBUF_OFF + wave * (kNB * 2048);
   const int erow = 8 * (col & 3) + (col >> 2);
   const int ew0 = erow * 64 + (((2 * g) ^ (col & 3)) * 16);
   const int ew1 = erow * 64 + (((2 * g + 1) ^ (col & 3)) * 16);
@@ -253,12 +259,14 @@ __device__ __forceinline__ void fused_body(const Layout& L, void* ws, char* lds,
     if (s1 > s0) {
       const int n = s1 - s0;                // tiles, a multiple of 4
       const int nst = n / kStageTiles;
-      float16v U[C::DT];
+      float16v U[kNB][C::DT];
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) U[dt] = float16v{};
-      float msum = 0.f;
-      half8 e[4][2];                         // ring of normalised exponentials (fp16)
-      float pl[4];                           // ... and the lane sums they were divided by
+      for (int b = 0; b < kNB; ++b)
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) U[b][dt] = float16v{};
+      float msum[kNB] = {};
+      half8 e[4][kNB][2];                    // ring of normalised exponentials (fp16)
+      float pl[4][kNB];                      // ... and the lane sums they were divided by
       uint64_t pw[(P >= 2) ? P / 2 : 1];     // exchange words in flight (wave 7)
 
       auto issue = [&](int ts, int b) {
@@ -289,15 +297,14 @@ __device__ __forceinline__ void fused_body(const Layout& L, void* ws, char* lds,
       auto publish = [&](int32_t sq, int ps, int zs, const char* vbase) {
         // every wave has stored its partial of this tile (progress words)
         const uint32_t want = (uint32_t)(sq + 1);
+        static_assert(kWaves == 4, "one 16-byte read of progress words");
         const u32x4* prog = reinterpret_cast<const u32x4*>(prog_words + ps * kWaves);
         int n_spin = 0;
         for (;;) {
           cbar();
-          const u32x4 a = prog[0], b = prog[1];
+          const u32x4 a = prog[0];
           cbar();
-          if (a[0] == want && a[1] == want && a[2] == want && a[3] == want && b[0] == want && b[1] == want &&
-              b[2] == want && b[3] == want)
-            break;
+          if (a[0] == want && a[1] == want && a[2] == want && a[3] == want) break;
           if (aborted()) break;
           if (++n_spin > kSpinMax) { give_up(); break; }
           __builtin_amdgcn_s_sleep(1);
@@ -319,7 +326,7 @@ __device__ __forceinline__ void fused_body(const Layout& L, void* ws, char* lds,
           // the workgroup holds every prototype: its partial is the total
           if (g == 0) {
             float r;
-            if (!EXACT) r = keep ? kShift / v : 0.f;
+            if (!EXACT) r = keep ? kShift * __builtin_amdgcn_rcpf(v) : 0.f;
             else r = keep ? v : INFINITY;
             zring[zs * kTile + col] = r;
           }
@@ -365,7 +372,7 @@ __device__ __forceinline__ void fused_body(const Layout& L, void* ws, char* lds,
         }
         if (g == 0) {
           float r;
-          if (!EXACT) r = (v == INFINITY) ? 0.f : kShift / v;
+          if (!EXACT) r = (v == INFINITY) ? 0.f : kShift * __builtin_amdgcn_rcpf(v);
           else r = (v == -INFINITY) ? INFINITY : v;
           zring[zs * kTile + col] = r;
         }
@@ -412,45 +419,58 @@ __device__ __forceinline__ void fused_body(const Layout& L, void* ws, char* lds,
 #pragma unroll
           for (int s = 0; s < C::S; ++s) ha[s] = *reinterpret_cast<const half8*>(rows + 32 * s);
         }
-        half8 ap[2];
+        half8 ap[kNB][2];
         if (CONS) {
           const float r = zring[zc * kTile + col];
-          float sc;
-          if (!EXACT) sc = pl[EC] * r;
-          else sc = __builtin_amdgcn_exp2f(pl[EC] - r + 14.0f);
-          const _Float16 hs = (_Float16)sc;
-          *reinterpret_cast<half8*>(ebuf + ew0) = e[EC][0] * hs;
-          *reinterpret_cast<half8*>(ebuf + ew1) = e[EC][1] * hs;
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(ebuf + kk * 256 + er_off[0]));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(ebuf + kk * 256 + er_off[1]));
-            const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            ap[kk] = __builtin_bit_cast(half8, v);
+          for (int b = 0; b < kNB; ++b) {
+            float sc;
+            if (!EXACT) sc = pl[EC][b] * r;
+            else sc = __builtin_amdgcn_exp2f(pl[EC][b] - r + 14.0f);
+            const _Float16 hs = (_Float16)sc;
+            char* eb = ebuf + b * 2048;
+            *reinterpret_cast<half8*>(eb + ew0) = e[EC][b][0] * hs;
+            *reinterpret_cast<half8*>(eb + ew1) = e[EC][b][1] * hs;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+              const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(eb + kk * 256 + er_off[0]));
+              const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(eb + kk * 256 + er_off[1]));
+              const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              ap[b][kk] = __builtin_bit_cast(half8, v);
+            }
           }
         }
-        float16v acc = float16v{};
+        float16v acc[kNB];
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) acc[b] = float16v{};
         if (G1) {
 #pragma unroll
-          for (int s = 0; s < C::S; ++s) acc = mfma32x32x16(qf[s], ha[s], acc);
+          for (int s = 0; s < C::S; ++s)
+#pragma unroll
+            for (int b = 0; b < kNB; ++b) acc[b] = mfma32x32x16(qf[b][s], ha[s], acc[b]);
+        }
+        if (CONS) {
+#pragma unroll
+          for (int b = 0; b < kNB; ++b)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const half2v pr = {ap[b][kk][2 * q], ap[b][kk][2 * q + 1]};
+                msum[b] = __builtin_amdgcn_fdot2(pr, ones, msum[b], false);
+              }
         }
         if (G1 && CONS) {
           __builtin_amdgcn_sched_group_barrier(0x100, C::S + 1, 0);   // GEMM1 operands, ring value
 #pragma unroll
-          for (int s = 0; s < C::S; ++s) {
+          for (int q = 0; q < kNB * C::S; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // 1 MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);        // 2 VALU
+            __builtin_amdgcn_sched_group_barrier(0x300, 1, 0);        // 1 LDS read or write
           }
         }
         __builtin_amdgcn_sched_barrier(0);
         if (CONS) {
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const half2v pr = {ap[kk][2 * q], ap[kk][2 * q + 1]};
-              msum = __builtin_amdgcn_fdot2(pr, ones, msum, false);
-            }
           const char* rows = lds + (B2 * C::STAGE_BYTES + t2 * C::TILE_BYTES + tr_base);
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk)
@@ -460,51 +480,61 @@ __device__ __forceinline__ void fused_body(const Layout& L, void* ws, char* lds,
               const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(pr0));
               const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(pr0 + C::PITCH));
               const s16x8 hb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-              U[dt] = mfma32x32x16(ap[kk], __builtin_bit_cast(half8, hb), U[dt]);
+#pragma unroll
+              for (int b = 0; b < kNB; ++b) U[b][dt] = mfma32x32x16(ap[b][kk], __builtin_bit_cast(half8, hb), U[b][dt]);
             }
         }
         if (G1) {
-          float E[16];
-          float pv;
-          if (!EXACT) {
-            float s0v = 0.f, s1v = 0.f;
+          float pv[kNB];
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-              E[r] = __builtin_amdgcn_exp2f(acc[r]);
-              E[r + 1] = __builtin_amdgcn_exp2f(acc[r + 1]);
-              s0v += E[r];
-              s1v += E[r + 1];
+          for (int b = 0; b < kNB; ++b) {
+            float E[16];
+            if (!EXACT) {
+              float s0v = 0.f, s1v = 0.f;
+#pragma unroll
+              for (int r = 0; r < 16; r += 2) {
+                E[r] = __builtin_amdgcn_exp2f(acc[b][r]);
+                E[r + 1] = __builtin_amdgcn_exp2f(acc[b][r + 1]);
+                s0v += E[r];
+                s1v += E[r + 1];
+              }
+              pv[b] = s0v + s1v;
+              pl[ER][b] = pv[b];
+            } else {
+              float m = acc[b][0];
+#pragma unroll
+              for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[b][r]);
+              float s0v = 0.f, s1v = 0.f;
+#pragma unroll
+              for (int r = 0; r < 16; r += 2) {
+                E[r] = __builtin_amdgcn_exp2f(acc[b][r] - m);
+                E[r + 1] = __builtin_amdgcn_exp2f(acc[b][r + 1] - m);
+                s0v += E[r];
+                s1v += E[r + 1];
+              }
+              pv[b] = s0v + s1v;
+              pl[ER][b] = m + log2f(pv[b]);
             }
-            pv = s0v + s1v;
-            pl[ER] = pv;
-          } else {
-            float m = acc[0];
+            const float rp = __builtin_amdgcn_rcpf(pv[b]);
 #pragma unroll
-            for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[r]);
-            float s0v = 0.f, s1v = 0.f;
+            for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-              E[r] = __builtin_amdgcn_exp2f(acc[r] - m);
-              E[r + 1] = __builtin_amdgcn_exp2f(acc[r + 1] - m);
-              s0v += E[r];
-              s1v += E[r + 1];
-            }
-            pv = s0v + s1v;
-            pl[ER] = m + log2f(pv);
+              for (int q = 0; q < 4; ++q) {
+                const float2v v = {E[8 * hh + 2 * q] * rp, E[8 * hh + 2 * q + 1] * rp};
+                const half2v hv = __builtin_convertvector(v, half2v);
+                e[ER][b][hh][2 * q] = hv[0];
+                e[ER][b][hh][2 * q + 1] = hv[1];
+              }
           }
-          const float rp = 1.0f / pv;
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float2v v = {E[8 * hh + 2 * q] * rp, E[8 * hh + 2 * q + 1] * rp};
-              const half2v hv = __builtin_convertvector(v, half2v);
-              e[ER][hh][2 * q] = hv[0];
-              e[ER][hh][2 * q + 1] = hv[1];
-            }
-          // the wave's partial over its 32 prototypes, into LDS slot t1
-          const HalfPair hp = lane_halves(!EXACT ? pv : pl[ER]);
-          const float wpart = !EXACT ? hp.lo + hp.hi : log_add_exp2(hp.lo, hp.hi);
+          // the wave's partial over its 64 prototypes, into LDS slot t1
+          float wpart;
+          if (!EXACT) {
+            const HalfPair hp = lane_halves(pv[0] + pv[1]);
+            wpart = hp.lo + hp.hi;
+          } else {
+            const HalfPair hp = lane_halves(log_add_exp2(pl[ER][0], pl[ER][1]));
+            wpart = log_add_exp2(hp.lo, hp.hi);
+          }
           if (g == 0) part[(t1 * kTile + col) * kWaves + wave] = wpart;
         }
         if (G1 && CONS) {
@@ -512,7 +542,9 @@ __device__ __forceinline__ void fused_body(const Layout& L, void* ws, char* lds,
           for (int q = 0; q < 2 * C::DT; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // 2 transposing reads
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // 1 MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);        // 5 VALU
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);        // 4 VALU
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);        // 4 VALU
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -578,12 +610,15 @@ __device__ __forceinline__ void fused_body(const Layout& L, void* ws, char* lds,
       float* part_u = part_u_all + (int64_t)(group + u) * L.k * D;
       float* part_m = part_m_all + (int64_t)(group + u) * L.k;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
+      for (int b = 0; b < kNB; ++b) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          part_u[(int64_t)(p0 + acc_row(r, g)) * D + 32 * dt + col] = U[dt][r];
-      const float m = msum + __shfl_xor(msum, 32);
-      if (g == 0) part_m[p0 + col] = m;
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            part_u[(int64_t)(p0 + 32 * b + acc_row(r, g)) * D + 32 * dt + col] = U[b][dt][r];
+        const float m = msum[b] + __shfl_xor(msum[b], 32);
+        if (g == 0) part_m[p0 + 32 * b + col] = m;
+      }
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       lds_barrier();     // every wave is done with the stage buffers
       seq0 += n;

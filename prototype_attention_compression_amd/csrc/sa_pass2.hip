@@ -28,10 +28,14 @@
 // The 2^14 scale cancels in U / m.
 //
 // Data movement: token rows reach LDS with direct global->LDS loads (16 B per
-// lane), 4 tiles (128 tokens) per stage, three stage buffers (loads run two
-// stages ahead).  Rows are XOR-swizzled by 16-byte chunk so that both the
-// 16-byte GEMM1 reads and the transposing 8-byte reads touch 64 distinct
-// banks per pass (gfx950 LDS: 64 banks of 4 bytes).
+// lane), 4 tiles (128 tokens) per stage, four stage buffers (loads run three
+// stages ahead: the loads are latency-bound, so the bytes in flight per CU
+// set their rate).  A row occupies 2d + 16 bytes (one 16-byte chunk of
+// padding, filled by the same loads); GEMM1's operand row m holds token
+// tau(m), which puts the 4 tokens of one transposing read 4 rows apart.  Then
+// the 16-byte GEMM1 reads and the transposing 8-byte reads both touch 64
+// distinct banks per pass (gfx950 LDS: 64 banks of 4 bytes), and every read
+// is one per-lane base register plus an immediate.
 // Every user's tile count is a multiple of 4 (pass 1 fills the padding tiles
 // with zero rows and A = 0), so every stage is full and the stage body is one
 // straight-line block.  A workgroup has up to 8 waves of 32 prototypes (two
@@ -57,32 +61,31 @@ namespace sa {
 namespace {
 
 constexpr int kStageTiles = 4;
-constexpr int kBufs = 3;           // stage buffers: loads run two stages ahead
+constexpr int kBufs = 4;           // stage buffers: loads run three stages ahead
 
 template <int D>
 struct P2 {
   static constexpr int S = D / 16;                   // MFMA K steps over d
   static constexpr int DT = D / 32;                  // 32-column output blocks
   static constexpr int CPR = D / 8;                  // 16-B chunks per token row
-  static constexpr int TILE_BYTES = kTile * D * 2;   // one tile of token rows
+  static constexpr int SLOTS = CPR + 1;              // ... plus one chunk of padding
+  static constexpr int PITCH = SLOTS * 16;           // LDS bytes per token row
+  static constexpr int TILE_BYTES = kTile * PITCH;   // one tile of token rows
   static constexpr int ROWS_BYTES = kStageTiles * TILE_BYTES;
   static constexpr int NL_OFF = ROWS_BYTES;          // (-l_hi, -l_lo) pairs of the stage
   static constexpr int STAGE_BYTES = NL_OFF + kStageTiles * kTile * 4;
-  static constexpr int LOADS_ROWS = ROWS_BYTES / 1024;   // 1-KB direct loads per stage
+  static constexpr int LOADS_ROWS = kStageTiles * kTile * SLOTS / 64;   // 1-KB direct loads per stage
+  static_assert(LOADS_ROWS * 64 == kStageTiles * kTile * SLOTS, "whole loads per stage");
 };
 
-// 16-byte chunk swizzle of a token row (t = row within the stage): a bit
-// permutation of t mod 16 (output bits 0..3 take input bits 2, 3, 1, 0),
-// reduced to the row's chunk count.  The 16-byte GEMM1 reads are served 16
-// lanes (16 tokens, one logical chunk) per pass and need distinct swizzles
-// over 16 consecutive tokens; the 8-byte transposing reads are served 32
-// lanes (4 consecutive tokens x 64 bytes) per pass and need the 4 tokens'
-// swizzles to differ in bits 2-3.  This permutation meets both at d = 64 and
-// d = 128.
-template <int D>
-__device__ __forceinline__ int swz(int t) {
-  const int x = t & 15;
-  return (((x >> 2) & 3) | ((x & 2) << 1) | ((x & 1) << 3)) & (P2<D>::CPR - 1);
+// Token held by GEMM1 operand row m (m = 16 kk + 8 h + 4 g + e in bits):
+// 16 kk + 4 e + 2 g + h.  GEMM1's accumulator rows are GEMM2's K order, so
+// the 4 tokens of one transposing read (e = 0..3) lie 4 rows apart; with the
+// padded row pitch (2d + 16 bytes) such a read (32 lanes: 4 tokens x 64
+// bytes) meets all 64 banks once, and so do the 16-byte GEMM1 reads (16
+// consecutive operand rows, one chunk).
+__device__ __forceinline__ int tau(int m) {
+  return (m & 16) | ((m & 3) << 2) | (((m >> 2) & 1) << 1) | ((m >> 3) & 1);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -94,7 +97,7 @@ constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 }  // namespace
 
-template <int D, int WAVES>
+template <int D, int WAVES, int NB>
 __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   using C = P2<D>;
   __shared__ __attribute__((aligned(1024))) char lds[kBufs * C::STAGE_BYTES];
@@ -116,15 +119,18 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, g = lane >> 5;
-  const int p0 = pb * (WAVES * kProtoPerWave) + wave * kProtoPerWave;
+  // the wave owns NB blocks of 32 prototypes: p0 + 32 b + (0 .. 31)
+  const int p0 = pb * (WAVES * NB * kProtoPerWave) + wave * (NB * kProtoPerWave);
 
-  // B operands of GEMM1: the wave's 32 query rows (kept in registers), and the
+  // B operands of GEMM1: the wave's query rows (kept in registers), and the
   // feature step's (1, 1, 0, ...) column pair
   const _Float16* q16 = ws_f16(ws, L.off_q16);
-  half8 qf[C::S];
+  half8 qf[NB][C::S];
 #pragma unroll
-  for (int s = 0; s < C::S; ++s)
-    qf[s] = *reinterpret_cast<const half8*>(q16 + (int64_t)(p0 + col) * D + 16 * s + 8 * g);
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int s = 0; s < C::S; ++s)
+      qf[b][s] = *reinterpret_cast<const half8*>(q16 + (int64_t)(p0 + 32 * b + col) * D + 16 * s + 8 * g);
   const half8 qfeat = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)0.0f, (_Float16)0.0f,
                        (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
 
@@ -133,20 +139,24 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
 
   // Direct loads of stage `ts` (tiles 4 ts .. 4 ts + 3 of the chunk) into
   // buffer b.  Load i fills LDS bytes [1024 i, 1024 i + 1024) of the stage:
-  // lane l writes chunk slot 64 i + l = (token, swizzled chunk).  Every wave
-  // issues the same number of loads per stage (LOADS_ROWS / WAVES rows plus
-  // one slice of the -l pairs), so a vmcnt wait can name a later stage.
-  constexpr int LPW = C::LOADS_ROWS / WAVES + 1;   // loads per wave per stage
-  static_assert(LPW < 64, "vmcnt range");
+  // lane l writes 16-byte slot 64 i + l = (row q / SLOTS, chunk q % SLOTS);
+  // the padding chunk re-reads chunk 0 of its row.  Row loads go round-robin
+  // over the waves, and every wave adds one slice of the -l pairs; a wave's
+  // vmcnt waits count its own loads (LMAX or LMIN per stage).
+  constexpr int LMAX = (C::LOADS_ROWS + WAVES - 1) / WAVES + 1;
+  constexpr int LMIN = C::LOADS_ROWS / WAVES + 1;
+  static_assert(2 * LMAX < 64, "vmcnt range");
+  const bool big = (C::LOADS_ROWS % WAVES == 0) || (wave < C::LOADS_ROWS % WAVES);
   auto issue = [&](int ts, int b) {
     char* base = lds + b * C::STAGE_BYTES;
     const int64_t tile0 = (int64_t)t0 + (int64_t)ts * kStageTiles;
-#pragma unroll
+#pragma unroll 1
     for (int i = wave; i < C::LOADS_ROWS; i += WAVES) {
       const int q = 64 * i + lane;
-      const int tok = q / C::CPR, cs = q % C::CPR;
-      const int c = cs ^ swz<D>(tok);
-      const char* src = h16 + (tile0 * kTile + tok) * (D * 2) + c * 16;
+      const int row = q / C::SLOTS;
+      int c = q - row * C::SLOTS;
+      c = c == C::CPR ? 0 : c;
+      const char* src = h16 + (tile0 * kTile + row) * (D * 2) + c * 16;
       __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(base + 1024 * i), 16, 0, 0);
     }
     constexpr int NL_LANES = kStageTiles * kTile * 4 / 16 / WAVES;   // 16-B pieces per wave
@@ -155,109 +165,114 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
       __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(base + C::NL_OFF + wave * NL_LANES * 16), 16, 0, 0);
     }
   };
-  static_assert(C::LOADS_ROWS % WAVES == 0, "row loads split evenly over waves");
-  static_assert(kBufs == 3, "the stage loop below is unrolled over 3 buffers");
+  // wait until only this wave's loads of the `later` stages after the
+  // current one are still in flight
+  auto wait_stage = [&](int later) {
+    if (later >= 2) {
+      if (big) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LMAX));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LMIN));
+    } else if (later == 1) {
+      if (big) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LMAX));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(LMIN));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+  };
+  static_assert(kBufs == 4, "the stage loop below is unrolled over 4 buffers");
 
-  // per-lane byte offsets of the transposing reads (GEMM2 B operands): for
-  // output block dt and token half h (tokens +0 / +8), source lane s = lane %
-  // 16 reads token 8 h + 4 g + s / 4 of the tile's first 16 tokens, columns
-  // 32 dt + 16 ((lane / 16) % 2) + 4 (s % 4) .. + 3; K step kk adds 16 tokens
-  // (same swizzle, a constant offset)
-  int tr_off[2][C::DT];
-  {
-    const int i16 = lane & 15, gh = (lane >> 4) & 1;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        const int tok = 8 * h + 4 * g + (i16 >> 2);
-        const int colm = 32 * dt + 16 * gh + 4 * (i16 & 3);
-        const int chunk = (colm >> 3) ^ swz<D>(tok);
-        tr_off[h][dt] = tok * (D * 2) + chunk * 16 + 8 * (i16 & 1);
-      }
-  }
+  // per-lane byte offsets of the transposing reads (GEMM2 B operands):
+  // source lane i16 of 16-lane group gh reads the row of token 4 (i16 / 4) +
+  // 2 g (+ 16 kk + h) at columns 16 gh + 4 (i16 % 4) (+ 32 dt) .. + 3, which
+  // is K element 4 h + i16 / 4 of lane half g in GEMM1's row order (tau)
+  const int i16 = lane & 15, gh = (lane >> 4) & 1;
+  const int tr_base = (4 * (i16 >> 2) + 2 * g) * C::PITCH + 32 * gh + 8 * (i16 & 3);
 
-  float16v U[C::DT];
+  float16v U[NB][C::DT];
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) U[dt] = float16v{};
-  float msum = 0.f;
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) U[b][dt] = float16v{};
+  float msum[NB] = {};
   const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  // per-lane byte offsets of the GEMM1 operand reads (token row `col`,
-  // swizzled chunk 2 s + g) within a tile
-  int ha_off[C::S];
-#pragma unroll
-  for (int s = 0; s < C::S; ++s) ha_off[s] = col * (D * 2) + (((2 * s + g) ^ swz<D>(col)) * 16);
+  // per-lane byte offset of the GEMM1 operand reads: row of token tau(col),
+  // chunk 2 s + g at + 32 s
+  const int tcol = tau(col);
+  const int ha_base = tcol * C::PITCH + 16 * g;
 
   // One stage held in buffer B (a compile-time constant, so every LDS read is
   // a per-lane offset register plus an immediate).
   const int nstages = nt / kStageTiles;
   auto stage = [&](int st, auto Bc) {
     constexpr int B = decltype(Bc)::value;
-    // this wave's loads of stage st have landed (those of st+1 may still fly)
-    if (st + 1 < nstages)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    // this wave's loads of stage st have landed (those of st+1, st+2 may still fly)
+    wait_stage(min(2, nstages - 1 - st));
     __syncthreads();                             // ... every wave's; stage st-1's buffer is free
-    if (st + 2 < nstages) issue(st + 2, (B + 2) % kBufs);
+    if (st + 3 < nstages) issue(st + 3, (B + 3) % kBufs);
     const char* base = lds + B * C::STAGE_BYTES;
     typedef __attribute__((address_space(3))) s16x4* tr_ptr;
     // GEMM1 of tile t: C[tok, proto] = h_tok . q_proto - l_tok
-    auto gemm1 = [&](int t, float16v& Cm) {
+    auto gemm1 = [&](int t, float16v (&Cm)[NB]) {
       const char* rows = base + t * C::TILE_BYTES;
-      const uint32_t nlp = reinterpret_cast<const uint32_t*>(base + C::NL_OFF)[t * kTile + col];
+      const uint32_t nlp = reinterpret_cast<const uint32_t*>(base + C::NL_OFF)[t * kTile + tcol];
       half8 ha[C::S];
 #pragma unroll
-      for (int s = 0; s < C::S; ++s) ha[s] = *reinterpret_cast<const half8*>(rows + ha_off[s]);
+      for (int s = 0; s < C::S; ++s) ha[s] = *reinterpret_cast<const half8*>(rows + ha_base + 32 * s);
       const u32x4 fv = {g == 0 ? nlp : 0u, 0u, 0u, 0u};
-      Cm = mfma32x32x16(__builtin_bit_cast(half8, fv), qfeat, float16v{});
 #pragma unroll
-      for (int s = 0; s < C::S; ++s) Cm = mfma32x32x16(ha[s], qf[s], Cm);
+      for (int b = 0; b < NB; ++b) Cm[b] = mfma32x32x16(__builtin_bit_cast(half8, fv), qfeat, float16v{});
+#pragma unroll
+      for (int s = 0; s < C::S; ++s)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) Cm[b] = mfma32x32x16(ha[s], qf[b][s], Cm[b]);
     };
     // allocations 2^C (= 2^14 A) in fp16, masses of the rounded values
-    auto expo = [&](const float16v& Cm, half8 (&ap)[2]) {
+    auto expo = [&](const float16v (&Cm)[NB], half8 (&ap)[NB][2]) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          float2v v = {__builtin_amdgcn_exp2f(Cm[8 * kk + e]), __builtin_amdgcn_exp2f(Cm[8 * kk + e + 1])};
-          half2v h = __builtin_convertvector(v, half2v);
-          msum = __builtin_amdgcn_fdot2(h, ones, msum, false);
-          ap[kk][e] = h[0];
-          ap[kk][e + 1] = h[1];
-        }
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            float2v v = {__builtin_amdgcn_exp2f(Cm[b][8 * kk + e]), __builtin_amdgcn_exp2f(Cm[b][8 * kk + e + 1])};
+            half2v h = __builtin_convertvector(v, half2v);
+            msum[b] = __builtin_amdgcn_fdot2(h, ones, msum[b], false);
+            ap[b][kk][e] = h[0];
+            ap[b][kk][e + 1] = h[1];
+          }
     };
     // GEMM2 of tile t: U[proto, c] += sum_tok A'[proto, tok] h_tok[c]
-    auto gemm2 = [&](int t, const half8 (&ap)[2]) {
-      const char* rows = base + t * C::TILE_BYTES;
+    auto gemm2 = [&](int t, const half8 (&ap)[NB][2]) {
+      const char* rows = base + t * C::TILE_BYTES + tr_base;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(rows + kk * 16 * (D * 2) + tr_off[0][dt]));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(rows + kk * 16 * (D * 2) + tr_off[1][dt]));
+          const char* pr0 = rows + 16 * kk * C::PITCH + 64 * dt;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(pr0));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(pr0 + C::PITCH));
           const s16x8 hb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          U[dt] = mfma32x32x16(ap[kk], __builtin_bit_cast(half8, hb), U[dt]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) U[b][dt] = mfma32x32x16(ap[b][kk], __builtin_bit_cast(half8, hb), U[b][dt]);
         }
     };
     // Pipeline within the stage: GEMM1 of tile t+1 is issued interleaved
     // with the exponentials of tile t (independent work), then GEMM2 of t.
-    float16v Ca, Cb;
-    half8 ap[2];
+    float16v Ca[NB], Cb[NB];
+    half8 ap[NB][2];
     __builtin_amdgcn_sched_barrier(0);
     gemm1(0, Ca);
 #pragma unroll
     for (int t = 0; t < kStageTiles; ++t) {
-      float16v& Cx = (t & 1) ? Cb : Ca;
-      float16v& Cy = (t & 1) ? Ca : Cb;
+      float16v (&Cx)[NB] = (t & 1) ? Cb : Ca;
+      float16v (&Cy)[NB] = (t & 1) ? Ca : Cb;
       __builtin_amdgcn_sched_barrier(0);
       if (t + 1 < kStageTiles) {
         gemm1(t + 1, Cy);
         expo(Cx, ap);
         __builtin_amdgcn_sched_group_barrier(0x100, C::S + 1, 0);   // GEMM1 LDS reads
 #pragma unroll
-        for (int i = 0; i < C::S + 1; ++i) {
+        for (int i = 0; i < NB * (C::S + 1); ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // 1 MFMA
           __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);        // 4 VALU
         }
@@ -270,21 +285,26 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   };
   issue(0, 0);
   if (nstages > 1) issue(1, 1);
+  if (nstages > 2) issue(2, 2);
   for (int st = 0; st < nstages; st += kBufs) {
     stage(st, std::integral_constant<int, 0>{});
     if (st + 1 < nstages) stage(st + 1, std::integral_constant<int, 1>{});
     if (st + 2 < nstages) stage(st + 2, std::integral_constant<int, 2>{});
+    if (st + 3 < nstages) stage(st + 3, std::integral_constant<int, 3>{});
   }
 
   float* part_u = ws_f32(ws, L.off_part_u) + (int64_t)chunk * L.k * D;
   float* part_m = ws_f32(ws, L.off_part_m) + (int64_t)chunk * L.k;
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt)
+  for (int b = 0; b < NB; ++b) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      part_u[(int64_t)(p0 + acc_row(r, g)) * D + 32 * dt + col] = U[dt][r];
-  const float m = msum + __shfl_xor(msum, 32);
-  if (g == 0) part_m[p0 + col] = m;
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        part_u[(int64_t)(p0 + 32 * b + acc_row(r, g)) * D + 32 * dt + col] = U[b][dt][r];
+    const float m = msum[b] + __shfl_xor(msum[b], 32);
+    if (g == 0) part_m[p0 + 32 * b + col] = m;
+  }
 }
 
 hipError_t launch_pass2(const Layout& L, void* ws, hipStream_t stream) {
@@ -292,7 +312,7 @@ hipError_t launch_pass2(const Layout& L, void* ws, hipStream_t stream) {
   const int64_t grid = padded * L.n_pblocks;
   if (grid == 0) return hipSuccess;
 #define SA_P2(DD, WW) \
-  hipLaunchKernelGGL((pass2_accum<DD, WW>), dim3((unsigned)grid), dim3(WW * 64), 0, stream, L, ws)
+  hipLaunchKernelGGL((pass2_accum<DD, WW, 1>), dim3((unsigned)grid), dim3(WW * 64), 0, stream, L, ws)
   if (L.d == 128) {
     switch (L.waves) {
       case 8: SA_P2(128, 8); break;
