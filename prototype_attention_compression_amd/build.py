@@ -50,6 +50,7 @@ def sources():
 FILE_FLAGS = {
     "sa_pass1.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "sa_pass2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "sa_pass1q.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

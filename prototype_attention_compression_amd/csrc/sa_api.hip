@@ -175,8 +175,11 @@ sa_status sa_compress_with_events(const sa_problem* problem, const void* H, cons
       if (!mark(2)) return SA_E_HIP;
       if (sa::launch_fused(L, workspace, s) != hipSuccess) return SA_E_HIP;
     } else if (p.dtype == SA_BF16) {
-      if (p.total_tokens > 0 && sa::launch_pass1(L, H, offsets, token_mask, workspace, s) != hipSuccess)
-        return SA_E_HIP;
+      if (p.total_tokens > 0) {
+        const hipError_t e = sa::pass1q_ok(L) ? sa::launch_pass1q(L, H, offsets, token_mask, workspace, s)
+                                              : sa::launch_pass1(L, H, offsets, token_mask, workspace, s);
+        if (e != hipSuccess) return SA_E_HIP;
+      }
       if (!mark(2)) return SA_E_HIP;
       if (p.total_tokens > 0 && sa::launch_pass2(L, workspace, s) != hipSuccess) return SA_E_HIP;
     } else {

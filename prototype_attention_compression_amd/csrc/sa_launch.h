@@ -15,6 +15,10 @@ hipError_t launch_prep(const Layout& L, const void* P, const void* Wk, const int
 // bf16 path, pass 1: per-token logsumexp, fp16 token rows and transposed tiles
 hipError_t launch_pass1(const Layout& L, const void* H, const int64_t* offsets, const uint8_t* mask,
                         void* ws, hipStream_t stream);
+// bf16 path, pass 1 with the queries resident in registers (k = 256, 512, 1024)
+bool pass1q_ok(const Layout& L);
+hipError_t launch_pass1q(const Layout& L, const void* H, const int64_t* offsets, const uint8_t* mask, void* ws,
+                         hipStream_t stream);
 // bf16 path, pass 2: allocations, per-chunk sums of A h and masses
 hipError_t launch_pass2(const Layout& L, void* ws, hipStream_t stream);
 // fp32 path, both passes
