@@ -93,7 +93,9 @@ typedef struct {
 /*
  * Workspace size for `problem`.  Writes the byte count to *bytes.  Returns
  * SA_E_INVALID / SA_E_UNSUPPORTED for a problem sa_compress would reject.
- * Pure host code; needs no GPU.  The size grows linearly in N, R and k.
+ * Pure host code; needs no GPU.  The size grows linearly in N, R and k; for
+ * bf16 the fp16 copy of the (tile-padded) token rows, 2d bytes per token,
+ * dominates for long histories.
  */
 sa_status sa_workspace_size(const sa_problem* problem, size_t* bytes);
 

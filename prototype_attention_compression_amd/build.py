@@ -68,6 +68,21 @@ def _compile(src: str, hipcc: str, verbose: bool) -> str:
     return obj
 
 
+def _check_kernel_stubs(lib: str) -> None:
+    """Fail if a kernel's host launch stub was left undefined.
+
+    clang can drop a kernel template's host-side instantiation without any
+    diagnostic; the shared library then links but cannot be loaded.
+    """
+    nm = shutil.which("nm")
+    if nm is None:
+        return
+    res = subprocess.run([nm, "-D", "--undefined-only", lib], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in res.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError("kernel launch stubs undefined in the linked library: " + ", ".join(missing))
+
+
 def build_library(verbose: bool = False) -> str:
     """Compile every HIP source and link libsa.so.  Returns the library path."""
     hipcc = _hipcc()
@@ -80,6 +95,7 @@ def build_library(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
+    _check_kernel_stubs(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

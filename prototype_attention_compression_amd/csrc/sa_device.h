@@ -29,6 +29,29 @@ __device__ __forceinline__ float16v mfma32x32x16(half8 a, half8 b, float16v c) {
 // Row of the 32x32 accumulator held in register r by lane half g.
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
+// Workgroup barrier for LDS only: this wave's LDS operations are complete,
+// then s_barrier.  Global loads and stores (direct-to-LDS loads included) stay
+// in flight; a language-level barrier also fences global memory and so waits
+// for every outstanding load of the wave, prefetches included.  Data that a
+// direct-to-LDS load writes is visible to other waves after the issuing wave's
+// own vmcnt wait and then this barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Row pitch of a padded fp16 token tile in LDS: 2d + 16 bytes (token t's
+// 16-byte chunk c at t * pitch + 16 c; the extra chunk shifts consecutive
+// rows by 4 of the 64 banks).
+template <int D>
+constexpr int tile_pitch() { return (D / 8 + 1) * 16; }
+
+// Token held by pass 2's GEMM1 operand row m (m = 16 kk + 8 h + 4 g + e in
+// bits): 16 kk + 4 e + 2 g + h.  GEMM1's accumulator rows are GEMM2's
+// contraction order, so the 4 tokens of one transposing read of GEMM2's
+// operand lie 4 rows apart in LDS, which with the padded pitch keeps every
+// read conflict-free.
+__device__ __forceinline__ int tau(int m) {
+  return (m & 16) | ((m & 3) << 2) | (((m >> 2) & 1) << 1) | ((m >> 3) & 1);
+}
+
 // Exact widening of 8 packed bf16 values (one 16-byte load) to fp16.  bf16
 // values whose magnitude lies in [2^-17, 65504] are exactly representable in
 // fp16; the conversion truncates toward zero so larger values saturate.

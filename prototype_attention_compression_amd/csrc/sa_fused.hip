@@ -161,11 +161,6 @@ __device__ __forceinline__ void lds_flag_store(uint32_t* p, uint32_t v) {
   *p = v;
   cbar();
 }
-// Workgroup barrier ordering LDS only: this wave's LDS operations are done,
-// its direct loads into the stage buffers were waited for explicitly before
-// (vmcnt), and the global loads in flight stay in flight.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 }  // namespace
 
 template <int D, int P, bool EXACT>

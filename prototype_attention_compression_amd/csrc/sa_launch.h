@@ -12,10 +12,11 @@ namespace sa {
 // queries + ragged schedule
 hipError_t launch_prep(const Layout& L, const void* P, const void* Wk, const int64_t* offsets, void* ws,
                        hipStream_t stream);
-// bf16 path, pass 1: per-token logsumexp, fp16 token rows and transposed tiles
+// bf16 path, pass 1: per-token logsumexp and fp16 token rows
 hipError_t launch_pass1(const Layout& L, const void* H, const int64_t* offsets, const uint8_t* mask,
                         void* ws, hipStream_t stream);
-// bf16 path, pass 1 with the queries resident in registers (k = 256, 512, 1024)
+// bf16 path, pass 1 with the queries resident in registers (k = 256, 512,
+// 1024): logsumexp and fp16 token rows
 bool pass1q_ok(const Layout& L);
 hipError_t launch_pass1q(const Layout& L, const void* H, const int64_t* offsets, const uint8_t* mask, void* ws,
                          hipStream_t stream);

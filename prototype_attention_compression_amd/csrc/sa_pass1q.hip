@@ -48,11 +48,6 @@ struct Q1 {
   static constexpr int CHUNKS = kTile * CPR;       // 16-B chunks per tile (<= 512)
 };
 
-// LDS barrier: this wave's LDS operations are complete; global loads and
-// stores in flight stay in flight (a language-level barrier would wait for
-// the row prefetches too).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 __device__ __forceinline__ float log_add_exp2(float a, float b) {
   const float m = fmaxf(a, b);
   if (m == -INFINITY) return -INFINITY;
@@ -92,7 +87,8 @@ __global__ __launch_bounds__(kWaves * 64) void pass1_qres(const uint16_t* __rest
   const float qmax = __int_as_float(hdr[kHdrQmax]);
   const float lim2 = 10000.0f / fmaxf(qmax * qmax, 1e-30f);   // |h|^2 >= lim2  <=>  qmax |h| >= 100
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches on it
   const int col = lane & 31, g = lane >> 5;
 
   // A operands: the wave's NBW blocks of 32 query rows (lane = prototype row)
@@ -132,7 +128,9 @@ __global__ __launch_bounds__(kWaves * 64) void pass1_qres(const uint16_t* __rest
   };
   // widen, store to LDS buffer b and to the fp16 rows; keep words and the
   // per-wave "some logit may reach 100" bit.  A dropped token's row becomes
-  // zero here (whatever it held, NaN included).
+  // zero here (whatever it held, NaN included).  Runs for every iteration,
+  // past the last tile too (into a buffer nobody reads, no global store), so
+  // that consuming the prefetched registers never sits behind a branch.
   auto convert = [&](int32_t tile, int b, const u32x4& raw_in, uint32_t mb, bool in) {
     const bool keep = in && mb != 0u;
     const u32x4 raw = keep ? raw_in : u32x4{0u, 0u, 0u, 0u};
@@ -147,7 +145,7 @@ __global__ __launch_bounds__(kWaves * 64) void pass1_qres(const uint16_t* __rest
     for (int o = 1; o < C::CPR; o <<= 1) n2 += __shfl_xor(n2, o);
     if (conv) {
       *reinterpret_cast<half8*>(&rows[b][crow * C::PITCH + 16 * cch]) = hv;
-      *reinterpret_cast<half8*>(h16 + ((int64_t)tile * kTile + crow) * D + 8 * cch) = hv;
+      if (tile < tb) *reinterpret_cast<half8*>(h16 + ((int64_t)tile * kTile + crow) * D + 8 * cch) = hv;
       if (cch == 0) keep_words[b][crow] = keep ? 1u : 0u;
     }
     const bool big = conv && keep && n2 >= lim2;
@@ -242,15 +240,17 @@ __global__ __launch_bounds__(kWaves * 64) void pass1_qres(const uint16_t* __rest
   load(ta + 2, raw[0], mb[0], in[0]);
 
   // iteration j: convert tile j + 1 (loaded two iterations ago) into buffer
-  // (j + 1) % 3, load tile j + 3, compute tile j, finalize tile j - 1
+  // (j + 1) % 3, finalize tile j - 1, compute tile j, then load tile j + 3.  The wait for tile j + 1's registers counts vector memory
+  // operations in issue order; with the newest load the last one issued
+  // before it, that load stays in flight across the wait.
   auto iteration = [&](int j, auto oddc) {
     constexpr int R = decltype(oddc)::value;   // raw slot of tile j + 1
     lds_barrier();
     const int b = j % kBufs;
+    convert(ta + j + 1, (j + 1) % kBufs, raw[R], mb[R], in[R]);
     if (j >= 1) finalize(j - 1, (j + kBufs - 1) % kBufs);
-    if (j + 1 < n) convert(ta + j + 1, (j + 1) % kBufs, raw[R], mb[R], in[R]);
-    load(ta + j + 3, raw[R], mb[R], in[R]);
     compute(j, b);
+    load(ta + j + 3, raw[R], mb[R], in[R]);
   };
   int j = 0;
   for (; j + 1 < n; j += 2) {

@@ -28,21 +28,23 @@
 // The 2^14 scale cancels in U / m.
 //
 // Data movement: token rows reach LDS with direct global->LDS loads (16 B per
-// lane), 4 tiles (128 tokens) per stage, four stage buffers (loads run three
-// stages ahead: the loads are latency-bound, so the bytes in flight per CU
-// set their rate).  A row occupies 2d + 16 bytes (one 16-byte chunk of
-// padding, filled by the same loads); GEMM1's operand row m holds token
-// tau(m), which puts the 4 tokens of one transposing read 4 rows apart.  Then
-// the 16-byte GEMM1 reads and the transposing 8-byte reads both touch 64
-// distinct banks per pass (gfx950 LDS: 64 banks of 4 bytes), and every read
-// is one per-lane base register plus an immediate.
-// Every user's tile count is a multiple of 4 (pass 1 fills the padding tiles
-// with zero rows and A = 0), so every stage is full and the stage body is one
-// straight-line block.  A workgroup has up to 8 waves of 32 prototypes (two
-// waves per SIMD, every MFMA operand and result in VGPRs), so one wave's
-// exponentials and LDS reads run while the other wave's MFMAs execute.  LDS
-// read traffic is about 1 KB per MFMA; the feature step keeps the per-token -l
+// lane), 2 tiles (64 tokens) per stage, four stage buffers, loads two stages
+// ahead.  A row occupies 2d + 16 bytes (the last 16 are never read and never
+// loaded); GEMM1's operand row m holds token tau(m), which puts the 4 tokens
+// of one transposing read 4 rows apart.  Then the 16-byte GEMM1 reads and the
+// transposing 8-byte reads both touch 64 distinct banks per pass (gfx950
+// LDS: 64 banks of 4 bytes), and every read is one per-lane base register
+// plus an immediate.  Every user's tile count is a multiple of 4 (pass 1
+// fills the padding tiles with zero rows and A = 0), so every stage is full.
+// A workgroup has up to 8 waves of 32 prototypes (two waves per SIMD, every
+// MFMA operand and result in VGPRs).  The feature step keeps the per-token -l
 // down to 4 bytes per lane.
+//
+// Measured on MI355X, random fp16 operands hold the matrix cores near 1.7
+// PFLOP/s (power-limited clock) rather than the 2.5 nominal, and any other
+// work shares that power: moving fewer bytes counts more than issuing fewer
+// instructions.  Hence one copy of the rows (transposing reads for GEMM2)
+// rather than a second, transposed copy.
 //
 // Work item = (chunk of <= tiles_per_chunk tiles of one user, prototype block
 // of waves*32).  Workgroups are numbered so that the prototype blocks of one
@@ -60,8 +62,8 @@ namespace sa {
 
 namespace {
 
-constexpr int kStageTiles = 4;
-constexpr int kBufs = 4;           // stage buffers: loads run three stages ahead
+constexpr int kStageTiles = 2;
+constexpr int kBufs = 4;           // stage buffers: loads run two stages ahead
 
 template <int D>
 struct P2 {
@@ -69,26 +71,21 @@ struct P2 {
   static constexpr int DT = D / 32;                  // 32-column output blocks
   static constexpr int CPR = D / 8;                  // 16-B chunks per token row
   static constexpr int SLOTS = CPR + 1;              // ... plus one chunk of padding
-  static constexpr int PITCH = SLOTS * 16;           // LDS bytes per token row
+  static constexpr int PITCH = tile_pitch<D>();      // LDS bytes per token row
+  static_assert(PITCH == SLOTS * 16, "padded row");
   static constexpr int TILE_BYTES = kTile * PITCH;   // one tile of token rows
-  static constexpr int ROWS_BYTES = kStageTiles * TILE_BYTES;
-  static constexpr int NL_OFF = ROWS_BYTES;          // (-l_hi, -l_lo) pairs of the stage
+  static constexpr int NL_OFF = kStageTiles * TILE_BYTES;   // (-l_hi, -l_lo) pairs of the stage
   static constexpr int STAGE_BYTES = NL_OFF + kStageTiles * kTile * 4;
-  static constexpr int LOADS_ROWS = kStageTiles * kTile * SLOTS / 64;   // 1-KB direct loads per stage
-  static_assert(LOADS_ROWS * 64 == kStageTiles * kTile * SLOTS, "whole loads per stage");
+  static constexpr int LOADS = kStageTiles * kTile * SLOTS / 64;   // 1-KB direct loads per stage
+  static_assert(LOADS * 64 == kStageTiles * kTile * SLOTS, "whole loads per stage");
+  static_assert(STAGE_BYTES % 256 == 0, "load alignment");
 };
 
-// Token held by GEMM1 operand row m (m = 16 kk + 8 h + 4 g + e in bits):
-// 16 kk + 4 e + 2 g + h.  GEMM1's accumulator rows are GEMM2's K order, so
-// the 4 tokens of one transposing read (e = 0..3) lie 4 rows apart; with the
-// padded row pitch (2d + 16 bytes) such a read (32 lanes: 4 tokens x 64
-// bytes) meets all 64 banks once, and so do the 16-byte GEMM1 reads (16
-// consecutive operand rows, one chunk).
-__device__ __forceinline__ int tau(int m) {
-  return (m & 16) | ((m & 3) << 2) | (((m >> 2) & 1) << 1) | ((m >> 3) & 1);
-}
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
@@ -117,7 +114,8 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   const int32_t t0 = tile_base[u] + ci * CT;
   const int nt = min(CT, tiles_u - ci * CT);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches on it
   const int col = lane & 31, g = lane >> 5;
   // the wave owns NB blocks of 32 prototypes: p0 + 32 b + (0 .. 31)
   const int p0 = pb * (WAVES * NB * kProtoPerWave) + wave * (NB * kProtoPerWave);
@@ -137,50 +135,70 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   const char* h16 = reinterpret_cast<const char*>(ws_f16(ws, L.off_h16));
   const char* nlg = reinterpret_cast<const char*>(ws_i32(ws, L.off_nl));
 
-  // Direct loads of stage `ts` (tiles 4 ts .. 4 ts + 3 of the chunk) into
+  // Direct loads of stage `ts` (tiles 2 ts, 2 ts + 1 of the chunk) into
   // buffer b.  Load i fills LDS bytes [1024 i, 1024 i + 1024) of the stage:
-  // lane l writes 16-byte slot 64 i + l = (row q / SLOTS, chunk q % SLOTS);
-  // the padding chunk re-reads chunk 0 of its row.  Row loads go round-robin
-  // over the waves, and every wave adds one slice of the -l pairs; a wave's
-  // vmcnt waits count its own loads (LMAX or LMIN per stage).
-  constexpr int LMAX = (C::LOADS_ROWS + WAVES - 1) / WAVES + 1;
-  constexpr int LMIN = C::LOADS_ROWS / WAVES + 1;
-  static_assert(2 * LMAX < 64, "vmcnt range");
-  const bool big = (C::LOADS_ROWS % WAVES == 0) || (wave < C::LOADS_ROWS % WAVES);
+  // lane l writes 16-byte slot 64 i + l = (row q / SLOTS, chunk q % SLOTS),
+  // except the padding chunk, which no lane loads.  Loads go round-robin over
+  // the waves (load i to wave i % WAVES), and every wave adds one slice of
+  // the -l pairs; a wave's vmcnt waits count its own loads (LMAX or LMIN per
+  // stage).  A lane's source offsets inside the stage's tiles are the same
+  // for every stage, so they are computed once (~0 marks a padding slot).
+  constexpr int KMAX = (C::LOADS + WAVES - 1) / WAVES;
+  constexpr int LMAX = KMAX + 1;
+  constexpr int LMIN = C::LOADS / WAVES + 1;
+  const bool big = (C::LOADS % WAVES == 0) || (wave < C::LOADS % WAVES);
+  uint32_t src_off[KMAX];
+#pragma unroll
+  for (int kq = 0; kq < KMAX; ++kq) {
+    const int q = 64 * (wave + kq * WAVES) + lane;
+    const int row = q / C::SLOTS;
+    const int c = q - row * C::SLOTS;
+    src_off[kq] = c == C::CPR ? ~0u : (uint32_t)(row * (D * 2) + c * 16);
+  }
   auto issue = [&](int ts, int b) {
     char* base = lds + b * C::STAGE_BYTES;
     const int64_t tile0 = (int64_t)t0 + (int64_t)ts * kStageTiles;
-#pragma unroll 1
-    for (int i = wave; i < C::LOADS_ROWS; i += WAVES) {
-      const int q = 64 * i + lane;
-      const int row = q / C::SLOTS;
-      int c = q - row * C::SLOTS;
-      c = c == C::CPR ? 0 : c;
-      const char* src = h16 + (tile0 * kTile + row) * (D * 2) + c * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(base + 1024 * i), 16, 0, 0);
+    const char* rows_src = h16 + tile0 * (kTile * D * 2);
+#pragma unroll
+    for (int kq = 0; kq < KMAX; ++kq) {
+      const int i = wave + kq * WAVES;
+      if (i < C::LOADS && src_off[kq] != ~0u) {   // i uniform; the padding slot per lane
+        // (a named pointer: given the sum directly, the host compilation pass
+        // silently drops this kernel's instantiation)
+        const char* src = rows_src + src_off[kq];
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(base + 1024 * i), 16, 0, 0);
+      }
     }
     constexpr int NL_LANES = kStageTiles * kTile * 4 / 16 / WAVES;   // 16-B pieces per wave
+    static_assert(NL_LANES * 16 * WAVES == kStageTiles * kTile * 4, "whole -l slices");
     if (lane < NL_LANES) {
       const char* src = nlg + tile0 * (kTile * 4) + (wave * NL_LANES + lane) * 16;
       __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(base + C::NL_OFF + wave * NL_LANES * 16), 16, 0, 0);
     }
   };
   // wait until only this wave's loads of the `later` stages after the
-  // current one are still in flight
+  // current one are still in flight (later <= kBufs - 2)
   auto wait_stage = [&](int later) {
-    if (later >= 2) {
-      if (big) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LMAX));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LMIN));
-    } else if (later == 1) {
-      if (big) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LMAX));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(LMIN));
-    } else {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if constexpr (kBufs > 3) {
+      if (later >= 2) {
+        if (big) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LMAX));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LMIN));
+        return;
+      }
     }
+    if constexpr (kBufs > 2) {
+      if (later == 1) {
+        if (big) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LMAX));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(LMIN));
+        return;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   };
-  static_assert(kBufs == 4, "the stage loop below is unrolled over 4 buffers");
+  static_assert(kBufs >= 3 && kBufs <= 4, "loads one or two stages ahead");
+  static_assert((kBufs - 1) * LMAX < 64, "vmcnt range");
 
-  // per-lane byte offsets of the transposing reads (GEMM2 B operands):
+  // per-lane byte offset of the transposing reads (GEMM2 B operands):
   // source lane i16 of 16-lane group gh reads the row of token 4 (i16 / 4) +
   // 2 g (+ 16 kk + h) at columns 16 gh + 4 (i16 % 4) (+ 32 dt) .. + 3, which
   // is K element 4 h + i16 / 4 of lane half g in GEMM1's row order (tau)
@@ -200,98 +218,216 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   const int tcol = tau(col);
   const int ha_base = tcol * C::PITCH + 16 * g;
 
-  // One stage held in buffer B (a compile-time constant, so every LDS read is
-  // a per-lane offset register plus an immediate).
+  // Per-tile software pipeline; period t (one tile) of a wave:
+  //   1. if tile t+1 opens stage s: wait for this wave's loads of stage s,
+  //      barrier, issue the loads of stage s + kAhead;
+  //   2. LDS reads of GEMM1's operands for tile t+1 (and its -l pair);
+  //   3. GEMM2 of tile t-1 (its operands in registers since period t-1),
+  //      interleaved with the exponentials of tile t (whose GEMM1 ran in
+  //      period t-1): these MFMAs cover step 2's latency and the VALU work;
+  //   4. LDS reads of GEMM2's operands for tile t;
+  //   5. GEMM1 of tile t+1, covering step 4's latency.
+  // Loads run kAhead = kBufs - 2 stages ahead, so the buffer of the stage
+  // before the current one still holds tile t when step 4 reads it.
+  constexpr int kAhead = kBufs - 2;
+  static_assert(kAhead >= 1, "at least one stage of loads in flight");
   const int nstages = nt / kStageTiles;
-  auto stage = [&](int st, auto Bc) {
-    constexpr int B = decltype(Bc)::value;
-    // this wave's loads of stage st have landed (those of st+1, st+2 may still fly)
-    wait_stage(min(2, nstages - 1 - st));
-    __syncthreads();                             // ... every wave's; stage st-1's buffer is free
-    if (st + 3 < nstages) issue(st + 3, (B + 3) % kBufs);
-    const char* base = lds + B * C::STAGE_BYTES;
-    typedef __attribute__((address_space(3))) s16x4* tr_ptr;
-    // GEMM1 of tile t: C[tok, proto] = h_tok . q_proto - l_tok
-    auto gemm1 = [&](int t, float16v (&Cm)[NB]) {
-      const char* rows = base + t * C::TILE_BYTES;
-      const uint32_t nlp = reinterpret_cast<const uint32_t*>(base + C::NL_OFF)[t * kTile + tcol];
-      half8 ha[C::S];
+  auto tile_lds = [&](int t) { return lds + ((t / kStageTiles) % kBufs) * C::STAGE_BYTES; };
+  auto boundary = [&](int t1) {   // before the first read of tile t1
+    if (t1 % kStageTiles == 0) {  // uniform
+      const int st = t1 / kStageTiles;
+      wait_stage(min(kAhead - 1, nstages - 1 - st));
+      lds_barrier();              // stage st in LDS; every read of stage st - 2 is done
+      if (st + kAhead < nstages) issue(st + kAhead, (st + kAhead) % kBufs);
+    }
+  };
+  // GEMM1 operands of tile t: row of token tau(col), chunk 2 s + g; -l pair
+  auto read_a = [&](int t, half8 (&ha)[C::S], uint32_t& nlp) {
+    const char* base = tile_lds(t);
+    const char* rows = base + (t % kStageTiles) * C::TILE_BYTES + ha_base;
 #pragma unroll
-      for (int s = 0; s < C::S; ++s) ha[s] = *reinterpret_cast<const half8*>(rows + ha_base + 32 * s);
-      const u32x4 fv = {g == 0 ? nlp : 0u, 0u, 0u, 0u};
+    for (int s = 0; s < C::S; ++s) ha[s] = *reinterpret_cast<const half8*>(rows + 32 * s);
+    nlp = reinterpret_cast<const uint32_t*>(base + C::NL_OFF)[(t % kStageTiles) * kTile + tcol];
+  };
+  // GEMM1: C[tok, proto] = h_tok . q_proto - l_tok (the feature step adds
+  // -l), split after its first K step
+  auto gemm1_head = [&](const half8 (&ha)[C::S], uint32_t nlp, float16v (&Cm)[NB]) {
+    const u32x4 fv = {g == 0 ? nlp : 0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int b = 0; b < NB; ++b) Cm[b] = mfma32x32x16(__builtin_bit_cast(half8, fv), qfeat, float16v{});
+    for (int b = 0; b < NB; ++b) Cm[b] = mfma32x32x16(__builtin_bit_cast(half8, fv), qfeat, float16v{});
 #pragma unroll
-      for (int s = 0; s < C::S; ++s)
+    for (int b = 0; b < NB; ++b) Cm[b] = mfma32x32x16(ha[0], qf[b][0], Cm[b]);
+  };
+  auto gemm1_tail = [&](const half8 (&ha)[C::S], float16v (&Cm)[NB]) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) Cm[b] = mfma32x32x16(ha[s], qf[b][s], Cm[b]);
-    };
-    // allocations 2^C (= 2^14 A) in fp16, masses of the rounded values
-    auto expo = [&](const float16v (&Cm)[NB], half8 (&ap)[NB][2]) {
+    for (int s = 1; s < C::S; ++s)
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            float2v v = {__builtin_amdgcn_exp2f(Cm[b][8 * kk + e]), __builtin_amdgcn_exp2f(Cm[b][8 * kk + e + 1])};
-            half2v h = __builtin_convertvector(v, half2v);
-            msum[b] = __builtin_amdgcn_fdot2(h, ones, msum[b], false);
-            ap[b][kk][e] = h[0];
-            ap[b][kk][e + 1] = h[1];
-          }
-    };
-    // GEMM2 of tile t: U[proto, c] += sum_tok A'[proto, tok] h_tok[c]
-    auto gemm2 = [&](int t, const half8 (&ap)[NB][2]) {
-      const char* rows = base + t * C::TILE_BYTES + tr_base;
+      for (int b = 0; b < NB; ++b) Cm[b] = mfma32x32x16(ha[s], qf[b][s], Cm[b]);
+  };
+  // GEMM2 operands of tile t: hb[kk][dt] = rows 16 kk + (0, 1) of the
+  // transposing read at columns 64 dt (lo, hi: one row pitch apart).  The
+  // reads are written out with their wait in one asm block: with direct
+  // loads into LDS in flight, the compiler would put a full vector-memory
+  // wait (every prefetch) in front of a transposing-read builtin.
+  auto read_b = [&](int t, half8 (&hb)[2][C::DT]) {
+    const uint32_t a = lds_addr(tile_lds(t) + (t % kStageTiles) * C::TILE_BYTES) + tr_base;
+    if constexpr (D == 128) {
+      static_assert(D != 128 || C::PITCH == 272, "offsets below: 16 kk PITCH + 64 dt + h PITCH");
+      s16x4 r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11, r12, r13, r14, r15;
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %16\n\t"
+          "ds_read_b64_tr_b16 %1, %16 offset:272\n\t"
+          "ds_read_b64_tr_b16 %2, %16 offset:64\n\t"
+          "ds_read_b64_tr_b16 %3, %16 offset:336\n\t"
+          "ds_read_b64_tr_b16 %4, %16 offset:128\n\t"
+          "ds_read_b64_tr_b16 %5, %16 offset:400\n\t"
+          "ds_read_b64_tr_b16 %6, %16 offset:192\n\t"
+          "ds_read_b64_tr_b16 %7, %16 offset:464\n\t"
+          "ds_read_b64_tr_b16 %8, %16 offset:4352\n\t"
+          "ds_read_b64_tr_b16 %9, %16 offset:4624\n\t"
+          "ds_read_b64_tr_b16 %10, %16 offset:4416\n\t"
+          "ds_read_b64_tr_b16 %11, %16 offset:4688\n\t"
+          "ds_read_b64_tr_b16 %12, %16 offset:4480\n\t"
+          "ds_read_b64_tr_b16 %13, %16 offset:4752\n\t"
+          "ds_read_b64_tr_b16 %14, %16 offset:4544\n\t"
+          "ds_read_b64_tr_b16 %15, %16 offset:4816\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7), "=&v"(r8),
+            "=&v"(r9), "=&v"(r10), "=&v"(r11), "=&v"(r12), "=&v"(r13), "=&v"(r14), "=&v"(r15)
+          : "v"(a));
+      const s16x4 r[16] = {r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11, r12, r13, r14, r15};
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) {
-          const char* pr0 = rows + 16 * kk * C::PITCH + 64 * dt;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(pr0));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(pr0 + C::PITCH));
-          const s16x8 hb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-          for (int b = 0; b < NB; ++b) U[b][dt] = mfma32x32x16(ap[b][kk], __builtin_bit_cast(half8, hb), U[b][dt]);
+        for (int dt = 0; dt < 4; ++dt) {
+          const s16x4 lo = r[8 * kk + 2 * dt], hi = r[8 * kk + 2 * dt + 1];
+          hb[kk][dt] = __builtin_bit_cast(half8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         }
-    };
-    // Pipeline within the stage: GEMM1 of tile t+1 is issued interleaved
-    // with the exponentials of tile t (independent work), then GEMM2 of t.
-    float16v Ca[NB], Cb[NB];
-    half8 ap[NB][2];
-    __builtin_amdgcn_sched_barrier(0);
-    gemm1(0, Ca);
+    } else {
+      static_assert(D != 64 || C::PITCH == 144, "offsets below: 16 kk PITCH + 64 dt + h PITCH");
+      s16x4 r0, r1, r2, r3, r4, r5, r6, r7;
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %8\n\t"
+          "ds_read_b64_tr_b16 %1, %8 offset:144\n\t"
+          "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+          "ds_read_b64_tr_b16 %3, %8 offset:208\n\t"
+          "ds_read_b64_tr_b16 %4, %8 offset:2304\n\t"
+          "ds_read_b64_tr_b16 %5, %8 offset:2448\n\t"
+          "ds_read_b64_tr_b16 %6, %8 offset:2368\n\t"
+          "ds_read_b64_tr_b16 %7, %8 offset:2512\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+          : "v"(a));
+      const s16x4 r[8] = {r0, r1, r2, r3, r4, r5, r6, r7};
 #pragma unroll
-    for (int t = 0; t < kStageTiles; ++t) {
-      float16v (&Cx)[NB] = (t & 1) ? Cb : Ca;
-      float16v (&Cy)[NB] = (t & 1) ? Ca : Cb;
-      __builtin_amdgcn_sched_barrier(0);
-      if (t + 1 < kStageTiles) {
-        gemm1(t + 1, Cy);
-        expo(Cx, ap);
-        __builtin_amdgcn_sched_group_barrier(0x100, C::S + 1, 0);   // GEMM1 LDS reads
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int i = 0; i < NB * (C::S + 1); ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // 1 MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);        // 4 VALU
+        for (int dt = 0; dt < 2; ++dt) {
+          const s16x4 lo = r[4 * kk + 2 * dt], hi = r[4 * kk + 2 * dt + 1];
+          hb[kk][dt] = __builtin_bit_cast(half8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         }
-      } else {
-        expo(Cx, ap);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      gemm2(t, ap);
     }
   };
-  issue(0, 0);
-  if (nstages > 1) issue(1, 1);
-  if (nstages > 2) issue(2, 2);
-  for (int st = 0; st < nstages; st += kBufs) {
-    stage(st, std::integral_constant<int, 0>{});
-    if (st + 1 < nstages) stage(st + 1, std::integral_constant<int, 1>{});
-    if (st + 2 < nstages) stage(st + 2, std::integral_constant<int, 2>{});
-    if (st + 3 < nstages) stage(st + 3, std::integral_constant<int, 3>{});
+  // allocations 2^C (= 2^14 A) in fp16 for accumulator elements 2 i, 2 i + 1
+  // (i = 0..7), and the masses of the rounded values
+  auto expo2 = [&](const float16v (&Cm)[NB], half8 (&ap)[NB][2], int i) {
+    const int kk = i >> 2, e = 2 * (i & 3);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float2v v = {__builtin_amdgcn_exp2f(Cm[b][8 * kk + e]), __builtin_amdgcn_exp2f(Cm[b][8 * kk + e + 1])};
+      half2v h = __builtin_convertvector(v, half2v);
+      // keep the conversion (and its exponentials) here, between this
+      // period's MFMAs, instead of next to the MFMA that consumes it
+      asm volatile("" ::"v"(h));
+      msum[b] = __builtin_amdgcn_fdot2(h, ones, msum[b], false);
+      ap[b][kk][e] = h[0];
+      ap[b][kk][e + 1] = h[1];
+    }
+  };
+  // GEMM2 step m (m = 0 .. 2 DT - 1): U[proto, c] += sum_tok A'[proto, tok] h_tok[c]
+  constexpr int M2 = 2 * C::DT;
+  constexpr int EPM = 8 / M2;     // exponential pairs per GEMM2 step
+  auto mma2 = [&](const half8 (&hb)[2][C::DT], const half8 (&ap)[NB][2], int m) {
+    const int kk = m / C::DT, dt = m % C::DT;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) U[b][dt] = mfma32x32x16(ap[b][kk], hb[kk][dt], U[b][dt]);
+  };
+
+  float16v C0[NB], C1[NB];
+  half8 ap0[NB][2], ap1[NB][2];
+  half8 ha[C::S], hb[2][C::DT];
+  uint32_t nlp;
+  // Period t runs GEMM2 of tile t-2 interleaved with the exponentials of
+  // tile t-1, then GEMM1 of tile t+1, so every MFMA result is consumed a
+  // whole period after its chain was issued (issue is in order per wave,
+  // and both waves of a SIMD would otherwise stall on the same chain).
+  // Registers: C(t-1) and C(t+1) share a set (GEMM1 of t+1 starts after the
+  // exponentials of t-1 have read it), C(t) the other; A'(t-2) and A'(t-1)
+  // one set each.  Flags (compile-time): G2 GEMM2 of t-2, EX exponentials
+  // of t-1, MORE a tile t+1 follows, RB GEMM2's reads of tile t-1.
+  // While direct-to-LDS loads are in flight the compiler can only wait for
+  // all outstanding LDS reads of the wave, so each batch of reads is issued
+  // one MFMA after the wait for the previous batch and consumed several MFMAs
+  // later: GEMM1's reads of tile t+1 after the first GEMM2 step, GEMM2's
+  // reads of tile t-1 after GEMM1's first step.
+  auto period = [&](int t, float16v (&Cx)[NB], half8 (&apc)[NB][2], half8 (&app)[NB][2], auto g2c, auto exc,
+                    auto morec, auto rbc) {
+    constexpr bool G2 = decltype(g2c)::value, EX = decltype(exc)::value;
+    constexpr bool MORE = decltype(morec)::value, RB = decltype(rbc)::value;
+    if constexpr (MORE) boundary(t + 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < M2; ++m) {
+      if constexpr (G2) mma2(hb, app, m);
+      if constexpr (EX) {
+#pragma unroll
+        for (int x = 0; x < EPM; ++x) expo2(Cx, apc, m * EPM + x);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MORE) {
+        if (m == 0) {
+          read_a(t + 1, ha, nlp);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    if constexpr (MORE) {
+      gemm1_head(ha, nlp, Cx);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (RB) {
+      read_b(t - 1, hb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (MORE) {
+      gemm1_tail(ha, Cx);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+
+#pragma unroll
+  for (int st = 0; st < kAhead; ++st)
+    if (st < nstages) issue(st, st);
+  boundary(0);
+  read_a(0, ha, nlp);
+  gemm1_head(ha, nlp, C0);
+  gemm1_tail(ha, C0);
+  // nt is a positive multiple of 4 (a chunk holds whole stages of a user's
+  // tiles).  Parity p = t % 2: C(t-1), C(t+1) in set p ^ 1, A'(t-1) in set
+  // p ^ 1, A'(t-2) in set p.
+  period(0, C1, ap1, ap0, F_{}, F_{}, T_{}, F_{});
+  period(1, C0, ap0, ap1, F_{}, T_{}, T_{}, T_{});
+  int t = 2;
+  for (; t < nt - 2; t += 2) {
+    period(t, C1, ap1, ap0, T_{}, T_{}, T_{}, T_{});
+    period(t + 1, C0, ap0, ap1, T_{}, T_{}, T_{}, T_{});
   }
+  period(nt - 2, C1, ap1, ap0, T_{}, T_{}, T_{}, T_{});
+  period(nt - 1, C0, ap0, ap1, T_{}, T_{}, F_{}, T_{});
+  period(nt, C1, ap1, ap0, T_{}, T_{}, F_{}, T_{});
+  period(nt + 1, C0, ap0, ap1, T_{}, F_{}, F_{}, F_{});
 
   float* part_u = ws_f32(ws, L.off_part_u) + (int64_t)chunk * L.k * D;
   float* part_m = ws_f32(ws, L.off_part_m) + (int64_t)chunk * L.k;
