@@ -52,6 +52,83 @@ __device__ __forceinline__ int tau(int m) {
   return (m & 16) | ((m & 3) << 2) | (((m >> 2) & 1) << 1) | ((m >> 3) & 1);
 }
 
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// GEMM2's B operands from one padded fp16 token tile in LDS (row pitch
+// tile_pitch<D>()), with the gfx950 transposing read ds_read_b64_tr_b16:
+// within each group of 16 lanes, destination lane i receives element i % 4 of
+// the 4-element vectors that source lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12
+// address.  `addr` is the tile's LDS address plus the lane's offset (source
+// lane i16 of 16-lane group gh, lane half g: row 4 (i16 / 4) + 2 g, column
+// 16 gh + 4 (i16 % 4)); hb[kk][dt] = the reads at rows + 16 kk (lo) and
+// + 16 kk + 1 (hi), columns + 32 dt.  Written with its wait in one asm
+// block: while direct loads into LDS are in flight, the compiler puts a wait
+// for every outstanding vector-memory operation (all prefetches) in front of
+// the builtin form of this read.
+template <int D>
+__device__ __forceinline__ void tile_tr_reads(uint32_t addr, half8 (&hb)[2][D / 32]) {
+  static_assert(D == 128 || D == 64, "d = 64 or 128");
+  if constexpr (D == 128) {
+    static_assert(tile_pitch<128>() == 272, "offsets below: 16 kk 272 + 64 dt (+ 272)");
+    s16x4 r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11, r12, r13, r14, r15;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:272\n\t"
+        "ds_read_b64_tr_b16 %2, %16 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %16 offset:336\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:128\n\t"
+        "ds_read_b64_tr_b16 %5, %16 offset:400\n\t"
+        "ds_read_b64_tr_b16 %6, %16 offset:192\n\t"
+        "ds_read_b64_tr_b16 %7, %16 offset:464\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:4352\n\t"
+        "ds_read_b64_tr_b16 %9, %16 offset:4624\n\t"
+        "ds_read_b64_tr_b16 %10, %16 offset:4416\n\t"
+        "ds_read_b64_tr_b16 %11, %16 offset:4688\n\t"
+        "ds_read_b64_tr_b16 %12, %16 offset:4480\n\t"
+        "ds_read_b64_tr_b16 %13, %16 offset:4752\n\t"
+        "ds_read_b64_tr_b16 %14, %16 offset:4544\n\t"
+        "ds_read_b64_tr_b16 %15, %16 offset:4816\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7), "=&v"(r8),
+          "=&v"(r9), "=&v"(r10), "=&v"(r11), "=&v"(r12), "=&v"(r13), "=&v"(r14), "=&v"(r15)
+        : "v"(addr));
+    const s16x4 r[16] = {r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11, r12, r13, r14, r15};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const s16x4 lo = r[8 * kk + 2 * dt], hi = r[8 * kk + 2 * dt + 1];
+        hb[kk][dt] = __builtin_bit_cast(half8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      }
+  } else {
+    static_assert(tile_pitch<64>() == 144, "offsets below: 16 kk 144 + 64 dt (+ 144)");
+    s16x4 r0, r1, r2, r3, r4, r5, r6, r7;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:144\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:208\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:2304\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:2448\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:2368\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:2512\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+        : "v"(addr));
+    const s16x4 r[8] = {r0, r1, r2, r3, r4, r5, r6, r7};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const s16x4 lo = r[4 * kk + 2 * dt], hi = r[4 * kk + 2 * dt + 1];
+        hb[kk][dt] = __builtin_bit_cast(half8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      }
+  }
+}
+
 // Exact widening of 8 packed bf16 values (one 16-byte load) to fp16.  bf16
 // values whose magnitude lies in [2^-17, 65504] are exactly representable in
 // fp16; the conversion truncates toward zero so larger values saturate.

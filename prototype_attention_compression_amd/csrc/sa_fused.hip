@@ -239,6 +239,43 @@ __device__ __forceinline__ void fused_body(const Layout& L, void* ws, char* lds,
     const int chunk = 2 * gh + ((i16 & 3) >> 1);
     er_off[h] = row * 64 + ((chunk ^ x) * 16) + 8 * (i16 & 1);
   }
+  // Allocation staging round trip of one tile (both blocks, block b at
+  // + 2048 b): the 16-byte writes (lane = token), then the transposing reads
+  // (lane = prototype), in one asm block with one wait at the end.  A wave's
+  // LDS operations complete in issue order, so the reads see the writes.  As
+  // builtins, the compiler would put a wait for every outstanding load (all
+  // direct-load prefetches) in front of them.
+  const uint32_t a_w0 = lds_addr(ebuf + ew0), a_w1 = lds_addr(ebuf + ew1);
+  const uint32_t a_r0 = lds_addr(ebuf + er_off[0]), a_r1 = lds_addr(ebuf + er_off[1]);
+  auto stage_allocations = [&](const half8 (&w)[kNB][2], half8 (&ap)[kNB][2]) {
+    static_assert(kNB == 2, "two blocks, at + 0 and + 2048");
+    s16x4 r0, r1, r2, r3, r4, r5, r6, r7;
+    asm volatile(
+        "ds_write_b128 %8, %12\n\t"
+        "ds_write_b128 %9, %13\n\t"
+        "ds_write_b128 %8, %14 offset:2048\n\t"
+        "ds_write_b128 %9, %15 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %0, %10\n\t"
+        "ds_read_b64_tr_b16 %1, %11\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:256\n\t"
+        "ds_read_b64_tr_b16 %3, %11 offset:256\n\t"
+        "ds_read_b64_tr_b16 %4, %10 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %5, %11 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %6, %10 offset:2304\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:2304\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+        : "v"(a_w0), "v"(a_w1), "v"(a_r0), "v"(a_r1), "v"(w[0][0]), "v"(w[0][1]), "v"(w[1][0]), "v"(w[1][1])
+        : "memory");
+    const s16x4 r[8] = {r0, r1, r2, r3, r4, r5, r6, r7};
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const s16x4 lo = r[4 * b + 2 * kk], hi = r[4 * b + 2 * kk + 1];
+        ap[b][kk] = __builtin_bit_cast(half8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      }
+  };
 
   const int32_t* tile_base = ws_i32(ws, L.off_tile_base);
   float* part_u_all = ws_f32(ws, L.off_part_u);
@@ -417,23 +454,17 @@ __device__ __forceinline__ void fused_body(const Layout& L, void* ws, char* lds,
         half8 ap[kNB][2];
         if (CONS) {
           const float r = zring[zc * kTile + col];
+          half8 w[kNB][2];
 #pragma unroll
           for (int b = 0; b < kNB; ++b) {
             float sc;
             if (!EXACT) sc = pl[EC][b] * r;
             else sc = __builtin_amdgcn_exp2f(pl[EC][b] - r + 14.0f);
             const _Float16 hs = (_Float16)sc;
-            char* eb = ebuf + b * 2048;
-            *reinterpret_cast<half8*>(eb + ew0) = e[EC][b][0] * hs;
-            *reinterpret_cast<half8*>(eb + ew1) = e[EC][b][1] * hs;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-              const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(eb + kk * 256 + er_off[0]));
-              const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(eb + kk * 256 + er_off[1]));
-              const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-              ap[b][kk] = __builtin_bit_cast(half8, v);
-            }
+            w[b][0] = e[EC][b][0] * hs;
+            w[b][1] = e[EC][b][1] * hs;
           }
+          stage_allocations(w, ap);
         }
         float16v acc[kNB];
 #pragma unroll
@@ -466,18 +497,14 @@ __device__ __forceinline__ void fused_body(const Layout& L, void* ws, char* lds,
         }
         __builtin_amdgcn_sched_barrier(0);
         if (CONS) {
-          const char* rows = lds + (B2 * C::STAGE_BYTES + t2 * C::TILE_BYTES + tr_base);
+          half8 hb[2][C::DT];
+          tile_tr_reads<D>(lds_addr(lds + (B2 * C::STAGE_BYTES + t2 * C::TILE_BYTES + tr_base)), hb);
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt) {
-              const char* pr0 = rows + 16 * kk * C::PITCH + 64 * dt;
-              const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(pr0));
-              const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(pr0 + C::PITCH));
-              const s16x8 hb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-              for (int b = 0; b < kNB; ++b) U[b][dt] = mfma32x32x16(ap[b][kk], __builtin_bit_cast(half8, hb), U[b][dt]);
-            }
+              for (int b = 0; b < kNB; ++b) U[b][dt] = mfma32x32x16(ap[b][kk], hb[kk][dt], U[b][dt]);
         }
         if (G1) {
           float pv[kNB];

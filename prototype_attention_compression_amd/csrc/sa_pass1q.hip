@@ -21,7 +21,8 @@
 //   * compute (each wave: its k/8 prototypes, NBW blocks of 32): 8 16-byte
 //     operand reads, NBW x 8 fp16 MFMAs (lane = token, so the sum over
 //     prototypes stays in the lane), exponentials and sums;
-//   * the first wave turns the previous tile's 8 partials into -l pairs.
+//   * every wave turns 4 tokens of the previous tile from 8 partials into
+//     -l pairs.
 // One barrier per tile; three LDS tile buffers (convert t+1 while computing
 // t); the global loads run two tiles ahead in registers.
 #include <hip/hip_runtime.h>
@@ -203,13 +204,16 @@ __global__ __launch_bounds__(kWaves * 64) void pass1_qres(const uint16_t* __rest
     if (g == 0) part[j & 1][col][wave] = wpart;
   };
 
-  // -l pairs of tile j (buffer b) from its 8 partials (first wave, lanes 0..31)
+  // -l pairs of tile j (buffer b) from its 8 partials: wave w, lanes 0..3,
+  // tokens 4 w .. 4 w + 3
   auto finalize = [&](int j, int b) {
-    if (wave != 0 || g != 0) return;
+    constexpr int TPW = kTile / kWaves;   // tokens per wave
+    if (lane >= TPW) return;
+    const int tok = wave * TPW + lane;
     const u32x4 e0 = *reinterpret_cast<const u32x4*>(&exact_bits[b][0]);
     const u32x4 e1 = *reinterpret_cast<const u32x4*>(&exact_bits[b][4]);
     const bool exact = (e0[0] | e0[1] | e0[2] | e0[3] | e1[0] | e1[1] | e1[2] | e1[3]) != 0u;
-    const float* pp = part[j & 1][col];
+    const float* pp = part[j & 1][tok];
     float lse;
     if (!exact) {
       float s = 0.f;
@@ -221,13 +225,13 @@ __global__ __launch_bounds__(kWaves * 64) void pass1_qres(const uint16_t* __rest
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) lse = log_add_exp2(lse, pp[w]);
     }
-    const bool keep = keep_words[b][col] != 0u;
+    const bool keep = keep_words[b][tok] != 0u;
     // -l = 14 - lse as an fp16 pair (hi, lo) with hi + lo = -l to ~2^-16
     const float nlv = keep ? kAllocShift - lse : -60000.0f;
     const _Float16 hi = (_Float16)nlv;
     const _Float16 lo = keep ? (_Float16)(nlv - (float)hi) : (_Float16)0.0f;
     const half2v pr = {hi, lo};
-    nl[(int64_t)(ta + j) * kTile + col] = __builtin_bit_cast(uint32_t, pr);
+    nl[(int64_t)(ta + j) * kTile + tok] = __builtin_bit_cast(uint32_t, pr);
   };
 
   // prologue: tiles 0 and 1 loaded, tile 0 converted into buffer 0

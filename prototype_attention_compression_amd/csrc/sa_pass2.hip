@@ -28,7 +28,7 @@
 // The 2^14 scale cancels in U / m.
 //
 // Data movement: token rows reach LDS with direct global->LDS loads (16 B per
-// lane), 2 tiles (64 tokens) per stage, four stage buffers, loads two stages
+// lane), 4 tiles (128 tokens) per stage, four stage buffers, loads two stages
 // ahead.  A row occupies 2d + 16 bytes (the last 16 are never read and never
 // loaded); GEMM1's operand row m holds token tau(m), which puts the 4 tokens
 // of one transposing read 4 rows apart.  Then the 16-byte GEMM1 reads and the
@@ -62,7 +62,7 @@ namespace sa {
 
 namespace {
 
-constexpr int kStageTiles = 2;
+constexpr int kStageTiles = 4;
 constexpr int kBufs = 4;           // stage buffers: loads run two stages ahead
 
 template <int D>
@@ -83,9 +83,6 @@ struct P2 {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
@@ -135,7 +132,7 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   const char* h16 = reinterpret_cast<const char*>(ws_f16(ws, L.off_h16));
   const char* nlg = reinterpret_cast<const char*>(ws_i32(ws, L.off_nl));
 
-  // Direct loads of stage `ts` (tiles 2 ts, 2 ts + 1 of the chunk) into
+  // Direct loads of stage `ts` (tiles 4 ts .. 4 ts + 3 of the chunk) into
   // buffer b.  Load i fills LDS bytes [1024 i, 1024 i + 1024) of the stage:
   // lane l writes 16-byte slot 64 i + l = (row q / SLOTS, chunk q % SLOTS),
   // except the padding chunk, which no lane loads.  Loads go round-robin over
@@ -264,69 +261,9 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) Cm[b] = mfma32x32x16(ha[s], qf[b][s], Cm[b]);
   };
-  // GEMM2 operands of tile t: hb[kk][dt] = rows 16 kk + (0, 1) of the
-  // transposing read at columns 64 dt (lo, hi: one row pitch apart).  The
-  // reads are written out with their wait in one asm block: with direct
-  // loads into LDS in flight, the compiler would put a full vector-memory
-  // wait (every prefetch) in front of a transposing-read builtin.
+  // GEMM2 operands of tile t (transposing reads, waited for inside)
   auto read_b = [&](int t, half8 (&hb)[2][C::DT]) {
-    const uint32_t a = lds_addr(tile_lds(t) + (t % kStageTiles) * C::TILE_BYTES) + tr_base;
-    if constexpr (D == 128) {
-      static_assert(D != 128 || C::PITCH == 272, "offsets below: 16 kk PITCH + 64 dt + h PITCH");
-      s16x4 r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11, r12, r13, r14, r15;
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %16\n\t"
-          "ds_read_b64_tr_b16 %1, %16 offset:272\n\t"
-          "ds_read_b64_tr_b16 %2, %16 offset:64\n\t"
-          "ds_read_b64_tr_b16 %3, %16 offset:336\n\t"
-          "ds_read_b64_tr_b16 %4, %16 offset:128\n\t"
-          "ds_read_b64_tr_b16 %5, %16 offset:400\n\t"
-          "ds_read_b64_tr_b16 %6, %16 offset:192\n\t"
-          "ds_read_b64_tr_b16 %7, %16 offset:464\n\t"
-          "ds_read_b64_tr_b16 %8, %16 offset:4352\n\t"
-          "ds_read_b64_tr_b16 %9, %16 offset:4624\n\t"
-          "ds_read_b64_tr_b16 %10, %16 offset:4416\n\t"
-          "ds_read_b64_tr_b16 %11, %16 offset:4688\n\t"
-          "ds_read_b64_tr_b16 %12, %16 offset:4480\n\t"
-          "ds_read_b64_tr_b16 %13, %16 offset:4752\n\t"
-          "ds_read_b64_tr_b16 %14, %16 offset:4544\n\t"
-          "ds_read_b64_tr_b16 %15, %16 offset:4816\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7), "=&v"(r8),
-            "=&v"(r9), "=&v"(r10), "=&v"(r11), "=&v"(r12), "=&v"(r13), "=&v"(r14), "=&v"(r15)
-          : "v"(a));
-      const s16x4 r[16] = {r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11, r12, r13, r14, r15};
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const s16x4 lo = r[8 * kk + 2 * dt], hi = r[8 * kk + 2 * dt + 1];
-          hb[kk][dt] = __builtin_bit_cast(half8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        }
-    } else {
-      static_assert(D != 64 || C::PITCH == 144, "offsets below: 16 kk PITCH + 64 dt + h PITCH");
-      s16x4 r0, r1, r2, r3, r4, r5, r6, r7;
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %8\n\t"
-          "ds_read_b64_tr_b16 %1, %8 offset:144\n\t"
-          "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
-          "ds_read_b64_tr_b16 %3, %8 offset:208\n\t"
-          "ds_read_b64_tr_b16 %4, %8 offset:2304\n\t"
-          "ds_read_b64_tr_b16 %5, %8 offset:2448\n\t"
-          "ds_read_b64_tr_b16 %6, %8 offset:2368\n\t"
-          "ds_read_b64_tr_b16 %7, %8 offset:2512\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
-          : "v"(a));
-      const s16x4 r[8] = {r0, r1, r2, r3, r4, r5, r6, r7};
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const s16x4 lo = r[4 * kk + 2 * dt], hi = r[4 * kk + 2 * dt + 1];
-          hb[kk][dt] = __builtin_bit_cast(half8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        }
-    }
+    tile_tr_reads<D>(lds_addr(tile_lds(t) + (t % kStageTiles) * C::TILE_BYTES) + tr_base, hb);
   };
   // allocations 2^C (= 2^14 A) in fp16 for accumulator elements 2 i, 2 i + 1
   // (i = 0..7), and the masses of the rounded values
