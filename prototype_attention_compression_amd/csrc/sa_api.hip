@@ -70,7 +70,12 @@ Layout make_layout(const sa_problem& p) {
   // the one-pass path: sized whenever its shape is built, used per call
   L.fused = 0;
   L.groups = 0;
-  int64_t parts = L.chunks_max;
+  L.p2_groups = 0;
+  int64_t parts = f32 ? L.chunks_max : 0;
+  if (!f32) {
+    L.p2_groups = std::max(1, kP2WGs / L.n_pblocks);
+    parts = std::max<int64_t>(parts, (int64_t)L.p2_groups + p.num_users);
+  }
   if (fused_shape_ok(L)) {
     L.groups = kFusedWGs / (p.k / kFusedProtos);
     parts = std::max<int64_t>(parts, (int64_t)L.groups + p.num_users);

@@ -41,18 +41,19 @@ __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout
   const int u = blockIdx.x / nrb, rb = blockIdx.x % nrb;
   const int j0 = rb * kFinRows;
   const int tid = threadIdx.x;
-  // the user's partial-sum slots: chunks c0 .. c1-1 (two-pass path), or
+  // the user's partial-sum slots: chunks c0 .. c1-1 (fp32 path), or
   // group + u for the groups g0 .. g1-1 whose tile ranges meet the user's
-  // (one-pass path)
+  // (bf16: pass 2 and the one-pass kernel walk equal tile ranges per group)
   int c0, c1;
-  if (!L.fused) {
+  if (L.dtype != 0) {
     const int32_t* chunk_base = ws_i32(ws, L.off_chunk_base);
     c0 = chunk_base[u];
     c1 = chunk_base[u + 1];
   } else {
     const int32_t* tile_base = ws_i32(ws, L.off_tile_base);
     const int32_t nt = ws_i32(ws, L.off_hdr)[kHdrTiles];
-    const int32_t Tg = (nt + 4 * L.groups - 1) / (4 * L.groups) * 4;
+    const int G = L.fused ? L.groups : L.p2_groups;
+    const int32_t Tg = (nt + 4 * G - 1) / (4 * G) * 4;
     const int32_t t0 = tile_base[u], t1 = tile_base[u + 1];
     c0 = c1 = 0;
     if (t1 > t0) {

@@ -9,9 +9,12 @@
 //
 // Two paths share the workspace:
 //   * two-pass: pass 1 (per-token logsumexp over prototypes) runs over tiles;
-//     pass 2 (allocation + accumulation) runs over CHUNKs of up to
-//     `tiles_per_chunk` consecutive tiles of one user, times prototype blocks
-//     (chunk_base[u] numbers them user by user); partial sums per chunk.
+//     pass 2 (allocation + accumulation, bf16) runs as p2_groups GROUPS of
+//     n_pblocks workgroups (one per prototype block), each group walking an
+//     equal contiguous tile range, with partial sums per (group, user) pair
+//     at index group + user as below.  The fp32 path instead cuts every user
+//     into CHUNKs of up to `tiles_per_chunk` tiles (chunk_base[u] numbers them
+//     user by user), with partial sums per chunk.
 //   * one-pass: a packing kernel writes the fp16 token rows; then GROUPS of
 //     n_pblocks co-resident workgroups (one per 256-prototype block) each walk
 //     an equal contiguous range of tiles, exchanging per-token partial
@@ -35,6 +38,7 @@ constexpr float kAllocShift = 14.0f; // fp16 allocations carry a 2^14 scale
 constexpr int kF32ChunkTiles = 8;    // tiles per chunk on the fp32 path
 constexpr int kFusedProtos = 256;    // prototypes per one-pass workgroup (8 waves x 32)
 constexpr int kFusedWGs = 256;       // one-pass grid: groups x n_pblocks workgroups
+constexpr int kP2WGs = 256;          // pass-2 grid (bf16): p2_groups x n_pblocks workgroups
 constexpr int kXSlots = 8;           // ring slots of the one-pass exchange
 
 // Device error flags (workspace header word 0, bitwise or).
@@ -55,8 +59,8 @@ struct Layout {
   int32_t chunks_max;      // bound on sum_u ceil(tiles_u / tiles_per_chunk)
   int32_t fused;           // 1: the one-pass path is built for this shape
   int32_t groups;          // one-pass groups (kFusedWGs / n_pblocks)
-  int32_t parts_max;       // partial-sum slots: max(chunks_max, groups + R)
-  int32_t pad_;
+  int32_t parts_max;       // partial-sum slots: chunks_max (fp32), else max(groups, p2_groups) + R
+  int32_t p2_groups;       // pass-2 groups (bf16): kP2WGs / n_pblocks
   // byte offsets into the workspace (all 256-aligned)
   size_t off_hdr;          // [64] int32: error flag, qmax (float), totals
   size_t off_tile_base;    // [R+1] int32

@@ -46,10 +46,15 @@
 // instructions.  Hence one copy of the rows (transposing reads for GEMM2)
 // rather than a second, transposed copy.
 //
-// Work item = (chunk of <= tiles_per_chunk tiles of one user, prototype block
-// of waves*32).  Workgroups are numbered so that the prototype blocks of one
-// chunk land on the same XCD back to back (dispatch goes round-robin over the
-// 8 XCDs), letting them share the chunk's tiles through that XCD's L2.
+// Work split: a persistent grid of about 256 workgroups (one per CU), in
+// groups of P = k / (waves*32) workgroups, one per prototype block.  Group g
+// walks an equal contiguous range of the batch's tiles, cut at user
+// boundaries into segments whose sums go to partial slot g + user; every
+// workgroup does the same work, so no partially filled last round of
+// workgroups idles the chip, and the partial sums are (groups + users) x k x d
+// rather than one per chunk.  The P workgroups of a group sit on one XCD
+// (dispatch goes round-robin over the 8 XCDs) and share the tiles through
+// its L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -96,20 +101,25 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   using C = P2<D>;
   __shared__ __attribute__((aligned(1024))) char lds[kBufs * C::STAGE_BYTES];
 
+  // Workgroup x sits on XCD x % 8 (dispatch is round-robin over the XCDs);
+  // the P workgroups of a group (one per prototype block) are consecutive
+  // slots x / 8 of one XCD, so they share the group's tiles through its L2.
+  // Group g walks tiles [g Tg, (g + 1) Tg), Tg = the total over the G
+  // groups rounded up to a multiple of 4: every workgroup does the same
+  // amount of work.
   const int32_t* hdr = ws_i32(ws, L.off_hdr);
-  const int x = blockIdx.x, xcd = x & 7, slot = x >> 3;
-  const int chunk = (slot / L.n_pblocks) * 8 + xcd;
-  const int pb = slot % L.n_pblocks;
-  if (chunk >= hdr[kHdrChunks]) return;  // uniform over the workgroup
-
+  const int P = L.n_pblocks, G = L.p2_groups;
+  const int x = blockIdx.x, xcd = x & 7, slotw = x >> 3;
+  const int group = xcd + 8 * (slotw / P);
+  const int pb = slotw % P;
+  if (group >= G) return;  // uniform over the workgroup
+  const int32_t T = hdr[kHdrTiles];
+  const int32_t Tg = (T + 4 * G - 1) / (4 * G) * 4;
+  const int32_t s0 = group * Tg, s1 = min(T, s0 + Tg);
+  if (s0 >= s1) return;
   const int32_t* tile_base = ws_i32(ws, L.off_tile_base);
-  const int32_t* chunk_base = ws_i32(ws, L.off_chunk_base);
-  const int u = find_user(chunk_base, L.R, chunk);
-  const int ci = chunk - chunk_base[u];
-  const int CT = L.tiles_per_chunk;
-  const int tiles_u = tile_base[u + 1] - tile_base[u];
-  const int32_t t0 = tile_base[u] + ci * CT;
-  const int nt = min(CT, tiles_u - ci * CT);
+  int32_t t0 = 0;   // the current segment: tiles t0 .. t0 + nt - 1 of one user
+  int nt = 0;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches on it
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   // before the current one still holds tile t when step 4 reads it.
   constexpr int kAhead = kBufs - 2;
   static_assert(kAhead >= 1, "at least one stage of loads in flight");
-  const int nstages = nt / kStageTiles;
+  int nstages = 0;
   auto tile_lds = [&](int t) { return lds + ((t / kStageTiles) % kBufs) * C::STAGE_BYTES; };
   auto boundary = [&](int t1) {   // before the first read of tile t1
     if (t1 % kStageTiles == 0) {  // uniform
@@ -344,45 +354,68 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   using T_ = std::true_type;
   using F_ = std::false_type;
 
+  // The group's range is cut at user boundaries into segments (each a
+  // multiple of 4 tiles); a segment's sums go to partial slot group + user,
+  // unique among the groups whose ranges meet that user.
+  float* part_u_all = ws_f32(ws, L.off_part_u);
+  float* part_m_all = ws_f32(ws, L.off_part_m);
+  int u = find_user(tile_base, L.R, s0);
+  for (;;) {
+    const int32_t ua = tile_base[u], ub = tile_base[u + 1];
+    t0 = max(s0, ua);
+    const int32_t te = min(s1, ub);
+    if (te > t0) {
+      nt = te - t0;
+      nstages = nt / kStageTiles;
 #pragma unroll
-  for (int st = 0; st < kAhead; ++st)
-    if (st < nstages) issue(st, st);
-  boundary(0);
-  read_a(0, ha, nlp);
-  gemm1_head(ha, nlp, C0);
-  gemm1_tail(ha, C0);
-  // nt is a positive multiple of 4 (a chunk holds whole stages of a user's
-  // tiles).  Parity p = t % 2: C(t-1), C(t+1) in set p ^ 1, A'(t-1) in set
-  // p ^ 1, A'(t-2) in set p.
-  period(0, C1, ap1, ap0, F_{}, F_{}, T_{}, F_{});
-  period(1, C0, ap0, ap1, F_{}, T_{}, T_{}, T_{});
-  int t = 2;
-  for (; t < nt - 2; t += 2) {
-    period(t, C1, ap1, ap0, T_{}, T_{}, T_{}, T_{});
-    period(t + 1, C0, ap0, ap1, T_{}, T_{}, T_{}, T_{});
-  }
-  period(nt - 2, C1, ap1, ap0, T_{}, T_{}, T_{}, T_{});
-  period(nt - 1, C0, ap0, ap1, T_{}, T_{}, F_{}, T_{});
-  period(nt, C1, ap1, ap0, T_{}, T_{}, F_{}, T_{});
-  period(nt + 1, C0, ap0, ap1, T_{}, F_{}, F_{}, F_{});
+      for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) U[b][dt] = float16v{};
+        msum[b] = 0.f;
+      }
+#pragma unroll
+      for (int st = 0; st < kAhead; ++st)
+        if (st < nstages) issue(st, st);
+      boundary(0);
+      read_a(0, ha, nlp);
+      gemm1_head(ha, nlp, C0);
+      gemm1_tail(ha, C0);
+      // nt is a positive multiple of 4 (a segment holds whole stages of one
+      // user's tiles).  Parity p = t % 2: C(t-1), C(t+1) in set p ^ 1, A'(t-1) in set
+      // p ^ 1, A'(t-2) in set p.
+      period(0, C1, ap1, ap0, F_{}, F_{}, T_{}, F_{});
+      period(1, C0, ap0, ap1, F_{}, T_{}, T_{}, T_{});
+      int t = 2;
+      for (; t < nt - 2; t += 2) {
+        period(t, C1, ap1, ap0, T_{}, T_{}, T_{}, T_{});
+        period(t + 1, C0, ap0, ap1, T_{}, T_{}, T_{}, T_{});
+      }
+      period(nt - 2, C1, ap1, ap0, T_{}, T_{}, T_{}, T_{});
+      period(nt - 1, C0, ap0, ap1, T_{}, T_{}, F_{}, T_{});
+      period(nt, C1, ap1, ap0, T_{}, T_{}, F_{}, T_{});
+      period(nt + 1, C0, ap0, ap1, T_{}, F_{}, F_{}, F_{});
 
-  float* part_u = ws_f32(ws, L.off_part_u) + (int64_t)chunk * L.k * D;
-  float* part_m = ws_f32(ws, L.off_part_m) + (int64_t)chunk * L.k;
+      float* part_u = part_u_all + (int64_t)(group + u) * L.k * D;
+      float* part_m = part_m_all + (int64_t)(group + u) * L.k;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
+      for (int b = 0; b < NB; ++b) {
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
+        for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        part_u[(int64_t)(p0 + 32 * b + acc_row(r, g)) * D + 32 * dt + col] = U[b][dt][r];
-    const float m = msum[b] + __shfl_xor(msum[b], 32);
-    if (g == 0) part_m[p0 + 32 * b + col] = m;
+          for (int r = 0; r < 16; ++r)
+            part_u[(int64_t)(p0 + 32 * b + acc_row(r, g)) * D + 32 * dt + col] = U[b][dt][r];
+        const float m = msum[b] + __shfl_xor(msum[b], 32);
+        if (g == 0) part_m[p0 + 32 * b + col] = m;
+      }
+      lds_barrier();   // every wave is done with the stage buffers the next segment refills
+    }
+    if (ub >= s1) break;
+    ++u;
   }
 }
 
 hipError_t launch_pass2(const Layout& L, void* ws, hipStream_t stream) {
-  const int64_t padded = ((int64_t)L.chunks_max + 7) / 8 * 8;
-  const int64_t grid = padded * L.n_pblocks;
+  const int64_t grid = (int64_t)8 * L.n_pblocks * ((L.p2_groups + 7) / 8);
   if (grid == 0) return hipSuccess;
 #define SA_P2(DD, WW) \
   hipLaunchKernelGGL((pass2_accum<DD, WW, 1>), dim3((unsigned)grid), dim3(WW * 64), 0, stream, L, ws)
