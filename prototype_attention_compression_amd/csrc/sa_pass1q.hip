@@ -36,9 +36,8 @@ namespace sa {
 
 namespace {
 
-constexpr int kWaves = 8;
 constexpr int kBufs = 3;
-constexpr int kWGs = 256;          // persistent grid: one workgroup per CU
+constexpr int kWGs = 256;          // persistent grid: workgroups per CU x 256 CUs
 
 template <int D>
 struct Q1 {
@@ -66,16 +65,17 @@ __device__ __forceinline__ HalfPair lane_halves(float x) {
 
 }  // namespace
 
-template <int D, int NBW, bool MASKED>
-__global__ __launch_bounds__(kWaves * 64) void pass1_qres(const uint16_t* __restrict__ H,
+template <int D, int NBW, bool MASKED, int W>
+__global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uint16_t* __restrict__ H,
                                                           const int64_t* __restrict__ offsets,
                                                           const uint8_t* __restrict__ mask,
                                                           const int32_t* __restrict__ tile_base, Layout L,
                                                           void* __restrict__ ws) {
   using C = Q1<D>;
   __shared__ __attribute__((aligned(1024))) char rows[kBufs][C::TILE_BYTES];
-  __shared__ float part[2][kTile][kWaves];
-  __shared__ __attribute__((aligned(16))) uint32_t exact_bits[kBufs][kWaves];
+  static_assert(W % 4 == 0 && kTile % W == 0, "wave count");
+  __shared__ float part[2][kTile][W];
+  __shared__ __attribute__((aligned(16))) uint32_t exact_bits[kBufs][W];
   __shared__ uint32_t keep_words[kBufs][kTile];
 
   const int32_t* hdr = ws_i32(ws, L.off_hdr);
@@ -154,52 +154,103 @@ __global__ __launch_bounds__(kWaves * 64) void pass1_qres(const uint16_t* __rest
     if (lane == 0) exact_bits[b][wave] = bal != 0 ? 1u : 0u;
   };
 
+  // whether some wave flagged tile buffer b for the exact form
+  auto tile_exact = [&](int b) {
+    uint32_t any = 0u;
+#pragma unroll
+    for (int w = 0; w < W; w += 4) {
+      const u32x4 e = *reinterpret_cast<const u32x4*>(&exact_bits[b][w]);
+      any |= e[0] | e[1] | e[2] | e[3];
+    }
+    return any != 0u;
+  };
+
   // partial of tile j (buffer b) into LDS slot j % 2
   const int hbase = col * C::PITCH + 16 * g;
-  auto compute = [&](int j, int b) {
-    const u32x4 e0 = *reinterpret_cast<const u32x4*>(&exact_bits[b][0]);
-    const u32x4 e1 = *reinterpret_cast<const u32x4*>(&exact_bits[b][4]);
-    const bool exact = (e0[0] | e0[1] | e0[2] | e0[3] | e1[0] | e1[1] | e1[2] | e1[3]) != 0u;
-    half8 ha[C::S];
+  // exact form: fold one block's 16 logits into the running maximum m and
+  // the sum p (rescaled when the maximum grows)
+  auto exact_block = [&](const float16v& a, float& m, float& p) {
+    float mb = a[0];
 #pragma unroll
-    for (int s = 0; s < C::S; ++s) ha[s] = *reinterpret_cast<const half8*>(&rows[b][hbase + 32 * s]);
-    float wpart;
+    for (int r = 1; r < 16; ++r) mb = fmaxf(mb, a[r]);
+    const float mn = fmaxf(m, mb);
+    p *= __builtin_amdgcn_exp2f(m - mn);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p += __builtin_amdgcn_exp2f(a[r] - mn);
+    m = mn;
+  };
+  // the wave's partial (sum of 2^L, or its log2 in the exact form) of the
+  // lane's token over its blocks, combined over the two lane halves
+  auto block_partials = [&](bool exact, const float16v (&a)[NBW]) {
     if (!exact) {
-      // block-major MFMA chains; the other wave on the SIMD runs its
-      // exponentials under these MFMAs
       float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-      for (int bl = 0; bl < NBW; ++bl) {
-        float16v a = float16v{};
-#pragma unroll
-        for (int s = 0; s < C::S; ++s) a = mfma32x32x16(qf[bl][s], ha[s], a);
+      for (int bl = 0; bl < NBW; ++bl)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          p0 += __builtin_amdgcn_exp2f(a[r]);
-          p1 += __builtin_amdgcn_exp2f(a[r + 1]);
+          p0 += __builtin_amdgcn_exp2f(a[bl][r]);
+          p1 += __builtin_amdgcn_exp2f(a[bl][r + 1]);
         }
-      }
       const HalfPair hp = lane_halves(p0 + p1);
-      wpart = hp.lo + hp.hi;
-    } else {
-      // exact: running maximum over the blocks, the sum rescaled when it grows
-      float m = -INFINITY, p = 0.f;
+      return hp.lo + hp.hi;
+    }
+    float m = -INFINITY, p = 0.f;
 #pragma unroll
-      for (int bl = 0; bl < NBW; ++bl) {
-        float16v a = float16v{};
+    for (int bl = 0; bl < NBW; ++bl) exact_block(a[bl], m, p);
+    const HalfPair hp = lane_halves(m + log2f(p));
+    return log_add_exp2(hp.lo, hp.hi);
+  };
+
+  auto compute = [&](int j, int b) {
+    const bool exact = tile_exact(b);
+    float wpart;
+    if constexpr (NBW == 1) {
+      // one block: each 16-byte operand read (8 features of the lane's
+      // token) feeds one MFMA as soon as it lands, so only a read or two is
+      // live (under 128 registers: two workgroups share a CU)
+      float16v a[NBW];
 #pragma unroll
-        for (int s = 0; s < C::S; ++s) a = mfma32x32x16(qf[bl][s], ha[s], a);
-        float mb = a[0];
+      for (int bl = 0; bl < NBW; ++bl) a[bl] = float16v{};
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mb = fmaxf(mb, a[r]);
-        const float mn = fmaxf(m, mb);
-        p *= __builtin_amdgcn_exp2f(m - mn);
+      for (int s = 0; s < C::S; ++s) {
+        const half8 h = *reinterpret_cast<const half8*>(&rows[b][hbase + 32 * s]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p += __builtin_amdgcn_exp2f(a[r] - mn);
-        m = mn;
+        for (int bl = 0; bl < NBW; ++bl) a[bl] = mfma32x32x16(qf[bl][s], h, a[bl]);
       }
-      const HalfPair hp = lane_halves(m + log2f(p));
-      wpart = log_add_exp2(hp.lo, hp.hi);
+      wpart = block_partials(exact, a);
+    } else {
+      // block-major MFMA chains over the tile's operands held in registers:
+      // the exponentials of block b run under the MFMAs of block b + 1
+      half8 ha[C::S];
+#pragma unroll
+      for (int s = 0; s < C::S; ++s) ha[s] = *reinterpret_cast<const half8*>(&rows[b][hbase + 32 * s]);
+      if (!exact) {
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int bl = 0; bl < NBW; ++bl) {
+          float16v a = float16v{};
+#pragma unroll
+          for (int s = 0; s < C::S; ++s) a = mfma32x32x16(qf[bl][s], ha[s], a);
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            p0 += __builtin_amdgcn_exp2f(a[r]);
+            p1 += __builtin_amdgcn_exp2f(a[r + 1]);
+          }
+        }
+        const HalfPair hp = lane_halves(p0 + p1);
+        wpart = hp.lo + hp.hi;
+      } else {
+        float m = -INFINITY, p = 0.f;
+#pragma unroll
+        for (int bl = 0; bl < NBW; ++bl) {
+          float16v a = float16v{};
+#pragma unroll
+          for (int s = 0; s < C::S; ++s) a = mfma32x32x16(qf[bl][s], ha[s], a);
+          exact_block(a, m, p);
+        }
+        const HalfPair hp = lane_halves(m + log2f(p));
+        wpart = log_add_exp2(hp.lo, hp.hi);
+      }
     }
     if (g == 0) part[j & 1][col][wave] = wpart;
   };
@@ -207,23 +258,21 @@ __global__ __launch_bounds__(kWaves * 64) void pass1_qres(const uint16_t* __rest
   // -l pairs of tile j (buffer b) from its 8 partials: wave w, lanes 0..3,
   // tokens 4 w .. 4 w + 3
   auto finalize = [&](int j, int b) {
-    constexpr int TPW = kTile / kWaves;   // tokens per wave
+    constexpr int TPW = kTile / W;   // tokens per wave
     if (lane >= TPW) return;
     const int tok = wave * TPW + lane;
-    const u32x4 e0 = *reinterpret_cast<const u32x4*>(&exact_bits[b][0]);
-    const u32x4 e1 = *reinterpret_cast<const u32x4*>(&exact_bits[b][4]);
-    const bool exact = (e0[0] | e0[1] | e0[2] | e0[3] | e1[0] | e1[1] | e1[2] | e1[3]) != 0u;
+    const bool exact = tile_exact(b);
     const float* pp = part[j & 1][tok];
     float lse;
     if (!exact) {
       float s = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) s += pp[w];
+      for (int w = 0; w < W; ++w) s += pp[w];
       lse = log2f(s);
     } else {
       lse = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) lse = log_add_exp2(lse, pp[w]);
+      for (int w = 0; w < W; ++w) lse = log_add_exp2(lse, pp[w]);
     }
     const bool keep = keep_words[b][tok] != 0u;
     // -l = 14 - lse as an fp16 pair (hi, lo) with hi + lo = -l to ~2^-16
@@ -272,27 +321,33 @@ bool pass1q_ok(const Layout& L) {
 
 hipError_t launch_pass1q(const Layout& L, const void* H, const int64_t* offsets, const uint8_t* mask, void* ws,
                          hipStream_t stream) {
-  const int grid = L.tiles_max < kWGs ? L.tiles_max : kWGs;
+  // 8 waves x k/8 prototypes.  At k = 256 (under 128 registers) two
+  // workgroups share a CU: four waves per SIMD, with independent barriers,
+  // hide the exponentials and row conversion that two waves per SIMD leave
+  // exposed (measured 24% faster).  Sixteen-wave workgroups were slower: one
+  // barrier per tile across 16 waves, and half of them idle in the
+  // conversion.
+  const int per_cu = L.k == 256 ? 2 : 1;
+  const int grid = L.tiles_max < kWGs * per_cu ? L.tiles_max : kWGs * per_cu;
   if (grid == 0) return hipSuccess;
-#define SA_P1Q(DD, NN)                                                                                     \
+  const int32_t* tile_base = reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + L.off_tile_base);
+#define SA_P1Q(DD, NN, WW)                                                                                 \
   do {                                                                                                     \
     if (mask != nullptr)                                                                                   \
-      hipLaunchKernelGGL((pass1_qres<DD, NN, true>), dim3(grid), dim3(kWaves * 64), 0, stream,           \
+      hipLaunchKernelGGL((pass1_qres<DD, NN, true, WW>), dim3(grid), dim3(WW * 64), 0, stream,            \
                          (const uint16_t*)H, offsets, mask, tile_base, L, ws);                             \
     else                                                                                                   \
-      hipLaunchKernelGGL((pass1_qres<DD, NN, false>), dim3(grid), dim3(kWaves * 64), 0, stream,          \
+      hipLaunchKernelGGL((pass1_qres<DD, NN, false, WW>), dim3(grid), dim3(WW * 64), 0, stream,           \
                          (const uint16_t*)H, offsets, mask, tile_base, L, ws);                             \
   } while (0)
-  const int32_t* tile_base = reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + L.off_tile_base);
-  const int nbw = L.k / 256;
   if (L.d == 128) {
-    if (nbw == 1) SA_P1Q(128, 1);
-    else if (nbw == 2) SA_P1Q(128, 2);
-    else SA_P1Q(128, 4);
+    if (L.k == 256) SA_P1Q(128, 1, 8);
+    else if (L.k == 512) SA_P1Q(128, 2, 8);
+    else SA_P1Q(128, 4, 8);
   } else {
-    if (nbw == 1) SA_P1Q(64, 1);
-    else if (nbw == 2) SA_P1Q(64, 2);
-    else SA_P1Q(64, 4);
+    if (L.k == 256) SA_P1Q(64, 1, 8);
+    else if (L.k == 512) SA_P1Q(64, 2, 8);
+    else SA_P1Q(64, 4, 8);
   }
 #undef SA_P1Q
   return hipGetLastError();
