@@ -58,6 +58,22 @@ def test_parity_one_pass_every_block_count(k, d):
     _check(inp, path="one")
 
 
+@pytest.mark.parametrize("k", [64, 320, 1024, 2048])
+@pytest.mark.parametrize("d", [64, 128])
+def test_parity_many_short_users(k, d):
+    """Pass 2's groups walk equal tile ranges cut at user boundaries: with 200
+    short ragged users (some empty) every group crosses many users, and each
+    user's sums come from several groups' partial slots.  k = 64 .. 2048
+    covers 1 .. 8 prototype blocks per group (k = 320: five blocks, a group
+    count that is not a multiple of 8)."""
+    from synth import make_inputs
+    rng = np.random.default_rng(2000 + k + d)
+    lens = rng.integers(0, 400, size=200)
+    lens[::17] = 0
+    inp = make_inputs(lens.tolist(), d=d, k=k, seed=3000 + k + d)
+    _check(inp, path="two")
+
+
 def _sample(inp, n_random=2, seed=0):
     lens = inp.lengths
     pick = {int(np.argmin(lens)), int(np.argmax(lens))}
