@@ -10,3 +10,4 @@ from .sa_oracle import (  # noqa: F401
     sketch_batch,
     sketch_one,
 )
+from .sa_oracle_grad import sketch_batch_grad, sketch_one_grad  # noqa: F401,E402
