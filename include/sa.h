@@ -169,6 +169,85 @@ sa_status sa_compress_with_events(const sa_problem* problem,
                                   void* stream,
                                   void* const* events);
 
+/*
+ * The backward pass (gradients of a loss through the sketches).
+ *
+ * SequenceO1 trains the compressor end to end: the blog "100,000 videos in
+ * your pocket" ("How it works", item 1) notes that the compression is
+ * differentiable, so the ranking loss's gradients flow back through it, and
+ * its "Takeaways" list training the compressor on the real loss.  The pages
+ * give no backward formulas; the library computes the chain rule of the
+ * forward definition above.  Given dS = dLoss/dS_u for every user:
+ *   dH    [N, d] float32   dLoss/dh_t for every token (zero rows for tokens
+ *                          that token_mask drops), fully overwritten;
+ *   dP    [k, d] float32   dLoss/dP,  summed over the users, overwritten;
+ *   dWk   [d, d] float32   dLoss/dWk, summed over the users, overwritten;
+ *   dWv   [d, d] float32   dLoss/dWv, summed over the users, overwritten.
+ * A sketch row with zero mass is the constant 0 and passes no gradient;
+ * empty users contribute nothing.
+ *
+ * Built for bf16 inputs (problem->dtype = SA_BF16) with the same d and k as
+ * sa_compress; SA_F32 or SA_FLAG_ONE_PASS give SA_E_UNSUPPORTED (the
+ * backward always recomputes the two forward passes it needs).  Internally
+ * the products use fp16 MFMA operands (the token rows widened exactly, the
+ * allocations, their gradients and dS / m scaled by powers of two into fp16
+ * range) with fp32 sums.  dS must be finite.
+ *
+ * Workspace: sa_backward_workspace_size bytes (more than sa_compress needs).
+ * Same ownership, stream and threading rules as sa_compress; the offsets
+ * contract is the same, and on a violation every user counts as empty (all
+ * four gradients zero) and the device error flag is raised.  R = 0 writes
+ * zero dP, dWk and dWv and needs no workspace or offsets.
+ */
+sa_status sa_backward_workspace_size(const sa_problem* problem, size_t* bytes);
+
+sa_status sa_compress_backward(const sa_problem* problem,
+                               const void* H,
+                               const int64_t* offsets,
+                               const uint8_t* token_mask,
+                               const void* Wk,
+                               const void* Wv,
+                               const void* P,
+                               const float* dS,      /* [R, k, d] float32 */
+                               float* dH,
+                               float* dP,
+                               float* dWk,
+                               float* dWv,
+                               void* workspace,
+                               size_t workspace_bytes,
+                               void* stream);
+
+/* Number of phase-boundary events sa_compress_backward_with_events records. */
+#define SA_NUM_BWD_PHASE_EVENTS 6
+
+/*
+ * sa_compress_backward, recording caller-created HIP events on `stream`:
+ *   events[0] before the first kernel,
+ *   events[1] after the forward recomputation (queries, per-token
+ *             logsumexps and fp16 rows, per-user sums),
+ *   events[2] after the per-user step (Z = (dS / m) Wv^T and its scale),
+ *   events[3] after the token-major kernel (dH),
+ *   events[4] after the prototype-major kernel (E = sum_t dL h_t),
+ *   events[5] after the last kernel (dP, dWk, dWv).
+ * `events` may be NULL.  Same arguments, errors and semantics otherwise.
+ */
+sa_status sa_compress_backward_with_events(const sa_problem* problem,
+                                           const void* H,
+                                           const int64_t* offsets,
+                                           const uint8_t* token_mask,
+                                           const void* Wk,
+                                           const void* Wv,
+                                           const void* P,
+                                           const float* dS,
+                                           float* dH,
+                                           float* dP,
+                                           float* dWk,
+                                           float* dWv,
+                                           void* workspace,
+                                           size_t workspace_bytes,
+                                           void* stream,
+                                           void* const* events);
+
 /* Device error flag bits. */
 #define SA_DEVICE_ERR_OFFSETS 1   /* offsets broke their contract: all users empty */
 #define SA_DEVICE_ERR_EXCHANGE 2  /* one-pass: a bounded wait between workgroups

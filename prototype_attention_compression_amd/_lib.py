@@ -20,8 +20,10 @@ _PATH_FLAGS = {None: 0, "auto": 0, "two": SA_FLAG_TWO_PASS, "one": SA_FLAG_ONE_P
 
 # functions declared in include/sa.h
 EXPORTS = ("sa_workspace_size", "sa_compress", "sa_compress_with_events",
+           "sa_backward_workspace_size", "sa_compress_backward", "sa_compress_backward_with_events",
            "sa_read_device_error", "sa_status_string", "sa_version")
 NUM_PHASE_EVENTS = 5
+NUM_BWD_PHASE_EVENTS = 6
 
 
 class SaProblem(ctypes.Structure):
@@ -70,6 +72,13 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sa_compress.restype = ctypes.c_int
     lib.sa_compress_with_events.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.sa_compress_with_events.restype = ctypes.c_int
+    lib.sa_backward_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
+    lib.sa_backward_workspace_size.restype = ctypes.c_int
+    lib.sa_compress_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sa_compress_backward.restype = ctypes.c_int
+    lib.sa_compress_backward_with_events.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                                     vp]
+    lib.sa_compress_backward_with_events.restype = ctypes.c_int
     lib.sa_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
     lib.sa_read_device_error.restype = ctypes.c_int
     lib.sa_status_string.argtypes = [ctypes.c_int]
@@ -101,6 +110,27 @@ def workspace_size(num_users: int, total_tokens: int, d: int, k: int, dtype: int
     if st != SA_OK:
         raise SaError(st, "sa_workspace_size")
     return int(out.value)
+
+
+def backward_workspace_size(num_users: int, total_tokens: int, d: int, k: int, dtype: int = SA_BF16) -> int:
+    """Bytes of device workspace sa_compress_backward needs (pure host call)."""
+    pb = problem(num_users, total_tokens, d, k, dtype)
+    out = ctypes.c_size_t(0)
+    st = load().sa_backward_workspace_size(ctypes.byref(pb), ctypes.byref(out))
+    if st != SA_OK:
+        raise SaError(st, "sa_backward_workspace_size")
+    return int(out.value)
+
+
+def raw_compress_backward(pb: SaProblem, H, offsets, mask, Wk, Wv, P, dS, dH, dP, dWk, dWv, workspace,
+                          workspace_bytes: int, stream, events=None) -> int:
+    """Direct call of sa_compress_backward(_with_events); returns the status."""
+    if events is None:
+        return int(load().sa_compress_backward(ctypes.byref(pb), H, offsets, mask, Wk, Wv, P, dS, dH, dP, dWk,
+                                               dWv, workspace, ctypes.c_size_t(workspace_bytes), stream))
+    return int(load().sa_compress_backward_with_events(ctypes.byref(pb), H, offsets, mask, Wk, Wv, P, dS, dH, dP,
+                                                       dWk, dWv, workspace, ctypes.c_size_t(workspace_bytes),
+                                                       stream, events))
 
 
 def raw_compress(pb: SaProblem, H, offsets, mask, Wk, Wv, P, S, mass, workspace,
@@ -195,3 +225,53 @@ def read_device_error(workspace) -> int:
     if st != SA_OK:
         raise SaError(st, "sa_read_device_error")
     return int(flag.value)
+
+
+def compress_backward(H, offsets, Wk, Wv, P, dS, mask=None, workspace=None, events=None):
+    """Gradients of a loss through the sketches, computed by libsa on the GPU.
+
+    Inputs as for ``compress`` (bfloat16 only), plus dS [R, k, d] float32 =
+    dLoss/dS.  Returns (dH [N, d], dP [k, d], dWk [d, d], dWv [d, d]), all
+    float32; dP, dWk and dWv are summed over the users.  Runs on torch's
+    current stream.
+    """
+    import torch
+
+    if H.dtype != torch.bfloat16:
+        raise ValueError("the backward pass is built for bfloat16 inputs")
+    for name, t in (("Wk", Wk), ("Wv", Wv), ("P", P)):
+        if t.dtype != H.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from H dtype {H.dtype}")
+    for name, t in (("H", H), ("Wk", Wk), ("Wv", Wv), ("P", P), ("offsets", offsets), ("dS", dS)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if offsets.dtype != torch.int64 or offsets.dim() != 1 or H.dim() != 2:
+        raise ValueError("offsets must be 1-D int64 and H [N, d]")
+    N, d = H.shape
+    k = P.shape[0]
+    R = offsets.shape[0] - 1
+    if Wk.shape != (d, d) or Wv.shape != (d, d) or P.shape != (k, d):
+        raise ValueError("shape mismatch: need Wk, Wv [d, d] and P [k, d]")
+    if dS.dtype != torch.float32 or dS.shape != (R, k, d):
+        raise ValueError("dS must be float32 [R, k, d]")
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        if mask.dtype != torch.uint8 or mask.shape != (N,) or not mask.is_cuda or not mask.is_contiguous():
+            raise ValueError("mask must be a contiguous [N] uint8/bool GPU tensor")
+    dev = H.device
+    pb = problem(R, N, d, k, SA_BF16)
+    wbytes = backward_workspace_size(R, N, d, k, SA_BF16)
+    if workspace is None or workspace.numel() * workspace.element_size() < wbytes:
+        workspace = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
+    dH = torch.empty((N, d), dtype=torch.float32, device=dev)
+    dP = torch.empty((k, d), dtype=torch.float32, device=dev)
+    dWk = torch.empty((d, d), dtype=torch.float32, device=dev)
+    dWv = torch.empty((d, d), dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = raw_compress_backward(pb, _ptr(H) if N > 0 else None, _ptr(offsets), _ptr(mask), _ptr(Wk), _ptr(Wv),
+                               _ptr(P), _ptr(dS), _ptr(dH) if N > 0 else None, _ptr(dP), _ptr(dWk), _ptr(dWv),
+                               _ptr(workspace), wbytes, stream, events)
+    if st != SA_OK:
+        raise SaError(st, "sa_compress_backward")
+    return dH, dP, dWk, dWv

@@ -33,6 +33,14 @@ sa_status check_problem(const sa_problem* p) {
   return SA_OK;
 }
 
+// The backward pass: bf16 inputs only; it always runs the two forward passes
+sa_status check_problem_bwd(const sa_problem* p) {
+  sa_status st = check_problem(p);
+  if (st != SA_OK) return st;
+  if (p->dtype != SA_BF16 || (p->flags & SA_FLAG_ONE_PASS)) return SA_E_UNSUPPORTED;
+  return SA_OK;
+}
+
 // pass-2 waves per workgroup: 8, 4 or 2, dividing k / 32 (k is a multiple of 64)
 int pick_waves(int k) {
   const int blocks = k / kProtoPerWave;
@@ -49,7 +57,8 @@ int pick_tiles_per_chunk(int64_t tiles_est, int n_pblocks, bool f32) {
   return (int)((ct + kUserTileAlign - 1) / kUserTileAlign * kUserTileAlign);
 }
 
-Layout make_layout(const sa_problem& p) {
+// `bwd`: also lay out the backward pass's buffers (sa_compress_backward)
+Layout make_layout(const sa_problem& p, bool bwd = false) {
   Layout L;
   memset(&L, 0, sizeof(L));
   L.N = p.total_tokens;
@@ -103,6 +112,26 @@ Layout make_layout(const sa_problem& p) {
   }
   L.off_part_u = take((size_t)L.parts_max * p.k * p.d * sizeof(float));
   L.off_part_m = take((size_t)L.parts_max * p.k * sizeof(float));
+  if (bwd) {
+    const size_t Rk = (size_t)p.num_users * p.k;
+    L.e_waves = (p.k / kProtoPerWave) % 4 == 0 ? 4 : 2;
+    L.e_pblocks = p.k / (kProtoPerWave * L.e_waves);
+    L.e_groups = std::max(1, kBwdEWGs / L.e_pblocks);
+    const int64_t rows = std::max<int64_t>((int64_t)Rk, p.k);
+    L.o_chunks = (int32_t)((rows + kOuterRows - 1) / kOuterRows);
+    L.off_bz32 = take(Rk * p.d * sizeof(float));
+    L.off_bsbar = take(Rk * p.d * sizeof(float));
+    L.off_bc = take(Rk * sizeof(float));
+    L.off_bzmax = take((size_t)p.num_users * (p.k / 32) * sizeof(float));
+    L.off_bz16 = take(Rk * p.d * 2);
+    L.off_bcz = take(Rk * sizeof(float));
+    L.off_bzs = take((size_t)p.num_users * sizeof(float));
+    L.off_bbmax = take((size_t)p.num_users * sizeof(uint32_t));
+    L.off_bdelta = take((size_t)tiles_max * kTile * sizeof(float));
+    L.off_bepart = take((size_t)L.e_groups * p.k * p.d * sizeof(float));
+    L.off_betot = take((size_t)p.k * p.d * sizeof(float));
+    L.off_bopart = take((size_t)L.o_chunks * p.d * p.d * sizeof(float));
+  }
   L.total = off;
   return L;
 }
@@ -210,6 +239,76 @@ sa_status sa_read_device_error(const void* workspace, void* stream, int32_t* fla
   if (hipStreamSynchronize(s) != hipSuccess) return SA_E_HIP;
   *flag = v;
   return SA_OK;
+}
+
+sa_status sa_backward_workspace_size(const sa_problem* problem, size_t* bytes) {
+  if (bytes == nullptr) return SA_E_INVALID;
+  sa_status st = sa::check_problem_bwd(problem);
+  if (st != SA_OK) return st;
+  *bytes = sa::make_layout(*problem, true).total;
+  return SA_OK;
+}
+
+sa_status sa_compress_backward(const sa_problem* problem, const void* H, const int64_t* offsets,
+                               const uint8_t* token_mask, const void* Wk, const void* Wv, const void* P,
+                               const float* dS, float* dH, float* dP, float* dWk, float* dWv, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return sa_compress_backward_with_events(problem, H, offsets, token_mask, Wk, Wv, P, dS, dH, dP, dWk, dWv,
+                                          workspace, workspace_bytes, stream, nullptr);
+}
+
+sa_status sa_compress_backward_with_events(const sa_problem* problem, const void* H, const int64_t* offsets,
+                                           const uint8_t* token_mask, const void* Wk, const void* Wv, const void* P,
+                                           const float* dS, float* dH, float* dP, float* dWk, float* dWv,
+                                           void* workspace, size_t workspace_bytes, void* stream,
+                                           void* const* events) {
+  try {
+    sa_status st = sa::check_problem_bwd(problem);
+    if (st != SA_OK) return st;
+    const sa_problem& p = *problem;
+    if (Wk == nullptr || Wv == nullptr || P == nullptr || dP == nullptr || dWk == nullptr || dWv == nullptr)
+      return SA_E_INVALID;
+    if (p.num_users > 0 && (offsets == nullptr || dS == nullptr)) return SA_E_INVALID;
+    if (p.total_tokens > 0 && (H == nullptr || dH == nullptr)) return SA_E_INVALID;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    auto mark = [&](int i) {
+      return events == nullptr || hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s) == hipSuccess;
+    };
+    const int64_t dd = (int64_t)p.d * p.d;
+    if (p.num_users == 0) {   // no users: the parameter gradients are empty sums
+      if (!mark(0)) return SA_E_HIP;
+      if (sa::launch_fill_zero(dP, (int64_t)p.k * p.d, s) != hipSuccess ||
+          sa::launch_fill_zero(dWk, dd, s) != hipSuccess || sa::launch_fill_zero(dWv, dd, s) != hipSuccess)
+        return SA_E_HIP;
+      for (int i = 1; i < SA_NUM_BWD_PHASE_EVENTS; ++i)
+        if (!mark(i)) return SA_E_HIP;
+      return SA_OK;
+    }
+    sa::Layout L = sa::make_layout(p, true);
+    if (workspace == nullptr || workspace_bytes < L.total) return SA_E_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % sa::kAlign != 0) return SA_E_INVALID;
+    if (!mark(0)) return SA_E_HIP;
+    // forward passes 1 and 2: fp16 token rows, logsumexps, partial sums
+    if (sa::launch_prep(L, P, Wk, offsets, workspace, s) != hipSuccess) return SA_E_HIP;
+    if (p.total_tokens > 0) {
+      const hipError_t e = sa::pass1q_ok(L) ? sa::launch_pass1q(L, H, offsets, token_mask, workspace, s)
+                                            : sa::launch_pass1(L, H, offsets, token_mask, workspace, s);
+      if (e != hipSuccess) return SA_E_HIP;
+      if (sa::launch_pass2(L, workspace, s) != hipSuccess) return SA_E_HIP;
+    }
+    if (!mark(1)) return SA_E_HIP;
+    if (sa::launch_bwd_user(L, Wv, dS, workspace, s) != hipSuccess) return SA_E_HIP;
+    if (!mark(2)) return SA_E_HIP;
+    if (sa::launch_bwd_dh(L, offsets, workspace, dH, s) != hipSuccess) return SA_E_HIP;
+    if (!mark(3)) return SA_E_HIP;
+    if (sa::launch_bwd_e(L, workspace, s) != hipSuccess) return SA_E_HIP;
+    if (!mark(4)) return SA_E_HIP;
+    if (sa::launch_bwd_params(L, P, Wk, dS, workspace, dP, dWk, dWv, s) != hipSuccess) return SA_E_HIP;
+    if (!mark(5)) return SA_E_HIP;
+    return SA_OK;
+  } catch (...) {
+    return SA_E_HIP;
+  }
 }
 
 const char* sa_status_string(sa_status status) {

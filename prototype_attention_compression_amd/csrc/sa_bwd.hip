@@ -1,0 +1,749 @@
+// sa_bwd.hip — the backward pass of Sketch Attention compression on gfx950
+// (bf16 inputs): given dS = dLoss/dS for every user's sketch, the gradients
+// dLoss/dH (per token) and dLoss/dP, dLoss/dWk, dLoss/dWv (summed over the
+// users).  SequenceO1 trains the compressor end to end through the ranking
+// loss (blog "100,000 videos in your pocket", "How it works" item 1: the
+// compression is differentiable and its gradients reach the prototypes and
+// projections; same page, "Takeaways": the compressor is trained on the real
+// loss).  The pages give no backward formulas; these follow from the chain
+// rule on the forward definition (softmax over prototypes per token, each
+// sketch row the mass-weighted mean of v_t = h_t Wv).
+//
+// With A[j,t] the allocations, m_j the masses, Sbar_j = (sum_t A[j,t] h_t) / m_j
+// (so S_j = Sbar_j Wv) and G = dS:
+//   Gm_j  = G_j / m_j,   Z_j = Gm_j Wv^T,   c_j = Z_j . Sbar_j        (per user)
+//   dA[j,t] = Z_j . h_t - c_j                  (through both U and the mass)
+//   delta_t = sum_j A[j,t] dA[j,t]
+//   dL[j,t] = A[j,t] (dA[j,t] - delta_t)       (softmax Jacobian per token)
+//   dh_t    = sum_j A[j,t] Z_j + dL[j,t] q'_j, q' = P Wk^T / sqrt(d)
+//   E_j     = sum_t dL[j,t] h_t  (over every token of the batch)
+//   dP = E Wk / sqrt(d),  dWk = E^T P / sqrt(d),  dWv = sum_u Sbar_u^T G_u
+// Every per-token product is a contraction with the token row h_t, so the
+// kernels reuse the fp16 token rows and logsumexps of forward passes 1 and 2
+// and never form a k x n array:
+//   bwd_user   per (user, 32 prototypes): sums pass 2's partial slots into
+//              U and m, writes Sbar, Z (fp32), c and the block's largest |Z|;
+//   bwd_zpack  per user scale zs (a power of two putting max |Z| in
+//              [2^13, 2^14)): Z zs in fp16 (MFMA operand), c zs;
+//   bwd_dh     token-major: a wave owns a 32-token tile with its rows as the
+//              B operand in registers and walks every prototype block twice
+//              (queries and Z rows staged in LDS): sweep 1 sums delta_t and
+//              the bound b_t = max_j |Y - c|; sweep 2 forms A and dL in fp16
+//              with a per-token power-of-two scale and accumulates dh_t
+//              with MFMAs whose B operands are the staged rows read with the
+//              transposing LDS read;
+//   bwd_e      prototype-major (like pass 2): E += dL h over token tiles,
+//              queries and Z rows resident, per-user scale, partial E per
+//              workgroup group;
+//   bwd_ereduce, bwd_outer, bwd_sum: E, dP, dWk, dWv.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "sa_device.h"
+#include "sa_launch.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kRows = 32;                         // prototypes per bwd_user workgroup
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kScaleMax = 16384.0f;             // 2^14
+
+__device__ __forceinline__ float bf16f(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// 2^e with 2^e x in [2^(t-1), 2^t) for finite x > 0 (e clamped to +-100);
+// 1 otherwise.
+__device__ __forceinline__ float pow2_scale(float x, int t) {
+  if (!(x > 0.f) || !(x < INFINITY)) return 1.f;
+  int ex = 0;
+  (void)frexpf(x, &ex);   // x = f 2^ex, f in [0.5, 1)
+  const int e = max(-100, min(100, t - ex));
+  return ldexpf(1.f, e);
+}
+
+// Scale for fp16 operands derived from a bound b on |Y - c|: |dL| <= 2 b, so
+// with s b < 2^14 the scaled dL stays below 2^15; the scaled allocations
+// (<= s <= 2^14) also fit fp16.
+__device__ __forceinline__ float operand_scale(float b) {
+  return b > 0.f ? fminf(kScaleMax, pow2_scale(b, 14)) : kScaleMax;
+}
+
+// Position of token i of a tile among the 16 accumulator registers of lane
+// half g (GEMM rows read from LDS row tau(m)): i = tau(acc_row(r, g)).
+__device__ __forceinline__ int acc_pos(int i) {
+  const int kk = i >> 4, g = (i >> 1) & 1, q = ((i & 1) << 2) | ((i >> 2) & 3);
+  return 16 * g + 8 * kk + q;
+}
+
+__device__ __forceinline__ float negl_of(uint32_t w) {
+  const half2v p = __builtin_bit_cast(half2v, w);
+  return (float)p[0] + (float)p[1] - kAllocShift;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- per user
+template <int D>
+__global__ __launch_bounds__(256) void bwd_user(const uint16_t* __restrict__ Wv, const float* __restrict__ dS,
+                                                Layout L, void* ws) {
+  constexpr int PER = kRows * D / 256;
+  constexpr int RPI = 256 / D;
+  __shared__ float sb[kRows][D + 1];   // U / m
+  __shared__ float gz[kRows][D + 1];   // dS / m, then Z
+  __shared__ float ms[kRows];
+  __shared__ float red[256];
+  const int nrb = L.k / kRows;
+  const int u = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+  const int j0 = rb * kRows;
+  const int tid = threadIdx.x;
+  // the user's partial slots: group + u for the pass-2 groups whose tile
+  // ranges meet the user's tiles
+  const int32_t* tile_base = ws_i32(ws, L.off_tile_base);
+  const int32_t nt = ws_i32(ws, L.off_hdr)[kHdrTiles];
+  const int G = L.p2_groups;
+  const int32_t Tg = (nt + 4 * G - 1) / (4 * G) * 4;
+  const int32_t t0 = tile_base[u], t1 = tile_base[u + 1];
+  int c0 = 0, c1 = 0;
+  if (t1 > t0) {
+    c0 = t0 / Tg + u;
+    c1 = (t1 - 1) / Tg + 1 + u;
+  }
+  const float* part_u = ws_f32(ws, L.off_part_u);
+  const float* part_m = ws_f32(ws, L.off_part_m);
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  for (int c = c0; c < c1; ++c) {
+    const float* base = part_u + ((int64_t)c * L.k + j0) * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
+  }
+  if (tid < kRows) {
+    float m = 0.f;
+    for (int c = c0; c < c1; ++c) m += part_m[(int64_t)c * L.k + j0 + tid];
+    ms[tid] = m;   // 2^14 m (the allocations of pass 2 carry 2^14)
+  }
+  __syncthreads();
+  const int64_t row0 = (int64_t)u * L.k + j0;
+  float* sbar = ws_f32(ws, L.off_bsbar) + row0 * D;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid + 256 * i, j = e / D, a = e % D;
+    const float m = ms[j];
+    const float v = m > 0.f ? acc[i] / m : 0.f;
+    sb[j][a] = v;
+    sbar[e] = v;
+    gz[j][a] = m > 0.f ? dS[row0 * D + e] * (kScaleMax / m) : 0.f;
+  }
+  __syncthreads();
+  // Z[j][a] = sum_b Gm[j][b] Wv[a][b]: thread (jr, a) takes rows jr + RPI i
+  const int a = tid % D, jr = tid / D;
+  float z[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) z[i] = 0.f;
+  const uint4* wrow = reinterpret_cast<const uint4*>(Wv + (int64_t)a * D);
+  for (int b8 = 0; b8 < D / 8; ++b8) {
+    const uint4 w = wrow[b8];
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float wlo = __uint_as_float(ww[h] << 16), whi = __uint_as_float(ww[h] & 0xffff0000u);
+      const int b = 8 * b8 + 2 * h;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) z[i] = fmaf(gz[jr + RPI * i][b + 1], whi, fmaf(gz[jr + RPI * i][b], wlo, z[i]));
+    }
+  }
+  __syncthreads();
+  float zm = 0.f;
+  float* z32 = ws_f32(ws, L.off_bz32) + row0 * D;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    gz[jr + RPI * i][a] = z[i];
+    z32[(int64_t)(jr + RPI * i) * D + a] = z[i];
+    zm = fmaxf(zm, fabsf(z[i]));
+  }
+  red[tid] = zm;
+  __syncthreads();
+  // c_j = Z_j . Sbar_j: 8 threads per row
+  {
+    const int j = tid >> 3, part = tid & 7;
+    float s = 0.f;
+    for (int e = part; e < D; e += 8) s = fmaf(gz[j][e], sb[j][e], s);
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    if (part == 0) ws_f32(ws, L.off_bc)[row0 + j] = s;
+  }
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+    __syncthreads();
+  }
+  if (tid == 0) ws_f32(ws, L.off_bzmax)[(int64_t)u * nrb + rb] = red[0];
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_zpack(Layout L, void* ws) {
+  constexpr int PER = kRows * D / 256;
+  __shared__ float red[256];
+  const int nrb = L.k / kRows;
+  const int u = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+  const int tid = threadIdx.x;
+  const float* bm = ws_f32(ws, L.off_bzmax) + (int64_t)u * nrb;
+  float m = 0.f;
+  for (int i = tid; i < nrb; i += 256) m = fmaxf(m, bm[i]);
+  red[tid] = m;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+    __syncthreads();
+  }
+  const float zs = pow2_scale(red[0], 14);
+  const int64_t row0 = (int64_t)u * L.k + rb * kRows;
+  const float* z32 = ws_f32(ws, L.off_bz32) + row0 * D;
+  _Float16* z16 = ws_f16(ws, L.off_bz16) + row0 * D;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) z16[tid + 256 * i] = (_Float16)(z32[tid + 256 * i] * zs);
+  if (tid < kRows) ws_f32(ws, L.off_bcz)[row0 + tid] = ws_f32(ws, L.off_bc)[row0 + tid] * zs;
+  if (rb == 0 && tid == 0) {
+    ws_f32(ws, L.off_bzs)[u] = zs;
+    ws_i32(ws, L.off_bbmax)[u] = 0;
+  }
+}
+
+// ---------------------------------------------------------------- dH
+// One workgroup = 4 waves = 4 consecutive tiles (one user: every user's tile
+// count is a multiple of 4).  Each wave keeps its tile's rows as the B
+// operand (token = lane % 32) of C[j, t] = q_j . h_t and Y[j, t] = Zs_j . h_t,
+// whose A operands (32 prototypes, row tau(m) of the staged block) come from
+// LDS.  The accumulators hold prototype tau(acc_row(r, g)) and token lane % 32,
+// which is exactly the A operand (row = token, contraction = prototypes) of
+// dh = sum_j (sA[j, t] Zs_j + sdL[j, t] ln2 q_j); its B operands are the
+// staged rows through the transposing read.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dh(const int64_t* __restrict__ offsets,
+                                              const int32_t* __restrict__ tile_base, Layout L, void* ws,
+                                              float* __restrict__ dH) {
+  constexpr int S = D / 16, DT = D / 32, PITCH = tile_pitch<D>(), BLK = kTile * PITCH, CPR = D / 8;
+  constexpr int LPT = kTile * CPR / 256;            // 16-B loads per thread per staged block
+  static_assert(LPT * 256 == kTile * CPR, "whole loads");
+  constexpr int STAGE = 2 * BLK + 2 * kTile * 4;
+  __shared__ __attribute__((aligned(16))) char lds[2][STAGE];
+  __shared__ float sinv[4][kTile];
+  const int32_t T = ws_i32(ws, L.off_hdr)[kHdrTiles];
+  const int tid = threadIdx.x;
+  if (T == 0) {
+    // offsets broke their contract: every user counts as empty, dh = 0
+    const int64_t n = L.N * D;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < n; i += (int64_t)gridDim.x * 256) dH[i] = 0.f;
+    return;
+  }
+  const int quad = blockIdx.x;
+  if (4 * quad >= T) return;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, g = lane >> 5;
+  const int tile = 4 * quad + wave;
+  const int u = find_user(tile_base, L.R, 4 * quad);
+  const int64_t tok0 = offsets[u] + (int64_t)(tile - tile_base[u]) * kTile;
+  const int64_t rem = offsets[u + 1] - tok0;
+  const int count = rem < 0 ? 0 : (rem < kTile ? (int)rem : kTile);
+
+  const _Float16* q16 = ws_f16(ws, L.off_q16);
+  const _Float16* z16 = ws_f16(ws, L.off_bz16) + (int64_t)u * L.k * D;
+  const float* czu = ws_f32(ws, L.off_bcz) + (int64_t)u * L.k;
+  const float zs = ws_f32(ws, L.off_bzs)[u];
+
+  const _Float16* hrow = ws_f16(ws, L.off_h16) + ((int64_t)tile * kTile + col) * D;
+  half8 hB[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) hB[s] = *reinterpret_cast<const half8*>(hrow + 16 * s + 8 * g);
+  const float negl = negl_of(reinterpret_cast<const uint32_t*>(ws_i32(ws, L.off_nl))[(int64_t)tile * kTile + col]);
+  const bool keep = negl > -30000.f;
+
+  const int NB = L.k / kTile;
+  uint4 pq[LPT], pz[LPT];
+  float pc = 0.f;
+  auto gload = [&](int i) {
+    const int jb = i % NB;
+#pragma unroll
+    for (int k2 = 0; k2 < LPT; ++k2) {
+      const int idx = tid + 256 * k2, row = idx / CPR, ch = idx % CPR;
+      pq[k2] = *reinterpret_cast<const uint4*>(q16 + (int64_t)(jb * kTile + row) * D + 8 * ch);
+      pz[k2] = *reinterpret_cast<const uint4*>(z16 + (int64_t)(jb * kTile + row) * D + 8 * ch);
+    }
+    if (tid < kTile) pc = czu[jb * kTile + tid];
+  };
+  auto swrite = [&](int buf) {
+    char* base = lds[buf];
+#pragma unroll
+    for (int k2 = 0; k2 < LPT; ++k2) {
+      const int idx = tid + 256 * k2, row = idx / CPR, ch = idx % CPR;
+      *reinterpret_cast<uint4*>(base + row * PITCH + 16 * ch) = pq[k2];
+      *reinterpret_cast<uint4*>(base + BLK + row * PITCH + 16 * ch) = pz[k2];
+    }
+    if (tid < kTile) reinterpret_cast<float*>(base + 2 * BLK)[acc_pos(tid)] = pc;
+  };
+
+  const int abase = tau(col) * PITCH + 16 * g;
+  const int i16 = lane & 15, gh = (lane >> 4) & 1;
+  const int tr_base = (4 * (i16 >> 2) + 2 * g) * PITCH + 32 * gh + 8 * (i16 & 3);
+
+  float dsum = 0.f, bmx = 0.f, delta = 0.f, sg = kScaleMax, sl = kScaleMax * kLn2;
+  float16v dHc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dHc[dt] = float16v{};
+
+  gload(0);
+  swrite(0);
+  __syncthreads();
+  for (int i = 0; i < 2 * NB; ++i) {
+    const int buf = i & 1;
+    if (i + 1 < 2 * NB) gload(i + 1);
+    const char* qb = lds[buf];
+    const char* zb = qb + BLK;
+    half8 a[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) a[s] = *reinterpret_cast<const half8*>(qb + abase + 32 * s);
+    float16v Lc = float16v{};
+#pragma unroll
+    for (int s = 0; s < S; ++s) Lc = mfma32x32x16(a[s], hB[s], Lc);
+#pragma unroll
+    for (int s = 0; s < S; ++s) a[s] = *reinterpret_cast<const half8*>(zb + abase + 32 * s);
+    float16v Yc = float16v{};
+#pragma unroll
+    for (int s = 0; s < S; ++s) Yc = mfma32x32x16(a[s], hB[s], Yc);
+    const float4* cp = reinterpret_cast<const float4*>(qb + 2 * BLK) + 4 * g;
+    float cr[16];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float4 c4 = cp[v];
+      cr[4 * v] = c4.x;
+      cr[4 * v + 1] = c4.y;
+      cr[4 * v + 2] = c4.z;
+      cr[4 * v + 3] = c4.w;
+    }
+    if (i < NB) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float A = __builtin_amdgcn_exp2f(Lc[r] + negl);
+        const float yc = Yc[r] - cr[r];
+        dsum = fmaf(A, yc, dsum);
+        bmx = fmaxf(bmx, fabsf(yc));
+      }
+      if (i == NB - 1) {
+        dsum += __shfl_xor(dsum, 32);
+        bmx = fmaxf(bmx, __shfl_xor(bmx, 32));
+        if (!keep) bmx = 0.f;
+        delta = dsum;
+        sg = operand_scale(bmx);
+        sl = sg * kLn2;
+        if (g == 0) {
+          sinv[wave][col] = 1.0f / (sg * zs);
+          ws_f32(ws, L.off_bdelta)[(int64_t)tile * kTile + col] = delta;
+        }
+        float wm = bmx;
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o));
+        if (lane == 0 && wm > 0.f)
+          atomicMax(reinterpret_cast<unsigned int*>(ws_i32(ws, L.off_bbmax)) + u, __float_as_uint(wm));
+      }
+    } else {
+      half8 al[2], ad[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float A = __builtin_amdgcn_exp2f(Lc[r] + negl);
+        const float dl = A * (Yc[r] - cr[r] - delta);
+        al[r >> 3][r & 7] = (_Float16)(dl * sl);
+        ad[r >> 3][r & 7] = (_Float16)(A * sg);
+      }
+      half8 hb[2][DT];
+      tile_tr_reads<D>(lds_addr(qb) + tr_base, hb);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) dHc[dt] = mfma32x32x16(al[kk], hb[kk][dt], dHc[dt]);
+      tile_tr_reads<D>(lds_addr(zb) + tr_base, hb);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) dHc[dt] = mfma32x32x16(ad[kk], hb[kk][dt], dHc[dt]);
+    }
+    if (i + 1 < 2 * NB) swrite(buf ^ 1);
+    __syncthreads();
+  }
+  // accumulator rows are tokens acc_row(r, g), columns 32 dt + col
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int t = acc_row(r, g);
+    if (t < count) {
+      const float sc = sinv[wave][t];
+      float* dst = dH + (tok0 + t) * D + col;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dst[32 * dt] = dHc[dt][r] * sc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- E
+// Prototype-major like pass 2: W waves of 32 prototypes; groups of
+// e_pblocks workgroups walk equal tile ranges; per tile
+//   C[t, j] = h_t . q_j, Y[t, j] = h_t . Zs_j (token rows from LDS as the A
+//   operand, queries and Z rows resident as B operands),
+//   sdL = s_u A (Y - cs_j - delta_t) in fp16, E += sdL h (transposing reads).
+// E is rescaled to true units at every user boundary and written once per
+// workgroup to partial slot `group`.
+template <int D, int W>
+__global__ __launch_bounds__(W * 64) void bwd_e(const int32_t* __restrict__ tile_base, Layout L, void* ws) {
+  constexpr int S = D / 16, DT = D / 32, PITCH = tile_pitch<D>(), TB = kTile * PITCH, CPR = D / 8;
+  constexpr int NT = W * 64;
+  constexpr int LPT = kTile * CPR / NT;
+  static_assert(LPT * NT == kTile * CPR, "whole loads");
+  constexpr int STAGE = TB + 2 * kTile * 4;
+  __shared__ __attribute__((aligned(16))) char lds[2][STAGE];
+  const int P = L.e_pblocks, G = L.e_groups;
+  const int x = blockIdx.x, xcd = x & 7, slotw = x >> 3;
+  const int group = xcd + 8 * (slotw / P);
+  const int pb = slotw % P;
+  if (group >= G) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, g = lane >> 5;
+  const int p0 = pb * (W * kTile) + wave * kTile;
+  float* epart = ws_f32(ws, L.off_bepart) + ((int64_t)group * L.k + p0) * D;
+
+  const int32_t T = ws_i32(ws, L.off_hdr)[kHdrTiles];
+  const int32_t Tg = (T + 4 * G - 1) / (4 * G) * 4;
+  const int32_t s0 = group * Tg, s1 = min(T, s0 + Tg);
+  float16v Er[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) Er[dt] = float16v{};
+  if (s0 < s1) {
+    const _Float16* q16 = ws_f16(ws, L.off_q16);
+    half8 qf[S], zf[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      qf[s] = *reinterpret_cast<const half8*>(q16 + (int64_t)(p0 + col) * D + 16 * s + 8 * g);
+    const _Float16* h16 = ws_f16(ws, L.off_h16);
+    const uint32_t* nlw = reinterpret_cast<const uint32_t*>(ws_i32(ws, L.off_nl));
+    const float* dlt = ws_f32(ws, L.off_bdelta);
+    uint4 pr[LPT];
+    uint32_t pn = 0;
+    float pd = 0.f;
+    auto gload = [&](int32_t t) {
+      const _Float16* src = h16 + (int64_t)t * kTile * D;
+#pragma unroll
+      for (int k2 = 0; k2 < LPT; ++k2) {
+        const int idx = tid + NT * k2, row = idx / CPR, ch = idx % CPR;
+        pr[k2] = *reinterpret_cast<const uint4*>(src + row * D + 8 * ch);
+      }
+      if (tid < kTile) {
+        pn = nlw[(int64_t)t * kTile + tid];
+        pd = dlt[(int64_t)t * kTile + tid];
+      }
+    };
+    auto swrite = [&](int buf) {
+      char* base = lds[buf];
+#pragma unroll
+      for (int k2 = 0; k2 < LPT; ++k2) {
+        const int idx = tid + NT * k2, row = idx / CPR, ch = idx % CPR;
+        *reinterpret_cast<uint4*>(base + row * PITCH + 16 * ch) = pr[k2];
+      }
+      if (tid < kTile) {
+        float* pv = reinterpret_cast<float*>(base + TB);
+        pv[acc_pos(tid)] = negl_of(pn);
+        pv[kTile + acc_pos(tid)] = pd;
+      }
+    };
+    const int abase = tau(col) * PITCH + 16 * g;
+    const int i16 = lane & 15, gh = (lane >> 4) & 1;
+    const int tr_base = (4 * (i16 >> 2) + 2 * g) * PITCH + 32 * gh + 8 * (i16 & 3);
+
+    int u = find_user(tile_base, L.R, s0);
+    int32_t ub = tile_base[u + 1];
+    float cz = 0.f, su = kScaleMax, back = 1.f;
+    auto load_user = [&]() {
+      const _Float16* z16 = ws_f16(ws, L.off_bz16) + ((int64_t)u * L.k + p0 + col) * D;
+#pragma unroll
+      for (int s = 0; s < S; ++s) zf[s] = *reinterpret_cast<const half8*>(z16 + 16 * s + 8 * g);
+      cz = ws_f32(ws, L.off_bcz)[(int64_t)u * L.k + p0 + col];
+      const float bm = __uint_as_float(reinterpret_cast<const uint32_t*>(ws_i32(ws, L.off_bbmax))[u]);
+      su = operand_scale(bm);
+      back = 1.0f / (su * ws_f32(ws, L.off_bzs)[u]);
+    };
+    load_user();
+    float16v Ea[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) Ea[dt] = float16v{};
+
+    gload(s0);
+    swrite(0);
+    __syncthreads();
+    for (int32_t t = s0; t < s1; ++t) {
+      const int buf = (t - s0) & 1;
+      if (t + 1 < s1) gload(t + 1);
+      if (t == ub) {   // uniform: the next user's tiles start here
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          Er[dt] += Ea[dt] * back;
+          Ea[dt] = float16v{};
+        }
+        while (tile_base[u + 1] <= t) ++u;
+        ub = tile_base[u + 1];
+        load_user();
+      }
+      const char* hb_ = lds[buf];
+      half8 ha[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) ha[s] = *reinterpret_cast<const half8*>(hb_ + abase + 32 * s);
+      float16v Lc = float16v{}, Yc = float16v{};
+#pragma unroll
+      for (int s = 0; s < S; ++s) Lc = mfma32x32x16(ha[s], qf[s], Lc);
+#pragma unroll
+      for (int s = 0; s < S; ++s) Yc = mfma32x32x16(ha[s], zf[s], Yc);
+      const float4* pv = reinterpret_cast<const float4*>(hb_ + TB);
+      float nl[16], dd[16];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float4 a4 = pv[4 * g + v], d4 = pv[8 + 4 * g + v];
+        nl[4 * v] = a4.x;
+        nl[4 * v + 1] = a4.y;
+        nl[4 * v + 2] = a4.z;
+        nl[4 * v + 3] = a4.w;
+        dd[4 * v] = d4.x;
+        dd[4 * v + 1] = d4.y;
+        dd[4 * v + 2] = d4.z;
+        dd[4 * v + 3] = d4.w;
+      }
+      half8 al[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float A = __builtin_amdgcn_exp2f(Lc[r] + nl[r]);
+        al[r >> 3][r & 7] = (_Float16)(A * (Yc[r] - cz - dd[r]) * su);
+      }
+      half8 hbv[2][DT];
+      tile_tr_reads<D>(lds_addr(hb_) + tr_base, hbv);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) Ea[dt] = mfma32x32x16(al[kk], hbv[kk][dt], Ea[dt]);
+      if (t + 1 < s1) swrite(buf ^ 1);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) Er[dt] += Ea[dt] * back;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) epart[(int64_t)acc_row(r, g) * D + 32 * dt + col] = Er[dt][r];
+}
+
+// ---------------------------------------------------------------- reductions
+// E = sum over the partial slots (fixed order), and dP = E Wk / sqrt(d)
+template <int D>
+__global__ __launch_bounds__(256) void bwd_ereduce(const uint16_t* __restrict__ Wk, Layout L, void* ws,
+                                                   float* __restrict__ dP) {
+  constexpr int PER = kRows * D / 256;
+  constexpr int RPI = 256 / D;
+  __shared__ float es[kRows][D + 1];
+  const int j0 = blockIdx.x * kRows, tid = threadIdx.x;
+  const float* ep = ws_f32(ws, L.off_bepart);
+  float* et = ws_f32(ws, L.off_betot) + (int64_t)j0 * D;
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  for (int gi = 0; gi < L.e_groups; ++gi) {
+    const float* base = ep + ((int64_t)gi * L.k + j0) * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid + 256 * i;
+    et[e] = acc[i];
+    es[e / D][e % D] = acc[i];
+  }
+  __syncthreads();
+  const int b = tid % D, jr = tid / D;
+  float out[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) out[i] = 0.f;
+  for (int a = 0; a < D; ++a) {
+    const float w = bf16f(Wk[(int64_t)a * D + b]);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) out[i] = fmaf(es[jr + RPI * i][a], w, out[i]);
+  }
+  const float rs = 1.0f / sqrtf((float)D);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) dP[(int64_t)(j0 + jr + RPI * i) * D + b] = out[i] * rs;
+}
+
+template <typename T>
+__device__ __forceinline__ float ld_any(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld_any<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld_any<uint16_t>(const uint16_t* p, int64_t i) { return bf16f(p[i]); }
+
+// part[c][a][b] = sum over rows i of chunk c of X[i][a] Y[i][b]
+template <int D, typename TY>
+__global__ __launch_bounds__(256) void bwd_outer(const float* __restrict__ X, const TY* __restrict__ Y, int64_t rows,
+                                                 float* __restrict__ part) {
+  constexpr int TA = D / 16;           // outputs per thread: TA x TA
+  constexpr int RB = 32;               // rows staged per round
+  __shared__ float xs[RB][D];
+  __shared__ float ys[RB][D];
+  const int tid = threadIdx.x;
+  const int a0 = (tid >> 4) * TA, b0 = (tid & 15) * TA;
+  const int64_t r0 = (int64_t)blockIdx.x * kOuterRows;
+  const int64_t r1 = min(rows, r0 + kOuterRows);
+  float acc[TA][TA];
+#pragma unroll
+  for (int i = 0; i < TA; ++i)
+#pragma unroll
+    for (int j = 0; j < TA; ++j) acc[i][j] = 0.f;
+  for (int64_t rb = r0; rb < r1; rb += RB) {
+    for (int e = tid; e < RB * D; e += 256) {
+      const int rr = e / D, cc = e % D;
+      const int64_t row = rb + rr;
+      const bool ok = row < r1;
+      xs[rr][cc] = ok ? X[row * D + cc] : 0.f;
+      ys[rr][cc] = ok ? ld_any<TY>(Y, row * D + cc) : 0.f;
+    }
+    __syncthreads();
+    for (int rr = 0; rr < RB; ++rr) {
+      float xv[TA], yv[TA];
+#pragma unroll
+      for (int i = 0; i < TA; ++i) {
+        xv[i] = xs[rr][a0 + i];
+        yv[i] = ys[rr][b0 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < TA; ++i)
+#pragma unroll
+        for (int j = 0; j < TA; ++j) acc[i][j] = fmaf(xv[i], yv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  float* dst = part + (int64_t)blockIdx.x * D * D;
+#pragma unroll
+  for (int i = 0; i < TA; ++i)
+#pragma unroll
+    for (int j = 0; j < TA; ++j) dst[(a0 + i) * D + b0 + j] = acc[i][j];
+}
+
+// out[e] = scale * sum_c part[c][e] (fixed order); n_chunks = 0 writes zeros
+__global__ __launch_bounds__(256) void bwd_sum(const float* __restrict__ part, int n_chunks, int64_t n, float scale,
+                                               float* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  float s = 0.f;
+  for (int c = 0; c < n_chunks; ++c) s += part[(int64_t)c * n + e];
+  out[e] = s * scale;
+}
+
+__global__ __launch_bounds__(256) void fill_zero(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
+}
+
+// ---------------------------------------------------------------- launchers
+template <typename T>
+static T* hptr(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t grid = std::min<int64_t>(1024, (n + 255) / 256);
+  hipLaunchKernelGGL(fill_zero, dim3((unsigned)grid), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_user(const Layout& L, const void* Wv, const float* dS, void* ws, hipStream_t stream) {
+  const int64_t grid = (int64_t)L.R * (L.k / kRows);
+  if (grid == 0) return hipSuccess;
+  if (L.d == 128) {
+    hipLaunchKernelGGL((bwd_user<128>), dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)Wv, dS, L, ws);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL((bwd_zpack<128>), dim3((unsigned)grid), dim3(256), 0, stream, L, ws);
+  } else {
+    hipLaunchKernelGGL((bwd_user<64>), dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)Wv, dS, L, ws);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL((bwd_zpack<64>), dim3((unsigned)grid), dim3(256), 0, stream, L, ws);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dh(const Layout& L, const int64_t* offsets, void* ws, float* dH, hipStream_t stream) {
+  if (L.N == 0) return hipSuccess;
+  const int64_t grid = std::max<int64_t>(1, L.tiles_max / kUserTileAlign);
+  const int32_t* tb = hptr<int32_t>(ws, L.off_tile_base);
+  if (L.d == 128)
+    hipLaunchKernelGGL((bwd_dh<128>), dim3((unsigned)grid), dim3(256), 0, stream, offsets, tb, L, ws, dH);
+  else
+    hipLaunchKernelGGL((bwd_dh<64>), dim3((unsigned)grid), dim3(256), 0, stream, offsets, tb, L, ws, dH);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_e(const Layout& L, void* ws, hipStream_t stream) {
+  const int64_t grid = (int64_t)8 * L.e_pblocks * ((L.e_groups + 7) / 8);
+  const int32_t* tb = hptr<int32_t>(ws, L.off_tile_base);
+  const dim3 g((unsigned)grid);
+  if (L.d == 128) {
+    if (L.e_waves == 4)
+      hipLaunchKernelGGL((bwd_e<128, 4>), g, dim3(256), 0, stream, tb, L, ws);
+    else
+      hipLaunchKernelGGL((bwd_e<128, 2>), g, dim3(128), 0, stream, tb, L, ws);
+  } else {
+    if (L.e_waves == 4)
+      hipLaunchKernelGGL((bwd_e<64, 4>), g, dim3(256), 0, stream, tb, L, ws);
+    else
+      hipLaunchKernelGGL((bwd_e<64, 2>), g, dim3(128), 0, stream, tb, L, ws);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_params(const Layout& L, const void* P, const void* Wk, const float* dS, void* ws, float* dP,
+                             float* dWk, float* dWv, hipStream_t stream) {
+  const int D = L.d;
+  const int64_t dd = (int64_t)D * D;
+  const dim3 gsum((unsigned)((dd + 255) / 256));
+  float* et = hptr<float>(ws, L.off_betot);
+  float* op = hptr<float>(ws, L.off_bopart);
+  const float* sbar = hptr<float>(ws, L.off_bsbar);
+  // E and dP
+  if (D == 128)
+    hipLaunchKernelGGL((bwd_ereduce<128>), dim3(L.k / kRows), dim3(256), 0, stream, (const uint16_t*)Wk, L, ws, dP);
+  else
+    hipLaunchKernelGGL((bwd_ereduce<64>), dim3(L.k / kRows), dim3(256), 0, stream, (const uint16_t*)Wk, L, ws, dP);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  // dWk = E^T P / sqrt(d)
+  const int ck = (L.k + kOuterRows - 1) / kOuterRows;
+  if (D == 128)
+    hipLaunchKernelGGL((bwd_outer<128, uint16_t>), dim3(ck), dim3(256), 0, stream, (const float*)et,
+                       (const uint16_t*)P, (int64_t)L.k, op);
+  else
+    hipLaunchKernelGGL((bwd_outer<64, uint16_t>), dim3(ck), dim3(256), 0, stream, (const float*)et,
+                       (const uint16_t*)P, (int64_t)L.k, op);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL(bwd_sum, gsum, dim3(256), 0, stream, (const float*)op, ck, dd, 1.0f / sqrtf((float)D), dWk);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  // dWv = sum_u Sbar_u^T dS_u
+  const int64_t rows = (int64_t)L.R * L.k;
+  const int cv = (int)((rows + kOuterRows - 1) / kOuterRows);
+  if (cv > 0) {
+    if (D == 128)
+      hipLaunchKernelGGL((bwd_outer<128, float>), dim3(cv), dim3(256), 0, stream, sbar, dS, rows, op);
+    else
+      hipLaunchKernelGGL((bwd_outer<64, float>), dim3(cv), dim3(256), 0, stream, sbar, dS, rows, op);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  hipLaunchKernelGGL(bwd_sum, gsum, dim3(256), 0, stream, (const float*)op, cv, dd, 1.0f, dWv);
+  return hipGetLastError();
+}
+
+}  // namespace sa

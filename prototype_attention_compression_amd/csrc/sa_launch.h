@@ -36,5 +36,16 @@ hipError_t launch_fused(const Layout& L, void* ws, hipStream_t stream);
 // partial-sum reduction, prototype-wise normalisation and the value projection
 hipError_t launch_finalize(const Layout& L, const void* Wv, void* ws, float* S, float* mass,
                            hipStream_t stream);
+// backward (bf16): per-user Z, c and scales from pass 2's partial sums and dS
+hipError_t launch_bwd_user(const Layout& L, const void* Wv, const float* dS, void* ws, hipStream_t stream);
+// backward: token-major dH (and the per-token delta the E pass reads)
+hipError_t launch_bwd_dh(const Layout& L, const int64_t* offsets, void* ws, float* dH, hipStream_t stream);
+// backward: prototype-major partial E = sum_t dL h_t
+hipError_t launch_bwd_e(const Layout& L, void* ws, hipStream_t stream);
+// backward: E, dP, dWk and dWv from the partials
+hipError_t launch_bwd_params(const Layout& L, const void* P, const void* Wk, const float* dS, void* ws, float* dP,
+                             float* dWk, float* dWv, hipStream_t stream);
+// zero fill (used when the batch has no users)
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 
 }  // namespace sa

@@ -40,6 +40,8 @@ constexpr int kFusedProtos = 256;    // prototypes per one-pass workgroup (8 wav
 constexpr int kFusedWGs = 256;       // one-pass grid: groups x n_pblocks workgroups
 constexpr int kP2WGs = 256;          // pass-2 grid (bf16): p2_groups x n_pblocks workgroups
 constexpr int kXSlots = 8;           // ring slots of the one-pass exchange
+constexpr int kBwdEWGs = 512;        // bwd_e grid: e_groups x e_pblocks workgroups
+constexpr int kOuterRows = 256;      // rows per chunk of the outer-product reductions
 
 // Device error flags (workspace header word 0, bitwise or).
 constexpr int32_t kErrBadOffsets = 1;
@@ -76,6 +78,23 @@ struct Layout {
   size_t off_lse32;        // [tiles_max*32] float, fp32 path
   size_t off_part_u;       // [parts_max, k, d] float  partial sums of A h
   size_t off_part_m;       // [parts_max, k] float     partial masses
+  // backward (bf16 only; laid out by the backward workspace query, else 0)
+  int32_t e_waves;         // bwd_e waves per workgroup (4 or 2), 32 prototypes each
+  int32_t e_pblocks;       // k / (32 e_waves)
+  int32_t e_groups;        // bwd_e groups: max(1, kBwdEWGs / e_pblocks)
+  int32_t o_chunks;        // row chunks of the outer-product reductions
+  size_t off_bz32;         // [R, k, d] float   Z = (dS / m) Wv^T
+  size_t off_bsbar;        // [R, k, d] float   U / m (the mass-normalised history rows)
+  size_t off_bc;           // [R, k] float      c_j = Z_j . (U_j / m_j)
+  size_t off_bzmax;        // [R, k / 32] float largest |Z| of each 32-row block
+  size_t off_bz16;         // [R, k, d] fp16    Z zs_u
+  size_t off_bcz;          // [R, k] float      c zs_u
+  size_t off_bzs;          // [R] float         zs_u, a power of two
+  size_t off_bbmax;        // [R] uint32        bits of the user's largest |Y - c| (scaled, >= 0)
+  size_t off_bdelta;       // [tiles_max, 32] float  delta_t zs_u
+  size_t off_bepart;       // [e_groups, k, d] float partial E
+  size_t off_betot;        // [k, d] float      E = sum_t dL[., t] h_t
+  size_t off_bopart;       // [o_chunks, d, d] float partial outer products
   size_t total;
 };
 

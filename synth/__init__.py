@@ -11,4 +11,5 @@ from .gen import (  # noqa: F401
     f32_to_bf16_bits,
     make_config,
     make_inputs,
+    make_sketch_grad,
 )

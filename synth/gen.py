@@ -43,6 +43,7 @@ __all__ = [
     "f32_to_bf16_bits",
     "make_config",
     "make_inputs",
+    "make_sketch_grad",
 ]
 
 
@@ -272,3 +273,20 @@ def make_config(name: str, **overrides) -> Inputs:
 
 def config_names() -> List[str]:
     return list(CONFIGS)
+
+
+def make_sketch_grad(R: int, k: int, d: int, seed: int, scale: float = 1.0, users=None) -> np.ndarray:
+    """Seeded upstream gradient dLoss/dS [R, k, d] float32 for the backward pass.
+
+    The pages train through a ranking loss whose gradients are not given;
+    this stands in with N(0, 1) entries times ``scale`` (float32), drawn from
+    ``numpy.random.default_rng(SeedSequence(seed))`` in one [R, k, d] draw.
+    ``users`` (optional) keeps those users' rows and zeroes the others.
+    """
+    g = np.random.default_rng(np.random.SeedSequence(seed))
+    G = g.standard_normal((R, k, d), dtype=np.float32) * np.float32(scale)
+    if users is not None:
+        keep = np.zeros(R, dtype=bool)
+        keep[list(users)] = True
+        G[~keep] = 0.0
+    return G

@@ -117,3 +117,60 @@ def test_binding_validates_before_library():
     off = torch.tensor([0, 4])
     with pytest.raises(ValueError):
         sa.compress(H, off, H[:0], H[:0], H[:0])   # CPU tensors are refused
+
+
+# ---------------------------------------------------------------- backward
+def _bws(R, N, d, k, dt, flags=0):
+    pb = _lib.SaProblem(R, N, d, k, dt, flags)
+    out = ctypes.c_size_t(0)
+    st = _lib.load().sa_backward_workspace_size(ctypes.byref(pb), ctypes.byref(out))
+    return st, out.value
+
+
+def test_backward_workspace_size():
+    assert _bws(2, 1000, 128, 1024, sa.SA_BF16)[0] == sa.SA_OK
+    assert _bws(2, 1000, 128, 1024, sa.SA_F32)[0] == sa.SA_E_UNSUPPORTED
+    assert _bws(2, 1000, 128, 1024, sa.SA_BF16, sa.SA_FLAG_ONE_PASS)[0] == sa.SA_E_UNSUPPORTED
+    assert _bws(2, 1000, 128, 1024, sa.SA_BF16, sa.SA_FLAG_TWO_PASS)[0] == sa.SA_OK
+    assert _bws(2, 1000, 96, 1024, sa.SA_BF16)[0] == sa.SA_E_UNSUPPORTED
+    assert _bws(2, 1000, 128, 1000, sa.SA_BF16)[0] == sa.SA_E_UNSUPPORTED
+    # the backward needs the forward's buffers and more
+    for R, N, d, k in ((2, 1000, 128, 1024), (40, 4_000_000, 128, 1024), (3, 77, 64, 320)):
+        st, b = _bws(R, N, d, k, sa.SA_BF16)
+        assert st == sa.SA_OK and b % 256 == 0
+        assert b > sa.workspace_size(R, N, d, k)
+    pb = _lib.problem(1, 10, 128, 1024, 0)
+    assert _lib.load().sa_backward_workspace_size(ctypes.byref(pb), None) == sa.SA_E_INVALID
+
+
+def _bcall(pb, H=FAKE, off=FAKE, mask=None, Wk=FAKE, Wv=FAKE, P=FAKE, dS=FAKE, dH=FAKE, dP=FAKE, dWk=FAKE,
+           dWv=FAKE, ws=FAKE, wsb=1 << 40):
+    return _lib.raw_compress_backward(pb, H, off, mask, Wk, Wv, P, dS, dH, dP, dWk, dWv, ws, wsb, None)
+
+
+def test_backward_argument_errors_before_launch():
+    lib = _lib.load()
+    vp = None
+    assert lib.sa_compress_backward(None, *([vp] * 12), 0, vp) == sa.SA_E_INVALID
+    pb = _lib.problem(2, 100, 128, 256, 0)
+    for name in ("off", "H", "Wk", "Wv", "P", "dS", "dH", "dP", "dWk", "dWv"):
+        assert _bcall(pb, **{name: None}) == sa.SA_E_INVALID, name
+    assert _bcall(pb, ws=None) == sa.SA_E_WORKSPACE
+    need = _bws(2, 100, 128, 256, 0)[1]
+    assert _bcall(pb, wsb=need - 1) == sa.SA_E_WORKSPACE
+    assert _bcall(pb, ws=FAKE + 16, wsb=need) == sa.SA_E_INVALID
+    assert _bcall(_lib.problem(2, 100, 128, 256, sa.SA_F32)) == sa.SA_E_UNSUPPORTED
+    assert _bcall(_lib.problem(2, 100, 128, 256, 0, sa.SA_FLAG_ONE_PASS)) == sa.SA_E_UNSUPPORTED
+    # no tokens: H and dH may be NULL (the call would then launch, so only
+    # the argument checks that come first are exercised here)
+    assert _bcall(_lib.problem(2, 0, 128, 256, 0), H=None, dH=None, ws=None) == sa.SA_E_WORKSPACE
+
+
+def test_backward_binding_validates_before_library():
+    import torch
+    H = torch.zeros(4, 128, dtype=torch.bfloat16)
+    off = torch.tensor([0, 4])
+    with pytest.raises(ValueError):
+        sa.compress_backward(H, off, H[:0], H[:0], H[:0], torch.zeros(1, 1, 128))
+    with pytest.raises(ValueError):
+        sa.compress_backward(H.float(), off, H[:0], H[:0], H[:0], torch.zeros(1, 1, 128))
