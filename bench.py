@@ -16,6 +16,11 @@ roofline object reports the dominant kernel (pass 2) against the fp16/bf16
 dense MFMA peak.  The CPU baseline times the fp64 oracle on a bounded sample
 of the same workload on the host cores and checks the GPU sketches of that
 sample against it.
+
+``--backward`` times one sa_compress_backward call per step instead (the
+gradients dH, dP, dWk, dWv for a seeded dS, forward recomputation included)
+on the same workload; its roofline object reports the token-major dH kernel
+and its CPU baseline times the fp64 gradient oracle.
 """
 from __future__ import annotations
 
@@ -136,6 +141,148 @@ def cpu_baseline(inp, S_gpu, budget_s: float):
     }
 
 
+def _calibration_copy(torch, dev):
+    """One plain device-to-device copy of known size, for counter scaling."""
+    src = torch.ones(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def cpu_baseline_backward(inp, dS, dH_gpu, budget_s: float):
+    """fp64 gradient oracle on the host cores over a bounded sample of users."""
+    import threadpoolctl
+
+    from oracle import sketch_one_grad
+
+    cores = len(os.sched_getaffinity(0))
+    with threadpoolctl.threadpool_limits(cores):
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        users, tokens, t_total = [], 0, 0.0
+        errs = []
+        for u in range(inp.R):
+            sl = inp.user_slice(u)
+            keep = slice(None) if inp.mask is None else (inp.mask[sl] != 0)
+            Hu = inp.H[sl][keep]
+            t0 = time.perf_counter()
+            gH, _, _, _ = sketch_one_grad(Hu, inp.Wk, inp.Wv, inp.P, dS[u])
+            t_total += time.perf_counter() - t0
+            users.append(u)
+            tokens += Hu.shape[0]
+            diff = np.abs(dH_gpu[sl][keep].astype(np.float64) - gH)
+            errs.append((diff.max(), np.abs(gH).max(), diff.sum(), np.abs(gH).sum()))
+            if t_total >= budget_s:
+                break
+    max_rel = max(e[0] for e in errs) / max(max(e[1] for e in errs), 1e-300)
+    mean_rel = sum(e[2] for e in errs) / max(sum(e[3] for e in errs), 1e-300)
+    return {
+        "value": tokens / t_total,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"users {users[0]}..{users[-1]} ({len(users)} of {inp.R}, {tokens} tokens), "
+                  f"numpy fp64 gradients, {t_total:.1f} s",
+        "parity_on_sample": {"dH_max_rel": max_rel, "dH_mean_rel": mean_rel},
+    }
+
+
+def bench_backward(args, inp, torch, dev, sa):
+    """Times sa_compress_backward (forward recomputation included)."""
+    from synth import make_sketch_grad
+
+    H, off, Wk, Wv, P, mask = _upload(inp, torch, dev)
+    R, N, d, k = inp.R, inp.N, inp.d, inp.k
+    n_valid = inp.valid_tokens()
+    dS_host = make_sketch_grad(R, k, d, seed=7)
+    dS = torch.from_numpy(dS_host).to(dev)
+    ws = torch.empty(sa.backward_workspace_size(R, N, d, k), dtype=torch.uint8, device=dev)
+    dH = torch.empty((N, d), dtype=torch.float32, device=dev)
+    dP = torch.empty((k, d), dtype=torch.float32, device=dev)
+    dWk = torch.empty((d, d), dtype=torch.float32, device=dev)
+    dWv = torch.empty((d, d), dtype=torch.float32, device=dev)
+    hip = _Hip()
+    n_ev = sa._lib.NUM_BWD_PHASE_EVENTS
+    step_events = [[hip.event() for _ in range(n_ev)] for _ in range(args.steps)]
+    ev_arrays = [(ctypes.c_void_p * n_ev)(*evs) for evs in step_events]
+    pb = sa._lib.problem(R, N, d, k, sa.SA_BF16)
+    ptr = sa._lib._ptr
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def step(events=None):
+        st = sa._lib.raw_compress_backward(pb, ptr(H), ptr(off), ptr(mask), ptr(Wk), ptr(Wv), ptr(P), ptr(dS),
+                                           ptr(dH), ptr(dP), ptr(dWk), ptr(dWv), ptr(ws), ws.numel(), stream,
+                                           events)
+        if st != sa.SA_OK:
+            raise sa.SaError(st, "sa_compress_backward")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(ev_arrays[i])
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(stop) / args.steps
+    phases = ["forward_recompute", "per_user", "dh", "e", "params"]
+    phase_ms = {p: 0.0 for p in phases}
+    for evs in step_events:
+        for i, p in enumerate(phases):
+            phase_ms[p] += hip.elapsed_ms(evs[i], evs[i + 1]) / args.steps
+        for e in evs:
+            hip.destroy(e)
+    nkd = float(n_valid) * k * d
+    # algorithmic work of the backward proper: logits and Z.h once (2 x 2nkd),
+    # E = dL h (2nkd), dh's two contractions (4nkd)
+    algo_flop = 10.0 * nkd
+    dh_flop = 8.0 * nkd     # bwd_dh: logits, Z.h and the two contractions of dh
+    dh_s = phase_ms["dh"] * 1e-3
+    dh_achieved = dh_flop / dh_s / 1e12 if dh_s > 0 else 0.0
+    out = {
+        "metric": "history tokens/s (backward: dH, dP, dWk, dWv), SA n=100K,k=1024,d=128",
+        "value": n_valid / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": inp.name, "users": R, "tokens": n_valid, "k": k, "d": d,
+                   "input_dtype": inp.dtype, "parallelism": "single_gpu", "pass": "backward"},
+        "tflops": algo_flop / (ms_step * 1e-3) / 1e12,
+        "phase_ms": phase_ms,
+        "wall_s_timed": t_wall,
+        "roofline": {
+            "kernel": "bwd_dh",
+            "bound": "mfma",
+            "achieved": dh_achieved,
+            "peak": PEAK_MFMA_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": dh_achieved / PEAK_MFMA_F16_TFLOPS,
+            "traffic": None,
+            "per_launch_flop": dh_flop,
+            "avg_launch_ms": phase_ms["dh"],
+        },
+    }
+    if args.calibrate_copy:
+        _calibration_copy(torch, dev)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_backward(inp, dS_host, dH.cpu().numpy(), args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +293,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", choices=["auto", "one", "two"], default="auto",
                     help="kernel path: the library's choice, the one-pass or the two-pass kernels")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (gradients through the sketches) instead")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device once (counter calibration)")
     args = ap.parse_args(argv)
@@ -165,6 +314,8 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = make_config(args.workload)
+    if args.backward:
+        return bench_backward(args, inp, torch, dev, sa)
     H, off, Wk, Wv, P, mask = _upload(inp, torch, dev)
     R, N, d, k = inp.R, inp.N, inp.d, inp.k
     n_valid = inp.valid_tokens()
@@ -244,12 +395,7 @@ def main(argv=None):
         "roofline": roofline,
     }
     if args.calibrate_copy:
-        src = torch.ones(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        _calibration_copy(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, S.cpu().numpy(), args.cpu_budget)
     print(json.dumps(out), flush=True)
