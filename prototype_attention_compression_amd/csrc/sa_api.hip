@@ -128,7 +128,7 @@ Layout make_layout(const sa_problem& p, bool bwd = false) {
     L.off_bzs = take((size_t)p.num_users * sizeof(float));
     L.off_bbmax = take((size_t)p.num_users * sizeof(uint32_t));
     L.off_bdelta = take((size_t)tiles_max * kTile * sizeof(float));
-    L.off_bepart = take((size_t)L.e_groups * p.k * p.d * sizeof(float));
+    L.off_bepart = take(((size_t)L.e_groups + p.num_users) * p.k * p.d * sizeof(float));
     L.off_betot = take((size_t)p.k * p.d * sizeof(float));
     L.off_bopart = take((size_t)L.o_chunks * p.d * p.d * sizeof(float));
   }

@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256) void bwd_zpack(Layout L, void* ws) {
 // dh = sum_j (sA[j, t] Zs_j + sdL[j, t] ln2 q_j); its B operands are the
 // staged rows through the transposing read.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dh(const int64_t* __restrict__ offsets,
+__global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ offsets,
                                               const int32_t* __restrict__ tile_base, Layout L, void* ws,
                                               float* __restrict__ dH) {
   constexpr int S = D / 16, DT = D / 32, PITCH = tile_pitch<D>(), BLK = kTile * PITCH, CPR = D / 8;
@@ -292,85 +292,111 @@ __global__ __launch_bounds__(256) void bwd_dh(const int64_t* __restrict__ offset
   const int i16 = lane & 15, gh = (lane >> 4) & 1;
   const int tr_base = (4 * (i16 >> 2) + 2 * g) * PITCH + 32 * gh + 8 * (i16 & 3);
 
-  float dsum = 0.f, bmx = 0.f, delta = 0.f, sg = kScaleMax, sl = kScaleMax * kLn2;
+  float dsum = 0.f, bmx = 0.f;
   float16v dHc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dHc[dt] = float16v{};
 
+  // C = q . h and Y = Zs . h of the staged block (A operands read in halves)
+  auto gemms = [&](const char* qb, float16v& Lc, float16v& Yc) {
+    Lc = float16v{};
+    Yc = float16v{};
+#pragma unroll
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      half8 a[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) a[s] = *reinterpret_cast<const half8*>(qb + abase + 32 * (s0 + s));
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Lc = mfma32x32x16(a[s], hB[s0 + s], Lc);
+    }
+#pragma unroll
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      half8 a[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) a[s] = *reinterpret_cast<const half8*>(qb + BLK + abase + 32 * (s0 + s));
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Yc = mfma32x32x16(a[s], hB[s0 + s], Yc);
+    }
+  };
+
   gload(0);
   swrite(0);
   __syncthreads();
-  for (int i = 0; i < 2 * NB; ++i) {
+  // sweep 1: delta_t and the bound b_t
+  for (int i = 0; i < NB; ++i) {
     const int buf = i & 1;
-    if (i + 1 < 2 * NB) gload(i + 1);
+    gload(i + 1);   // i + 1 <= NB < 2 NB: the first block of sweep 2 at the end
     const char* qb = lds[buf];
-    const char* zb = qb + BLK;
-    half8 a[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) a[s] = *reinterpret_cast<const half8*>(qb + abase + 32 * s);
-    float16v Lc = float16v{};
-#pragma unroll
-    for (int s = 0; s < S; ++s) Lc = mfma32x32x16(a[s], hB[s], Lc);
-#pragma unroll
-    for (int s = 0; s < S; ++s) a[s] = *reinterpret_cast<const half8*>(zb + abase + 32 * s);
-    float16v Yc = float16v{};
-#pragma unroll
-    for (int s = 0; s < S; ++s) Yc = mfma32x32x16(a[s], hB[s], Yc);
+    float16v Lc, Yc;
+    gemms(qb, Lc, Yc);
     const float4* cp = reinterpret_cast<const float4*>(qb + 2 * BLK) + 4 * g;
-    float cr[16];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const float4 c4 = cp[v];
-      cr[4 * v] = c4.x;
-      cr[4 * v + 1] = c4.y;
-      cr[4 * v + 2] = c4.z;
-      cr[4 * v + 3] = c4.w;
-    }
-    if (i < NB) {
+      const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float A = __builtin_amdgcn_exp2f(Lc[r] + negl);
-        const float yc = Yc[r] - cr[r];
+      for (int e = 0; e < 4; ++e) {
+        const float A = __builtin_amdgcn_exp2f(Lc[4 * v + e] + negl);
+        const float yc = Yc[4 * v + e] - cv[e];
         dsum = fmaf(A, yc, dsum);
         bmx = fmaxf(bmx, fabsf(yc));
       }
-      if (i == NB - 1) {
-        dsum += __shfl_xor(dsum, 32);
-        bmx = fmaxf(bmx, __shfl_xor(bmx, 32));
-        if (!keep) bmx = 0.f;
-        delta = dsum;
-        sg = operand_scale(bmx);
-        sl = sg * kLn2;
-        if (g == 0) {
-          sinv[wave][col] = 1.0f / (sg * zs);
-          ws_f32(ws, L.off_bdelta)[(int64_t)tile * kTile + col] = delta;
-        }
-        float wm = bmx;
+    }
+    swrite(buf ^ 1);
+    __syncthreads();
+  }
+  dsum += __shfl_xor(dsum, 32);
+  bmx = fmaxf(bmx, __shfl_xor(bmx, 32));
+  if (!keep) bmx = 0.f;
+  const float delta = dsum;
+  const float sg = operand_scale(bmx);
+  const float sl = sg * kLn2;
+  if (g == 0) {
+    sinv[wave][col] = 1.0f / (sg * zs);
+    ws_f32(ws, L.off_bdelta)[(int64_t)tile * kTile + col] = delta;
+  }
+  {
+    float wm = bmx;
 #pragma unroll
-        for (int o = 16; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o));
-        if (lane == 0 && wm > 0.f)
-          atomicMax(reinterpret_cast<unsigned int*>(ws_i32(ws, L.off_bbmax)) + u, __float_as_uint(wm));
-      }
-    } else {
-      half8 al[2], ad[2];
+    for (int o = 16; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o));
+    if (lane == 0 && wm > 0.f)
+      atomicMax(reinterpret_cast<unsigned int*>(ws_i32(ws, L.off_bbmax)) + u, __float_as_uint(wm));
+  }
+  // sweep 2: dh += (sl dL)^T q + (sg A)^T Zs
+  for (int i = NB; i < 2 * NB; ++i) {
+    const int buf = i & 1;
+    if (i + 1 < 2 * NB) gload(i + 1);
+    const char* qb = lds[buf];
+    float16v Lc, Yc;
+    gemms(qb, Lc, Yc);
+    const float4* cp = reinterpret_cast<const float4*>(qb + 2 * BLK) + 4 * g;
+    half8 al[2], ad[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+    for (int v = 0; v < 4; ++v) {
+      const float4 c4 = cp[v];
+      const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * v + e;
         const float A = __builtin_amdgcn_exp2f(Lc[r] + negl);
-        const float dl = A * (Yc[r] - cr[r] - delta);
+        const float dl = A * (Yc[r] - cv[e] - delta);
         al[r >> 3][r & 7] = (_Float16)(dl * sl);
         ad[r >> 3][r & 7] = (_Float16)(A * sg);
       }
-      half8 hb[2][DT];
-      tile_tr_reads<D>(lds_addr(qb) + tr_base, hb);
+    }
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < 2; ++kk) {
+      half8 hb[DT];
+      tile_tr_reads_kk<D>(lds_addr(qb) + tr_base + kk * 16 * PITCH, hb);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) dHc[dt] = mfma32x32x16(al[kk], hb[kk][dt], dHc[dt]);
-      tile_tr_reads<D>(lds_addr(zb) + tr_base, hb);
+      for (int dt = 0; dt < DT; ++dt) dHc[dt] = mfma32x32x16(al[kk], hb[dt], dHc[dt]);
+    }
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < 2; ++kk) {
+      half8 hb[DT];
+      tile_tr_reads_kk<D>(lds_addr(qb + BLK) + tr_base + kk * 16 * PITCH, hb);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) dHc[dt] = mfma32x32x16(ad[kk], hb[kk][dt], dHc[dt]);
+      for (int dt = 0; dt < DT; ++dt) dHc[dt] = mfma32x32x16(ad[kk], hb[dt], dHc[dt]);
     }
     if (i + 1 < 2 * NB) swrite(buf ^ 1);
     __syncthreads();
@@ -390,14 +416,15 @@ __global__ __launch_bounds__(256) void bwd_dh(const int64_t* __restrict__ offset
 
 // ---------------------------------------------------------------- E
 // Prototype-major like pass 2: W waves of 32 prototypes; groups of
-// e_pblocks workgroups walk equal tile ranges; per tile
+// e_pblocks workgroups walk equal tile ranges cut at user boundaries; per
+// tile
 //   C[t, j] = h_t . q_j, Y[t, j] = h_t . Zs_j (token rows from LDS as the A
 //   operand, queries and Z rows resident as B operands),
 //   sdL = s_u A (Y - cs_j - delta_t) in fp16, E += sdL h (transposing reads).
-// E is rescaled to true units at every user boundary and written once per
-// workgroup to partial slot `group`.
+// A segment's E, rescaled to true units, goes to partial slot group + user
+// (unique among the groups whose ranges meet that user, as in pass 2).
 template <int D, int W>
-__global__ __launch_bounds__(W * 64) void bwd_e(const int32_t* __restrict__ tile_base, Layout L, void* ws) {
+__global__ __launch_bounds__(W * 64, 2) void bwd_e(const int32_t* __restrict__ tile_base, Layout L, void* ws) {
   constexpr int S = D / 16, DT = D / 32, PITCH = tile_pitch<D>(), TB = kTile * PITCH, CPR = D / 8;
   constexpr int NT = W * 64;
   constexpr int LPT = kTile * CPR / NT;
@@ -409,137 +436,130 @@ __global__ __launch_bounds__(W * 64) void bwd_e(const int32_t* __restrict__ tile
   const int group = xcd + 8 * (slotw / P);
   const int pb = slotw % P;
   if (group >= G) return;
+  const int32_t T = ws_i32(ws, L.off_hdr)[kHdrTiles];
+  const int32_t Tg = (T + 4 * G - 1) / (4 * G) * 4;
+  const int32_t s0 = group * Tg, s1 = min(T, s0 + Tg);
+  if (s0 >= s1) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, g = lane >> 5;
   const int p0 = pb * (W * kTile) + wave * kTile;
-  float* epart = ws_f32(ws, L.off_bepart) + ((int64_t)group * L.k + p0) * D;
 
-  const int32_t T = ws_i32(ws, L.off_hdr)[kHdrTiles];
-  const int32_t Tg = (T + 4 * G - 1) / (4 * G) * 4;
-  const int32_t s0 = group * Tg, s1 = min(T, s0 + Tg);
-  float16v Er[DT];
+  const _Float16* q16 = ws_f16(ws, L.off_q16);
+  half8 qf[S], zf[S];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) Er[dt] = float16v{};
-  if (s0 < s1) {
-    const _Float16* q16 = ws_f16(ws, L.off_q16);
-    half8 qf[S], zf[S];
+  for (int s = 0; s < S; ++s) qf[s] = *reinterpret_cast<const half8*>(q16 + (int64_t)(p0 + col) * D + 16 * s + 8 * g);
+  const _Float16* h16 = ws_f16(ws, L.off_h16);
+  const uint32_t* nlw = reinterpret_cast<const uint32_t*>(ws_i32(ws, L.off_nl));
+  const float* dlt = ws_f32(ws, L.off_bdelta);
+  uint4 pr[LPT];
+  uint32_t pn = 0;
+  float pd = 0.f;
+  auto gload = [&](int32_t t) {
+    const _Float16* src = h16 + (int64_t)t * kTile * D;
 #pragma unroll
-    for (int s = 0; s < S; ++s)
-      qf[s] = *reinterpret_cast<const half8*>(q16 + (int64_t)(p0 + col) * D + 16 * s + 8 * g);
-    const _Float16* h16 = ws_f16(ws, L.off_h16);
-    const uint32_t* nlw = reinterpret_cast<const uint32_t*>(ws_i32(ws, L.off_nl));
-    const float* dlt = ws_f32(ws, L.off_bdelta);
-    uint4 pr[LPT];
-    uint32_t pn = 0;
-    float pd = 0.f;
-    auto gload = [&](int32_t t) {
-      const _Float16* src = h16 + (int64_t)t * kTile * D;
+    for (int k2 = 0; k2 < LPT; ++k2) {
+      const int idx = tid + NT * k2, row = idx / CPR, ch = idx % CPR;
+      pr[k2] = *reinterpret_cast<const uint4*>(src + row * D + 8 * ch);
+    }
+    if (tid < kTile) {
+      pn = nlw[(int64_t)t * kTile + tid];
+      pd = dlt[(int64_t)t * kTile + tid];
+    }
+  };
+  auto swrite = [&](int buf) {
+    char* base = lds[buf];
 #pragma unroll
-      for (int k2 = 0; k2 < LPT; ++k2) {
-        const int idx = tid + NT * k2, row = idx / CPR, ch = idx % CPR;
-        pr[k2] = *reinterpret_cast<const uint4*>(src + row * D + 8 * ch);
-      }
-      if (tid < kTile) {
-        pn = nlw[(int64_t)t * kTile + tid];
-        pd = dlt[(int64_t)t * kTile + tid];
-      }
-    };
-    auto swrite = [&](int buf) {
-      char* base = lds[buf];
-#pragma unroll
-      for (int k2 = 0; k2 < LPT; ++k2) {
-        const int idx = tid + NT * k2, row = idx / CPR, ch = idx % CPR;
-        *reinterpret_cast<uint4*>(base + row * PITCH + 16 * ch) = pr[k2];
-      }
-      if (tid < kTile) {
-        float* pv = reinterpret_cast<float*>(base + TB);
-        pv[acc_pos(tid)] = negl_of(pn);
-        pv[kTile + acc_pos(tid)] = pd;
-      }
-    };
-    const int abase = tau(col) * PITCH + 16 * g;
-    const int i16 = lane & 15, gh = (lane >> 4) & 1;
-    const int tr_base = (4 * (i16 >> 2) + 2 * g) * PITCH + 32 * gh + 8 * (i16 & 3);
+    for (int k2 = 0; k2 < LPT; ++k2) {
+      const int idx = tid + NT * k2, row = idx / CPR, ch = idx % CPR;
+      *reinterpret_cast<uint4*>(base + row * PITCH + 16 * ch) = pr[k2];
+    }
+    if (tid < kTile) {
+      float* pv = reinterpret_cast<float*>(base + TB);
+      pv[acc_pos(tid)] = negl_of(pn);
+      pv[kTile + acc_pos(tid)] = pd;
+    }
+  };
+  const int abase = tau(col) * PITCH + 16 * g;
+  const int i16 = lane & 15, gh = (lane >> 4) & 1;
+  const int tr_base = (4 * (i16 >> 2) + 2 * g) * PITCH + 32 * gh + 8 * (i16 & 3);
 
-    int u = find_user(tile_base, L.R, s0);
-    int32_t ub = tile_base[u + 1];
-    float cz = 0.f, su = kScaleMax, back = 1.f;
-    auto load_user = [&]() {
-      const _Float16* z16 = ws_f16(ws, L.off_bz16) + ((int64_t)u * L.k + p0 + col) * D;
+  int u = find_user(tile_base, L.R, s0);
+  int32_t ub = tile_base[u + 1];
+  float cz = 0.f, su = kScaleMax, back = 1.f;
+  auto load_user = [&]() {
+    const _Float16* z16 = ws_f16(ws, L.off_bz16) + ((int64_t)u * L.k + p0 + col) * D;
 #pragma unroll
-      for (int s = 0; s < S; ++s) zf[s] = *reinterpret_cast<const half8*>(z16 + 16 * s + 8 * g);
-      cz = ws_f32(ws, L.off_bcz)[(int64_t)u * L.k + p0 + col];
-      const float bm = __uint_as_float(reinterpret_cast<const uint32_t*>(ws_i32(ws, L.off_bbmax))[u]);
-      su = operand_scale(bm);
-      back = 1.0f / (su * ws_f32(ws, L.off_bzs)[u]);
-    };
-    load_user();
-    float16v Ea[DT];
+    for (int s = 0; s < S; ++s) zf[s] = *reinterpret_cast<const half8*>(z16 + 16 * s + 8 * g);
+    cz = ws_f32(ws, L.off_bcz)[(int64_t)u * L.k + p0 + col];
+    const float bm = __uint_as_float(reinterpret_cast<const uint32_t*>(ws_i32(ws, L.off_bbmax))[u]);
+    su = operand_scale(bm);
+    back = 1.0f / (su * ws_f32(ws, L.off_bzs)[u]);
+  };
+  float16v Ea[DT];
+  auto flush = [&]() {   // the segment of user u: true units to slot group + u
+    float* dst = ws_f32(ws, L.off_bepart) + ((int64_t)(group + u) * L.k + p0) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) Ea[dt] = float16v{};
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dst[(int64_t)acc_row(r, g) * D + 32 * dt + col] = Ea[dt][r] * back;
+  };
+  load_user();
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) Ea[dt] = float16v{};
 
-    gload(s0);
-    swrite(0);
-    __syncthreads();
-    for (int32_t t = s0; t < s1; ++t) {
-      const int buf = (t - s0) & 1;
-      if (t + 1 < s1) gload(t + 1);
-      if (t == ub) {   // uniform: the next user's tiles start here
+  gload(s0);
+  swrite(0);
+  __syncthreads();
+  for (int32_t t = s0; t < s1; ++t) {
+    const int buf = (t - s0) & 1;
+    if (t + 1 < s1) gload(t + 1);
+    if (t == ub) {   // uniform: the next user's tiles start here
+      flush();
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          Er[dt] += Ea[dt] * back;
-          Ea[dt] = float16v{};
-        }
-        while (tile_base[u + 1] <= t) ++u;
-        ub = tile_base[u + 1];
-        load_user();
+      for (int dt = 0; dt < DT; ++dt) Ea[dt] = float16v{};
+      while (tile_base[u + 1] <= t) ++u;
+      ub = tile_base[u + 1];
+      load_user();
+    }
+    const char* hb_ = lds[buf];
+    float16v Lc = float16v{}, Yc = float16v{};
+#pragma unroll
+    for (int s0h = 0; s0h < S; s0h += 4) {
+      half8 ha[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ha[s] = *reinterpret_cast<const half8*>(hb_ + abase + 32 * (s0h + s));
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        Lc = mfma32x32x16(ha[s], qf[s0h + s], Lc);
+        Yc = mfma32x32x16(ha[s], zf[s0h + s], Yc);
       }
-      const char* hb_ = lds[buf];
-      half8 ha[S];
+    }
+    const float4* pv = reinterpret_cast<const float4*>(hb_ + TB);
+    half8 al[2];
 #pragma unroll
-      for (int s = 0; s < S; ++s) ha[s] = *reinterpret_cast<const half8*>(hb_ + abase + 32 * s);
-      float16v Lc = float16v{}, Yc = float16v{};
+    for (int v = 0; v < 4; ++v) {
+      const float4 a4 = pv[4 * g + v], d4 = pv[8 + 4 * g + v];
+      const float nl[4] = {a4.x, a4.y, a4.z, a4.w};
+      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-      for (int s = 0; s < S; ++s) Lc = mfma32x32x16(ha[s], qf[s], Lc);
-#pragma unroll
-      for (int s = 0; s < S; ++s) Yc = mfma32x32x16(ha[s], zf[s], Yc);
-      const float4* pv = reinterpret_cast<const float4*>(hb_ + TB);
-      float nl[16], dd[16];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float4 a4 = pv[4 * g + v], d4 = pv[8 + 4 * g + v];
-        nl[4 * v] = a4.x;
-        nl[4 * v + 1] = a4.y;
-        nl[4 * v + 2] = a4.z;
-        nl[4 * v + 3] = a4.w;
-        dd[4 * v] = d4.x;
-        dd[4 * v + 1] = d4.y;
-        dd[4 * v + 2] = d4.z;
-        dd[4 * v + 3] = d4.w;
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * v + e;
+        const float A = __builtin_amdgcn_exp2f(Lc[r] + nl[e]);
+        al[r >> 3][r & 7] = (_Float16)(A * (Yc[r] - cz - dd[e]) * su);
       }
-      half8 al[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float A = __builtin_amdgcn_exp2f(Lc[r] + nl[r]);
-        al[r >> 3][r & 7] = (_Float16)(A * (Yc[r] - cz - dd[r]) * su);
-      }
-      half8 hbv[2][DT];
-      tile_tr_reads<D>(lds_addr(hb_) + tr_base, hbv);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) Ea[dt] = mfma32x32x16(al[kk], hbv[kk][dt], Ea[dt]);
-      if (t + 1 < s1) swrite(buf ^ 1);
-      __syncthreads();
     }
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) Er[dt] += Ea[dt] * back;
+    for (int kk = 0; kk < 2; ++kk) {
+      half8 hbv[DT];
+      tile_tr_reads_kk<D>(lds_addr(hb_) + tr_base + kk * 16 * PITCH, hbv);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) Ea[dt] = mfma32x32x16(al[kk], hbv[dt], Ea[dt]);
+    }
+    if (t + 1 < s1) swrite(buf ^ 1);
+    __syncthreads();
   }
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) epart[(int64_t)acc_row(r, g) * D + 32 * dt + col] = Er[dt][r];
+  flush();
 }
 
 // ---------------------------------------------------------------- reductions
@@ -556,10 +576,21 @@ __global__ __launch_bounds__(256) void bwd_ereduce(const uint16_t* __restrict__ 
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  for (int gi = 0; gi < L.e_groups; ++gi) {
-    const float* base = ep + ((int64_t)gi * L.k + j0) * D;
+  // the slots bwd_e wrote: group + u for every group whose tile range meets
+  // user u's tiles (users in order, then groups in order)
+  const int32_t* tile_base = ws_i32(ws, L.off_tile_base);
+  const int32_t T = ws_i32(ws, L.off_hdr)[kHdrTiles];
+  const int G = L.e_groups;
+  const int32_t Tg = (T + 4 * G - 1) / (4 * G) * 4;
+  for (int u = 0; u < L.R; ++u) {
+    const int32_t t0 = tile_base[u], t1 = tile_base[u + 1];
+    if (t1 <= t0) continue;
+    const int c1 = (t1 - 1) / Tg + 1 + u;
+    for (int c = t0 / Tg + u; c < c1; ++c) {
+      const float* base = ep + ((int64_t)c * L.k + j0) * D;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
+      for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
+    }
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {

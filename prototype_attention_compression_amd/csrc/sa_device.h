@@ -129,6 +129,51 @@ __device__ __forceinline__ void tile_tr_reads(uint32_t addr, half8 (&hb)[2][D / 
   }
 }
 
+// Half of tile_tr_reads: the B operands of one contraction step kk, read
+// at `addr` = the tile's LDS address + the lane's offset + 16 kk rows
+// (hb[dt] = hb[kk][dt] of tile_tr_reads).  Same wait-inside-the-asm rule.
+template <int D>
+__device__ __forceinline__ void tile_tr_reads_kk(uint32_t addr, half8 (&hb)[D / 32]) {
+  static_assert(D == 128 || D == 64, "d = 64 or 128");
+  if constexpr (D == 128) {
+    s16x4 r0, r1, r2, r3, r4, r5, r6, r7;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:272\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:336\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:128\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:400\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:192\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:464\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+        : "v"(addr));
+    const s16x4 r[8] = {r0, r1, r2, r3, r4, r5, r6, r7};
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const s16x4 lo = r[2 * dt], hi = r[2 * dt + 1];
+      hb[dt] = __builtin_bit_cast(half8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    }
+  } else {
+    s16x4 r0, r1, r2, r3;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:144\n\t"
+        "ds_read_b64_tr_b16 %2, %4 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %4 offset:208\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(addr));
+    const s16x4 r[4] = {r0, r1, r2, r3};
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      const s16x4 lo = r[2 * dt], hi = r[2 * dt + 1];
+      hb[dt] = __builtin_bit_cast(half8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    }
+  }
+}
+
 // Exact widening of 8 packed bf16 values (one 16-byte load) to fp16.  bf16
 // values whose magnitude lies in [2^-17, 65504] are exactly representable in
 // fp16; the conversion truncates toward zero so larger values saturate.

@@ -92,7 +92,7 @@ struct Layout {
   size_t off_bzs;          // [R] float         zs_u, a power of two
   size_t off_bbmax;        // [R] uint32        bits of the user's largest |Y - c| (scaled, >= 0)
   size_t off_bdelta;       // [tiles_max, 32] float  delta_t zs_u
-  size_t off_bepart;       // [e_groups, k, d] float partial E
+  size_t off_bepart;       // [e_groups + R, k, d] float partial E per (group, user) at group + user
   size_t off_betot;        // [k, d] float      E = sum_t dL[., t] h_t
   size_t off_bopart;       // [o_chunks, d, d] float partial outer products
   size_t total;
