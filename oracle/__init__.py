@@ -11,3 +11,4 @@ from .sa_oracle import (  # noqa: F401
     sketch_one,
 )
 from .sa_oracle_grad import sketch_batch_grad, sketch_one_grad  # noqa: F401,E402
+from .sa_oracle_target import target_attention_batch, target_attention_one  # noqa: F401,E402
