@@ -17,6 +17,9 @@ dense MFMA peak.  The CPU baseline times the fp64 oracle on a bounded sample
 of the same workload on the host cores and checks the GPU sketches of that
 sample against it.
 
+``--target-attention`` times sa_target_attention (300 users x 300
+candidates over 1K x 128 sketches) with an HBM roofline.
+
 ``--backward`` times one sa_compress_backward call per step instead (the
 gradients dH, dP, dWk, dWv for a seeded dS, forward recomputation included)
 on the same workload; its roofline object reports the token-major dH kernel
@@ -283,6 +286,96 @@ def bench_backward(args, inp, torch, dev, sa):
     return 0
 
 
+TA_USERS, TA_CANDIDATES = 300, 300   # serving: ~300 candidates per request against one sketch
+
+
+def bench_target(args, torch, dev, sa):
+    """Times sa_target_attention: 300 users x 300 candidates over 1K x 128
+    sketches (the serving reuse operating point), inputs resident in HBM."""
+    from synth import make_candidates, make_sketches
+
+    R, C_u, k, d = TA_USERS, TA_CANDIDATES, 1024, 128
+    Qf, Qbits, off_h = make_candidates([C_u] * R, d, seed=11)
+    S_h = make_sketches(R, k, d, seed=12)
+    C = int(off_h[-1])
+    Q = torch.from_numpy(Qbits.view(np.int16)).view(torch.bfloat16).to(dev)
+    off = torch.from_numpy(off_h).to(dev)
+    S = torch.from_numpy(S_h).to(dev)
+    out_t = torch.empty((C, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(sa.target_attention_workspace_size(R, C, d, k), dtype=torch.uint8, device=dev)
+
+    def step():
+        sa.target_attention(Q, off, S, out=out_t, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(stop) / args.steps
+    flop = 4.0 * C * k * d                       # logits and the weighted sum, once each
+    nbytes = 4.0 * R * k * d + 2.0 * C * d + 4.0 * C * d   # sketches once per user, queries, outputs
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    out = {
+        "metric": "candidates/s (sketch-branch target attention), 1K x 128 sketches",
+        "value": C / (ms_step * 1e-3),
+        "unit": "candidates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"target_r{R}_c{C_u}_d{d}_k{k}", "users": R, "candidates": C, "k": k, "d": d,
+                   "parallelism": "single_gpu", "op": "target_attention"},
+        "tflops": flop / (ms_step * 1e-3) / 1e12,
+        "wall_s_timed": t_wall,
+        "roofline": {
+            "kernel": "ta_attend",
+            "bound": "hbm",
+            "achieved": gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS,
+            "traffic": None,
+            "per_launch_bytes": nbytes,
+            "avg_launch_ms": ms_step,
+        },
+    }
+    if args.calibrate_copy:
+        _calibration_copy(torch, dev)
+    if not args.no_cpu_baseline:
+        import threadpoolctl
+
+        from oracle import target_attention_one
+        cores = len(os.sched_getaffinity(0))
+        with threadpoolctl.threadpool_limits(cores):
+            threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+            n_c, t_total, u = 0, 0.0, 0
+            while u < R and t_total < args.cpu_budget:
+                lo, hi = int(off_h[u]), int(off_h[u + 1])
+                t0 = time.perf_counter()
+                target_attention_one(Qf[lo:hi], S_h[u])
+                t_total += time.perf_counter() - t0
+                n_c += hi - lo
+                u += 1
+        out["cpu_baseline"] = {"value": n_c / t_total, "unit": "candidates/s", "cores": threads, "kind": "oracle",
+                               "sample": f"users 0..{u - 1} ({u} of {R}, {n_c} candidates), numpy fp64, "
+                                         f"{t_total:.1f} s"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,6 +386,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", choices=["auto", "one", "two"], default="auto",
                     help="kernel path: the library's choice, the one-pass or the two-pass kernels")
+    ap.add_argument("--target-attention", action="store_true",
+                    help="time sketch-branch target attention (300 users x 300 candidates) instead")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (gradients through the sketches) instead")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -313,6 +408,8 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.target_attention:
+        return bench_target(args, torch, dev, sa)
     inp = make_config(args.workload)
     if args.backward:
         return bench_backward(args, inp, torch, dev, sa)

@@ -248,6 +248,50 @@ sa_status sa_compress_backward_with_events(const sa_problem* problem,
                                            void* stream,
                                            void* const* events);
 
+/*
+ * Sketch-branch target attention with user-level batching.
+ *
+ * After compression each candidate item attends over its user's cached
+ * sketch (blog "100,000 videos in your pocket", "How it works" item 2: the
+ * sketch branch of STCA), and a user's many candidates share one read of the
+ * sketch (same page, item 3: multi-request user-level batching).  The pages
+ * define STCA's stacking only by reference to an earlier paper; this is the
+ * single-layer reading, single-head scaled dot-product attention whose keys
+ * and values are the k sketch rows s_j of the candidate's user:
+ *     out_c = sum_j softmax_j(q_c . s_j / sqrt(d)) s_j
+ * Projections of the candidate or the sketch, further layers and the fusion
+ * with the recent-history branch are the caller's.
+ *
+ *   problem       num_users R, total_tokens = C (the total candidate count),
+ *                 d and k as for sa_compress; dtype SA_BF16 (the candidate
+ *                 queries); flags 0.
+ *   Q             [C, d] bf16 candidate queries, user by user, 16-byte aligned.
+ *   cand_offsets  [R+1] int64 device: user u owns candidates
+ *                 cand_offsets[u] .. cand_offsets[u+1]-1 (same contract and
+ *                 device error flag as sa_compress's offsets; on a violation
+ *                 out and lse are zero).
+ *   S             [R, k, d] float32 sketches (sa_compress's output layout),
+ *                 16-byte aligned; entries must be below 65504 in magnitude
+ *                 (fp16 MFMA operands).
+ *   out           [C, d] float32, fully overwritten.
+ *   lse           [C] float32 natural-log normaliser log sum_j exp(q . s_j /
+ *                 sqrt(d)), or NULL.
+ *   workspace     sa_target_attention_workspace_size bytes, 256-byte aligned.
+ * Candidate queries are widened exactly to fp16, sketch rows rounded to fp16,
+ * sums in fp32.  Asynchronous on `stream`; R = 0 is a no-op.
+ */
+sa_status sa_target_attention_workspace_size(const sa_problem* problem, size_t* bytes);
+
+sa_status sa_target_attention(const sa_problem* problem,
+                              const void* Q,
+                              const int64_t* cand_offsets,
+                              const float* S,
+                              float* out,
+                              float* lse,
+                              void* workspace,
+                              size_t workspace_bytes,
+                              void* stream);
+
 /* Device error flag bits. */
 #define SA_DEVICE_ERR_OFFSETS 1   /* offsets broke their contract: all users empty */
 #define SA_DEVICE_ERR_EXCHANGE 2  /* one-pass: a bounded wait between workgroups

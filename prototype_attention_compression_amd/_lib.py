@@ -21,6 +21,7 @@ _PATH_FLAGS = {None: 0, "auto": 0, "two": SA_FLAG_TWO_PASS, "one": SA_FLAG_ONE_P
 # functions declared in include/sa.h
 EXPORTS = ("sa_workspace_size", "sa_compress", "sa_compress_with_events",
            "sa_backward_workspace_size", "sa_compress_backward", "sa_compress_backward_with_events",
+           "sa_target_attention_workspace_size", "sa_target_attention",
            "sa_read_device_error", "sa_status_string", "sa_version")
 NUM_PHASE_EVENTS = 5
 NUM_BWD_PHASE_EVENTS = 6
@@ -79,6 +80,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sa_compress_backward_with_events.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                      vp]
     lib.sa_compress_backward_with_events.restype = ctypes.c_int
+    lib.sa_target_attention_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
+    lib.sa_target_attention_workspace_size.restype = ctypes.c_int
+    lib.sa_target_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sa_target_attention.restype = ctypes.c_int
     lib.sa_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
     lib.sa_read_device_error.restype = ctypes.c_int
     lib.sa_status_string.argtypes = [ctypes.c_int]
@@ -275,3 +280,60 @@ def compress_backward(H, offsets, Wk, Wv, P, dS, mask=None, workspace=None, even
     if st != SA_OK:
         raise SaError(st, "sa_compress_backward")
     return dH, dP, dWk, dWv
+
+
+def target_attention_workspace_size(num_users: int, total_candidates: int, d: int, k: int) -> int:
+    """Bytes of device workspace sa_target_attention needs (pure host call)."""
+    pb = problem(num_users, total_candidates, d, k, SA_BF16)
+    out = ctypes.c_size_t(0)
+    st = load().sa_target_attention_workspace_size(ctypes.byref(pb), ctypes.byref(out))
+    if st != SA_OK:
+        raise SaError(st, "sa_target_attention_workspace_size")
+    return int(out.value)
+
+
+def raw_target_attention(pb: SaProblem, Q, cand_offsets, S, out, lse, workspace, workspace_bytes: int,
+                         stream) -> int:
+    """Direct call of sa_target_attention; returns the status."""
+    return int(load().sa_target_attention(ctypes.byref(pb), Q, cand_offsets, S, out, lse, workspace,
+                                          ctypes.c_size_t(workspace_bytes), stream))
+
+
+def target_attention(Q, cand_offsets, S, return_lse: bool = False, out=None, workspace=None):
+    """Sketch-branch target attention, computed by libsa on the GPU.
+
+    Q [C, d] bfloat16 candidate queries packed user by user, cand_offsets
+    [R+1] int64, S [R, k, d] float32 sketches (as ``compress`` returns).
+    Returns out [C, d] float32 (and the natural-log normalisers [C] if
+    ``return_lse``).  Runs on torch's current stream.
+    """
+    import torch
+
+    if Q.dtype != torch.bfloat16 or S.dtype != torch.float32:
+        raise ValueError("Q must be bfloat16 and S float32")
+    for name, t in (("Q", Q), ("cand_offsets", cand_offsets), ("S", S)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if cand_offsets.dtype != torch.int64 or cand_offsets.dim() != 1 or Q.dim() != 2 or S.dim() != 3:
+        raise ValueError("need Q [C, d], cand_offsets [R+1] int64, S [R, k, d]")
+    C, d = Q.shape
+    R = cand_offsets.shape[0] - 1
+    if S.shape[0] != R or S.shape[2] != d:
+        raise ValueError("S must be [R, k, d] with the candidates' d and one sketch per user")
+    k = S.shape[1]
+    dev = Q.device
+    pb = problem(R, C, d, k, SA_BF16)
+    wbytes = target_attention_workspace_size(R, C, d, k)
+    if workspace is None or workspace.numel() * workspace.element_size() < wbytes:
+        workspace = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
+    o = out if out is not None else torch.empty((C, d), dtype=torch.float32, device=dev)
+    if o.shape != (C, d) or o.dtype != torch.float32 or not o.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [C, d] tensor")
+    lse = torch.empty((C,), dtype=torch.float32, device=dev) if return_lse else None
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = raw_target_attention(pb, _ptr(Q) if C > 0 else None, _ptr(cand_offsets), _ptr(S),
+                              _ptr(o) if C > 0 else None, _ptr(lse) if C > 0 else None, _ptr(workspace), wbytes,
+                              stream)
+    if st != SA_OK:
+        raise SaError(st, "sa_target_attention")
+    return (o, lse) if return_lse else o

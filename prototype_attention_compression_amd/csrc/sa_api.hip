@@ -136,6 +136,41 @@ Layout make_layout(const sa_problem& p, bool bwd = false) {
   return L;
 }
 
+// Target attention: the candidate tiles' schedule only (total_tokens =
+// total candidates); dtype f32 makes the schedule kernel skip the query
+// norms, which this call has none of.
+Layout make_layout_target(const sa_problem& p) {
+  Layout L;
+  memset(&L, 0, sizeof(L));
+  L.N = p.total_tokens;
+  L.R = (int32_t)p.num_users;
+  L.d = p.d;
+  L.k = p.k;
+  L.dtype = SA_F32;
+  const int64_t span = (int64_t)kTile * kUserTileAlign;
+  L.tiles_max = (int32_t)((p.total_tokens + (span - 1) * p.num_users) / span * kUserTileAlign);
+  L.tiles_per_chunk = kUserTileAlign;
+  const size_t R1 = (size_t)p.num_users + 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.off_hdr = take(64 * sizeof(int32_t));
+  L.off_tile_base = take(R1 * sizeof(int32_t));
+  L.off_chunk_base = take(R1 * sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+
+sa_status check_problem_target(const sa_problem* p) {
+  sa_status st = check_problem(p);
+  if (st != SA_OK) return st;
+  if (p->dtype != SA_BF16 || p->flags != 0) return SA_E_UNSUPPORTED;
+  return SA_OK;
+}
+
 // Whether the one-pass cooperative grid fits `device`, asked once per device.
 bool device_fits_fused(const Layout& L) {
   constexpr int kMaxDev = 64;
@@ -305,6 +340,35 @@ sa_status sa_compress_backward_with_events(const sa_problem* problem, const void
     if (!mark(4)) return SA_E_HIP;
     if (sa::launch_bwd_params(L, P, Wk, dS, workspace, dP, dWk, dWv, s) != hipSuccess) return SA_E_HIP;
     if (!mark(5)) return SA_E_HIP;
+    return SA_OK;
+  } catch (...) {
+    return SA_E_HIP;
+  }
+}
+
+sa_status sa_target_attention_workspace_size(const sa_problem* problem, size_t* bytes) {
+  if (bytes == nullptr) return SA_E_INVALID;
+  sa_status st = sa::check_problem_target(problem);
+  if (st != SA_OK) return st;
+  *bytes = sa::make_layout_target(*problem).total;
+  return SA_OK;
+}
+
+sa_status sa_target_attention(const sa_problem* problem, const void* Q, const int64_t* cand_offsets, const float* S,
+                              float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    sa_status st = sa::check_problem_target(problem);
+    if (st != SA_OK) return st;
+    const sa_problem& p = *problem;
+    if (p.num_users == 0) return SA_OK;
+    if (cand_offsets == nullptr || S == nullptr) return SA_E_INVALID;
+    if (p.total_tokens > 0 && (Q == nullptr || out == nullptr)) return SA_E_INVALID;
+    if (reinterpret_cast<uintptr_t>(S) % 16 != 0 || reinterpret_cast<uintptr_t>(Q) % 16 != 0) return SA_E_INVALID;
+    const sa::Layout L = sa::make_layout_target(p);
+    if (workspace == nullptr || workspace_bytes < L.total) return SA_E_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % sa::kAlign != 0) return SA_E_INVALID;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (sa::launch_target_attention(L, Q, cand_offsets, S, workspace, out, lse, s) != hipSuccess) return SA_E_HIP;
     return SA_OK;
   } catch (...) {
     return SA_E_HIP;

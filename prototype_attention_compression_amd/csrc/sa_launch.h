@@ -45,6 +45,11 @@ hipError_t launch_bwd_e(const Layout& L, void* ws, hipStream_t stream);
 // backward: E, dP, dWk and dWv from the partials
 hipError_t launch_bwd_params(const Layout& L, const void* P, const void* Wk, const float* dS, void* ws, float* dP,
                              float* dWk, float* dWv, hipStream_t stream);
+// the ragged schedule alone (tile prefix sums and the offsets check)
+hipError_t launch_schedule(const Layout& L, const int64_t* offsets, void* ws, hipStream_t stream);
+// sketch-branch target attention (schedule + attention kernel)
+hipError_t launch_target_attention(const Layout& L, const void* Q, const int64_t* cand_offsets, const float* S,
+                                   void* ws, float* out, float* lse, hipStream_t stream);
 // zero fill (used when the batch has no users)
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 

@@ -147,6 +147,11 @@ __global__ __launch_bounds__(256) void clear_words(uint64_t* __restrict__ p, int
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0ull;
 }
 
+hipError_t launch_schedule(const Layout& L, const int64_t* offsets, void* ws, hipStream_t stream) {
+  hipLaunchKernelGGL(prep_schedule, dim3(1), dim3(1024), 0, stream, offsets, L, ws);
+  return hipGetLastError();
+}
+
 hipError_t launch_prep(const Layout& L, const void* P, const void* Wk, const int64_t* offsets, void* ws,
                        hipStream_t stream) {
   const int PR = 256 / L.d;

@@ -9,7 +9,9 @@ from .gen import (  # noqa: F401
     Inputs,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    make_candidates,
     make_config,
     make_inputs,
     make_sketch_grad,
+    make_sketches,
 )

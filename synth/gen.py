@@ -43,7 +43,9 @@ __all__ = [
     "f32_to_bf16_bits",
     "make_config",
     "make_inputs",
+    "make_candidates",
     "make_sketch_grad",
+    "make_sketches",
 ]
 
 
@@ -290,3 +292,27 @@ def make_sketch_grad(R: int, k: int, d: int, seed: int, scale: float = 1.0, user
         keep[list(users)] = True
         G[~keep] = 0.0
     return G
+
+
+def make_candidates(counts, d: int, seed: int):
+    """Seeded candidate queries for sketch-branch target attention.
+
+    ``counts[u]`` candidates for user u, packed user by user.  Entries
+    N(0, 1) drawn in float32 from ``default_rng(SeedSequence(seed))`` in one
+    [C, d] draw, rounded to bfloat16 (RNE).  Returns (Q float32 holding the
+    bf16 values, Q_bits uint16, cand_offsets int64 [R+1]).  The pages give
+    about 300 candidates per request scored against one user's sketch.
+    """
+    counts = np.asarray(list(counts), dtype=np.int64)
+    off = np.zeros(counts.shape[0] + 1, dtype=np.int64)
+    np.cumsum(counts, out=off[1:])
+    g = np.random.default_rng(np.random.SeedSequence(seed))
+    Q32 = g.standard_normal((int(off[-1]), d), dtype=np.float32)
+    bits = f32_to_bf16_bits(Q32)
+    return bf16_bits_to_f32(bits), bits, off
+
+
+def make_sketches(R: int, k: int, d: int, seed: int, scale: float = 1.0) -> np.ndarray:
+    """Seeded stand-in sketches [R, k, d] float32: N(0, 1) times ``scale``."""
+    g = np.random.default_rng(np.random.SeedSequence(seed))
+    return g.standard_normal((R, k, d), dtype=np.float32) * np.float32(scale)

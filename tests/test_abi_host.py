@@ -174,3 +174,28 @@ def test_backward_binding_validates_before_library():
         sa.compress_backward(H, off, H[:0], H[:0], H[:0], torch.zeros(1, 1, 128))
     with pytest.raises(ValueError):
         sa.compress_backward(H.float(), off, H[:0], H[:0], H[:0], torch.zeros(1, 1, 128))
+
+
+# ---------------------------------------------------------------- target attention
+def test_target_attention_argument_errors_before_launch():
+    lib = _lib.load()
+    out = ctypes.c_size_t(0)
+    pb = _lib.problem(3, 900, 128, 1024, sa.SA_BF16)
+    assert lib.sa_target_attention_workspace_size(ctypes.byref(pb), ctypes.byref(out)) == sa.SA_OK
+    need = out.value
+    assert need % 256 == 0 and need > 0
+    for bad in (_lib.problem(3, 900, 128, 1024, sa.SA_F32), _lib.problem(3, 900, 128, 1024, 0, 1),
+                _lib.problem(3, 900, 96, 1024, 0)):
+        assert lib.sa_target_attention_workspace_size(ctypes.byref(bad), ctypes.byref(out)) == sa.SA_E_UNSUPPORTED
+
+    def call(pb, Q=FAKE, off=FAKE, S=FAKE, o=FAKE, lse=None, ws=FAKE, wsb=1 << 40):
+        return _lib.raw_target_attention(pb, Q, off, S, o, lse, ws, wsb, None)
+
+    assert call(pb, off=None) == sa.SA_E_INVALID
+    assert call(pb, S=None) == sa.SA_E_INVALID
+    assert call(pb, Q=None) == sa.SA_E_INVALID
+    assert call(pb, o=None) == sa.SA_E_INVALID
+    assert call(pb, S=FAKE + 4) == sa.SA_E_INVALID          # misaligned sketch
+    assert call(pb, ws=None) == sa.SA_E_WORKSPACE
+    assert call(pb, wsb=need - 1) == sa.SA_E_WORKSPACE
+    assert call(_lib.problem(0, 0, 128, 1024, 0), Q=None, off=None, S=None, o=None, ws=None, wsb=0) == sa.SA_OK
