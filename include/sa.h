@@ -292,6 +292,67 @@ sa_status sa_target_attention(const sa_problem* problem,
                               size_t workspace_bytes,
                               void* stream);
 
+/*
+ * User-keyed sketch cache and its cache-miss driver.
+ *
+ * The sketch is user-only and target-agnostic, so it is cached: a local
+ * cache in training reuses a user's sketch across repeated instances (3 h
+ * lifetime, hit rate about 0.5) and a serving cache across consecutive
+ * requests (1 h, about 0.6); a hit skips storing, moving and processing the
+ * raw history, and computing the misses overlaps other work (blog "100,000
+ * videos in your pocket", "How it works" item 3 and "The numbers"; review
+ * page, "Summary").
+ *
+ * sa_cache_create: a host object over a caller-owned device slab
+ *   slab [capacity, k, d] float32 (16-byte aligned) and optionally
+ *   mass_slab [capacity, k] float32; slot i holds one user's sketch.  An
+ *   entry is fresh while now - t_computed < ttl_seconds.  The object is not
+ *   thread-safe; sa_cache_destroy frees it (not the slab).
+ * sa_cache_lookup (pure host): for requests users[0..n-1] at time `now`,
+ *   in order, writes slots[i] (where request i's sketch is, once the misses
+ *   are filled) and the miss list (miss_users, miss_slots, *n_miss; arrays
+ *   of n entries).  A fresh entry is a hit; the first request of any other
+ *   user is a miss and takes a slot: a free one, else an expired entry, else
+ *   the least recently used entry that no request of this batch uses; later
+ *   requests of the same user in the batch share that slot and count as
+ *   hits.  A stale entry is recomputed in place (counted as a miss and as
+ *   expired).  More distinct users in one batch than slots is SA_E_INVALID
+ *   (and leaves the cache in an unspecified but consistent state).
+ * sa_cache_fill: gathers the miss users' history rows from the caller's
+ *   packed store (H_store [N_store, d] with host store_offsets [R_store+1],
+ *   optional mask_store [N_store]; `store` describes it: num_users =
+ *   R_store, total_tokens = N_store, d, k, dtype) into one ragged batch,
+ *   runs one sa_compress on it and scatters the sketches (and masses) into
+ *   the miss slots.  Stream-ordered on `stream` (typically a side stream:
+ *   the caller makes the consumers wait on an event after it).  At most
+ *   65535 misses per call.  Workspace: sa_cache_fill_workspace_size for the
+ *   largest (miss users, miss tokens) a call will see, 256-byte aligned.
+ */
+typedef struct sa_cache sa_cache;
+
+typedef struct {
+  int64_t hits;
+  int64_t misses;
+  int64_t evictions;   /* entries of other users removed to make room */
+  int64_t expired;     /* misses that recomputed a stale entry in place */
+} sa_cache_stats;
+
+sa_status sa_cache_create(int32_t capacity, int32_t k, int32_t d, double ttl_seconds, float* slab,
+                          float* mass_slab, sa_cache** cache);
+
+sa_status sa_cache_destroy(sa_cache* cache);
+
+sa_status sa_cache_lookup(sa_cache* cache, const int64_t* users, int64_t n, double now, int32_t* slots,
+                          int64_t* miss_users, int32_t* miss_slots, int64_t* n_miss, sa_cache_stats* stats);
+
+sa_status sa_cache_fill_workspace_size(const sa_problem* store, int64_t max_miss_users, int64_t max_miss_tokens,
+                                       size_t* bytes);
+
+sa_status sa_cache_fill(sa_cache* cache, const sa_problem* store, const void* H_store, const int64_t* store_offsets,
+                        const uint8_t* mask_store, const void* Wk, const void* Wv, const void* P,
+                        const int64_t* miss_users, const int32_t* miss_slots, int64_t n_miss, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /* Device error flag bits. */
 #define SA_DEVICE_ERR_OFFSETS 1   /* offsets broke their contract: all users empty */
 #define SA_DEVICE_ERR_EXCHANGE 2  /* one-pass: a bounded wait between workgroups

@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     SA_FLAG_TWO_PASS,
     SA_OK,
     SaError,
+    SketchCache,
     backward_workspace_size,
     compress,
     compress_backward,
@@ -29,6 +30,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
+    "SketchCache",
     "compress", "compress_backward", "backward_workspace_size", "target_attention",
     "target_attention_workspace_size", "load", "read_device_error", "status_string", "version", "workspace_size",
     "SaError", "SA_OK", "SA_E_INVALID", "SA_E_UNSUPPORTED", "SA_E_WORKSPACE", "SA_E_HIP",

@@ -22,6 +22,8 @@ _PATH_FLAGS = {None: 0, "auto": 0, "two": SA_FLAG_TWO_PASS, "one": SA_FLAG_ONE_P
 EXPORTS = ("sa_workspace_size", "sa_compress", "sa_compress_with_events",
            "sa_backward_workspace_size", "sa_compress_backward", "sa_compress_backward_with_events",
            "sa_target_attention_workspace_size", "sa_target_attention",
+           "sa_cache_create", "sa_cache_destroy", "sa_cache_lookup", "sa_cache_fill_workspace_size",
+           "sa_cache_fill",
            "sa_read_device_error", "sa_status_string", "sa_version")
 NUM_PHASE_EVENTS = 5
 NUM_BWD_PHASE_EVENTS = 6
@@ -36,6 +38,11 @@ class SaProblem(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("flags", ctypes.c_int32),
     ]
+
+
+class SaCacheStats(ctypes.Structure):
+    _fields_ = [("hits", ctypes.c_int64), ("misses", ctypes.c_int64), ("evictions", ctypes.c_int64),
+                ("expired", ctypes.c_int64)]
 
 
 class SaError(RuntimeError):
@@ -84,6 +91,19 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sa_target_attention_workspace_size.restype = ctypes.c_int
     lib.sa_target_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sa_target_attention.restype = ctypes.c_int
+    i64p, i32p = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)
+    lib.sa_cache_create.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_double, vp, vp,
+                                    ctypes.POINTER(vp)]
+    lib.sa_cache_create.restype = ctypes.c_int
+    lib.sa_cache_destroy.argtypes = [vp]
+    lib.sa_cache_destroy.restype = ctypes.c_int
+    lib.sa_cache_lookup.argtypes = [vp, i64p, ctypes.c_int64, ctypes.c_double, i32p, i64p, i32p, i64p,
+                                    ctypes.POINTER(SaCacheStats)]
+    lib.sa_cache_lookup.restype = ctypes.c_int
+    lib.sa_cache_fill_workspace_size.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(sz)]
+    lib.sa_cache_fill_workspace_size.restype = ctypes.c_int
+    lib.sa_cache_fill.argtypes = [vp, P, vp, i64p, vp, vp, vp, vp, i64p, i32p, ctypes.c_int64, vp, sz, vp]
+    lib.sa_cache_fill.restype = ctypes.c_int
     lib.sa_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
     lib.sa_read_device_error.restype = ctypes.c_int
     lib.sa_status_string.argtypes = [ctypes.c_int]
@@ -337,3 +357,94 @@ def target_attention(Q, cand_offsets, S, return_lse: bool = False, out=None, wor
     if st != SA_OK:
         raise SaError(st, "sa_target_attention")
     return (o, lse) if return_lse else o
+
+
+class SketchCache:
+    """User-keyed sketch cache over a device slab (sa_cache_* in include/sa.h).
+
+    ``slab`` [capacity, k, d] float32 and optional ``mass_slab`` [capacity, k]
+    float32 are caller-owned GPU tensors (kept referenced here).  ``lookup``
+    is pure host code; ``fill`` runs the misses' compression on a stream.
+    """
+
+    def __init__(self, capacity: int, k: int, d: int, ttl_seconds: float, slab, mass_slab=None):
+        import numpy as np  # noqa: F401
+
+        self._slab, self._mass = slab, mass_slab
+        self.capacity, self.k, self.d = int(capacity), int(k), int(d)
+        h = ctypes.c_void_p()
+        st = load().sa_cache_create(self.capacity, self.k, self.d, float(ttl_seconds), _addr(slab),
+                                    _addr(mass_slab), ctypes.byref(h))
+        if st != SA_OK:
+            raise SaError(st, "sa_cache_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            load().sa_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def lookup(self, users, now: float):
+        """Returns (slots int32 [n], miss_users int64, miss_slots int32, stats dict)."""
+        import numpy as np
+
+        u = np.ascontiguousarray(users, dtype=np.int64)
+        n = u.shape[0]
+        slots = np.empty(n, dtype=np.int32)
+        mu = np.empty(max(n, 1), dtype=np.int64)
+        ms = np.empty(max(n, 1), dtype=np.int32)
+        nm = ctypes.c_int64(0)
+        stats = SaCacheStats()
+        st = load().sa_cache_lookup(self._h, u.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, float(now),
+                                    slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                    mu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                    ms.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(nm),
+                                    ctypes.byref(stats))
+        if st != SA_OK:
+            raise SaError(st, "sa_cache_lookup")
+        m = int(nm.value)
+        return slots, mu[:m].copy(), ms[:m].copy(), {f: int(getattr(stats, f)) for f, _ in SaCacheStats._fields_}
+
+    def fill(self, H_store, store_offsets_host, Wk, Wv, P, miss_users, miss_slots, mask_store=None,
+             workspace=None, stream=None):
+        """Compress the misses (one sa_compress launch) into their slab slots on
+        ``stream`` (a torch stream; default: the current one)."""
+        import numpy as np
+        import torch
+
+        mu = np.ascontiguousarray(miss_users, dtype=np.int64)
+        ms = np.ascontiguousarray(miss_slots, dtype=np.int32)
+        off = np.ascontiguousarray(store_offsets_host, dtype=np.int64)
+        if mu.shape[0] == 0:
+            return
+        dt = SA_BF16 if H_store.dtype == torch.bfloat16 else SA_F32
+        pb = problem(off.shape[0] - 1, int(off[-1]), self.d, self.k, dt)
+        lens = off[mu + 1] - off[mu]
+        need = ctypes.c_size_t(0)
+        st = load().sa_cache_fill_workspace_size(ctypes.byref(pb), mu.shape[0], int(lens.sum()), ctypes.byref(need))
+        if st != SA_OK:
+            raise SaError(st, "sa_cache_fill_workspace_size")
+        dev = H_store.device
+        if workspace is None or workspace.numel() < need.value:
+            workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        st = load().sa_cache_fill(self._h, ctypes.byref(pb), _addr(H_store),
+                                  off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _addr(mask_store), _addr(Wk),
+                                  _addr(Wv), _addr(P), mu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                  ms.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), mu.shape[0], _addr(workspace),
+                                  need.value, ctypes.c_void_p(s.cuda_stream))
+        if st != SA_OK:
+            raise SaError(st, "sa_cache_fill")
+        self._last_ws = workspace   # keep alive until the stream has used it
+
+
+def _addr(t):
+    """Device address of a tensor, or a plain integer address, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
