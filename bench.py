@@ -20,6 +20,10 @@ sample against it.
 ``--target-attention`` times sa_target_attention (300 users x 300
 candidates over 1K x 128 sketches) with an HBM roofline.
 
+``--cache-serving`` runs a serving trace through the sketch cache: per
+step one host lookup of 300 requests (120 of them users not cached) and one
+fill (gather + one sa_compress + scatter) on a side stream.
+
 ``--backward`` times one sa_compress_backward call per step instead (the
 gradients dH, dP, dWk, dWv for a seeded dS, forward recomputation included)
 on the same workload; its roofline object reports the token-major dH kernel
@@ -376,6 +380,86 @@ def bench_target(args, torch, dev, sa):
     return 0
 
 
+def bench_cache(args, torch, dev, sa):
+    """Serving trace through the sketch cache: batches of 300 requests of
+    which 120 are users not in the cache (the miss fraction 0.4 of the
+    serving operating point), compressed by one fill per batch."""
+    from synth import make_inputs
+
+    R_req, n_new, k, d = 300, 120, 1024, 128
+    R_store = R_req + n_new
+    g = np.random.default_rng(3)
+    lens = np.clip(np.round(g.lognormal(np.log(30000.0), 0.8, size=R_store)), 1000, 100000).astype(np.int64)
+    inp = make_inputs(lens, d=d, k=k, seed=13, name="cache_store")
+    H, off, Wk, Wv, P, mask = _upload(inp, torch, dev)
+    slab = torch.empty((R_req, k, d), dtype=torch.float32, device=dev)
+    mass = torch.empty((R_req, k), dtype=torch.float32, device=dev)
+    cache = sa.SketchCache(R_req, k, d, 3600.0, slab, mass)
+    # workspace for the largest miss batch of the trace
+    worst = int(np.sort(lens)[-n_new:].sum())
+    pb = sa._lib.problem(R_store, int(inp.offsets[-1]), d, k, sa.SA_BF16)
+    need = ctypes.c_size_t(0)
+    sa._lib.load().sa_cache_fill_workspace_size(ctypes.byref(pb), R_req, worst, ctypes.byref(need))
+    ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream()
+
+    def batch_users(b):   # a window sliding by n_new users: 180 repeat, 120 new
+        return (np.arange(R_req, dtype=np.int64) + n_new * b) % R_store
+
+    b = 0
+    slots, mu, ms, st = cache.lookup(batch_users(b), 0.0)   # cold start: all misses
+    cache.fill(H, inp.offsets, Wk, Wv, P, mu, ms, workspace=ws, stream=side)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        b += 1
+        _, mu, ms, _ = cache.lookup(batch_users(b), float(b))
+        cache.fill(H, inp.offsets, Wk, Wv, P, mu, ms, workspace=ws, stream=side)
+    torch.cuda.synchronize()
+    host_s, gpu_ms, hits, misses, miss_tokens = 0.0, 0.0, 0, 0, 0
+    t_wall = time.perf_counter()
+    for _ in range(args.steps):
+        b += 1
+        t0 = time.perf_counter()
+        _, mu, ms, st = cache.lookup(batch_users(b), float(b))
+        host_s += time.perf_counter() - t0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(side)
+        cache.fill(H, inp.offsets, Wk, Wv, P, mu, ms, workspace=ws, stream=side)
+        e1.record(side)
+        e1.synchronize()
+        gpu_ms += e0.elapsed_time(e1)
+        hits += st["hits"]
+        misses += st["misses"]
+        miss_tokens += int((inp.offsets[mu + 1] - inp.offsets[mu]).sum())
+    t_wall = time.perf_counter() - t_wall
+    ms_step = t_wall * 1e3 / args.steps
+    out = {
+        "metric": "serving batches/s through the sketch cache (300 requests, miss fraction 0.4)",
+        "value": args.steps / t_wall,
+        "unit": "batches/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"cache_serving_r{R_req}_new{n_new}_d{d}_k{k}", "requests": R_req,
+                   "store_users": R_store, "k": k, "d": d, "parallelism": "single_gpu", "op": "cache_fill"},
+        "hit_rate": hits / max(1, hits + misses),
+        "misses_per_batch": misses / args.steps,
+        "miss_tokens_per_batch": miss_tokens / args.steps,
+        "phase_ms": {"lookup_host": host_s * 1e3 / args.steps, "fill_gpu": gpu_ms / args.steps},
+        "miss_tokens_per_s_gpu": miss_tokens / (gpu_ms * 1e-3),
+        "roofline": None,
+    }
+    cache.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -388,6 +472,8 @@ def main(argv=None):
                     help="kernel path: the library's choice, the one-pass or the two-pass kernels")
     ap.add_argument("--target-attention", action="store_true",
                     help="time sketch-branch target attention (300 users x 300 candidates) instead")
+    ap.add_argument("--cache-serving", action="store_true",
+                    help="time the cache-miss driver on a serving trace (300 requests, 120 misses per batch)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (gradients through the sketches) instead")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -410,6 +496,8 @@ def main(argv=None):
     torch.cuda.set_device(dev)
     if args.target_attention:
         return bench_target(args, torch, dev, sa)
+    if args.cache_serving:
+        return bench_cache(args, torch, dev, sa)
     inp = make_config(args.workload)
     if args.backward:
         return bench_backward(args, inp, torch, dev, sa)

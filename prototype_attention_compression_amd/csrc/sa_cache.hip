@@ -38,36 +38,28 @@
 
 namespace sa {
 
-// dst row block i = src rows [src_start[i], src_start[i] + len_i), where the
-// destination offsets dst_off[0..n] are the exclusive prefix sums of len
+// Row gather: miss user i = blockIdx.y copies its rows [src_start[i],
+// src_start[i] + len_i) to [dst_off[i], dst_off[i+1]) -- one contiguous,
+// coalesced 16-byte-per-lane copy per user (rows of row_vec 16-byte words)
 __global__ __launch_bounds__(256) void gather_rows(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                    const int64_t* __restrict__ src_start,
-                                                   const int64_t* __restrict__ dst_off, int32_t n, int32_t row_vec,
-                                                   int64_t total_vec) {
-  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < total_vec; v += (int64_t)gridDim.x * 256) {
-    const int64_t row = v / row_vec;
-    int lo = 0, hi = n;   // dst_off[lo] <= row < dst_off[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (dst_off[mid] <= row) lo = mid; else hi = mid;
-    }
-    const int64_t srow = src_start[lo] + (row - dst_off[lo]);
-    dst[v] = src[srow * row_vec + (v - row * row_vec)];
-  }
+                                                   const int64_t* __restrict__ dst_off, int32_t row_vec) {
+  const int i = blockIdx.y;
+  const int64_t d0 = dst_off[i], n = (dst_off[i + 1] - d0) * row_vec;
+  const uint4* s = src + src_start[i] * row_vec;
+  uint4* t = dst + d0 * row_vec;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < n; v += (int64_t)gridDim.x * 256) t[v] = s[v];
 }
 
 // same for one byte per row (the token mask)
 __global__ __launch_bounds__(256) void gather_bytes(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                                     const int64_t* __restrict__ src_start,
-                                                    const int64_t* __restrict__ dst_off, int32_t n, int64_t total) {
-  for (int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x; row < total; row += (int64_t)gridDim.x * 256) {
-    int lo = 0, hi = n;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (dst_off[mid] <= row) lo = mid; else hi = mid;
-    }
-    dst[row] = src[src_start[lo] + (row - dst_off[lo])];
-  }
+                                                    const int64_t* __restrict__ dst_off) {
+  const int i = blockIdx.y;
+  const int64_t d0 = dst_off[i], n = dst_off[i + 1] - d0;
+  const uint8_t* s = src + src_start[i];
+  uint8_t* t = dst + d0;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < n; v += (int64_t)gridDim.x * 256) t[v] = s[v];
 }
 
 // slab[slot[i]] = S[i] (k d floats) and mass_slab[slot[i]] = mass[i]
@@ -314,16 +306,14 @@ sa_status sa_cache_fill(sa_cache* c, const sa_problem* store, const void* H_stor
     const size_t row_bytes = (size_t)store->d * elem;
     if (tokens > 0) {
       const int32_t row_vec = (int32_t)(row_bytes / 16);
-      const int64_t total_vec = tokens * row_vec;
-      const int64_t grid = std::min<int64_t>(4096, (total_vec + 255) / 256);
-      hipLaunchKernelGGL(sa::gather_rows, dim3((unsigned)grid), dim3(256), 0, s,
-                         static_cast<const uint4*>(H_store), reinterpret_cast<uint4*>(ws + F.off_H), d_src, d_dst,
-                         (int32_t)n_miss, row_vec, total_vec);
+      // enough workgroups per user to spread the longest histories
+      const dim3 grid(64, (unsigned)n_miss);
+      hipLaunchKernelGGL(sa::gather_rows, grid, dim3(256), 0, s, static_cast<const uint4*>(H_store),
+                         reinterpret_cast<uint4*>(ws + F.off_H), d_src, d_dst, row_vec);
       if (hipGetLastError() != hipSuccess) return SA_E_HIP;
       if (mask_store != nullptr) {
-        const int64_t g2 = std::min<int64_t>(4096, (tokens + 255) / 256);
-        hipLaunchKernelGGL(sa::gather_bytes, dim3((unsigned)g2), dim3(256), 0, s, mask_store,
-                           reinterpret_cast<uint8_t*>(ws + F.off_mask), d_src, d_dst, (int32_t)n_miss, tokens);
+        hipLaunchKernelGGL(sa::gather_bytes, dim3(16, (unsigned)n_miss), dim3(256), 0, s, mask_store,
+                           reinterpret_cast<uint8_t*>(ws + F.off_mask), d_src, d_dst);
         if (hipGetLastError() != hipSuccess) return SA_E_HIP;
       }
     }
