@@ -89,6 +89,12 @@ typedef struct {
  */
 #define SA_FLAG_TWO_PASS 1
 #define SA_FLAG_ONE_PASS 2
+/* Backward only (sa_compress_backward): reuse the forward state the
+ * workspace already holds instead of recomputing it -- meant for right
+ * after an sa_compress of the same problem and inputs on the same
+ * workspace.  Currently switched off: sa_compress_backward and
+ * sa_backward_workspace_size return SA_E_UNSUPPORTED for it. */
+#define SA_FLAG_REUSE_FORWARD 4
 
 /*
  * Workspace size for `problem`.  Writes the byte count to *bytes.  Returns
@@ -188,7 +194,8 @@ sa_status sa_compress_with_events(const sa_problem* problem,
  *
  * Built for bf16 inputs (problem->dtype = SA_BF16) with the same d and k as
  * sa_compress; SA_F32 or SA_FLAG_ONE_PASS give SA_E_UNSUPPORTED (the
- * backward always recomputes the two forward passes it needs).  Internally
+ * backward needs the two-pass forward's state: it recomputes it, or with
+ * SA_FLAG_REUSE_FORWARD takes it from the workspace).  Internally
  * the products use fp16 MFMA operands (the token rows widened exactly, the
  * allocations, their gradients and dS / m scaled by powers of two into fp16
  * range) with fp32 sums.  dS must be finite.

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_PKG, "libsa.so")
 
 SA_OK, SA_E_INVALID, SA_E_UNSUPPORTED, SA_E_WORKSPACE, SA_E_HIP = range(5)
 SA_BF16, SA_F32 = 0, 1
-SA_FLAG_TWO_PASS, SA_FLAG_ONE_PASS = 1, 2
+SA_FLAG_TWO_PASS, SA_FLAG_ONE_PASS, SA_FLAG_REUSE_FORWARD = 1, 2, 4
 SA_DEVICE_ERR_OFFSETS, SA_DEVICE_ERR_EXCHANGE = 1, 2
 _PATH_FLAGS = {None: 0, "auto": 0, "two": SA_FLAG_TWO_PASS, "one": SA_FLAG_ONE_PASS}
 
@@ -252,13 +252,16 @@ def read_device_error(workspace) -> int:
     return int(flag.value)
 
 
-def compress_backward(H, offsets, Wk, Wv, P, dS, mask=None, workspace=None, events=None):
+def compress_backward(H, offsets, Wk, Wv, P, dS, mask=None, workspace=None, events=None,
+                      reuse_forward: bool = False):
     """Gradients of a loss through the sketches, computed by libsa on the GPU.
 
     Inputs as for ``compress`` (bfloat16 only), plus dS [R, k, d] float32 =
     dLoss/dS.  Returns (dH [N, d], dP [k, d], dWk [d, d], dWv [d, d]), all
     float32; dP, dWk and dWv are summed over the users.  Runs on torch's
-    current stream.
+    current stream.  ``reuse_forward`` (SA_FLAG_REUSE_FORWARD): ``workspace``
+    holds the two-pass forward of these same inputs (a ``compress`` call on
+    it just before), which the backward then does not recompute.
     """
     import torch
 
@@ -285,9 +288,11 @@ def compress_backward(H, offsets, Wk, Wv, P, dS, mask=None, workspace=None, even
         if mask.dtype != torch.uint8 or mask.shape != (N,) or not mask.is_cuda or not mask.is_contiguous():
             raise ValueError("mask must be a contiguous [N] uint8/bool GPU tensor")
     dev = H.device
-    pb = problem(R, N, d, k, SA_BF16)
+    pb = problem(R, N, d, k, SA_BF16, SA_FLAG_REUSE_FORWARD if reuse_forward else 0)
     wbytes = backward_workspace_size(R, N, d, k, SA_BF16)
     if workspace is None or workspace.numel() * workspace.element_size() < wbytes:
+        if reuse_forward:
+            raise ValueError("reuse_forward needs the workspace the forward ran on")
         workspace = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
     dH = torch.empty((N, d), dtype=torch.float32, device=dev)
     dP = torch.empty((k, d), dtype=torch.float32, device=dev)

@@ -35,9 +35,15 @@ sa_status check_problem(const sa_problem* p) {
 
 // The backward pass: bf16 inputs only; it always runs the two forward passes
 sa_status check_problem_bwd(const sa_problem* p) {
-  sa_status st = check_problem(p);
+  if (p == nullptr) return SA_E_INVALID;
+  sa_problem q = *p;
+  q.flags &= ~SA_FLAG_REUSE_FORWARD;
+  sa_status st = check_problem(&q);
   if (st != SA_OK) return st;
   if (p->dtype != SA_BF16 || (p->flags & SA_FLAG_ONE_PASS)) return SA_E_UNSUPPORTED;
+  // Reusing the forward's state is switched off: the first GPU run that
+  // exercised it ended in a device fault whose cause has not been found.
+  if (p->flags & SA_FLAG_REUSE_FORWARD) return SA_E_UNSUPPORTED;
   return SA_OK;
 }
 
@@ -324,8 +330,10 @@ sa_status sa_compress_backward_with_events(const sa_problem* problem, const void
     if (reinterpret_cast<uintptr_t>(workspace) % sa::kAlign != 0) return SA_E_INVALID;
     if (!mark(0)) return SA_E_HIP;
     // forward passes 1 and 2: fp16 token rows, logsumexps, partial sums
-    if (sa::launch_prep(L, P, Wk, offsets, workspace, s) != hipSuccess) return SA_E_HIP;
-    if (p.total_tokens > 0) {
+    // (already in the workspace when the caller asks to reuse them)
+    const bool reuse = (p.flags & SA_FLAG_REUSE_FORWARD) != 0;
+    if (!reuse && sa::launch_prep(L, P, Wk, offsets, workspace, s) != hipSuccess) return SA_E_HIP;
+    if (!reuse && p.total_tokens > 0) {
       const hipError_t e = sa::pass1q_ok(L) ? sa::launch_pass1q(L, H, offsets, token_mask, workspace, s)
                                             : sa::launch_pass1(L, H, offsets, token_mask, workspace, s);
       if (e != hipSuccess) return SA_E_HIP;

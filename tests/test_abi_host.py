@@ -199,3 +199,10 @@ def test_target_attention_argument_errors_before_launch():
     assert call(pb, ws=None) == sa.SA_E_WORKSPACE
     assert call(pb, wsb=need - 1) == sa.SA_E_WORKSPACE
     assert call(_lib.problem(0, 0, 128, 1024, 0), Q=None, off=None, S=None, o=None, ws=None, wsb=0) == sa.SA_OK
+
+
+def test_reuse_forward_flag_is_backward_only():
+    assert _ws(1, 10, 128, 1024, 0, flags=sa.SA_FLAG_REUSE_FORWARD)[0] == sa.SA_E_INVALID
+    # switched off (see the note on SA_FLAG_REUSE_FORWARD in include/sa.h)
+    assert _bws(1, 10, 128, 1024, 0, flags=sa.SA_FLAG_REUSE_FORWARD)[0] == sa.SA_E_UNSUPPORTED
+    assert _bws(1, 10, 128, 1024, 0, flags=sa.SA_FLAG_REUSE_FORWARD | sa.SA_FLAG_ONE_PASS)[0] == sa.SA_E_UNSUPPORTED
