@@ -41,6 +41,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "sa_device.h"
 #include "sa_launch.h"
@@ -265,28 +266,49 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
   const bool keep = negl > -30000.f;
 
   const int NB = L.k / kTile;
-  uint4 pq[LPT], pz[LPT];
-  float pc = 0.f;
-  auto gload = [&](int i) {
+  // Staging of the 2 NB block steps (block i % NB of sweep i / NB): two
+  // register sets, so the global loads of step i + 2 are issued while step i
+  // is computed and step i + 1 (loaded an iteration earlier) goes to LDS at
+  // the end of the iteration.
+  u32x4 qa[LPT], za[LPT], qb2[LPT], zb2[LPT];
+  float ca = 0.f, cb = 0.f;
+  auto gload = [&](int i, u32x4 (&q)[LPT], u32x4 (&z)[LPT], float& c) {
     const int jb = i % NB;
 #pragma unroll
     for (int k2 = 0; k2 < LPT; ++k2) {
       const int idx = tid + 256 * k2, row = idx / CPR, ch = idx % CPR;
-      pq[k2] = *reinterpret_cast<const uint4*>(q16 + (int64_t)(jb * kTile + row) * D + 8 * ch);
-      pz[k2] = *reinterpret_cast<const uint4*>(z16 + (int64_t)(jb * kTile + row) * D + 8 * ch);
+      q[k2] = *reinterpret_cast<const u32x4*>(q16 + (int64_t)(jb * kTile + row) * D + 8 * ch);
+      z[k2] = *reinterpret_cast<const u32x4*>(z16 + (int64_t)(jb * kTile + row) * D + 8 * ch);
     }
-    if (tid < kTile) pc = czu[jb * kTile + tid];
+    if (tid < kTile) c = czu[jb * kTile + tid];
   };
-  auto swrite = [&](int buf) {
+  auto swrite = [&](int buf, const u32x4 (&q)[LPT], const u32x4 (&z)[LPT], float c) {
     char* base = lds[buf];
 #pragma unroll
     for (int k2 = 0; k2 < LPT; ++k2) {
       const int idx = tid + 256 * k2, row = idx / CPR, ch = idx % CPR;
-      *reinterpret_cast<uint4*>(base + row * PITCH + 16 * ch) = pq[k2];
-      *reinterpret_cast<uint4*>(base + BLK + row * PITCH + 16 * ch) = pz[k2];
+      *reinterpret_cast<u32x4*>(base + row * PITCH + 16 * ch) = q[k2];
+      *reinterpret_cast<u32x4*>(base + BLK + row * PITCH + 16 * ch) = z[k2];
     }
-    if (tid < kTile) reinterpret_cast<float*>(base + 2 * BLK)[acc_pos(tid)] = pc;
+    if (tid < kTile) reinterpret_cast<float*>(base + 2 * BLK)[acc_pos(tid)] = c;
   };
+  // step i (even: set b holds step i + 1, set a is free; odd: the reverse)
+  auto run = [&](int i, auto odd, auto&& body) {
+    if constexpr (!decltype(odd)::value) {
+      if (i + 2 < 2 * NB) gload(i + 2, qa, za, ca);
+    } else {
+      if (i + 2 < 2 * NB) gload(i + 2, qb2, zb2, cb);
+    }
+    body(static_cast<const char*>(lds[i & 1]));
+    if constexpr (!decltype(odd)::value) {
+      if (i + 1 < 2 * NB) swrite((i + 1) & 1, qb2, zb2, cb);
+    } else {
+      if (i + 1 < 2 * NB) swrite((i + 1) & 1, qa, za, ca);
+    }
+    __syncthreads();
+  };
+  using Even = std::false_type;
+  using Odd = std::true_type;
 
   const int abase = tau(col) * PITCH + 16 * g;
   const int i16 = lane & 15, gh = (lane >> 4) & 1;
@@ -319,14 +341,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
     }
   };
 
-  gload(0);
-  swrite(0);
-  __syncthreads();
   // sweep 1: delta_t and the bound b_t
-  for (int i = 0; i < NB; ++i) {
-    const int buf = i & 1;
-    gload(i + 1);   // i + 1 <= NB < 2 NB: the first block of sweep 2 at the end
-    const char* qb = lds[buf];
+  auto sweep1 = [&](const char* qb) {
     float16v Lc, Yc;
     gemms(qb, Lc, Yc);
     const float4* cp = reinterpret_cast<const float4*>(qb + 2 * BLK) + 4 * g;
@@ -342,8 +358,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
         bmx = fmaxf(bmx, fabsf(yc));
       }
     }
-    swrite(buf ^ 1);
-    __syncthreads();
+  };
+  gload(0, qa, za, ca);
+  swrite(0, qa, za, ca);
+  gload(1, qb2, zb2, cb);
+  __syncthreads();
+  for (int i = 0; i < NB; i += 2) {   // NB = k / 32 is even
+    run(i, Even{}, sweep1);
+    run(i + 1, Odd{}, sweep1);
   }
   dsum += __shfl_xor(dsum, 32);
   bmx = fmaxf(bmx, __shfl_xor(bmx, 32));
@@ -363,10 +385,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
       atomicMax(reinterpret_cast<unsigned int*>(ws_i32(ws, L.off_bbmax)) + u, __float_as_uint(wm));
   }
   // sweep 2: dh += (sl dL)^T q + (sg A)^T Zs
-  for (int i = NB; i < 2 * NB; ++i) {
-    const int buf = i & 1;
-    if (i + 1 < 2 * NB) gload(i + 1);
-    const char* qb = lds[buf];
+  auto sweep2 = [&](const char* qb) {
     float16v Lc, Yc;
     gemms(qb, Lc, Yc);
     const float4* cp = reinterpret_cast<const float4*>(qb + 2 * BLK) + 4 * g;
@@ -398,8 +417,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) dHc[dt] = mfma32x32x16(ad[kk], hb[dt], dHc[dt]);
     }
-    if (i + 1 < 2 * NB) swrite(buf ^ 1);
-    __syncthreads();
+  };
+  for (int i = NB; i < 2 * NB; i += 2) {
+    run(i, Even{}, sweep2);
+    run(i + 1, Odd{}, sweep2);
   }
   // accumulator rows are tokens acc_row(r, g), columns 32 dt + col
 #pragma unroll
@@ -452,7 +473,7 @@ __global__ __launch_bounds__(W * 64, 2) void bwd_e(const int32_t* __restrict__ t
   const _Float16* h16 = ws_f16(ws, L.off_h16);
   const uint32_t* nlw = reinterpret_cast<const uint32_t*>(ws_i32(ws, L.off_nl));
   const float* dlt = ws_f32(ws, L.off_bdelta);
-  uint4 pr[LPT];
+  u32x4 pr[LPT];
   uint32_t pn = 0;
   float pd = 0.f;
   auto gload = [&](int32_t t) {
@@ -460,7 +481,7 @@ __global__ __launch_bounds__(W * 64, 2) void bwd_e(const int32_t* __restrict__ t
 #pragma unroll
     for (int k2 = 0; k2 < LPT; ++k2) {
       const int idx = tid + NT * k2, row = idx / CPR, ch = idx % CPR;
-      pr[k2] = *reinterpret_cast<const uint4*>(src + row * D + 8 * ch);
+      pr[k2] = *reinterpret_cast<const u32x4*>(src + row * D + 8 * ch);
     }
     if (tid < kTile) {
       pn = nlw[(int64_t)t * kTile + tid];
@@ -472,7 +493,7 @@ __global__ __launch_bounds__(W * 64, 2) void bwd_e(const int32_t* __restrict__ t
 #pragma unroll
     for (int k2 = 0; k2 < LPT; ++k2) {
       const int idx = tid + NT * k2, row = idx / CPR, ch = idx % CPR;
-      *reinterpret_cast<uint4*>(base + row * PITCH + 16 * ch) = pr[k2];
+      *reinterpret_cast<u32x4*>(base + row * PITCH + 16 * ch) = pr[k2];
     }
     if (tid < kTile) {
       float* pv = reinterpret_cast<float*>(base + TB);

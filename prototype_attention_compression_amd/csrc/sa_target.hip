@@ -88,13 +88,16 @@ __global__ __launch_bounds__(256, 2) void ta_attend(const uint16_t* __restrict__
 
   const float* Su = Sk + (int64_t)u * L.k * D;
   const int NB = L.k / kTile;
-  float4 pf[LPT];
-  auto gload = [&](int i) {
+  // two register sets: the global loads of block i + 2 are issued while
+  // block i is computed, and block i + 1 (loaded an iteration earlier) goes
+  // to LDS at the end of the iteration
+  float4 pfa[LPT], pfb[LPT];
+  auto gload = [&](int i, float4 (&pf)[LPT]) {
     const float* src = Su + (int64_t)i * kTile * D;
 #pragma unroll
     for (int k2 = 0; k2 < LPT; ++k2) pf[k2] = reinterpret_cast<const float4*>(src)[tid + 256 * k2];
   };
-  auto swrite = [&](int buf) {
+  auto swrite = [&](int buf, const float4 (&pf)[LPT]) {
 #pragma unroll
     for (int k2 = 0; k2 < LPT; ++k2) {
       const int idx = tid + 256 * k2, row = idx / F4R, c4 = idx % F4R;
@@ -133,13 +136,9 @@ __global__ __launch_bounds__(256, 2) void ta_attend(const uint16_t* __restrict__
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) O[dt] = float16v{};
 
-  gload(0);
-  swrite(0);
-  __syncthreads();
-  for (int i = 0; i < NB; ++i) {
-    const int buf = i & 1;
-    if (i + 1 < NB) gload(i + 1);
-    const char* sb = lds[buf];
+  auto step = [&](int i, float4 (&pf_next)[LPT], float4 (&pf_free)[LPT]) {
+    if (i + 2 < NB) gload(i + 2, pf_free);
+    const char* sb = lds[i & 1];
     float16v C = float16v{};
 #pragma unroll
     for (int s0 = 0; s0 < S; s0 += 4) {
@@ -181,8 +180,16 @@ __global__ __launch_bounds__(256, 2) void ta_attend(const uint16_t* __restrict__
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) O[dt] = mfma32x32x16(ap[kk], hb[dt], O[dt]);
     }
-    if (i + 1 < NB) swrite(buf ^ 1);
+    if (i + 1 < NB) swrite((i + 1) & 1, pf_next);
     __syncthreads();
+  };
+  gload(0, pfa);
+  swrite(0, pfa);
+  if (NB > 1) gload(1, pfb);
+  __syncthreads();
+  for (int i = 0; i < NB; i += 2) {
+    step(i, pfb, pfa);
+    if (i + 1 < NB) step(i + 1, pfa, pfb);
   }
   l += __shfl_xor(l, 32);
   if (g == 0) wx[col] = 1.0f / (16384.0f * l);
