@@ -22,10 +22,12 @@
 //   running maximum m and sum l per candidate (lane = candidate), P =
 //   2^(logit - m) in fp16 -- the accumulator registers are exactly the A
 //   operand of out = P s (candidate = lane, sketch rows in the transposing
-//   read's order) -- and out = out 2^(m_old - m) + P s with B operands from
-//   the staged block through ds_read_b64_tr_b16.  The output rows sit in
-//   another lane layout than the per-candidate statistics, so the rescale
-//   factors (and finally 1 / l) pass through a small per-wave LDS area.
+//   read's order) -- and out += P s with B operands from the staged block
+//   through ds_read_b64_tr_b16.  m moves only when a logit exceeds it by
+//   more than 2^8 (then out and l are rescaled by 2^(m_old - m)), so after
+//   the first blocks the rescale is rare.  The output rows sit in another
+//   lane layout than the per-candidate statistics, so the rescale factors
+//   (and finally 1 / l) pass through a small per-wave LDS area.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -152,27 +154,33 @@ __global__ __launch_bounds__(256, 2) void ta_attend(const uint16_t* __restrict__
 #pragma unroll
     for (int r = 1; r < 16; ++r) bm = fmaxf(bm, C[r]);
     bm = fmaxf(bm, __shfl_xor(bm, 32)) * sc2;
-    const float mn = fmaxf(m, bm);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first block
-    m = mn;
+    // Lazy rescale: the running maximum m moves (and O, l are rescaled)
+    // only when some candidate of the wave sees a logit more than 2^8 above
+    // it; otherwise P = 2^(logit - m) <= 2^8 and 2^6 P stays in fp16 range.
+    if (__any(bm > m + 8.0f)) {   // uniform over the wave
+      const float mn = fmaxf(m, bm);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first block
+      m = mn;
+      l *= alpha;
+      if (i > 0) {
+        if (g == 0) wx[col] = alpha;
+        float f[16];
+        row_factors(f);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) O[dt][r] *= f[r];
+      }
+    }
     half8 ap[2];
     float sum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(C[r] * sc2 - mn);
+      const float p = __builtin_amdgcn_exp2f(C[r] * sc2 - m);
       sum += p;
-      ap[r >> 3][r & 7] = (_Float16)(p * 16384.0f);   // 2^14 P: small weights stay normal fp16
+      ap[r >> 3][r & 7] = (_Float16)(p * 64.0f);   // 2^6 P <= 2^14: small weights stay normal fp16
     }
-    l = l * alpha + sum;
-    if (i > 0) {
-      if (g == 0) wx[col] = alpha;
-      float f[16];
-      row_factors(f);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[dt][r] *= f[r];
-    }
+    l += sum;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       half8 hb[DT];
@@ -192,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void ta_attend(const uint16_t* __restrict__
     if (i + 1 < NB) step(i + 1, pfa, pfb);
   }
   l += __shfl_xor(l, 32);
-  if (g == 0) wx[col] = 1.0f / (16384.0f * l);
+  if (g == 0) wx[col] = 1.0f / (64.0f * l);
   float f[16];
   row_factors(f);
   // output rows are candidates acc_row(r, g), columns 32 dt + col

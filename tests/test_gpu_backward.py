@@ -69,6 +69,14 @@ def test_backward_small_ragged(k, d):
     _check(inp, make_sketch_grad(inp.R, k, d, seed=5000 + k + d))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_largest_k(d):
+    """k = 4096, the largest built: 128 prototype blocks per token sweep,
+    32 prototype-major workgroups per group."""
+    inp = make_inputs([1500, 0, 33, 700], d=d, k=4096, seed=4900 + d, name=f"bwd_k4096_d{d}")
+    _check(inp, make_sketch_grad(inp.R, 4096, d, seed=5900 + d))
+
+
 @pytest.mark.parametrize("scale", [1e-7, 1e-2, 1e5])
 def test_backward_dS_scale(scale):
     """The per-user and per-token power-of-two scales keep the fp16 operands

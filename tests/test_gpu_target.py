@@ -50,6 +50,11 @@ def test_target_small_ragged(k, d):
     _check([0, 1, 31, 33, 300, 700], k, d, seed=6000 + k + d)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_target_largest_k(d):
+    _check([300, 1, 100], 4096, d, seed=6500 + d)
+
+
 @pytest.mark.parametrize("scale", [0.01, 4.0])
 def test_target_flat_and_sharp(scale):
     """Nearly uniform weights (small sketch) and peaked weights (logit std 4)."""
