@@ -24,6 +24,10 @@ candidates over 1K x 128 sketches) with an HBM roofline.
 step one host lookup of 300 requests (120 of them users not cached) and one
 fill (gather + one sa_compress + scatter) on a side stream.
 
+``--serving-pipeline`` adds the sketch branch to that trace: per batch the
+300 requests (300 candidates each) attend their cached sketches in place,
+timed with the misses' fill serial and overlapped on a side stream.
+
 ``--backward`` times one sa_compress_backward call per step instead (the
 gradients dH, dP, dWk, dWv for a seeded dS, forward recomputation included)
 on the same workload; its roofline object reports the token-major dH kernel
@@ -460,6 +464,108 @@ def bench_cache(args, torch, dev, sa):
     return 0
 
 
+def bench_serving_pipeline(args, torch, dev, sa):
+    """Serving batches through the cache with the sketch branch: 300 requests
+    (300 candidates each), 180 cached users and 120 misses per batch.
+    Serial: fill the misses, then attend all requests.  Overlapped ("pipeline
+    lift"): the misses' fill on a side stream while the cached requests are
+    attended on the main stream, then the missed requests."""
+    from synth import make_candidates, make_inputs
+
+    R_req, n_new, k, d, C_u = 300, 120, 1024, 128, 300
+    R_store = R_req + n_new
+    g = np.random.default_rng(3)
+    lens = np.clip(np.round(g.lognormal(np.log(30000.0), 0.8, size=R_store)), 1000, 100000).astype(np.int64)
+    inp = make_inputs(lens, d=d, k=k, seed=13, name="cache_store")
+    H, off, Wk, Wv, P, mask = _upload(inp, torch, dev)
+    slab = torch.empty((R_req, k, d), dtype=torch.float32, device=dev)
+    cache = sa.SketchCache(R_req, k, d, 3600.0, slab)
+    worst = int(np.sort(lens)[-n_new:].sum())
+    pb = sa._lib.problem(R_store, int(inp.offsets[-1]), d, k, sa.SA_BF16)
+    need = ctypes.c_size_t(0)
+    sa._lib.load().sa_cache_fill_workspace_size(ctypes.byref(pb), R_req, worst, ctypes.byref(need))
+    ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    _, Qbits, coff = make_candidates([C_u] * R_req, d, seed=14)
+    Q = torch.from_numpy(Qbits.view(np.int16)).view(torch.bfloat16).to(dev)
+    off_all = torch.from_numpy(coff).to(dev)
+    n_hit = R_req - n_new
+    off_hit = torch.from_numpy(coff[:n_hit + 1]).to(dev)
+    off_miss = torch.from_numpy(coff[n_hit:] - coff[n_hit]).to(dev)
+    Q_hit, Q_miss = Q[:n_hit * C_u], Q[n_hit * C_u:]
+    out = torch.empty((R_req * C_u, d), dtype=torch.float32, device=dev)
+    out_hit, out_miss = out[:n_hit * C_u], out[n_hit * C_u:]
+    ta_ws = torch.empty(sa.target_attention_workspace_size(R_req, R_req * C_u, d, k), dtype=torch.uint8,
+                        device=dev)
+    ta_ws2 = torch.empty_like(ta_ws)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+
+    def window(b):   # hits first: the 180 users of the previous window, then 120 new ones
+        return (np.arange(R_req, dtype=np.int64) + n_new * b) % R_store
+
+    def batch(b, overlapped):
+        slots, mu, ms, st = cache.lookup(window(b), float(b))
+        rows = torch.from_numpy(slots).to(dev)
+        if overlapped:
+            side.wait_stream(main)
+            cache.fill(H, inp.offsets, Wk, Wv, P, mu, ms, workspace=ws, stream=side)
+            ev = torch.cuda.Event()
+            ev.record(side)
+            sa.target_attention(Q_hit, off_hit, slab, out=out_hit, workspace=ta_ws, sketch_rows=rows[:n_hit])
+            main.wait_event(ev)
+            sa.target_attention(Q_miss, off_miss, slab, out=out_miss, workspace=ta_ws2, sketch_rows=rows[n_hit:])
+        else:
+            cache.fill(H, inp.offsets, Wk, Wv, P, mu, ms, workspace=ws, stream=main)
+            sa.target_attention(Q, off_all, slab, out=out, workspace=ta_ws, sketch_rows=rows)
+        return st
+
+    b = 0
+    batch(b, False)   # cold start
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        for ov in (False, True):
+            b += 1
+            batch(b, ov)
+    torch.cuda.synchronize()
+    t = {False: 0.0, True: 0.0}
+    hits = misses = 0
+    for _ in range(args.steps):
+        for ov in (False, True):
+            b += 1
+            t0 = time.perf_counter()
+            st = batch(b, ov)
+            torch.cuda.synchronize()
+            t[ov] += time.perf_counter() - t0
+            hits += st["hits"]
+            misses += st["misses"]
+    ms_serial = t[False] * 1e3 / args.steps
+    ms_overlap = t[True] * 1e3 / args.steps
+    res = {
+        "metric": "serving batches/s, cache + sketch-branch attention (300 requests x 300 candidates)",
+        "value": 1e3 / ms_overlap,
+        "unit": "batches/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_overlap,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"serving_pipeline_r{R_req}_new{n_new}_c{C_u}_d{d}_k{k}", "requests": R_req,
+                   "candidates_per_request": C_u, "store_users": R_store, "k": k, "d": d,
+                   "parallelism": "single_gpu", "op": "cache_fill+target_attention"},
+        "hit_rate": hits / max(1, hits + misses),
+        "ms_serial": ms_serial,
+        "ms_overlapped": ms_overlap,
+        "roofline": None,
+    }
+    cache.close()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -474,6 +580,8 @@ def main(argv=None):
                     help="time sketch-branch target attention (300 users x 300 candidates) instead")
     ap.add_argument("--cache-serving", action="store_true",
                     help="time the cache-miss driver on a serving trace (300 requests, 120 misses per batch)")
+    ap.add_argument("--serving-pipeline", action="store_true",
+                    help="cache + sketch-branch attention per serving batch, serial vs overlapped fill")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (gradients through the sketches) instead")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -498,6 +606,8 @@ def main(argv=None):
         return bench_target(args, torch, dev, sa)
     if args.cache_serving:
         return bench_cache(args, torch, dev, sa)
+    if args.serving_pipeline:
+        return bench_serving_pipeline(args, torch, dev, sa)
     inp = make_config(args.workload)
     if args.backward:
         return bench_backward(args, inp, torch, dev, sa)

@@ -300,6 +300,25 @@ sa_status sa_target_attention(const sa_problem* problem,
                               void* stream);
 
 /*
+ * sa_target_attention with the sketches read through a row index: user u's
+ * sketch is S[sketch_rows[u]] (sketch_rows: [R] int32 device, each in
+ * [0, rows of S)), e.g. the slots of a sketch cache's slab (sa_cache_*), so
+ * cached sketches are attended in place without a gather.  The caller
+ * guarantees the indices are in range (they are not checked on the device).
+ * sketch_rows = NULL is sa_target_attention.
+ */
+sa_status sa_target_attention_rows(const sa_problem* problem,
+                                   const void* Q,
+                                   const int64_t* cand_offsets,
+                                   const float* S,
+                                   const int32_t* sketch_rows,
+                                   float* out,
+                                   float* lse,
+                                   void* workspace,
+                                   size_t workspace_bytes,
+                                   void* stream);
+
+/*
  * User-keyed sketch cache and its cache-miss driver.
  *
  * The sketch is user-only and target-agnostic, so it is cached: a local

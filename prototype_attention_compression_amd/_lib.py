@@ -21,7 +21,7 @@ _PATH_FLAGS = {None: 0, "auto": 0, "two": SA_FLAG_TWO_PASS, "one": SA_FLAG_ONE_P
 # functions declared in include/sa.h
 EXPORTS = ("sa_workspace_size", "sa_compress", "sa_compress_with_events",
            "sa_backward_workspace_size", "sa_compress_backward", "sa_compress_backward_with_events",
-           "sa_target_attention_workspace_size", "sa_target_attention",
+           "sa_target_attention_workspace_size", "sa_target_attention", "sa_target_attention_rows",
            "sa_cache_create", "sa_cache_destroy", "sa_cache_lookup", "sa_cache_fill_workspace_size",
            "sa_cache_fill",
            "sa_read_device_error", "sa_status_string", "sa_version")
@@ -91,6 +91,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sa_target_attention_workspace_size.restype = ctypes.c_int
     lib.sa_target_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sa_target_attention.restype = ctypes.c_int
+    lib.sa_target_attention_rows.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sa_target_attention_rows.restype = ctypes.c_int
     i64p, i32p = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)
     lib.sa_cache_create.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_double, vp, vp,
                                     ctypes.POINTER(vp)]
@@ -318,17 +320,22 @@ def target_attention_workspace_size(num_users: int, total_candidates: int, d: in
 
 
 def raw_target_attention(pb: SaProblem, Q, cand_offsets, S, out, lse, workspace, workspace_bytes: int,
-                         stream) -> int:
-    """Direct call of sa_target_attention; returns the status."""
-    return int(load().sa_target_attention(ctypes.byref(pb), Q, cand_offsets, S, out, lse, workspace,
-                                          ctypes.c_size_t(workspace_bytes), stream))
+                         stream, sketch_rows=None) -> int:
+    """Direct call of sa_target_attention(_rows); returns the status."""
+    if sketch_rows is None:
+        return int(load().sa_target_attention(ctypes.byref(pb), Q, cand_offsets, S, out, lse, workspace,
+                                              ctypes.c_size_t(workspace_bytes), stream))
+    return int(load().sa_target_attention_rows(ctypes.byref(pb), Q, cand_offsets, S, sketch_rows, out, lse,
+                                               workspace, ctypes.c_size_t(workspace_bytes), stream))
 
 
-def target_attention(Q, cand_offsets, S, return_lse: bool = False, out=None, workspace=None):
+def target_attention(Q, cand_offsets, S, return_lse: bool = False, out=None, workspace=None, sketch_rows=None):
     """Sketch-branch target attention, computed by libsa on the GPU.
 
     Q [C, d] bfloat16 candidate queries packed user by user, cand_offsets
     [R+1] int64, S [R, k, d] float32 sketches (as ``compress`` returns).
+    With ``sketch_rows`` ([R] int32 GPU tensor), user u's sketch is
+    S[sketch_rows[u]] and S may hold any number of rows (e.g. a cache slab).
     Returns out [C, d] float32 (and the natural-log normalisers [C] if
     ``return_lse``).  Runs on torch's current stream.
     """
@@ -343,7 +350,13 @@ def target_attention(Q, cand_offsets, S, return_lse: bool = False, out=None, wor
         raise ValueError("need Q [C, d], cand_offsets [R+1] int64, S [R, k, d]")
     C, d = Q.shape
     R = cand_offsets.shape[0] - 1
-    if S.shape[0] != R or S.shape[2] != d:
+    if sketch_rows is not None:
+        if (sketch_rows.dtype != torch.int32 or sketch_rows.shape != (R,) or not sketch_rows.is_cuda
+                or not sketch_rows.is_contiguous()):
+            raise ValueError("sketch_rows must be a contiguous [R] int32 GPU tensor")
+        if S.shape[2] != d:
+            raise ValueError("S must be [rows, k, d] with the candidates' d")
+    elif S.shape[0] != R or S.shape[2] != d:
         raise ValueError("S must be [R, k, d] with the candidates' d and one sketch per user")
     k = S.shape[1]
     dev = Q.device
@@ -358,7 +371,7 @@ def target_attention(Q, cand_offsets, S, return_lse: bool = False, out=None, wor
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     st = raw_target_attention(pb, _ptr(Q) if C > 0 else None, _ptr(cand_offsets), _ptr(S),
                               _ptr(o) if C > 0 else None, _ptr(lse) if C > 0 else None, _ptr(workspace), wbytes,
-                              stream)
+                              stream, _ptr(sketch_rows))
     if st != SA_OK:
         raise SaError(st, "sa_target_attention")
     return (o, lse) if return_lse else o

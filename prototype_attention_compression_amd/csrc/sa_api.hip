@@ -364,6 +364,13 @@ sa_status sa_target_attention_workspace_size(const sa_problem* problem, size_t* 
 
 sa_status sa_target_attention(const sa_problem* problem, const void* Q, const int64_t* cand_offsets, const float* S,
                               float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return sa_target_attention_rows(problem, Q, cand_offsets, S, nullptr, out, lse, workspace, workspace_bytes,
+                                  stream);
+}
+
+sa_status sa_target_attention_rows(const sa_problem* problem, const void* Q, const int64_t* cand_offsets,
+                                   const float* S, const int32_t* sketch_rows, float* out, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
   try {
     sa_status st = sa::check_problem_target(problem);
     if (st != SA_OK) return st;
@@ -376,7 +383,8 @@ sa_status sa_target_attention(const sa_problem* problem, const void* Q, const in
     if (workspace == nullptr || workspace_bytes < L.total) return SA_E_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % sa::kAlign != 0) return SA_E_INVALID;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (sa::launch_target_attention(L, Q, cand_offsets, S, workspace, out, lse, s) != hipSuccess) return SA_E_HIP;
+    if (sa::launch_target_attention(L, Q, cand_offsets, S, sketch_rows, workspace, out, lse, s) != hipSuccess)
+      return SA_E_HIP;
     return SA_OK;
   } catch (...) {
     return SA_E_HIP;

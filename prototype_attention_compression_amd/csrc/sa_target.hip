@@ -43,6 +43,7 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void ta_attend(const uint16_t* __restrict__ Q,
                                                     const int64_t* __restrict__ cand_offsets,
                                                     const float* __restrict__ Sk,
+                                                    const int32_t* __restrict__ sketch_rows,
                                                     const int32_t* __restrict__ tile_base, Layout L, void* ws,
                                                     float* __restrict__ out, float* __restrict__ lse_out) {
   constexpr int S = D / 16, DT = D / 32, PITCH = tile_pitch<D>(), BLK = kTile * PITCH;
@@ -88,7 +89,9 @@ __global__ __launch_bounds__(256, 2) void ta_attend(const uint16_t* __restrict__
     for (int s = 0; s < S; ++s) qB[s] = half8{};
   }
 
-  const float* Su = Sk + (int64_t)u * L.k * D;
+  // the user's sketch: row u of Sk, or row sketch_rows[u] (e.g. a cache slot)
+  const int64_t srow = sketch_rows != nullptr ? (int64_t)sketch_rows[u] : (int64_t)u;
+  const float* Su = Sk + srow * L.k * D;
   const int NB = L.k / kTile;
   // two register sets: the global loads of block i + 2 are issued while
   // block i is computed, and block i + 1 (loaded an iteration earlier) goes
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void ta_attend(const uint16_t* __restrict__
 }
 
 hipError_t launch_target_attention(const Layout& L, const void* Q, const int64_t* cand_offsets, const float* S,
-                                   void* ws, float* out, float* lse, hipStream_t stream) {
+                                   const int32_t* sketch_rows, void* ws, float* out, float* lse, hipStream_t stream) {
   if (launch_schedule(L, cand_offsets, ws, stream) != hipSuccess) return hipErrorLaunchFailure;
   if (L.N == 0) return hipSuccess;
   // a multiple of 8 workgroups covering every quad of tiles (see ta_attend)
@@ -225,10 +228,10 @@ hipError_t launch_target_attention(const Layout& L, const void* Q, const int64_t
   const int32_t* tb = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(ws) + L.off_tile_base);
   if (L.d == 128)
     hipLaunchKernelGGL((ta_attend<128>), dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)Q, cand_offsets,
-                       S, tb, L, ws, out, lse);
+                       S, sketch_rows, tb, L, ws, out, lse);
   else
     hipLaunchKernelGGL((ta_attend<64>), dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)Q, cand_offsets,
-                       S, tb, L, ws, out, lse);
+                       S, sketch_rows, tb, L, ws, out, lse);
   return hipGetLastError();
 }
 

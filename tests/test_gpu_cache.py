@@ -64,4 +64,18 @@ def test_cache_fill_matches_direct_calls():
                 assert omx <= TOL["bf16"][0] and omean <= TOL["bf16"][1], (u, omx, omean)
             else:
                 assert not got[s].any()
+    # the sketch branch reads the cached sketches in place: one launch over
+    # the last batch's requests through their slots
+    from oracle import target_attention_batch
+    from synth import make_candidates
+    users, _ = trace[-1]
+    slots = torch.tensor(cache.lookup(users, trace[-1][1])[0], dtype=torch.int32, device="cuda")
+    Qf, Qbits, coff = make_candidates([64] * len(users), 128, seed=7001)
+    q = torch.from_numpy(Qbits.view(np.int16)).view(torch.bfloat16).to("cuda")
+    out = sa.target_attention(q, torch.from_numpy(coff).to("cuda"), slab, sketch_rows=slots)
+    torch.cuda.synchronize()
+    S_users = np.stack([direct_sketch(u)[0] for u in users])
+    ref, _ = target_attention_batch(Qf, coff, S_users)
+    mx, mean = rel_errors(out.cpu().numpy(), ref)
+    assert mx <= TOL["bf16"][0] and mean <= TOL["bf16"][1], (mx, mean)
     cache.close()

@@ -93,3 +93,24 @@ def test_target_bad_offsets_zero_output():
     o, lse = sa.target_attention(q, bad, S, return_lse=True)
     torch.cuda.synchronize()
     assert not o.any() and not lse.any()
+
+
+def test_target_rows_index_a_slab():
+    """sa_target_attention_rows: user u reads slab row sketch_rows[u] (rows
+    repeated and out of order); equal, bit for bit, to attention over the
+    gathered sketches."""
+    import torch
+
+    import prototype_attention_compression_amd as sa
+    Q, Qbits, off = make_candidates([300, 0, 45, 128], 128, seed=6600)
+    slab = torch.from_numpy(make_sketches(7, 512, 128, seed=6601)).to("cuda")
+    rows = torch.tensor([5, 2, 5, 0], dtype=torch.int32, device="cuda")
+    q = torch.from_numpy(Qbits.view(np.int16)).view(torch.bfloat16).to("cuda")
+    o = torch.from_numpy(off).to("cuda")
+    got = sa.target_attention(q, o, slab, sketch_rows=rows)
+    want = sa.target_attention(q, o, slab[rows.long()].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    ref, _ = target_attention_batch(Q, off, slab[rows.long()].cpu().numpy())
+    mx, mean = rel_errors(got.cpu().numpy(), ref)
+    assert mx <= TOL["bf16"][0] and mean <= TOL["bf16"][1]
