@@ -34,8 +34,12 @@
 //              transposing LDS read;
 //   bwd_e      prototype-major (like pass 2): E += dL h over token tiles,
 //              queries and Z rows resident, per-user scale, partial E per
-//              workgroup group;
+//              (group, user) segment;
 //   bwd_ereduce, bwd_outer, bwd_sum: E, dP, dWk, dWv.
+// Both token kernels run two waves per SIMD and stage their operand blocks
+// two steps ahead through registers of a native vector type (an array of
+// the struct-typed uint4 stayed in scratch memory, with a wait right after
+// every prefetch).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -584,7 +588,8 @@ __global__ __launch_bounds__(W * 64, 2) void bwd_e(const int32_t* __restrict__ t
 }
 
 // ---------------------------------------------------------------- reductions
-// E = sum over the partial slots (fixed order), and dP = E Wk / sqrt(d)
+// E = sum over the (group, user) partial slots (users, then groups, in
+// order: bitwise repeatable), and dP = E Wk / sqrt(d)
 template <int D>
 __global__ __launch_bounds__(256) void bwd_ereduce(const uint16_t* __restrict__ Wk, Layout L, void* ws,
                                                    float* __restrict__ dP) {
