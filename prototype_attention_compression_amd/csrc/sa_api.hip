@@ -120,9 +120,10 @@ Layout make_layout(const sa_problem& p, bool bwd = false) {
   L.off_part_m = take((size_t)L.parts_max * p.k * sizeof(float));
   if (bwd) {
     const size_t Rk = (size_t)p.num_users * p.k;
-    L.e_waves = (p.k / kProtoPerWave) % 4 == 0 ? 4 : 2;
+    // 8 waves (d = 128 only: one 16-byte load per thread and tile), else 4 or 2
+    L.e_waves = (p.d == 128 && (p.k / kProtoPerWave) % 8 == 0) ? 8 : ((p.k / kProtoPerWave) % 4 == 0 ? 4 : 2);
     L.e_pblocks = p.k / (kProtoPerWave * L.e_waves);
-    L.e_groups = std::max(1, kBwdEWGs / L.e_pblocks);
+    L.e_groups = std::max(1, (L.e_waves == 8 ? kBwdEWGs / 2 : kBwdEWGs) / L.e_pblocks);
     const int64_t rows = std::max<int64_t>((int64_t)Rk, p.k);
     L.o_chunks = (int32_t)((rows + kOuterRows - 1) / kOuterRows);
     L.off_bz32 = take(Rk * p.d * sizeof(float));

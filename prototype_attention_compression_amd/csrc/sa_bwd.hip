@@ -449,7 +449,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
 // A segment's E, rescaled to true units, goes to partial slot group + user
 // (unique among the groups whose ranges meet that user, as in pass 2).
 template <int D, int W>
-__global__ __launch_bounds__(W * 64, 2) void bwd_e(const int32_t* __restrict__ tile_base, Layout L, void* ws) {
+__global__ __launch_bounds__(W * 64, W == 8 ? 1 : 2) void bwd_e(const int32_t* __restrict__ tile_base, Layout L, void* ws) {
   constexpr int S = D / 16, DT = D / 32, PITCH = tile_pitch<D>(), TB = kTile * PITCH, CPR = D / 8;
   constexpr int NT = W * 64;
   constexpr int LPT = kTile * CPR / NT;
@@ -751,7 +751,9 @@ hipError_t launch_bwd_e(const Layout& L, void* ws, hipStream_t stream) {
   const int32_t* tb = hptr<int32_t>(ws, L.off_tile_base);
   const dim3 g((unsigned)grid);
   if (L.d == 128) {
-    if (L.e_waves == 4)
+    if (L.e_waves == 8)
+      hipLaunchKernelGGL((bwd_e<128, 8>), g, dim3(512), 0, stream, tb, L, ws);
+    else if (L.e_waves == 4)
       hipLaunchKernelGGL((bwd_e<128, 4>), g, dim3(256), 0, stream, tb, L, ws);
     else
       hipLaunchKernelGGL((bwd_e<128, 2>), g, dim3(128), 0, stream, tb, L, ws);
