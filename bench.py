@@ -201,7 +201,10 @@ def cpu_baseline_backward(inp, dS, dH_gpu, budget_s: float):
 
 
 def bench_backward(args, inp, torch, dev, sa):
-    """Times sa_compress_backward (forward recomputation included)."""
+    """Times sa_compress_backward (forward recomputation included), or with
+    ``--with-sbar`` sa_compress_backward_with_sbar on the forward's Sbar and
+    masses (computed once before the timed region, as a training step's
+    forward leaves them), plus the forward that writes them, timed apart."""
     from synth import make_sketch_grad
 
     H, off, Wk, Wv, P, mask = _upload(inp, torch, dev)
@@ -222,10 +225,39 @@ def bench_backward(args, inp, torch, dev, sa):
     ptr = sa._lib._ptr
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
+    fwd_ms = None
+    if args.with_sbar:
+        S = torch.empty((R, k, d), dtype=torch.float32, device=dev)
+        mass = torch.empty((R, k), dtype=torch.float32, device=dev)
+        Sbar = torch.empty((R, k, d), dtype=torch.float32, device=dev)
+
+        def fwd():
+            st = sa._lib.raw_compress_with_sbar(pb, ptr(H), ptr(off), ptr(mask), ptr(Wk), ptr(Wv), ptr(P), ptr(S),
+                                                ptr(mass), ptr(Sbar), ptr(ws), ws.numel(), stream, None)
+            if st != sa.SA_OK:
+                raise sa.SaError(st, "sa_compress_with_sbar")
+
+        for _ in range(args.warmup):
+            fwd()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fwd()
+        e1.record()
+        torch.cuda.synchronize()
+        fwd_ms = e0.elapsed_time(e1) / args.steps
+
     def step(events=None):
-        st = sa._lib.raw_compress_backward(pb, ptr(H), ptr(off), ptr(mask), ptr(Wk), ptr(Wv), ptr(P), ptr(dS),
-                                           ptr(dH), ptr(dP), ptr(dWk), ptr(dWv), ptr(ws), ws.numel(), stream,
-                                           events)
+        if args.with_sbar:
+            st = sa._lib.raw_compress_backward_with_sbar(pb, ptr(H), ptr(off), ptr(mask), ptr(Wk), ptr(Wv), ptr(P),
+                                                         ptr(Sbar), ptr(mass), ptr(dS), ptr(dH), ptr(dP), ptr(dWk),
+                                                         ptr(dWv), ptr(ws), ws.numel(), stream, events)
+        else:
+            st = sa._lib.raw_compress_backward(pb, ptr(H), ptr(off), ptr(mask), ptr(Wk), ptr(Wv), ptr(P), ptr(dS),
+                                               ptr(dH), ptr(dP), ptr(dWk), ptr(dWv), ptr(ws), ws.numel(), stream,
+                                               events)
         if st != sa.SA_OK:
             raise sa.SaError(st, "sa_compress_backward")
 
@@ -242,7 +274,7 @@ def bench_backward(args, inp, torch, dev, sa):
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_step = start.elapsed_time(stop) / args.steps
-    phases = ["forward_recompute", "per_user", "dh", "e", "params"]
+    phases = ["forward_pass1" if args.with_sbar else "forward_recompute", "per_user", "dh", "e", "params"]
     phase_ms = {p: 0.0 for p in phases}
     for evs in step_events:
         for i, p in enumerate(phases):
@@ -270,7 +302,8 @@ def bench_backward(args, inp, torch, dev, sa):
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": inp.name, "users": R, "tokens": n_valid, "k": k, "d": d,
-                   "input_dtype": inp.dtype, "parallelism": "single_gpu", "pass": "backward"},
+                   "input_dtype": inp.dtype, "parallelism": "single_gpu",
+                   "pass": "backward_with_sbar" if args.with_sbar else "backward"},
         "tflops": algo_flop / (ms_step * 1e-3) / 1e12,
         "phase_ms": phase_ms,
         "wall_s_timed": t_wall,
@@ -286,6 +319,10 @@ def bench_backward(args, inp, torch, dev, sa):
             "avg_launch_ms": phase_ms["dh"],
         },
     }
+    if fwd_ms is not None:
+        # the training step's forward (sa_compress_with_sbar) and the sum
+        out["forward_with_sbar_ms"] = fwd_ms
+        out["train_step_ms"] = fwd_ms + ms_step
     if args.calibrate_copy:
         _calibration_copy(torch, dev)
     if not args.no_cpu_baseline:
@@ -584,6 +621,9 @@ def main(argv=None):
                     help="cache + sketch-branch attention per serving batch, serial vs overlapped fill")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (gradients through the sketches) instead")
+    ap.add_argument("--with-sbar", action="store_true",
+                    help="with --backward: hand the forward's Sbar and masses to the backward "
+                         "(sa_compress_backward_with_sbar) instead of recomputing its sums")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device once (counter calibration)")
     args = ap.parse_args(argv)

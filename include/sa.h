@@ -176,6 +176,30 @@ sa_status sa_compress_with_events(const sa_problem* problem,
                                   void* const* events);
 
 /*
+ * sa_compress_with_events that also writes the mass-normalised rows
+ *     Sbar [R, k, d] float32,  Sbar_u[j] = (sum_t A[j,t] h_t) / m_j
+ * (0 where m_j = 0), i.e. S_u = Sbar_u Wv before the value projection.  A
+ * training step keeps Sbar and mass and hands both to
+ * sa_compress_backward_with_sbar, which then skips recomputing the per-user
+ * sums.  mass and Sbar must be non-NULL when R > 0 (SA_E_INVALID otherwise);
+ * S, events and everything else as sa_compress_with_events.
+ */
+sa_status sa_compress_with_sbar(const sa_problem* problem,
+                                const void* H,
+                                const int64_t* offsets,
+                                const uint8_t* token_mask,
+                                const void* Wk,
+                                const void* Wv,
+                                const void* P,
+                                float* S,
+                                float* mass,
+                                float* Sbar,
+                                void* workspace,
+                                size_t workspace_bytes,
+                                void* stream,
+                                void* const* events);
+
+/*
  * The backward pass (gradients of a loss through the sketches).
  *
  * SequenceO1 trains the compressor end to end: the blog "100,000 videos in
@@ -254,6 +278,38 @@ sa_status sa_compress_backward_with_events(const sa_problem* problem,
                                            size_t workspace_bytes,
                                            void* stream,
                                            void* const* events);
+
+/*
+ * sa_compress_backward_with_events given the forward's Sbar [R, k, d] and
+ * mass [R, k] (both float32, device, from sa_compress_with_sbar on the same
+ * problem and inputs): the per-user sums are taken from them instead of
+ * being recomputed, which removes the forward's accumulation pass from the
+ * backward (events[1] then marks the end of the per-token logsumexp pass).
+ * The chain rule needs Sbar and m; the per-token allocations are still
+ * recomputed.  Sbar and mass must be non-NULL when R > 0 and
+ * SA_FLAG_REUSE_FORWARD must not be set (SA_E_INVALID).  If they do not come
+ * from the same inputs the gradients are those of a different forward; no
+ * memory outside the stated shapes is read either way.  Same workspace
+ * (sa_backward_workspace_size), outputs, errors and semantics otherwise.
+ */
+sa_status sa_compress_backward_with_sbar(const sa_problem* problem,
+                                         const void* H,
+                                         const int64_t* offsets,
+                                         const uint8_t* token_mask,
+                                         const void* Wk,
+                                         const void* Wv,
+                                         const void* P,
+                                         const float* Sbar,
+                                         const float* mass,
+                                         const float* dS,
+                                         float* dH,
+                                         float* dP,
+                                         float* dWk,
+                                         float* dWv,
+                                         void* workspace,
+                                         size_t workspace_bytes,
+                                         void* stream,
+                                         void* const* events);
 
 /*
  * Sketch-branch target attention with user-level batching.

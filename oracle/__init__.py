@@ -7,6 +7,7 @@ GPU library; the two share only the seeded inputs of ``synth``.
 from .sa_oracle import (  # noqa: F401
     allocations,
     logits,
+    normalised_rows_batch,
     sketch_batch,
     sketch_one,
 )

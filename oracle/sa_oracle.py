@@ -42,7 +42,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["logits", "allocations", "sketch_one", "sketch_batch"]
+__all__ = ["logits", "allocations", "sketch_one", "sketch_batch", "normalised_rows_batch"]
 
 
 def _f64(x) -> np.ndarray:
@@ -121,3 +121,27 @@ def sketch_batch(H, offsets, Wk, Wv, P, mask=None, users=None):
             Hu = Hu[np.asarray(mask[lo:hi]) != 0]
         S[u], m[u] = sketch_one(Hu, Wk, Wv, P)
     return S, m
+
+
+def normalised_rows_batch(H, offsets, Wk, P, mask=None):
+    """The mass-normalised history rows Sbar_u[j] = (sum_t A[j,t] h_t) / m_j
+    of every user (0 where m_j = 0), so that S_u = Sbar_u Wv.  The value
+    projection is linear, so averaging the h rows and then applying Wv equals
+    averaging the v rows (blog "How it works" item 1: the sketch of softly
+    assigned items).  Returns [R, k, d] (fp64)."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    R = offsets.shape[0] - 1
+    k, d = np.shape(P)[0], np.shape(H)[1]
+    out = np.zeros((R, k, d))
+    for u in range(R):
+        lo, hi = int(offsets[u]), int(offsets[u + 1])
+        Hu = _f64(H[lo:hi])
+        if mask is not None:
+            Hu = Hu[np.asarray(mask[lo:hi]) != 0]
+        if Hu.shape[0] == 0:
+            continue
+        A = allocations(logits(Hu, Wk, P))
+        m = A.sum(axis=1)
+        ok = m > 0
+        out[u][ok] = (A @ Hu)[ok] / m[ok, None]
+    return out

@@ -19,8 +19,9 @@ SA_DEVICE_ERR_OFFSETS, SA_DEVICE_ERR_EXCHANGE = 1, 2
 _PATH_FLAGS = {None: 0, "auto": 0, "two": SA_FLAG_TWO_PASS, "one": SA_FLAG_ONE_PASS}
 
 # functions declared in include/sa.h
-EXPORTS = ("sa_workspace_size", "sa_compress", "sa_compress_with_events",
+EXPORTS = ("sa_workspace_size", "sa_compress", "sa_compress_with_events", "sa_compress_with_sbar",
            "sa_backward_workspace_size", "sa_compress_backward", "sa_compress_backward_with_events",
+           "sa_compress_backward_with_sbar",
            "sa_target_attention_workspace_size", "sa_target_attention", "sa_target_attention_rows",
            "sa_cache_create", "sa_cache_destroy", "sa_cache_lookup", "sa_cache_fill_workspace_size",
            "sa_cache_fill",
@@ -80,6 +81,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sa_compress.restype = ctypes.c_int
     lib.sa_compress_with_events.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.sa_compress_with_events.restype = ctypes.c_int
+    lib.sa_compress_with_sbar.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    lib.sa_compress_with_sbar.restype = ctypes.c_int
     lib.sa_backward_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
     lib.sa_backward_workspace_size.restype = ctypes.c_int
     lib.sa_compress_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -87,6 +90,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sa_compress_backward_with_events.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                      vp]
     lib.sa_compress_backward_with_events.restype = ctypes.c_int
+    lib.sa_compress_backward_with_sbar.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                                   vp, vp]
+    lib.sa_compress_backward_with_sbar.restype = ctypes.c_int
     lib.sa_target_attention_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
     lib.sa_target_attention_workspace_size.restype = ctypes.c_int
     lib.sa_target_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -160,6 +166,21 @@ def raw_compress_backward(pb: SaProblem, H, offsets, mask, Wk, Wv, P, dS, dH, dP
                                                        stream, events))
 
 
+def raw_compress_backward_with_sbar(pb: SaProblem, H, offsets, mask, Wk, Wv, P, Sbar, mass, dS, dH, dP, dWk, dWv,
+                                    workspace, workspace_bytes: int, stream, events=None) -> int:
+    """Direct call of sa_compress_backward_with_sbar; returns the status."""
+    return int(load().sa_compress_backward_with_sbar(ctypes.byref(pb), H, offsets, mask, Wk, Wv, P, Sbar, mass, dS,
+                                                     dH, dP, dWk, dWv, workspace, ctypes.c_size_t(workspace_bytes),
+                                                     stream, events))
+
+
+def raw_compress_with_sbar(pb: SaProblem, H, offsets, mask, Wk, Wv, P, S, mass, Sbar, workspace,
+                           workspace_bytes: int, stream, events=None) -> int:
+    """Direct call of sa_compress_with_sbar; returns the status."""
+    return int(load().sa_compress_with_sbar(ctypes.byref(pb), H, offsets, mask, Wk, Wv, P, S, mass, Sbar,
+                                            workspace, ctypes.c_size_t(workspace_bytes), stream, events))
+
+
 def raw_compress(pb: SaProblem, H, offsets, mask, Wk, Wv, P, S, mass, workspace,
                  workspace_bytes: int, stream, events=None) -> int:
     """Direct call with device addresses (or None); returns the status.
@@ -179,7 +200,8 @@ def _ptr(t):
 
 
 def compress(H, offsets, Wk, Wv, P, mask=None, return_mass: bool = False,
-             out=None, mass_out=None, workspace=None, events=None, path: Optional[str] = None):
+             out=None, mass_out=None, workspace=None, events=None, path: Optional[str] = None,
+             return_sbar: bool = False):
     """Sketches of a packed ragged batch, computed by libsa on the GPU.
 
     H [N, d], Wk/Wv [d, d], P [k, d]: torch tensors on the current ROCm device,
@@ -187,7 +209,10 @@ def compress(H, offsets, Wk, Wv, P, mask=None, return_mass: bool = False,
     mask [N] uint8/bool or None.  Returns S [R, k, d] float32 (and the masses
     [R, k] if ``return_mass``).  Runs on torch's current stream.  ``path``:
     None/"auto" (library's choice), "one" or "two" (SA_FLAG_ONE_PASS /
-    SA_FLAG_TWO_PASS).
+    SA_FLAG_TWO_PASS).  ``return_sbar`` (sa_compress_with_sbar): also return
+    the mass-normalised rows Sbar [R, k, d] float32, so that the result is
+    (S, mass, Sbar), the forward state ``compress_backward(sbar=, mass=)``
+    takes.
     """
     import torch
 
@@ -232,9 +257,19 @@ def compress(H, offsets, Wk, Wv, P, mask=None, return_mass: bool = False,
     if S.shape != (R, k, d) or S.dtype != torch.float32 or not S.is_contiguous():
         raise ValueError("out must be a contiguous float32 [R, k, d] tensor")
     m = None
-    if return_mass:
+    if return_mass or return_sbar:
         m = mass_out if mass_out is not None else torch.empty((R, k), dtype=torch.float32, device=dev)
+        if m.shape != (R, k) or m.dtype != torch.float32 or not m.is_contiguous():
+            raise ValueError("mass_out must be a contiguous float32 [R, k] tensor")
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if return_sbar:
+        Sbar = torch.empty((R, k, d), dtype=torch.float32, device=dev)
+        st = raw_compress_with_sbar(pb, _ptr(H) if N > 0 else None, _ptr(offsets), _ptr(mask), _ptr(Wk),
+                                    _ptr(Wv), _ptr(P), _ptr(S), _ptr(m), _ptr(Sbar), _ptr(workspace), wbytes,
+                                    stream, events)
+        if st != SA_OK:
+            raise SaError(st, "sa_compress_with_sbar")
+        return S, m, Sbar
     st = raw_compress(pb, _ptr(H) if N > 0 else None, _ptr(offsets), _ptr(mask), _ptr(Wk), _ptr(Wv),
                       _ptr(P), _ptr(S), _ptr(m), _ptr(workspace), wbytes, stream, events)
     if st != SA_OK:
@@ -255,7 +290,7 @@ def read_device_error(workspace) -> int:
 
 
 def compress_backward(H, offsets, Wk, Wv, P, dS, mask=None, workspace=None, events=None,
-                      reuse_forward: bool = False):
+                      reuse_forward: bool = False, sbar=None, mass=None):
     """Gradients of a loss through the sketches, computed by libsa on the GPU.
 
     Inputs as for ``compress`` (bfloat16 only), plus dS [R, k, d] float32 =
@@ -263,7 +298,10 @@ def compress_backward(H, offsets, Wk, Wv, P, dS, mask=None, workspace=None, even
     float32; dP, dWk and dWv are summed over the users.  Runs on torch's
     current stream.  ``reuse_forward`` (SA_FLAG_REUSE_FORWARD): ``workspace``
     holds the two-pass forward of these same inputs (a ``compress`` call on
-    it just before), which the backward then does not recompute.
+    it just before), which the backward then does not recompute.  ``sbar``
+    and ``mass`` (sa_compress_backward_with_sbar): the forward's Sbar
+    [R, k, d] and masses [R, k] from ``compress(return_sbar=True)`` on the
+    same inputs; the per-user sums are then not recomputed.
     """
     import torch
 
@@ -289,6 +327,17 @@ def compress_backward(H, offsets, Wk, Wv, P, dS, mask=None, workspace=None, even
             mask = mask.view(torch.uint8)
         if mask.dtype != torch.uint8 or mask.shape != (N,) or not mask.is_cuda or not mask.is_contiguous():
             raise ValueError("mask must be a contiguous [N] uint8/bool GPU tensor")
+    if (sbar is None) != (mass is None):
+        raise ValueError("sbar and mass go together")
+    if sbar is not None:
+        if reuse_forward:
+            raise ValueError("sbar/mass and reuse_forward are exclusive")
+        if (sbar.dtype != torch.float32 or sbar.shape != (R, k, d) or mass.dtype != torch.float32
+                or mass.shape != (R, k)):
+            raise ValueError("sbar must be float32 [R, k, d] and mass float32 [R, k]")
+        for name, t in (("sbar", sbar), ("mass", mass)):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous GPU tensor")
     dev = H.device
     pb = problem(R, N, d, k, SA_BF16, SA_FLAG_REUSE_FORWARD if reuse_forward else 0)
     wbytes = backward_workspace_size(R, N, d, k, SA_BF16)
@@ -301,6 +350,14 @@ def compress_backward(H, offsets, Wk, Wv, P, dS, mask=None, workspace=None, even
     dWk = torch.empty((d, d), dtype=torch.float32, device=dev)
     dWv = torch.empty((d, d), dtype=torch.float32, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if sbar is not None:
+        st = raw_compress_backward_with_sbar(pb, _ptr(H) if N > 0 else None, _ptr(offsets), _ptr(mask), _ptr(Wk),
+                                             _ptr(Wv), _ptr(P), _ptr(sbar), _ptr(mass), _ptr(dS),
+                                             _ptr(dH) if N > 0 else None, _ptr(dP), _ptr(dWk), _ptr(dWv),
+                                             _ptr(workspace), wbytes, stream, events)
+        if st != SA_OK:
+            raise SaError(st, "sa_compress_backward_with_sbar")
+        return dH, dP, dWk, dWv
     st = raw_compress_backward(pb, _ptr(H) if N > 0 else None, _ptr(offsets), _ptr(mask), _ptr(Wk), _ptr(Wv),
                                _ptr(P), _ptr(dS), _ptr(dH) if N > 0 else None, _ptr(dP), _ptr(dWk), _ptr(dWv),
                                _ptr(workspace), wbytes, stream, events)

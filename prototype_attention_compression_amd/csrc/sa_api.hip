@@ -203,30 +203,12 @@ bool use_fused(const sa_problem& p, const Layout& L) {
   return device_fits_fused(L);
 }
 
-}  // namespace
-}  // namespace sa
 
-extern "C" {
-
-sa_status sa_workspace_size(const sa_problem* problem, size_t* bytes) {
-  if (bytes == nullptr) return SA_E_INVALID;
-  sa_status st = sa::check_problem(problem);
-  if (st != SA_OK) return st;
-  *bytes = sa::make_layout(*problem).total;
-  return SA_OK;
-}
-
-sa_status sa_compress(const sa_problem* problem, const void* H, const int64_t* offsets, const uint8_t* token_mask,
-                      const void* Wk, const void* Wv, const void* P, float* S, float* mass, void* workspace,
-                      size_t workspace_bytes, void* stream) {
-  return sa_compress_with_events(problem, H, offsets, token_mask, Wk, Wv, P, S, mass, workspace, workspace_bytes,
-                                 stream, nullptr);
-}
-
-sa_status sa_compress_with_events(const sa_problem* problem, const void* H, const int64_t* offsets,
-                                  const uint8_t* token_mask, const void* Wk, const void* Wv, const void* P, float* S,
-                                  float* mass, void* workspace, size_t workspace_bytes, void* stream,
-                                  void* const* events) {
+// The forward: prep, passes 1 and 2 (or the one-pass kernel, or the fp32
+// launcher), finalize.  Sbar (optional) receives the mass-normalised rows.
+sa_status compress_impl(const sa_problem* problem, const void* H, const int64_t* offsets, const uint8_t* token_mask,
+                        const void* Wk, const void* Wv, const void* P, float* S, float* mass, float* Sbar,
+                        void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
   try {
     sa_status st = sa::check_problem(problem);
     if (st != SA_OK) return st;
@@ -265,12 +247,108 @@ sa_status sa_compress_with_events(const sa_problem* problem, const void* H, cons
       if (!mark(2)) return SA_E_HIP;
     }
     if (!mark(3)) return SA_E_HIP;
-    if (sa::launch_finalize(L, Wv, workspace, S, mass, s) != hipSuccess) return SA_E_HIP;
+    if (sa::launch_finalize(L, Wv, workspace, S, mass, Sbar, s) != hipSuccess) return SA_E_HIP;
     if (!mark(4)) return SA_E_HIP;
     return SA_OK;
   } catch (...) {
     return SA_E_HIP;
   }
+}
+
+
+// The backward: forward passes 1 (and 2 unless Sbar_in and mass_in are
+// given), then the per-user, per-token, E and parameter kernels.
+sa_status backward_impl(const sa_problem* problem, const void* H, const int64_t* offsets, const uint8_t* token_mask,
+                        const void* Wk, const void* Wv, const void* P, const float* Sbar_in, const float* mass_in,
+                        const float* dS, float* dH, float* dP, float* dWk, float* dWv, void* workspace,
+                        size_t workspace_bytes, void* stream, void* const* events) {
+  try {
+    sa_status st = sa::check_problem_bwd(problem);
+    if (st != SA_OK) return st;
+    const sa_problem& p = *problem;
+    if (Wk == nullptr || Wv == nullptr || P == nullptr || dP == nullptr || dWk == nullptr || dWv == nullptr)
+      return SA_E_INVALID;
+    if (p.num_users > 0 && (offsets == nullptr || dS == nullptr)) return SA_E_INVALID;
+    if (p.total_tokens > 0 && (H == nullptr || dH == nullptr)) return SA_E_INVALID;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    auto mark = [&](int i) {
+      return events == nullptr || hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s) == hipSuccess;
+    };
+    const int64_t dd = (int64_t)p.d * p.d;
+    if (p.num_users == 0) {   // no users: the parameter gradients are empty sums
+      if (!mark(0)) return SA_E_HIP;
+      if (sa::launch_fill_zero(dP, (int64_t)p.k * p.d, s) != hipSuccess ||
+          sa::launch_fill_zero(dWk, dd, s) != hipSuccess || sa::launch_fill_zero(dWv, dd, s) != hipSuccess)
+        return SA_E_HIP;
+      for (int i = 1; i < SA_NUM_BWD_PHASE_EVENTS; ++i)
+        if (!mark(i)) return SA_E_HIP;
+      return SA_OK;
+    }
+    sa::Layout L = sa::make_layout(p, true);
+    if (workspace == nullptr || workspace_bytes < L.total) return SA_E_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % sa::kAlign != 0) return SA_E_INVALID;
+    if (!mark(0)) return SA_E_HIP;
+    // forward passes 1 and 2: fp16 token rows, logsumexps, partial sums
+    // (already in the workspace when the caller asks to reuse them); pass 2
+    // is not needed when the caller hands in the forward's Sbar and masses
+    const bool reuse = (p.flags & SA_FLAG_REUSE_FORWARD) != 0;
+    if (!reuse && sa::launch_prep(L, P, Wk, offsets, workspace, s) != hipSuccess) return SA_E_HIP;
+    if (!reuse && p.total_tokens > 0) {
+      const hipError_t e = sa::pass1q_ok(L) ? sa::launch_pass1q(L, H, offsets, token_mask, workspace, s)
+                                            : sa::launch_pass1(L, H, offsets, token_mask, workspace, s);
+      if (e != hipSuccess) return SA_E_HIP;
+      if (Sbar_in == nullptr && sa::launch_pass2(L, workspace, s) != hipSuccess) return SA_E_HIP;
+    }
+    if (!mark(1)) return SA_E_HIP;
+    if (sa::launch_bwd_user(L, Wv, dS, Sbar_in, mass_in, workspace, s) != hipSuccess) return SA_E_HIP;
+    if (!mark(2)) return SA_E_HIP;
+    if (sa::launch_bwd_dh(L, offsets, workspace, dH, s) != hipSuccess) return SA_E_HIP;
+    if (!mark(3)) return SA_E_HIP;
+    if (sa::launch_bwd_e(L, workspace, s) != hipSuccess) return SA_E_HIP;
+    if (!mark(4)) return SA_E_HIP;
+    if (sa::launch_bwd_params(L, P, Wk, dS, workspace, dP, dWk, dWv, s) != hipSuccess) return SA_E_HIP;
+    if (!mark(5)) return SA_E_HIP;
+    return SA_OK;
+  } catch (...) {
+    return SA_E_HIP;
+  }
+}
+
+}  // namespace
+}  // namespace sa
+
+extern "C" {
+
+sa_status sa_workspace_size(const sa_problem* problem, size_t* bytes) {
+  if (bytes == nullptr) return SA_E_INVALID;
+  sa_status st = sa::check_problem(problem);
+  if (st != SA_OK) return st;
+  *bytes = sa::make_layout(*problem).total;
+  return SA_OK;
+}
+
+sa_status sa_compress(const sa_problem* problem, const void* H, const int64_t* offsets, const uint8_t* token_mask,
+                      const void* Wk, const void* Wv, const void* P, float* S, float* mass, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return sa_compress_with_events(problem, H, offsets, token_mask, Wk, Wv, P, S, mass, workspace, workspace_bytes,
+                                 stream, nullptr);
+}
+
+sa_status sa_compress_with_events(const sa_problem* problem, const void* H, const int64_t* offsets,
+                                  const uint8_t* token_mask, const void* Wk, const void* Wv, const void* P, float* S,
+                                  float* mass, void* workspace, size_t workspace_bytes, void* stream,
+                                  void* const* events) {
+  return sa::compress_impl(problem, H, offsets, token_mask, Wk, Wv, P, S, mass, nullptr, workspace, workspace_bytes,
+                           stream, events);
+}
+
+sa_status sa_compress_with_sbar(const sa_problem* problem, const void* H, const int64_t* offsets,
+                                const uint8_t* token_mask, const void* Wk, const void* Wv, const void* P, float* S,
+                                float* mass, float* Sbar, void* workspace, size_t workspace_bytes, void* stream,
+                                void* const* events) {
+  if (problem != nullptr && problem->num_users > 0 && (mass == nullptr || Sbar == nullptr)) return SA_E_INVALID;
+  return sa::compress_impl(problem, H, offsets, token_mask, Wk, Wv, P, S, mass, Sbar, workspace, workspace_bytes,
+                           stream, events);
 }
 
 sa_status sa_read_device_error(const void* workspace, void* stream, int32_t* flag) {
@@ -304,55 +382,20 @@ sa_status sa_compress_backward_with_events(const sa_problem* problem, const void
                                            const float* dS, float* dH, float* dP, float* dWk, float* dWv,
                                            void* workspace, size_t workspace_bytes, void* stream,
                                            void* const* events) {
-  try {
-    sa_status st = sa::check_problem_bwd(problem);
-    if (st != SA_OK) return st;
-    const sa_problem& p = *problem;
-    if (Wk == nullptr || Wv == nullptr || P == nullptr || dP == nullptr || dWk == nullptr || dWv == nullptr)
-      return SA_E_INVALID;
-    if (p.num_users > 0 && (offsets == nullptr || dS == nullptr)) return SA_E_INVALID;
-    if (p.total_tokens > 0 && (H == nullptr || dH == nullptr)) return SA_E_INVALID;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    auto mark = [&](int i) {
-      return events == nullptr || hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s) == hipSuccess;
-    };
-    const int64_t dd = (int64_t)p.d * p.d;
-    if (p.num_users == 0) {   // no users: the parameter gradients are empty sums
-      if (!mark(0)) return SA_E_HIP;
-      if (sa::launch_fill_zero(dP, (int64_t)p.k * p.d, s) != hipSuccess ||
-          sa::launch_fill_zero(dWk, dd, s) != hipSuccess || sa::launch_fill_zero(dWv, dd, s) != hipSuccess)
-        return SA_E_HIP;
-      for (int i = 1; i < SA_NUM_BWD_PHASE_EVENTS; ++i)
-        if (!mark(i)) return SA_E_HIP;
-      return SA_OK;
-    }
-    sa::Layout L = sa::make_layout(p, true);
-    if (workspace == nullptr || workspace_bytes < L.total) return SA_E_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(workspace) % sa::kAlign != 0) return SA_E_INVALID;
-    if (!mark(0)) return SA_E_HIP;
-    // forward passes 1 and 2: fp16 token rows, logsumexps, partial sums
-    // (already in the workspace when the caller asks to reuse them)
-    const bool reuse = (p.flags & SA_FLAG_REUSE_FORWARD) != 0;
-    if (!reuse && sa::launch_prep(L, P, Wk, offsets, workspace, s) != hipSuccess) return SA_E_HIP;
-    if (!reuse && p.total_tokens > 0) {
-      const hipError_t e = sa::pass1q_ok(L) ? sa::launch_pass1q(L, H, offsets, token_mask, workspace, s)
-                                            : sa::launch_pass1(L, H, offsets, token_mask, workspace, s);
-      if (e != hipSuccess) return SA_E_HIP;
-      if (sa::launch_pass2(L, workspace, s) != hipSuccess) return SA_E_HIP;
-    }
-    if (!mark(1)) return SA_E_HIP;
-    if (sa::launch_bwd_user(L, Wv, dS, workspace, s) != hipSuccess) return SA_E_HIP;
-    if (!mark(2)) return SA_E_HIP;
-    if (sa::launch_bwd_dh(L, offsets, workspace, dH, s) != hipSuccess) return SA_E_HIP;
-    if (!mark(3)) return SA_E_HIP;
-    if (sa::launch_bwd_e(L, workspace, s) != hipSuccess) return SA_E_HIP;
-    if (!mark(4)) return SA_E_HIP;
-    if (sa::launch_bwd_params(L, P, Wk, dS, workspace, dP, dWk, dWv, s) != hipSuccess) return SA_E_HIP;
-    if (!mark(5)) return SA_E_HIP;
-    return SA_OK;
-  } catch (...) {
-    return SA_E_HIP;
-  }
+  return sa::backward_impl(problem, H, offsets, token_mask, Wk, Wv, P, nullptr, nullptr, dS, dH, dP, dWk, dWv,
+                           workspace, workspace_bytes, stream, events);
+}
+
+sa_status sa_compress_backward_with_sbar(const sa_problem* problem, const void* H, const int64_t* offsets,
+                                         const uint8_t* token_mask, const void* Wk, const void* Wv, const void* P,
+                                         const float* Sbar, const float* mass, const float* dS, float* dH, float* dP,
+                                         float* dWk, float* dWv, void* workspace, size_t workspace_bytes,
+                                         void* stream, void* const* events) {
+  if (problem == nullptr) return SA_E_INVALID;
+  if (problem->flags & SA_FLAG_REUSE_FORWARD) return SA_E_INVALID;
+  if (problem->num_users > 0 && (Sbar == nullptr || mass == nullptr)) return SA_E_INVALID;
+  return sa::backward_impl(problem, H, offsets, token_mask, Wk, Wv, P, Sbar, mass, dS, dH, dP, dWk, dWv, workspace,
+                           workspace_bytes, stream, events);
 }
 
 sa_status sa_target_attention_workspace_size(const sa_problem* problem, size_t* bytes) {

@@ -92,8 +92,11 @@ __device__ __forceinline__ float negl_of(uint32_t w) {
 }  // namespace
 
 // ---------------------------------------------------------------- per user
+// Sbar_in / mass_in (optional): the forward's mass-normalised rows and
+// masses of these inputs, given instead of pass 2's partial sums.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_user(const uint16_t* __restrict__ Wv, const float* __restrict__ dS,
+                                                const float* __restrict__ Sbar_in, const float* __restrict__ mass_in,
                                                 Layout L, void* ws) {
   constexpr int PER = kRows * D / 256;
   constexpr int RPI = 256 / D;
@@ -105,41 +108,47 @@ __global__ __launch_bounds__(256) void bwd_user(const uint16_t* __restrict__ Wv,
   const int u = blockIdx.x / nrb, rb = blockIdx.x % nrb;
   const int j0 = rb * kRows;
   const int tid = threadIdx.x;
-  // the user's partial slots: group + u for the pass-2 groups whose tile
-  // ranges meet the user's tiles
-  const int32_t* tile_base = ws_i32(ws, L.off_tile_base);
-  const int32_t nt = ws_i32(ws, L.off_hdr)[kHdrTiles];
-  const int G = L.p2_groups;
-  const int32_t Tg = (nt + 4 * G - 1) / (4 * G) * 4;
-  const int32_t t0 = tile_base[u], t1 = tile_base[u + 1];
-  int c0 = 0, c1 = 0;
-  if (t1 > t0) {
-    c0 = t0 / Tg + u;
-    c1 = (t1 - 1) / Tg + 1 + u;
-  }
-  const float* part_u = ws_f32(ws, L.off_part_u);
-  const float* part_m = ws_f32(ws, L.off_part_m);
+  const int64_t row0 = (int64_t)u * L.k + j0;
   float acc[PER];
+  if (Sbar_in == nullptr) {
+    // the user's partial slots: group + u for the pass-2 groups whose tile
+    // ranges meet the user's tiles
+    const int32_t* tile_base = ws_i32(ws, L.off_tile_base);
+    const int32_t nt = ws_i32(ws, L.off_hdr)[kHdrTiles];
+    const int G = L.p2_groups;
+    const int32_t Tg = (nt + 4 * G - 1) / (4 * G) * 4;
+    const int32_t t0 = tile_base[u], t1 = tile_base[u + 1];
+    int c0 = 0, c1 = 0;
+    if (t1 > t0) {
+      c0 = t0 / Tg + u;
+      c1 = (t1 - 1) / Tg + 1 + u;
+    }
+    const float* part_u = ws_f32(ws, L.off_part_u);
+    const float* part_m = ws_f32(ws, L.off_part_m);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  for (int c = c0; c < c1; ++c) {
-    const float* base = part_u + ((int64_t)c * L.k + j0) * D;
+    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+    for (int c = c0; c < c1; ++c) {
+      const float* base = part_u + ((int64_t)c * L.k + j0) * D;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
-  }
-  if (tid < kRows) {
-    float m = 0.f;
-    for (int c = c0; c < c1; ++c) m += part_m[(int64_t)c * L.k + j0 + tid];
-    ms[tid] = m;   // 2^14 m (the allocations of pass 2 carry 2^14)
+      for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
+    }
+    if (tid < kRows) {
+      float m = 0.f;
+      for (int c = c0; c < c1; ++c) m += part_m[(int64_t)c * L.k + j0 + tid];
+      ms[tid] = m;   // 2^14 m (the allocations of pass 2 carry 2^14)
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] = Sbar_in[row0 * D + tid + 256 * i];
+    if (tid < kRows) ms[tid] = mass_in[row0 + tid] * kScaleMax;   // 2^14 m, as above
   }
   __syncthreads();
-  const int64_t row0 = (int64_t)u * L.k + j0;
   float* sbar = ws_f32(ws, L.off_bsbar) + row0 * D;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = tid + 256 * i, j = e / D, a = e % D;
     const float m = ms[j];
-    const float v = m > 0.f ? acc[i] / m : 0.f;
+    const float v = m > 0.f ? (Sbar_in == nullptr ? acc[i] / m : acc[i]) : 0.f;
     sb[j][a] = v;
     sbar[e] = v;
     gz[j][a] = m > 0.f ? dS[row0 * D + e] * (kScaleMax / m) : 0.f;
@@ -720,15 +729,18 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_user(const Layout& L, const void* Wv, const float* dS, void* ws, hipStream_t stream) {
+hipError_t launch_bwd_user(const Layout& L, const void* Wv, const float* dS, const float* Sbar_in,
+                           const float* mass_in, void* ws, hipStream_t stream) {
   const int64_t grid = (int64_t)L.R * (L.k / kRows);
   if (grid == 0) return hipSuccess;
   if (L.d == 128) {
-    hipLaunchKernelGGL((bwd_user<128>), dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)Wv, dS, L, ws);
+    hipLaunchKernelGGL((bwd_user<128>), dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)Wv, dS, Sbar_in,
+                       mass_in, L, ws);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL((bwd_zpack<128>), dim3((unsigned)grid), dim3(256), 0, stream, L, ws);
   } else {
-    hipLaunchKernelGGL((bwd_user<64>), dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)Wv, dS, L, ws);
+    hipLaunchKernelGGL((bwd_user<64>), dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)Wv, dS, Sbar_in,
+                       mass_in, L, ws);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL((bwd_zpack<64>), dim3((unsigned)grid), dim3(256), 0, stream, L, ws);
   }

@@ -32,7 +32,8 @@ __device__ __forceinline__ float wv_load<float>(const float* p, int64_t i) {
 
 template <int D, typename T>
 __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout L, void* ws, float* __restrict__ S,
-                                                float* __restrict__ mass, float mass_scale) {
+                                                float* __restrict__ mass, float* __restrict__ Sbar,
+                                                float mass_scale) {
   constexpr int PER = kFinRows * D / 256;   // elements per thread
   constexpr int RPI = 256 / D;              // rows per output pass
   __shared__ float sh[kFinRows][D + 1];
@@ -82,7 +83,9 @@ __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout
   for (int i = 0; i < PER; ++i) {
     const int e = tid + 256 * i, j = e / D, a = e % D;
     const float m = ms[j];
-    sh[j][a] = m > 0.f ? acc[i] / m : 0.f;
+    const float v = m > 0.f ? acc[i] / m : 0.f;
+    sh[j][a] = v;
+    if (Sbar != nullptr) Sbar[((int64_t)u * L.k + j0) * D + e] = v;   // the mass-normalised rows
   }
   __syncthreads();
   const int c = tid % D, jr = tid / D;
@@ -100,24 +103,25 @@ __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout
   if (mass != nullptr && tid < kFinRows) mass[(int64_t)u * L.k + j0 + tid] = ms[tid] * mass_scale;
 }
 
-hipError_t launch_finalize(const Layout& L, const void* Wv, void* ws, float* S, float* mass, hipStream_t stream) {
+hipError_t launch_finalize(const Layout& L, const void* Wv, void* ws, float* S, float* mass, float* Sbar,
+                           hipStream_t stream) {
   const int64_t grid = (int64_t)L.R * (L.k / kFinRows);
   if (grid == 0) return hipSuccess;
   if (L.dtype == 0) {
     const float scale = 1.0f / 16384.0f;  // allocations were scaled by 2^14
     if (L.d == 128)
       hipLaunchKernelGGL((finalize<128, uint16_t>), dim3((unsigned)grid), dim3(256), 0, stream,
-                         (const uint16_t*)Wv, L, ws, S, mass, scale);
+                         (const uint16_t*)Wv, L, ws, S, mass, Sbar, scale);
     else
       hipLaunchKernelGGL((finalize<64, uint16_t>), dim3((unsigned)grid), dim3(256), 0, stream,
-                         (const uint16_t*)Wv, L, ws, S, mass, scale);
+                         (const uint16_t*)Wv, L, ws, S, mass, Sbar, scale);
   } else {
     if (L.d == 128)
       hipLaunchKernelGGL((finalize<128, float>), dim3((unsigned)grid), dim3(256), 0, stream, (const float*)Wv, L,
-                         ws, S, mass, 1.0f);
+                         ws, S, mass, Sbar, 1.0f);
     else
       hipLaunchKernelGGL((finalize<64, float>), dim3((unsigned)grid), dim3(256), 0, stream, (const float*)Wv, L,
-                         ws, S, mass, 1.0f);
+                         ws, S, mass, Sbar, 1.0f);
   }
   return hipGetLastError();
 }

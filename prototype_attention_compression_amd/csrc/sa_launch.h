@@ -34,10 +34,11 @@ bool fused_shape_ok(const Layout& L);
 bool fused_fits_device(const Layout& L, int device);
 hipError_t launch_fused(const Layout& L, void* ws, hipStream_t stream);
 // partial-sum reduction, prototype-wise normalisation and the value projection
-hipError_t launch_finalize(const Layout& L, const void* Wv, void* ws, float* S, float* mass,
+hipError_t launch_finalize(const Layout& L, const void* Wv, void* ws, float* S, float* mass, float* Sbar,
                            hipStream_t stream);
 // backward (bf16): per-user Z, c and scales from pass 2's partial sums and dS
-hipError_t launch_bwd_user(const Layout& L, const void* Wv, const float* dS, void* ws, hipStream_t stream);
+hipError_t launch_bwd_user(const Layout& L, const void* Wv, const float* dS, const float* Sbar_in,
+                           const float* mass_in, void* ws, hipStream_t stream);
 // backward: token-major dH (and the per-token delta the E pass reads)
 hipError_t launch_bwd_dh(const Layout& L, const int64_t* offsets, void* ws, float* dH, hipStream_t stream);
 // backward: prototype-major partial E = sum_t dL h_t

@@ -206,3 +206,50 @@ def test_reuse_forward_flag_is_backward_only():
     # switched off (see the note on SA_FLAG_REUSE_FORWARD in include/sa.h)
     assert _bws(1, 10, 128, 1024, 0, flags=sa.SA_FLAG_REUSE_FORWARD)[0] == sa.SA_E_UNSUPPORTED
     assert _bws(1, 10, 128, 1024, 0, flags=sa.SA_FLAG_REUSE_FORWARD | sa.SA_FLAG_ONE_PASS)[0] == sa.SA_E_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- forward state for the backward
+def test_compress_with_sbar_argument_errors_before_launch():
+    pb = _lib.problem(2, 100, 128, 256, 0)
+
+    def call(pb, mass=FAKE, Sbar=FAKE, ws=FAKE, wsb=1 << 40, S=FAKE):
+        return _lib.raw_compress_with_sbar(pb, FAKE, FAKE, None, FAKE, FAKE, FAKE, S, mass, Sbar, ws, wsb, None)
+
+    assert call(pb, mass=None) == sa.SA_E_INVALID
+    assert call(pb, Sbar=None) == sa.SA_E_INVALID
+    assert call(pb, S=None) == sa.SA_E_INVALID
+    assert call(pb, ws=None) == sa.SA_E_WORKSPACE
+    assert call(_lib.problem(2, 100, 96, 256, 0)) == sa.SA_E_UNSUPPORTED
+    # R = 0 is a no-op whatever the pointers
+    assert call(_lib.problem(0, 0, 128, 256, 0), mass=None, Sbar=None, S=None, ws=None, wsb=0) == sa.SA_OK
+    assert _lib.load().sa_compress_with_sbar(None, *([None] * 10), 0, None, None) == sa.SA_E_INVALID
+
+
+def test_backward_with_sbar_argument_errors_before_launch():
+    pb = _lib.problem(2, 100, 128, 256, 0)
+
+    def call(pb, Sbar=FAKE, mass=FAKE, ws=FAKE, wsb=1 << 40, **kw):
+        a = dict(H=FAKE, off=FAKE, Wk=FAKE, Wv=FAKE, P=FAKE, dS=FAKE, dH=FAKE, dP=FAKE, dWk=FAKE, dWv=FAKE)
+        a.update(kw)
+        return _lib.raw_compress_backward_with_sbar(pb, a["H"], a["off"], None, a["Wk"], a["Wv"], a["P"], Sbar,
+                                                    mass, a["dS"], a["dH"], a["dP"], a["dWk"], a["dWv"], ws, wsb,
+                                                    None)
+
+    assert call(pb, Sbar=None) == sa.SA_E_INVALID
+    assert call(pb, mass=None) == sa.SA_E_INVALID
+    for name in ("off", "H", "Wk", "Wv", "P", "dS", "dH", "dP", "dWk", "dWv"):
+        assert call(pb, **{name: None}) == sa.SA_E_INVALID, name
+    assert call(pb, ws=None) == sa.SA_E_WORKSPACE
+    need = _bws(2, 100, 128, 256, 0)[1]
+    assert call(pb, wsb=need - 1) == sa.SA_E_WORKSPACE
+    assert call(_lib.problem(2, 100, 128, 256, 0, sa.SA_FLAG_REUSE_FORWARD)) == sa.SA_E_INVALID
+    assert call(_lib.problem(2, 100, 128, 256, sa.SA_F32)) == sa.SA_E_UNSUPPORTED
+    assert _lib.load().sa_compress_backward_with_sbar(None, *([None] * 14), 0, None, None) == sa.SA_E_INVALID
+
+
+def test_sbar_binding_validates_before_library():
+    import torch
+    H = torch.zeros(4, 128, dtype=torch.bfloat16)
+    off = torch.tensor([0, 4])
+    with pytest.raises(ValueError):   # sbar without mass
+        sa.compress_backward(H, off, H[:0], H[:0], H[:0], torch.zeros(1, 1, 128), sbar=torch.zeros(1, 1, 128))

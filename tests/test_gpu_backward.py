@@ -12,7 +12,7 @@ zero."""
 import numpy as np
 import pytest
 
-from oracle import sketch_batch_grad
+from oracle import normalised_rows_batch, sketch_batch, sketch_batch_grad
 from synth import make_config, make_inputs, make_sketch_grad
 from tests.gpu_util import TOL, rel_errors, upload
 
@@ -166,6 +166,97 @@ def test_backward_ragged_training_batch_sampled():
     inp = make_config("c3_r40_ragged_d128_k1024")
     users = [int(np.argmin(inp.lengths)), int(np.argmax(inp.lengths))]
     _check(inp, make_sketch_grad(inp.R, inp.k, inp.d, seed=5900, users=users), users=users)
+
+
+# ------------------------------------------------ the forward's state handed to the backward
+@pytest.mark.parametrize("d,k", [(64, 320), (128, 1024)])
+def test_forward_sbar_matches_oracle(d, k):
+    """sa_compress_with_sbar: S and mass equal sa_compress's bit for bit, and
+    Sbar matches the oracle's mass-normalised rows (same bar as S)."""
+    import torch
+
+    import prototype_attention_compression_amd as sa
+    inp = make_inputs([0, 1, 700, 2049, 33], d=d, k=k, seed=6000 + d, mask_tail_frac=0.1, name=f"sbar_d{d}")
+    print(f"[case] forward with Sbar R={inp.R} N={inp.N} k={k} d={d}", flush=True)
+    dev = upload(inp)
+    args = (dev["H"], dev["offsets"], dev["Wk"], dev["Wv"], dev["P"])
+    S0, m0 = sa.compress(*args, mask=dev["mask"], return_mass=True)
+    S, m, Sbar = sa.compress(*args, mask=dev["mask"], return_sbar=True)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S0) and torch.equal(m, m0)
+    ref = normalised_rows_batch(inp.H, inp.offsets, inp.Wk, inp.P, mask=inp.mask)
+    mx, mean = rel_errors(Sbar.cpu().numpy(), ref)
+    print(f"   Sbar: max_rel={mx:.3e} mean_rel={mean:.3e}", flush=True)
+    tmax, tmean = TOL["bf16"]
+    assert mx <= tmax and mean <= tmean
+    Sref, _ = sketch_batch(inp.H, inp.offsets, inp.Wk, inp.Wv, inp.P, mask=inp.mask)
+    mx, mean = rel_errors(Sbar.cpu().numpy().astype(np.float64) @ inp.Wv, Sref)
+    assert mx <= tmax and mean <= tmean
+    assert not Sbar[0].any() and not m[0].any()    # the empty user
+
+
+@pytest.mark.parametrize("d,k", [(64, 320), (128, 1024)])
+def test_backward_with_sbar_equals_recompute(d, k):
+    """sa_compress_backward_with_sbar on the forward's Sbar and masses gives
+    the same gradients, bit for bit, as the backward that recomputes the
+    per-user sums (the same fixed-order sums and divisions either way), and
+    they meet the gradient oracle's bar."""
+    import torch
+
+    import prototype_attention_compression_amd as sa
+    inp = make_inputs([3000, 0, 17, 2500, 1], d=d, k=k, seed=6100 + d, mask_tail_frac=0.1, name=f"sbar_bwd_d{d}")
+    print(f"[case] backward with Sbar R={inp.R} N={inp.N} k={k} d={d}", flush=True)
+    dev = upload(inp)
+    args = (dev["H"], dev["offsets"], dev["Wk"], dev["Wv"], dev["P"])
+    dS_np = make_sketch_grad(inp.R, k, d, seed=6200 + d)
+    dS = torch.from_numpy(dS_np).to("cuda")
+    ref = sa.compress_backward(*args, dS, mask=dev["mask"])
+    _, m, Sbar = sa.compress(*args, mask=dev["mask"], return_sbar=True)
+    got = sa.compress_backward(*args, dS, mask=dev["mask"], sbar=Sbar, mass=m)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dH", "dP", "dWk", "dWv"), ref, got):
+        assert torch.equal(a, b), name
+    oref = sketch_batch_grad(inp.H, inp.offsets, inp.Wk, inp.Wv, inp.P, dS_np, mask=inp.mask)
+    tmax, tmean = TOL["bf16"]
+    for name, g, r in zip(("dH", "dP", "dWk", "dWv"), got, oref):
+        mx, mean = rel_errors(g.cpu().numpy(), r)
+        print(f"   {name}: max_rel={mx:.3e} mean_rel={mean:.3e}", flush=True)
+        assert mx <= tmax and mean <= tmean, (name, mx, mean)
+
+
+def test_backward_with_sbar_bench_workload_sampled():
+    """40 users x 100,000 tokens, k = 1024, d = 128, the forward state from
+    sa_compress_with_sbar, dS nonzero for users 5 and 31 only."""
+    import torch
+
+    import prototype_attention_compression_amd as sa
+    inp = make_config("c3lit_r40_n100k_d128_k1024")
+    users = [5, 31]
+    print(f"[case] backward with Sbar {inp.name} users={users}", flush=True)
+    dev = upload(inp)
+    args = (dev["H"], dev["offsets"], dev["Wk"], dev["Wv"], dev["P"])
+    dS_np = make_sketch_grad(inp.R, inp.k, inp.d, seed=6300, users=users)
+    _, m, Sbar = sa.compress(*args, mask=dev["mask"], return_sbar=True)
+    del _
+    dH, dP, dWk, dWv = sa.compress_backward(*args, torch.from_numpy(dS_np).to("cuda"), mask=dev["mask"],
+                                            sbar=Sbar, mass=m)
+    torch.cuda.synchronize()
+    sel = sorted(users)
+    rows = np.concatenate([np.arange(inp.offsets[u], inp.offsets[u + 1]) for u in sel])
+    lens = [int(inp.offsets[u + 1] - inp.offsets[u]) for u in sel]
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    mask = None if inp.mask is None else inp.mask[rows]
+    ref = sketch_batch_grad(inp.H[rows], off, inp.Wk, inp.Wv, inp.P, dS_np[sel], mask=mask)
+    dH = dH.cpu().numpy()
+    other = np.ones(inp.N, dtype=bool)
+    other[rows] = False
+    assert not dH[other].any()
+    tmax, tmean = TOL["bf16"]
+    for name, g, r in zip(("dH", "dP", "dWk", "dWv"), (dH[rows], dP.cpu().numpy(), dWk.cpu().numpy(),
+                                                       dWv.cpu().numpy()), ref):
+        mx, mean = rel_errors(g, r)
+        print(f"   {name}: max_rel={mx:.3e} mean_rel={mean:.3e}", flush=True)
+        assert mx <= tmax and mean <= tmean, (name, mx, mean)
 
 
 @pytest.mark.skip(reason="SA_FLAG_REUSE_FORWARD is switched off: the GPU run that first exercised it "

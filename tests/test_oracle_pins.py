@@ -254,3 +254,24 @@ def test_planted_transpose_is_caught_by_golden():
     o = json.load(open(os.path.join(GOLDEN, "hand_d2.json")))
     S_bad, _ = sketch_one(o["H"], np.array(o["Wk"]).T, o["Wv"], o["P"])
     assert np.abs(S_bad - np.array(_frac(o["expected_S"]))).max() > 1e-3
+
+
+def test_normalised_rows_times_wv_is_the_sketch():
+    """Sbar Wv = S for every user (the value projection is linear), with
+    masked tokens, an empty user and a one-token user."""
+    from oracle import normalised_rows_batch
+    g = np.random.default_rng(77)
+    lens = [9, 0, 1, 14]
+    off = np.concatenate([[0], np.cumsum(lens)])
+    d, k = 5, 6
+    H = g.standard_normal((off[-1], d))
+    Wk, Wv, P = g.standard_normal((d, d)), g.standard_normal((d, d)), g.standard_normal((k, d))
+    mask = (g.random(off[-1]) > 0.3).astype(np.uint8)
+    Sbar = normalised_rows_batch(H, off, Wk, P, mask)
+    S, _ = sketch_batch(H, off, Wk, Wv, P, mask)
+    np.testing.assert_allclose(Sbar @ Wv, S, rtol=1e-12, atol=1e-13)
+    assert not Sbar[1].any()
+    # one token: every prototype's weighted mean is that token's row
+    i = int(off[2])
+    if mask[i]:
+        np.testing.assert_allclose(Sbar[2], np.tile(H[i], (k, 1)), rtol=1e-13)
