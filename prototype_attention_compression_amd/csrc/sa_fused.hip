@@ -84,7 +84,6 @@ constexpr int kXWave = kWaves - 1;
 constexpr int kNB = 2;            // 32-prototype blocks per wave
 constexpr int kStageTiles = 4;
 constexpr int kBufs = 4;
-constexpr int kLag = 3;           // GEMM2 of tile i runs in iteration i + kLag
 constexpr int kPSlots = 4;        // LDS slots of per-wave partials
 constexpr int kSpinMax = 1 << 18; // bound on every wait on LDS (about 20 ms)
 constexpr int kPollMax = 1 << 16; // bound on every wait on another workgroup (about 0.1 s)
