@@ -53,27 +53,42 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "history tokens/s + TFLOP/s (%bf16 MFMA peak), SA n=100K,k=1024,d=128"
 DEFAULT_WORKLOAD = "c3lit_r40_n100k_d128_k1024"
 
-# HBM bytes per pass-2 launch on the default workload: rocprofv3 --pmc
-# FETCH_SIZE + WRITE_SIZE (KiB per dispatch), each scaled by what the same
-# counter reads for a plain device copy of known size (--calibrate-copy).
-# Valid only for the kernel source it was measured on: the digest of the
-# pass-2 sources is recorded beside it and the figure is reported as null
-# once they differ.
-PASS2_TRAFFIC_BYTES = 1126671448      # 1.0702e9 fetched + 0.0565e9 written
-PASS2_TRAFFIC_SOURCES_SHA256 = "106926115929e4c35f66bb44da9f6cb58f6424a9449823e6a4de3926fbb74eed"
-PASS2_SOURCES = ("sa_pass2.hip", "sa_layout.h", "sa_device.h")
+# HBM bytes per launch of each bench mode's dominant kernel on that mode's
+# workload: rocprofv3 --pmc FETCH_SIZE + WRITE_SIZE (KiB per dispatch), each
+# scaled by what the same counter reads for a plain device copy of known size
+# (--calibrate-copy).  A figure is valid only for the kernel source it was
+# measured on: the sha256 of the kernel's sources is recorded beside it and
+# the figure is reported as null once they differ.
 COPY_CALIBRATION_BYTES = 1 << 30
+TRAFFIC = {
+    # 1.0702e9 fetched + 0.0565e9 written (40 x 100K tokens, k = 1024, d = 128)
+    "pass2_accum": (1126671448, "106926115929e4c35f66bb44da9f6cb58f6424a9449823e6a4de3926fbb74eed",
+                    ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
+    # 1.308e9 fetched + 2.068e9 written (same workload, --backward)
+    "bwd_dh": (3376019593, "1342d878d261aed6f6699e99dfabbe8f196779b267e9646083df909352a96347",
+               ("sa_bwd.hip", "sa_layout.h", "sa_device.h")),
+    # 1.862e8 fetched + 0.461e8 written (300 users x 300 candidates, --target-attention)
+    "ta_attend": (232284006, "5baccbb48a7aadc0f935ccfaec6d6a621cc3c9799c13818aa00a4800c7dd9e1b",
+                  ("sa_target.hip", "sa_layout.h", "sa_device.h")),
+}
 
 
-def pass2_sources_digest() -> str:
+def sources_digest(names) -> str:
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "prototype_attention_compression_amd", "csrc")
-    for name in PASS2_SOURCES:
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """Counter-measured HBM bytes per launch of ``kernel``, or None when its
+    sources changed since the counters were taken."""
+    nbytes, digest, names = TRAFFIC[kernel]
+    return nbytes if sources_digest(names) == digest else None
 
 
 class _Hip:
@@ -314,7 +329,7 @@ def bench_backward(args, inp, torch, dev, sa):
             "peak": PEAK_MFMA_F16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": dh_achieved / PEAK_MFMA_F16_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic("bwd_dh") if inp.name == DEFAULT_WORKLOAD else None,
             "per_launch_flop": dh_flop,
             "avg_launch_ms": phase_ms["dh"],
         },
@@ -392,7 +407,7 @@ def bench_target(args, torch, dev, sa):
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": gbs / PEAK_HBM_GBS,
-            "traffic": None,
+            "traffic": measured_traffic("ta_attend"),
             "per_launch_bytes": nbytes,
             "avg_launch_ms": ms_step,
         },
@@ -704,7 +719,8 @@ def main(argv=None):
         "peak": PEAK_MFMA_F16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": p2_achieved / PEAK_MFMA_F16_TFLOPS,
-        "traffic": PASS2_TRAFFIC_BYTES if PASS2_TRAFFIC_SOURCES_SHA256 == pass2_sources_digest() else None,
+        # counters were taken on the default workload's two-pass kernels
+        "traffic": measured_traffic("pass2_accum") if inp.name == DEFAULT_WORKLOAD and args.path != "one" else None,
         "per_launch_flop": algo_flop,
         "avg_launch_ms": phase_ms["pass2_accum"],
     }
