@@ -108,19 +108,20 @@ sa_status sa_workspace_size(const sa_problem* problem, size_t* bytes);
 /*
  * Compress a ragged batch of R user histories into R sketches.
  *
- *   H           [N, d] row-major, dtype `problem->dtype`.  User u owns rows
- *               offsets[u] .. offsets[u+1]-1.  For SA_BF16, magnitudes of
- *               unmasked entries must be below 65504: they are widened
- *               exactly to fp16 MFMA operands, larger ones saturate.
+ *   H           [N, d] row-major, dtype `problem->dtype`, 16-byte aligned.
+ *               User u owns rows offsets[u] .. offsets[u+1]-1.  For SA_BF16,
+ *               magnitudes of unmasked entries must be below 65504: they are
+ *               widened exactly to fp16 MFMA operands, larger ones saturate.
  *   offsets     [R+1] int64, 0 = offsets[0] <= offsets[1] <= ... <= offsets[R]
- *               = N.  Device memory.  If the sequence breaks this contract
+ *               = N.  Device memory, 8-byte aligned.  If the sequence breaks this contract
  *               the kernels treat every user as empty (S = 0, mass = 0) and
  *               raise the device error flag read by sa_read_device_error.
  *   token_mask  [N] uint8, 1 = keep the token, 0 = drop it entirely (it takes
  *               no part in allocation, mass or sums; NaN in a dropped row
  *               does not propagate).  NULL keeps every token.
- *   Wk, Wv      [d, d] row-major, K = H Wk and V = H Wv.
- *   P           [k, d] row-major prototypes.
+ *   Wk, Wv      [d, d] row-major, K = H Wk and V = H Wv, 16-byte aligned.
+ *   P           [k, d] row-major prototypes, 16-byte aligned.
+ *               (A misaligned H, Wk, Wv, P or offsets is SA_E_INVALID.)
  *   S           [R, k, d] float32 output, fully overwritten.
  *   mass        [R, k] float32 output m_j (fully overwritten), or NULL.
  *   workspace   device scratch of at least sa_workspace_size bytes, 256-byte

@@ -21,6 +21,8 @@ constexpr int64_t kMaxUsers = (int64_t)1 << 28;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
 sa_status check_problem(const sa_problem* p) {
   if (p == nullptr) return SA_E_INVALID;
   if (p->num_users < 0 || p->total_tokens < 0 || p->d <= 0 || p->k <= 0) return SA_E_INVALID;
@@ -217,6 +219,10 @@ sa_status compress_impl(const sa_problem* problem, const void* H, const int64_t*
     if (offsets == nullptr || Wk == nullptr || Wv == nullptr || P == nullptr || S == nullptr)
       return SA_E_INVALID;
     if (p.total_tokens > 0 && H == nullptr) return SA_E_INVALID;
+    // the kernels read H, Wk, Wv and P in 16-byte vectors and offsets as int64
+    if (!aligned16(H) || !aligned16(Wk) || !aligned16(Wv) || !aligned16(P) ||
+        reinterpret_cast<uintptr_t>(offsets) % 8 != 0)
+      return SA_E_INVALID;
     sa::Layout L = sa::make_layout(p);
     if (workspace == nullptr || workspace_bytes < L.total) return SA_E_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % sa::kAlign != 0) return SA_E_INVALID;
@@ -270,6 +276,9 @@ sa_status backward_impl(const sa_problem* problem, const void* H, const int64_t*
       return SA_E_INVALID;
     if (p.num_users > 0 && (offsets == nullptr || dS == nullptr)) return SA_E_INVALID;
     if (p.total_tokens > 0 && (H == nullptr || dH == nullptr)) return SA_E_INVALID;
+    if (!aligned16(H) || !aligned16(Wk) || !aligned16(Wv) || !aligned16(P) ||
+        reinterpret_cast<uintptr_t>(offsets) % 8 != 0)
+      return SA_E_INVALID;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     auto mark = [&](int i) {
       return events == nullptr || hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s) == hipSuccess;

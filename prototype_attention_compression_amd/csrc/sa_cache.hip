@@ -273,6 +273,10 @@ sa_status sa_cache_fill(sa_cache* c, const sa_problem* store, const void* H_stor
     if (store->k != c->k || store->d != c->d || store->num_users <= 0) return SA_E_INVALID;
     if (n_miss > 65535) return SA_E_UNSUPPORTED;   // one scatter grid row per miss
     if (reinterpret_cast<uintptr_t>(H_store) % 16 != 0) return SA_E_INVALID;
+    if (Wk == nullptr || Wv == nullptr || P == nullptr) return SA_E_INVALID;
+    if (reinterpret_cast<uintptr_t>(Wk) % 16 != 0 || reinterpret_cast<uintptr_t>(Wv) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(P) % 16 != 0)
+      return SA_E_INVALID;
     // host: the miss batch's layout from the store's (host) offsets
     std::vector<int64_t> src_start((size_t)n_miss), dst_off((size_t)n_miss + 1);
     dst_off[0] = 0;

@@ -20,28 +20,42 @@
 namespace sa {
 
 template <typename T>
-__device__ __forceinline__ float wv_load(const T* p, int64_t i);
+__device__ __forceinline__ float wv_value(T v);
 template <>
-__device__ __forceinline__ float wv_load<uint16_t>(const uint16_t* p, int64_t i) {
-  return __uint_as_float(((uint32_t)p[i]) << 16);
+__device__ __forceinline__ float wv_value<uint16_t>(uint16_t v) {
+  return __uint_as_float(((uint32_t)v) << 16);
 }
 template <>
-__device__ __forceinline__ float wv_load<float>(const float* p, int64_t i) {
-  return p[i];
+__device__ __forceinline__ float wv_value<float>(float v) {
+  return v;
 }
 
+// One workgroup = one user and kFinRows prototypes.  Wv (D x D) is staged in
+// LDS once per workgroup with all of its 16-byte loads in flight together, and
+// the partial slots are read four at a time (the sums still run in slot
+// order): both loops would otherwise wait on one global load per step.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout L, void* ws, float* __restrict__ S,
                                                 float* __restrict__ mass, float* __restrict__ Sbar,
                                                 float mass_scale) {
   constexpr int PER = kFinRows * D / 256;   // elements per thread
   constexpr int RPI = 256 / D;              // rows per output pass
+  constexpr int WCH = D * D * (int)sizeof(T) / 16 / 256;   // 16-byte chunks of Wv per thread
+  static_assert(WCH * 256 * 16 == D * D * (int)sizeof(T), "whole chunks");
   __shared__ float sh[kFinRows][D + 1];
   __shared__ float ms[kFinRows];
+  __shared__ __attribute__((aligned(16))) T wsh[D * D];
   const int nrb = L.k / kFinRows;
   const int u = blockIdx.x / nrb, rb = blockIdx.x % nrb;
   const int j0 = rb * kFinRows;
   const int tid = threadIdx.x;
+  {
+    u32x4 w[WCH];
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) w[i] = reinterpret_cast<const u32x4*>(Wv)[tid + 256 * i];
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) reinterpret_cast<u32x4*>(wsh)[tid + 256 * i] = w[i];
+  }
   // the user's partial-sum slots: chunks c0 .. c1-1 (fp32 path), or
   // group + u for the groups g0 .. g1-1 whose tile ranges meet the user's
   // (bf16: pass 2 and the one-pass kernel walk equal tile ranges per group)
@@ -68,14 +82,28 @@ __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  for (int c = c0; c < c1; ++c) {
+  int c = c0;
+  for (; c + 4 <= c1; c += 4) {
+    float v[4][PER];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float* base = part_u + ((int64_t)(c + q) * L.k + j0) * D;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) v[q][i] = base[tid + 256 * i];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] += v[q][i];
+  }
+  for (; c < c1; ++c) {
     const float* base = part_u + ((int64_t)c * L.k + j0) * D;
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
   }
   if (tid < kFinRows) {
     float m = 0.f;
-    for (int c = c0; c < c1; ++c) m += part_m[(int64_t)c * L.k + j0 + tid];
+    for (int cc = c0; cc < c1; ++cc) m += part_m[(int64_t)cc * L.k + j0 + tid];
     ms[tid] = m;
   }
   __syncthreads();
@@ -88,18 +116,19 @@ __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout
     if (Sbar != nullptr) Sbar[((int64_t)u * L.k + j0) * D + e] = v;   // the mass-normalised rows
   }
   __syncthreads();
-  const int c = tid % D, jr = tid / D;
+  const int cl = tid % D, jr = tid / D;
   float out[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) out[i] = 0.f;
+#pragma unroll 4
   for (int a = 0; a < D; ++a) {
-    const float w = wv_load<T>(Wv, (int64_t)a * D + c);
+    const float w = wv_value<T>(wsh[a * D + cl]);
 #pragma unroll
     for (int i = 0; i < PER; ++i) out[i] = fmaf(sh[jr + RPI * i][a], w, out[i]);
   }
   float* dst = S + ((int64_t)u * L.k + j0) * D;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) dst[(int64_t)(jr + RPI * i) * D + c] = out[i];
+  for (int i = 0; i < PER; ++i) dst[(int64_t)(jr + RPI * i) * D + cl] = out[i];
   if (mass != nullptr && tid < kFinRows) mass[(int64_t)u * L.k + j0 + tid] = ms[tid] * mass_scale;
 }
 

@@ -253,3 +253,14 @@ def test_sbar_binding_validates_before_library():
     off = torch.tensor([0, 4])
     with pytest.raises(ValueError):   # sbar without mass
         sa.compress_backward(H, off, H[:0], H[:0], H[:0], torch.zeros(1, 1, 128), sbar=torch.zeros(1, 1, 128))
+
+
+def test_misaligned_inputs_rejected_before_launch():
+    """H, Wk, Wv and P are read in 16-byte vectors and offsets as int64: a
+    misaligned pointer is an argument error, caught on the host."""
+    pb = _lib.problem(2, 100, 128, 256, 0)
+    for name in ("H", "Wk", "Wv", "P"):
+        assert _call(pb, **{name: FAKE + 2}) == sa.SA_E_INVALID, name
+        assert _bcall(pb, **{name: FAKE + 8}) == sa.SA_E_INVALID, name
+    assert _call(pb, off=FAKE + 4) == sa.SA_E_INVALID
+    assert _bcall(pb, off=FAKE + 4) == sa.SA_E_INVALID
