@@ -57,6 +57,7 @@ namespace {
 constexpr int kRows = 32;                         // prototypes per bwd_user workgroup
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kScaleMax = 16384.0f;             // 2^14
+constexpr int kSlotBatch = 4;                     // partial slots whose loads are in flight together
 
 __device__ __forceinline__ float bf16f(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
 
@@ -127,14 +128,30 @@ __global__ __launch_bounds__(256) void bwd_user(const uint16_t* __restrict__ Wv,
     const float* part_m = ws_f32(ws, L.off_part_m);
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-    for (int c = c0; c < c1; ++c) {
+    // kSlotBatch slots' loads in flight at a time; the sums run in slot
+    // order, as in the forward's finalize (the same values to the bit)
+    int c = c0;
+    for (; c + kSlotBatch <= c1; c += kSlotBatch) {
+      float v[kSlotBatch][PER];
+#pragma unroll
+      for (int q = 0; q < kSlotBatch; ++q) {
+        const float* base = part_u + ((int64_t)(c + q) * L.k + j0) * D;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v[q][i] = base[tid + 256 * i];
+      }
+#pragma unroll
+      for (int q = 0; q < kSlotBatch; ++q)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] += v[q][i];
+    }
+    for (; c < c1; ++c) {
       const float* base = part_u + ((int64_t)c * L.k + j0) * D;
 #pragma unroll
       for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
     }
     if (tid < kRows) {
       float m = 0.f;
-      for (int c = c0; c < c1; ++c) m += part_m[(int64_t)c * L.k + j0 + tid];
+      for (int cc = c0; cc < c1; ++cc) m += part_m[(int64_t)cc * L.k + j0 + tid];
       ms[tid] = m;   // 2^14 m (the allocations of pass 2 carry 2^14)
     }
   } else {
@@ -159,10 +176,15 @@ __global__ __launch_bounds__(256) void bwd_user(const uint16_t* __restrict__ Wv,
   float z[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) z[i] = 0.f;
-  const uint4* wrow = reinterpret_cast<const uint4*>(Wv + (int64_t)a * D);
+  // the thread's row of Wv, all of its loads in flight together
+  const u32x4* wrow = reinterpret_cast<const u32x4*>(Wv + (int64_t)a * D);
+  u32x4 wr[D / 8];
+#pragma unroll
+  for (int b8 = 0; b8 < D / 8; ++b8) wr[b8] = wrow[b8];
+#pragma unroll
   for (int b8 = 0; b8 < D / 8; ++b8) {
-    const uint4 w = wrow[b8];
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    const u32x4 w = wr[b8];
+    const uint32_t ww[4] = {w[0], w[1], w[2], w[3]};
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const float wlo = __uint_as_float(ww[h] << 16), whi = __uint_as_float(ww[h] & 0xffff0000u);

@@ -14,10 +14,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "sa_device.h"
 #include "sa_launch.h"
 
 namespace sa {
+
+namespace {
+constexpr int kSlotBatch = 4;   // partial slots whose loads are in flight together
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+}  // namespace
 
 template <typename T>
 __device__ __forceinline__ float wv_value(T v);
@@ -32,7 +39,7 @@ __device__ __forceinline__ float wv_value<float>(float v) {
 
 // One workgroup = one user and kFinRows prototypes.  Wv (D x D) is staged in
 // LDS once per workgroup with all of its 16-byte loads in flight together, and
-// the partial slots are read four at a time (the sums still run in slot
+// the partial slots are read kSlotBatch at a time (the sums still run in slot
 // order): both loops would otherwise wait on one global load per step.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout L, void* ws, float* __restrict__ S,
@@ -42,9 +49,13 @@ __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout
   constexpr int RPI = 256 / D;              // rows per output pass
   constexpr int WCH = D * D * (int)sizeof(T) / 16 / 256;   // 16-byte chunks of Wv per thread
   static_assert(WCH * 256 * 16 == D * D * (int)sizeof(T), "whole chunks");
+  constexpr bool kMfma = std::is_same<T, uint16_t>::value;
+  // bf16 Wv: staged transposed, Wv^T[n][k] with a padded pitch, as the B
+  // operand of the value projection on MFMAs; fp32 Wv: staged as it is
+  constexpr int WP = kMfma ? D + 8 : D;
   __shared__ float sh[kFinRows][D + 1];
   __shared__ float ms[kFinRows];
-  __shared__ __attribute__((aligned(16))) T wsh[D * D];
+  __shared__ __attribute__((aligned(16))) T wsh[D * WP];
   const int nrb = L.k / kFinRows;
   const int u = blockIdx.x / nrb, rb = blockIdx.x % nrb;
   const int j0 = rb * kFinRows;
@@ -54,7 +65,17 @@ __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout
 #pragma unroll
     for (int i = 0; i < WCH; ++i) w[i] = reinterpret_cast<const u32x4*>(Wv)[tid + 256 * i];
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) reinterpret_cast<u32x4*>(wsh)[tid + 256 * i] = w[i];
+    for (int i = 0; i < WCH; ++i) {
+      if constexpr (kMfma) {
+        // chunk q = row k, columns n0 .. n0 + 7
+        const int q = tid + 256 * i, k = q / (D / 8), n0 = 8 * (q % (D / 8));
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          wsh[(n0 + e) * WP + k] = (uint16_t)(w[i][e >> 1] >> (16 * (e & 1)));
+      } else {
+        reinterpret_cast<u32x4*>(wsh)[tid + 256 * i] = w[i];
+      }
+    }
   }
   // the user's partial-sum slots: chunks c0 .. c1-1 (fp32 path), or
   // group + u for the groups g0 .. g1-1 whose tile ranges meet the user's
@@ -83,16 +104,16 @@ __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   int c = c0;
-  for (; c + 4 <= c1; c += 4) {
-    float v[4][PER];
+  for (; c + kSlotBatch <= c1; c += kSlotBatch) {
+    float v[kSlotBatch][PER];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kSlotBatch; ++q) {
       const float* base = part_u + ((int64_t)(c + q) * L.k + j0) * D;
 #pragma unroll
       for (int i = 0; i < PER; ++i) v[q][i] = base[tid + 256 * i];
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < kSlotBatch; ++q)
 #pragma unroll
       for (int i = 0; i < PER; ++i) acc[i] += v[q][i];
   }
@@ -116,19 +137,51 @@ __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout
     if (Sbar != nullptr) Sbar[((int64_t)u * L.k + j0) * D + e] = v;   // the mass-normalised rows
   }
   __syncthreads();
-  const int cl = tid % D, jr = tid / D;
-  float out[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) out[i] = 0.f;
-#pragma unroll 4
-  for (int a = 0; a < D; ++a) {
-    const float w = wv_value<T>(wsh[a * D + cl]);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) out[i] = fmaf(sh[jr + RPI * i][a], w, out[i]);
-  }
   float* dst = S + ((int64_t)u * L.k + j0) * D;
+  if constexpr (kMfma) {
+    // S rows = Sbar rows x Wv: wave w takes output columns 32 w .. 32 w + 31
+    // (D = 64: waves 0 and 1).  Wv is exact in bf16; each fp32 Sbar value is
+    // split into three bf16 terms hi + mid + lo (24 significant bits, as
+    // fp32), so the products carry fp32 accuracy with fp32 sums.
+    const int lane = tid & 63, wave = tid >> 6, col = lane & 31, g = lane >> 5;
+    if (32 * wave < D) {   // uniform over the wave
+      float16v acc = float16v{};
 #pragma unroll
-  for (int i = 0; i < PER; ++i) dst[(int64_t)(jr + RPI * i) * D + cl] = out[i];
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int k0 = 16 * ks + 8 * g;
+        bf16x8 hi, mid, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = sh[col][k0 + e];
+          const __bf16 h = (__bf16)x;
+          const float r1 = x - (float)h;
+          const __bf16 m1 = (__bf16)r1;
+          hi[e] = h;
+          mid[e] = m1;
+          lo[e] = (__bf16)(r1 - (float)m1);
+        }
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(&wsh[(32 * wave + col) * WP + k0]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, b, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dst[(int64_t)acc_row(r, g) * D + 32 * wave + col] = acc[r];
+    }
+  } else {
+    const int cl = tid % D, jr = tid / D;
+    float out[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) out[i] = 0.f;
+#pragma unroll 4
+    for (int a = 0; a < D; ++a) {
+      const float w = wv_value<T>(wsh[a * D + cl]);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) out[i] = fmaf(sh[jr + RPI * i][a], w, out[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) dst[(int64_t)(jr + RPI * i) * D + cl] = out[i];
+  }
   if (mass != nullptr && tid < kFinRows) mass[(int64_t)u * L.k + j0 + tid] = ms[tid] * mass_scale;
 }
 
