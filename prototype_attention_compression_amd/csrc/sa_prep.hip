@@ -34,17 +34,36 @@ template <int D, typename T>
 __global__ __launch_bounds__(256) void prep_queries(const T* __restrict__ P, const T* __restrict__ Wk,
                                                     Layout L, void* ws) {
   constexpr int PR = 256 / D;
+  // Wk staged in LDS with all of its 16-byte loads in flight together (a
+  // row-per-thread walk through global memory waited on each load); the
+  // padded pitch keeps the row-per-thread LDS reads on distinct banks
+  constexpr int EPC = 16 / (int)sizeof(T);                 // elements per 16-byte chunk
+  constexpr int WCH = D * D / EPC / 256;                   // chunks per thread
+  constexpr int WP = D + (sizeof(T) == 2 ? 2 : 1);
+  static_assert(WCH * 256 * EPC == D * D, "whole chunks");
   __shared__ float prow[PR][D];
   __shared__ float red[256];
+  __shared__ T wk[D * WP];
   const int tid = threadIdx.x;
+  {
+    u32x4 w[WCH];
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) w[i] = reinterpret_cast<const u32x4*>(Wk)[tid + 256 * i];
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) {
+      const int q = tid + 256 * i, row = q / (D / EPC), e0 = EPC * (q % (D / EPC));
+      const T* v = reinterpret_cast<const T*>(&w[i]);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) wk[row * WP + e0 + e] = v[e];
+    }
+  }
   const int jl = tid / D, c = tid % D;
   const int j = blockIdx.x * PR + jl;
   prow[jl][c] = load_in<T>(P, (int64_t)j * D + c);
   __syncthreads();
   float acc = 0.f;
-  const int64_t wrow = (int64_t)c * D;
 #pragma unroll 8
-  for (int a = 0; a < D; ++a) acc = fmaf(prow[jl][a], load_in<T>(Wk, wrow + a), acc);
+  for (int a = 0; a < D; ++a) acc = fmaf(prow[jl][a], load_in<T>(wk, c * WP + a), acc);
   const float scale = 1.4426950408889634f / sqrtf((float)D);
   const float q = acc * scale;
   if (L.dtype == 1) {
