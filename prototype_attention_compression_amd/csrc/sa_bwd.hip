@@ -622,32 +622,73 @@ __global__ __launch_bounds__(W * 64, W == 8 ? 1 : 2) void bwd_e(const int32_t* _
 // E = sum over the (group, user) partial slots (users, then groups, in
 // order: bitwise repeatable), and dP = E Wk / sqrt(d)
 template <int D>
-__global__ __launch_bounds__(256) void bwd_ereduce(const uint16_t* __restrict__ Wk, Layout L, void* ws,
+__global__ __launch_bounds__(256) void bwd_ereduce(const uint16_t* __restrict__ Wk,
+                                                   const int32_t* __restrict__ tile_base, Layout L, void* ws,
                                                    float* __restrict__ dP) {
   constexpr int PER = kRows * D / 256;
   constexpr int RPI = 256 / D;
+  constexpr int WCH = D * D / 8 / 256;   // 16-byte chunks of Wk per thread
   __shared__ float es[kRows][D + 1];
+  __shared__ __attribute__((aligned(16))) uint16_t wk[D * D];
   const int j0 = blockIdx.x * kRows, tid = threadIdx.x;
+  {
+    // Wk staged in LDS, all of its loads in flight together
+    u32x4 w[WCH];
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) w[i] = reinterpret_cast<const u32x4*>(Wk)[tid + 256 * i];
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) reinterpret_cast<u32x4*>(wk)[tid + 256 * i] = w[i];
+  }
   const float* ep = ws_f32(ws, L.off_bepart);
   float* et = ws_f32(ws, L.off_betot) + (int64_t)j0 * D;
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   // the slots bwd_e wrote: group + u for every group whose tile range meets
-  // user u's tiles (users in order, then groups in order)
-  const int32_t* tile_base = ws_i32(ws, L.off_tile_base);
+  // user u's tiles, walked users in order, then groups in order, with the
+  // loads of kSlotBatch consecutive slots of that walk in flight together
   const int32_t T = ws_i32(ws, L.off_hdr)[kHdrTiles];
   const int G = L.e_groups;
   const int32_t Tg = (T + 4 * G - 1) / (4 * G) * 4;
-  for (int u = 0; u < L.R; ++u) {
-    const int32_t t0 = tile_base[u], t1 = tile_base[u + 1];
-    if (t1 <= t0) continue;
-    const int c1 = (t1 - 1) / Tg + 1 + u;
-    for (int c = t0 / Tg + u; c < c1; ++c) {
-      const float* base = ep + ((int64_t)c * L.k + j0) * D;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
+  int u = 0, c = 0, cend = 0;   // next user to open; the open user's remaining slots [c, cend)
+  auto seek = [&]() {
+    while (c >= cend) {
+      if (u >= L.R) return false;
+      const int32_t t0 = tile_base[u], t1 = tile_base[u + 1];
+      if (t1 > t0) {
+        c = t0 / Tg + u;
+        cend = (t1 - 1) / Tg + 1 + u;
+      }
+      ++u;
     }
+    return true;
+  };
+  for (;;) {
+    int sl[kSlotBatch];
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < kSlotBatch; ++q) {
+      sl[q] = 0;
+      if (n == q && seek()) {
+        sl[q] = c++;
+        ++n;
+      }
+    }
+    if (n == 0) break;
+    float v[kSlotBatch][PER];
+#pragma unroll
+    for (int q = 0; q < kSlotBatch; ++q) {
+      if (q < n) {
+        const float* base = ep + ((int64_t)sl[q] * L.k + j0) * D;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v[q][i] = base[tid + 256 * i];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kSlotBatch; ++q)
+      if (q < n)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] += v[q][i];
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -660,8 +701,9 @@ __global__ __launch_bounds__(256) void bwd_ereduce(const uint16_t* __restrict__ 
   float out[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) out[i] = 0.f;
+#pragma unroll 4
   for (int a = 0; a < D; ++a) {
-    const float w = bf16f(Wk[(int64_t)a * D + b]);
+    const float w = bf16f(wk[a * D + b]);
 #pragma unroll
     for (int i = 0; i < PER; ++i) out[i] = fmaf(es[jr + RPI * i][a], w, out[i]);
   }
@@ -680,27 +722,37 @@ __device__ __forceinline__ float ld_any<uint16_t>(const uint16_t* p, int64_t i) 
 // part[c][a][b] = sum over rows i of chunk c of X[i][a] Y[i][b]
 template <int D, typename TY>
 __global__ __launch_bounds__(256) void bwd_outer(const float* __restrict__ X, const TY* __restrict__ Y, int64_t rows,
-                                                 float* __restrict__ part) {
+                                                 int chunk_rows, float* __restrict__ part) {
   constexpr int TA = D / 16;           // outputs per thread: TA x TA
   constexpr int RB = 32;               // rows staged per round
+  constexpr int SL = RB * D / 256;     // staged elements per thread and operand
   __shared__ float xs[RB][D];
   __shared__ float ys[RB][D];
   const int tid = threadIdx.x;
   const int a0 = (tid >> 4) * TA, b0 = (tid & 15) * TA;
-  const int64_t r0 = (int64_t)blockIdx.x * kOuterRows;
-  const int64_t r1 = min(rows, r0 + kOuterRows);
+  const int64_t r0 = (int64_t)blockIdx.x * chunk_rows;
+  const int64_t r1 = min(rows, r0 + chunk_rows);
   float acc[TA][TA];
 #pragma unroll
   for (int i = 0; i < TA; ++i)
 #pragma unroll
     for (int j = 0; j < TA; ++j) acc[i][j] = 0.f;
   for (int64_t rb = r0; rb < r1; rb += RB) {
-    for (int e = tid; e < RB * D; e += 256) {
-      const int rr = e / D, cc = e % D;
+    // every load of the round in flight before the LDS stores
+    float xv_[SL], yv_[SL];
+#pragma unroll
+    for (int q = 0; q < SL; ++q) {
+      const int e = tid + 256 * q, rr = e / D, cc = e % D;
       const int64_t row = rb + rr;
       const bool ok = row < r1;
-      xs[rr][cc] = ok ? X[row * D + cc] : 0.f;
-      ys[rr][cc] = ok ? ld_any<TY>(Y, row * D + cc) : 0.f;
+      xv_[q] = ok ? X[row * D + cc] : 0.f;
+      yv_[q] = ok ? ld_any<TY>(Y, row * D + cc) : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < SL; ++q) {
+      const int e = tid + 256 * q, rr = e / D, cc = e % D;
+      xs[rr][cc] = xv_[q];
+      ys[rr][cc] = yv_[q];
     }
     __syncthreads();
     for (int rr = 0; rr < RB; ++rr) {
@@ -808,20 +860,26 @@ hipError_t launch_bwd_params(const Layout& L, const void* P, const void* Wk, con
   float* et = hptr<float>(ws, L.off_betot);
   float* op = hptr<float>(ws, L.off_bopart);
   const float* sbar = hptr<float>(ws, L.off_bsbar);
+  const int32_t* tb = hptr<const int32_t>(ws, L.off_tile_base);
   // E and dP
   if (D == 128)
-    hipLaunchKernelGGL((bwd_ereduce<128>), dim3(L.k / kRows), dim3(256), 0, stream, (const uint16_t*)Wk, L, ws, dP);
+    hipLaunchKernelGGL((bwd_ereduce<128>), dim3(L.k / kRows), dim3(256), 0, stream, (const uint16_t*)Wk, tb, L, ws,
+                       dP);
   else
-    hipLaunchKernelGGL((bwd_ereduce<64>), dim3(L.k / kRows), dim3(256), 0, stream, (const uint16_t*)Wk, L, ws, dP);
+    hipLaunchKernelGGL((bwd_ereduce<64>), dim3(L.k / kRows), dim3(256), 0, stream, (const uint16_t*)Wk, tb, L, ws,
+                       dP);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  // dWk = E^T P / sqrt(d)
-  const int ck = (L.k + kOuterRows - 1) / kOuterRows;
+  // dWk = E^T P / sqrt(d): k rows in as many chunks of a multiple of 32 rows
+  // as the partial buffer holds (o_chunks >= k / 256)
+  const int64_t per = (L.k + L.o_chunks - 1) / L.o_chunks;
+  const int rk = (int)std::max<int64_t>(32, (per + 31) / 32 * 32);
+  const int ck = (L.k + rk - 1) / rk;
   if (D == 128)
     hipLaunchKernelGGL((bwd_outer<128, uint16_t>), dim3(ck), dim3(256), 0, stream, (const float*)et,
-                       (const uint16_t*)P, (int64_t)L.k, op);
+                       (const uint16_t*)P, (int64_t)L.k, rk, op);
   else
     hipLaunchKernelGGL((bwd_outer<64, uint16_t>), dim3(ck), dim3(256), 0, stream, (const float*)et,
-                       (const uint16_t*)P, (int64_t)L.k, op);
+                       (const uint16_t*)P, (int64_t)L.k, rk, op);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL(bwd_sum, gsum, dim3(256), 0, stream, (const float*)op, ck, dd, 1.0f / sqrtf((float)D), dWk);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
@@ -830,9 +888,10 @@ hipError_t launch_bwd_params(const Layout& L, const void* P, const void* Wk, con
   const int cv = (int)((rows + kOuterRows - 1) / kOuterRows);
   if (cv > 0) {
     if (D == 128)
-      hipLaunchKernelGGL((bwd_outer<128, float>), dim3(cv), dim3(256), 0, stream, sbar, dS, rows, op);
+      hipLaunchKernelGGL((bwd_outer<128, float>), dim3(cv), dim3(256), 0, stream, sbar, dS, rows, (int)kOuterRows,
+                         op);
     else
-      hipLaunchKernelGGL((bwd_outer<64, float>), dim3(cv), dim3(256), 0, stream, sbar, dS, rows, op);
+      hipLaunchKernelGGL((bwd_outer<64, float>), dim3(cv), dim3(256), 0, stream, sbar, dS, rows, (int)kOuterRows, op);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   hipLaunchKernelGGL(bwd_sum, gsum, dim3(256), 0, stream, (const float*)op, cv, dd, 1.0f, dWv);
