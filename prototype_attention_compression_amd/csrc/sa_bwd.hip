@@ -781,8 +781,17 @@ __global__ __launch_bounds__(256) void bwd_sum(const float* __restrict__ part, i
                                                float* __restrict__ out) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= n) return;
+  // chunk order, with eight chunks' loads in flight at a time
   float s = 0.f;
-  for (int c = 0; c < n_chunks; ++c) s += part[(int64_t)c * n + e];
+  int c = 0;
+  for (; c + 8 <= n_chunks; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = part[(int64_t)(c + q) * n + e];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s += v[q];
+  }
+  for (; c < n_chunks; ++c) s += part[(int64_t)c * n + e];
   out[e] = s * scale;
 }
 
