@@ -62,19 +62,27 @@ __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout
   const int tid = threadIdx.x;
   {
     u32x4 w[WCH];
+    if constexpr (kMfma) {
+      // thread chunk i: row k = q % D, columns n0 .. n0 + 7 (n0 = 8 (q / D)),
+      // so the lanes of a wave write consecutive k of one transposed row:
+      // no LDS bank conflicts
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) w[i] = reinterpret_cast<const u32x4*>(Wv)[tid + 256 * i];
+      for (int i = 0; i < WCH; ++i) {
+        const int q = tid + 256 * i, k = q % D, n0 = 8 * (q / D);
+        w[i] = reinterpret_cast<const u32x4*>(Wv)[k * (D / 8) + n0 / 8];
+      }
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) {
-      if constexpr (kMfma) {
-        // chunk q = row k, columns n0 .. n0 + 7
-        const int q = tid + 256 * i, k = q / (D / 8), n0 = 8 * (q % (D / 8));
+      for (int i = 0; i < WCH; ++i) {
+        const int q = tid + 256 * i, k = q % D, n0 = 8 * (q / D);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           wsh[(n0 + e) * WP + k] = (uint16_t)(w[i][e >> 1] >> (16 * (e & 1)));
-      } else {
-        reinterpret_cast<u32x4*>(wsh)[tid + 256 * i] = w[i];
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < WCH; ++i) w[i] = reinterpret_cast<const u32x4*>(Wv)[tid + 256 * i];
+#pragma unroll
+      for (int i = 0; i < WCH; ++i) reinterpret_cast<u32x4*>(wsh)[tid + 256 * i] = w[i];
     }
   }
   // the user's partial-sum slots: chunks c0 .. c1-1 (fp32 path), or
