@@ -49,6 +49,7 @@
 
 #include "sa_device.h"
 #include "sa_launch.h"
+#include "sa_slots.h"
 
 namespace sa {
 
@@ -98,7 +99,7 @@ __device__ __forceinline__ float negl_of(uint32_t w) {
 template <int D>
 __global__ __launch_bounds__(256) void bwd_user(const uint16_t* __restrict__ Wv, const float* __restrict__ dS,
                                                 const float* __restrict__ Sbar_in, const float* __restrict__ mass_in,
-                                                Layout L, void* ws) {
+                                                Layout L, void* ws, int presummed) {
   constexpr int PER = kRows * D / 256;
   constexpr int RPI = 256 / D;
   __shared__ float sb[kRows][D + 1];   // U / m
@@ -112,46 +113,57 @@ __global__ __launch_bounds__(256) void bwd_user(const uint16_t* __restrict__ Wv,
   const int64_t row0 = (int64_t)u * L.k + j0;
   float acc[PER];
   if (Sbar_in == nullptr) {
-    // the user's partial slots: group + u for the pass-2 groups whose tile
-    // ranges meet the user's tiles
-    const int32_t* tile_base = ws_i32(ws, L.off_tile_base);
-    const int32_t nt = ws_i32(ws, L.off_hdr)[kHdrTiles];
-    const int G = L.p2_groups;
-    const int32_t Tg = (nt + 4 * G - 1) / (4 * G) * 4;
-    const int32_t t0 = tile_base[u], t1 = tile_base[u + 1];
-    int c0 = 0, c1 = 0;
-    if (t1 > t0) {
-      c0 = t0 / Tg + u;
-      c1 = (t1 - 1) / Tg + 1 + u;
-    }
+    // the user's partial slots, or the heads of their pre-summed sub-ranges,
+    // added in slot order exactly as the forward's finalize adds them (the
+    // same values to the bit)
+    int c0, c1;
+    user_slots(L, ws, u, c0, c1);
+    const int n = c1 - c0;
+    const bool pre = presummed && n > kPreMin;
     const float* part_u = ws_f32(ws, L.off_part_u);
     const float* part_m = ws_f32(ws, L.off_part_m);
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-    // kSlotBatch slots' loads in flight at a time; the sums run in slot
-    // order, as in the forward's finalize (the same values to the bit)
-    int c = c0;
-    for (; c + kSlotBatch <= c1; c += kSlotBatch) {
-      float v[kSlotBatch][PER];
+    if (pre) {
+      float v[kPreSplit][PER];
 #pragma unroll
-      for (int q = 0; q < kSlotBatch; ++q) {
-        const float* base = part_u + ((int64_t)(c + q) * L.k + j0) * D;
+      for (int q = 0; q < kPreSplit; ++q) {
+        const float* base = part_u + ((int64_t)sub_head(c0, n, q) * L.k + j0) * D;
 #pragma unroll
         for (int i = 0; i < PER; ++i) v[q][i] = base[tid + 256 * i];
       }
 #pragma unroll
-      for (int q = 0; q < kSlotBatch; ++q)
+      for (int q = 0; q < kPreSplit; ++q)
 #pragma unroll
         for (int i = 0; i < PER; ++i) acc[i] += v[q][i];
-    }
-    for (; c < c1; ++c) {
-      const float* base = part_u + ((int64_t)c * L.k + j0) * D;
+    } else {
+      int c = c0;
+      for (; c + kSlotBatch <= c1; c += kSlotBatch) {
+        float v[kSlotBatch][PER];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
+        for (int q = 0; q < kSlotBatch; ++q) {
+          const float* base = part_u + ((int64_t)(c + q) * L.k + j0) * D;
+#pragma unroll
+          for (int i = 0; i < PER; ++i) v[q][i] = base[tid + 256 * i];
+        }
+#pragma unroll
+        for (int q = 0; q < kSlotBatch; ++q)
+#pragma unroll
+          for (int i = 0; i < PER; ++i) acc[i] += v[q][i];
+      }
+      for (; c < c1; ++c) {
+        const float* base = part_u + ((int64_t)c * L.k + j0) * D;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
+      }
     }
     if (tid < kRows) {
       float m = 0.f;
-      for (int cc = c0; cc < c1; ++cc) m += part_m[(int64_t)cc * L.k + j0 + tid];
+      if (pre) {
+        for (int q = 0; q < kPreSplit; ++q) m += part_m[(int64_t)sub_head(c0, n, q) * L.k + j0 + tid];
+      } else {
+        for (int cc = c0; cc < c1; ++cc) m += part_m[(int64_t)cc * L.k + j0 + tid];
+      }
       ms[tid] = m;   // 2^14 m (the allocations of pass 2 carry 2^14)
     }
   } else {
@@ -816,14 +828,17 @@ hipError_t launch_bwd_user(const Layout& L, const void* Wv, const float* dS, con
                            const float* mass_in, void* ws, hipStream_t stream) {
   const int64_t grid = (int64_t)L.R * (L.k / kRows);
   if (grid == 0) return hipSuccess;
+  // the partial slots are reduced as the forward's finalize reduces them
+  const int pre = (Sbar_in == nullptr && presum_launch(L)) ? 1 : 0;
+  if (pre && launch_presum(L, ws, stream) != hipSuccess) return hipErrorLaunchFailure;
   if (L.d == 128) {
     hipLaunchKernelGGL((bwd_user<128>), dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)Wv, dS, Sbar_in,
-                       mass_in, L, ws);
+                       mass_in, L, ws, pre);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL((bwd_zpack<128>), dim3((unsigned)grid), dim3(256), 0, stream, L, ws);
   } else {
     hipLaunchKernelGGL((bwd_user<64>), dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)Wv, dS, Sbar_in,
-                       mass_in, L, ws);
+                       mass_in, L, ws, pre);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL((bwd_zpack<64>), dim3((unsigned)grid), dim3(256), 0, stream, L, ws);
   }

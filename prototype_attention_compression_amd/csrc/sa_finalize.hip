@@ -18,6 +18,7 @@
 
 #include "sa_device.h"
 #include "sa_launch.h"
+#include "sa_slots.h"
 
 namespace sa {
 
@@ -44,7 +45,7 @@ __device__ __forceinline__ float wv_value<float>(float v) {
 template <int D, typename T>
 __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout L, void* ws, float* __restrict__ S,
                                                 float* __restrict__ mass, float* __restrict__ Sbar,
-                                                float mass_scale) {
+                                                float mass_scale, int presummed) {
   constexpr int PER = kFinRows * D / 256;   // elements per thread
   constexpr int RPI = 256 / D;              // rows per output pass
   constexpr int WCH = D * D * (int)sizeof(T) / 16 / 256;   // 16-byte chunks of Wv per thread
@@ -85,54 +86,58 @@ __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout
       for (int i = 0; i < WCH; ++i) reinterpret_cast<u32x4*>(wsh)[tid + 256 * i] = w[i];
     }
   }
-  // the user's partial-sum slots: chunks c0 .. c1-1 (fp32 path), or
-  // group + u for the groups g0 .. g1-1 whose tile ranges meet the user's
-  // (bf16: pass 2 and the one-pass kernel walk equal tile ranges per group)
+  // the user's partial-sum slots, or the heads of their pre-summed
+  // sub-ranges (sa_slots.h), added in slot order
   int c0, c1;
-  if (L.dtype != 0) {
-    const int32_t* chunk_base = ws_i32(ws, L.off_chunk_base);
-    c0 = chunk_base[u];
-    c1 = chunk_base[u + 1];
-  } else {
-    const int32_t* tile_base = ws_i32(ws, L.off_tile_base);
-    const int32_t nt = ws_i32(ws, L.off_hdr)[kHdrTiles];
-    const int G = L.fused ? L.groups : L.p2_groups;
-    const int32_t Tg = (nt + 4 * G - 1) / (4 * G) * 4;
-    const int32_t t0 = tile_base[u], t1 = tile_base[u + 1];
-    c0 = c1 = 0;
-    if (t1 > t0) {
-      c0 = t0 / Tg + u;
-      c1 = (t1 - 1) / Tg + 1 + u;
-    }
-  }
+  user_slots(L, ws, u, c0, c1);
+  const int n = c1 - c0;
+  const bool pre = presummed && n > kPreMin;
   const float* part_u = ws_f32(ws, L.off_part_u);
   const float* part_m = ws_f32(ws, L.off_part_m);
 
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  int c = c0;
-  for (; c + kSlotBatch <= c1; c += kSlotBatch) {
-    float v[kSlotBatch][PER];
+  if (pre) {
+    float v[kPreSplit][PER];
 #pragma unroll
-    for (int q = 0; q < kSlotBatch; ++q) {
-      const float* base = part_u + ((int64_t)(c + q) * L.k + j0) * D;
+    for (int q = 0; q < kPreSplit; ++q) {
+      const float* base = part_u + ((int64_t)sub_head(c0, n, q) * L.k + j0) * D;
 #pragma unroll
       for (int i = 0; i < PER; ++i) v[q][i] = base[tid + 256 * i];
     }
 #pragma unroll
-    for (int q = 0; q < kSlotBatch; ++q)
+    for (int q = 0; q < kPreSplit; ++q)
 #pragma unroll
       for (int i = 0; i < PER; ++i) acc[i] += v[q][i];
-  }
-  for (; c < c1; ++c) {
-    const float* base = part_u + ((int64_t)c * L.k + j0) * D;
+  } else {
+    int c = c0;
+    for (; c + kSlotBatch <= c1; c += kSlotBatch) {
+      float v[kSlotBatch][PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
+      for (int q = 0; q < kSlotBatch; ++q) {
+        const float* base = part_u + ((int64_t)(c + q) * L.k + j0) * D;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v[q][i] = base[tid + 256 * i];
+      }
+#pragma unroll
+      for (int q = 0; q < kSlotBatch; ++q)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] += v[q][i];
+    }
+    for (; c < c1; ++c) {
+      const float* base = part_u + ((int64_t)c * L.k + j0) * D;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
+    }
   }
   if (tid < kFinRows) {
     float m = 0.f;
-    for (int cc = c0; cc < c1; ++cc) m += part_m[(int64_t)cc * L.k + j0 + tid];
+    if (pre) {
+      for (int q = 0; q < kPreSplit; ++q) m += part_m[(int64_t)sub_head(c0, n, q) * L.k + j0 + tid];
+    } else {
+      for (int cc = c0; cc < c1; ++cc) m += part_m[(int64_t)cc * L.k + j0 + tid];
+    }
     ms[tid] = m;
   }
   __syncthreads();
@@ -193,25 +198,88 @@ __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout
   if (mass != nullptr && tid < kFinRows) mass[(int64_t)u * L.k + j0 + tid] = ms[tid] * mass_scale;
 }
 
+// Pre-reduction for users with many slots: workgroup (user, 32-row block,
+// sub-range s) adds the slots of sub-range s in order and writes the sum to
+// the sub-range's first slot (sub-ranges are disjoint, so workgroups never
+// touch each other's slots).
+template <int D>
+__global__ __launch_bounds__(256) void presum_slots(Layout L, void* ws) {
+  constexpr int PER = kFinRows * D / 256;
+  const int nrb = L.k / kFinRows;
+  const int sidx = blockIdx.x % kPreSplit, ub = blockIdx.x / kPreSplit;
+  const int u = ub / nrb, rb = ub % nrb;
+  const int j0 = rb * kFinRows;
+  const int tid = threadIdx.x;
+  int c0, c1;
+  user_slots(L, ws, u, c0, c1);
+  const int n = c1 - c0;
+  if (n <= kPreMin) return;   // uniform over the workgroup
+  const int a = sub_head(c0, n, sidx), b = sub_head(c0, n, sidx + 1);
+  float* part_u = ws_f32(ws, L.off_part_u);
+  float* part_m = ws_f32(ws, L.off_part_m);
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  int c = a;
+  for (; c + kSlotBatch <= b; c += kSlotBatch) {
+    float v[kSlotBatch][PER];
+#pragma unroll
+    for (int q = 0; q < kSlotBatch; ++q) {
+      const float* base = part_u + ((int64_t)(c + q) * L.k + j0) * D;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) v[q][i] = base[tid + 256 * i];
+    }
+#pragma unroll
+    for (int q = 0; q < kSlotBatch; ++q)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] += v[q][i];
+  }
+  for (; c < b; ++c) {
+    const float* base = part_u + ((int64_t)c * L.k + j0) * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
+  }
+  float m = 0.f;
+  if (tid < kFinRows)
+    for (int cc = a; cc < b; ++cc) m += part_m[(int64_t)cc * L.k + j0 + tid];
+  __syncthreads();   // every read of slot a is done before it is overwritten
+  float* dst = part_u + ((int64_t)a * L.k + j0) * D;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) dst[tid + 256 * i] = acc[i];
+  if (tid < kFinRows) part_m[(int64_t)a * L.k + j0 + tid] = m;
+}
+
+hipError_t launch_presum(const Layout& L, void* ws, hipStream_t stream) {
+  if (!presum_launch(L)) return hipSuccess;
+  const int64_t grid = (int64_t)L.R * (L.k / kFinRows) * kPreSplit;
+  if (L.d == 128)
+    hipLaunchKernelGGL((presum_slots<128>), dim3((unsigned)grid), dim3(256), 0, stream, L, ws);
+  else
+    hipLaunchKernelGGL((presum_slots<64>), dim3((unsigned)grid), dim3(256), 0, stream, L, ws);
+  return hipGetLastError();
+}
+
 hipError_t launch_finalize(const Layout& L, const void* Wv, void* ws, float* S, float* mass, float* Sbar,
                            hipStream_t stream) {
   const int64_t grid = (int64_t)L.R * (L.k / kFinRows);
   if (grid == 0) return hipSuccess;
+  const int pre = presum_launch(L) ? 1 : 0;
+  if (pre && launch_presum(L, ws, stream) != hipSuccess) return hipErrorLaunchFailure;
   if (L.dtype == 0) {
     const float scale = 1.0f / 16384.0f;  // allocations were scaled by 2^14
     if (L.d == 128)
       hipLaunchKernelGGL((finalize<128, uint16_t>), dim3((unsigned)grid), dim3(256), 0, stream,
-                         (const uint16_t*)Wv, L, ws, S, mass, Sbar, scale);
+                         (const uint16_t*)Wv, L, ws, S, mass, Sbar, scale, pre);
     else
       hipLaunchKernelGGL((finalize<64, uint16_t>), dim3((unsigned)grid), dim3(256), 0, stream,
-                         (const uint16_t*)Wv, L, ws, S, mass, Sbar, scale);
+                         (const uint16_t*)Wv, L, ws, S, mass, Sbar, scale, pre);
   } else {
     if (L.d == 128)
       hipLaunchKernelGGL((finalize<128, float>), dim3((unsigned)grid), dim3(256), 0, stream, (const float*)Wv, L,
-                         ws, S, mass, Sbar, 1.0f);
+                         ws, S, mass, Sbar, 1.0f, pre);
     else
       hipLaunchKernelGGL((finalize<64, float>), dim3((unsigned)grid), dim3(256), 0, stream, (const float*)Wv, L,
-                         ws, S, mass, Sbar, 1.0f);
+                         ws, S, mass, Sbar, 1.0f, pre);
   }
   return hipGetLastError();
 }

@@ -34,6 +34,9 @@ bool fused_shape_ok(const Layout& L);
 bool fused_fits_device(const Layout& L, int device);
 hipError_t launch_fused(const Layout& L, void* ws, hipStream_t stream);
 // partial-sum reduction, prototype-wise normalisation and the value projection
+// Pre-reduction of the partial slots of users with many slots (sa_slots.h);
+// launch_finalize runs it itself, the backward before its per-user step.
+hipError_t launch_presum(const Layout& L, void* ws, hipStream_t stream);
 hipError_t launch_finalize(const Layout& L, const void* Wv, void* ws, float* S, float* mass, float* Sbar,
                            hipStream_t stream);
 // backward (bf16): per-user Z, c and scales from pass 2's partial sums and dS

@@ -195,16 +195,18 @@ def test_forward_sbar_matches_oracle(d, k):
     assert not Sbar[0].any() and not m[0].any()    # the empty user
 
 
-@pytest.mark.parametrize("d,k", [(64, 320), (128, 1024)])
-def test_backward_with_sbar_equals_recompute(d, k):
+@pytest.mark.parametrize("d,k,lengths", [(64, 320, (3000, 0, 17, 2500, 1)), (128, 1024, (3000, 0, 17, 2500, 1)),
+                                          (128, 1024, (60000, 5))])
+def test_backward_with_sbar_equals_recompute(d, k, lengths):
     """sa_compress_backward_with_sbar on the forward's Sbar and masses gives
     the same gradients, bit for bit, as the backward that recomputes the
-    per-user sums (the same fixed-order sums and divisions either way), and
-    they meet the gradient oracle's bar."""
+    per-user sums (the same fixed-order sums and divisions either way, also
+    when a long user's slots are pre-summed), and they meet the gradient
+    oracle's bar."""
     import torch
 
     import prototype_attention_compression_amd as sa
-    inp = make_inputs([3000, 0, 17, 2500, 1], d=d, k=k, seed=6100 + d, mask_tail_frac=0.1, name=f"sbar_bwd_d{d}")
+    inp = make_inputs(list(lengths), d=d, k=k, seed=6100 + d, mask_tail_frac=0.1, name=f"sbar_bwd_d{d}")
     print(f"[case] backward with Sbar R={inp.R} N={inp.N} k={k} d={d}", flush=True)
     dev = upload(inp)
     args = (dev["H"], dev["offsets"], dev["Wk"], dev["Wv"], dev["P"])

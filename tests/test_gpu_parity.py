@@ -88,6 +88,16 @@ def test_parity_c2_single_user_100k(path):
     _check(make_config("c2_n100k_d128_k1024"), path=path)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_parity_few_long_users_presummed(dtype):
+    """Few users, one of them long: its many partial slots are pre-summed in
+    sub-ranges before the finalize (the fp32 path's chunks and the bf16
+    path's group slots), next to short users that are not."""
+    from synth import make_inputs
+    inp = make_inputs([20000, 3, 0, 1500], d=64, k=128, seed=1400, dtype=dtype, name=f"presum_{dtype}")
+    _check(inp, path="two")
+
+
 def test_parity_bench_workload_sampled():
     """40 users x 100,000 tokens, k = 1024, d = 128: the bench's workload and
     launch configuration."""
