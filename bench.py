@@ -64,8 +64,8 @@ TRAFFIC = {
     # 1.0702e9 fetched + 0.0565e9 written (40 x 100K tokens, k = 1024, d = 128)
     "pass2_accum": (1126671448, "106926115929e4c35f66bb44da9f6cb58f6424a9449823e6a4de3926fbb74eed",
                     ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
-    # 1.308e9 fetched + 2.068e9 written (same workload, --backward)
-    "bwd_dh": (3376143292, "ec965c96f2896ea13f781a5c1ff123c39d2b7057c39953489aa62eaf9899596c",
+    # 1.317e9 fetched + 2.068e9 written (same workload, --backward)
+    "bwd_dh": (3384763648, "0a0ca9686b693975e26b017dc5b8ef1a67d547137b2b1b8b9c4097eb6b965b31",
                ("sa_bwd.hip", "sa_layout.h", "sa_device.h")),
     # 1.862e8 fetched + 0.461e8 written (300 users x 300 candidates, --target-attention)
     "ta_attend": (232284006, "5baccbb48a7aadc0f935ccfaec6d6a621cc3c9799c13818aa00a4800c7dd9e1b",
