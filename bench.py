@@ -67,8 +67,8 @@ TRAFFIC = {
     # 1.317e9 fetched + 2.068e9 written (same workload, --backward)
     "bwd_dh": (3384763648, "0a0ca9686b693975e26b017dc5b8ef1a67d547137b2b1b8b9c4097eb6b965b31",
                ("sa_bwd.hip", "sa_layout.h", "sa_device.h")),
-    # 1.862e8 fetched + 0.461e8 written (300 users x 300 candidates, --target-attention)
-    "ta_attend": (232284006, "5baccbb48a7aadc0f935ccfaec6d6a621cc3c9799c13818aa00a4800c7dd9e1b",
+    # 1.866e8 fetched + 0.461e8 written (300 users x 300 candidates, --target-attention)
+    "ta_attend": (232643200, "11b373b6d79b31a2e8df715ce2921d811169938d1f4e8e23ab76e504573584f6",
                   ("sa_target.hip", "sa_layout.h", "sa_device.h")),
 }
 

@@ -78,6 +78,7 @@ __global__ __launch_bounds__(256, 2) void ta_attend(const uint16_t* __restrict__
   const int64_t c0 = cand_offsets[u] + (int64_t)(tile - tile_base[u]) * kTile;
   const int64_t rem = cand_offsets[u + 1] - c0;
   const int count = rem < 0 ? 0 : (rem < kTile ? (int)rem : kTile);
+  const bool active = __builtin_amdgcn_readfirstlane(count) > 0;   // uniform over the wave
 
   half8 qB[S];
   if (col < count) {
@@ -144,52 +145,56 @@ __global__ __launch_bounds__(256, 2) void ta_attend(const uint16_t* __restrict__
   auto step = [&](int i, float4 (&pf_next)[LPT], float4 (&pf_free)[LPT]) {
     if (i + 2 < NB) gload(i + 2, pf_free);
     const char* sb = lds[i & 1];
-    float16v C = float16v{};
+    // a wave whose tile is padding (the user's tile count rounded up to 4)
+    // only helps stage the blocks
+    if (active) {
+      float16v C = float16v{};
 #pragma unroll
-    for (int s0 = 0; s0 < S; s0 += 4) {
-      half8 a[4];
+      for (int s0 = 0; s0 < S; s0 += 4) {
+        half8 a[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) a[s] = *reinterpret_cast<const half8*>(sb + abase + 32 * (s0 + s));
+        for (int s = 0; s < 4; ++s) a[s] = *reinterpret_cast<const half8*>(sb + abase + 32 * (s0 + s));
 #pragma unroll
-      for (int s = 0; s < 4; ++s) C = mfma32x32x16(a[s], qB[s0 + s], C);
-    }
-    float bm = C[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) bm = fmaxf(bm, C[r]);
-    bm = fmaxf(bm, __shfl_xor(bm, 32)) * sc2;
-    // Lazy rescale: the running maximum m moves (and O, l are rescaled)
-    // only when some candidate of the wave sees a logit more than 2^8 above
-    // it; otherwise P = 2^(logit - m) <= 2^8 and 2^6 P stays in fp16 range.
-    if (__any(bm > m + 8.0f)) {   // uniform over the wave
-      const float mn = fmaxf(m, bm);
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first block
-      m = mn;
-      l *= alpha;
-      if (i > 0) {
-        if (g == 0) wx[col] = alpha;
-        float f[16];
-        row_factors(f);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) O[dt][r] *= f[r];
+        for (int s = 0; s < 4; ++s) C = mfma32x32x16(a[s], qB[s0 + s], C);
       }
-    }
-    half8 ap[2];
-    float sum = 0.f;
+      float bm = C[0];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(C[r] * sc2 - m);
-      sum += p;
-      ap[r >> 3][r & 7] = (_Float16)(p * 64.0f);   // 2^6 P <= 2^14: small weights stay normal fp16
-    }
-    l += sum;
+      for (int r = 1; r < 16; ++r) bm = fmaxf(bm, C[r]);
+      bm = fmaxf(bm, __shfl_xor(bm, 32)) * sc2;
+      // Lazy rescale: the running maximum m moves (and O, l are rescaled)
+      // only when some candidate of the wave sees a logit more than 2^8 above
+      // it; otherwise P = 2^(logit - m) <= 2^8 and 2^6 P stays in fp16 range.
+      if (__any(bm > m + 8.0f)) {   // uniform over the wave
+        const float mn = fmaxf(m, bm);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first block
+        m = mn;
+        l *= alpha;
+        if (i > 0) {
+          if (g == 0) wx[col] = alpha;
+          float f[16];
+          row_factors(f);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      half8 hb[DT];
-      tile_tr_reads_kk<D>(lds_addr(sb) + tr_base + kk * 16 * PITCH, hb);
+          for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) O[dt] = mfma32x32x16(ap[kk], hb[dt], O[dt]);
+            for (int r = 0; r < 16; ++r) O[dt][r] *= f[r];
+        }
+      }
+      half8 ap[2];
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(C[r] * sc2 - m);
+        sum += p;
+        ap[r >> 3][r & 7] = (_Float16)(p * 64.0f);   // 2^6 P <= 2^14: small weights stay normal fp16
+      }
+      l += sum;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        half8 hb[DT];
+        tile_tr_reads_kk<D>(lds_addr(sb) + tr_base + kk * 16 * PITCH, hb);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) O[dt] = mfma32x32x16(ap[kk], hb[dt], O[dt]);
+      }
     }
     if (i + 1 < NB) swrite((i + 1) & 1, pf_next);
     __syncthreads();
