@@ -59,6 +59,7 @@ constexpr int kRows = 32;                         // prototypes per bwd_user wor
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kScaleMax = 16384.0f;             // 2^14
 constexpr int kSlotBatch = 4;                     // partial slots whose loads are in flight together
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16f(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
 
@@ -101,7 +102,6 @@ __global__ __launch_bounds__(256) void bwd_user(const uint16_t* __restrict__ Wv,
                                                 const float* __restrict__ Sbar_in, const float* __restrict__ mass_in,
                                                 Layout L, void* ws, int presummed) {
   constexpr int PER = kRows * D / 256;
-  constexpr int RPI = 256 / D;
   __shared__ float sb[kRows][D + 1];   // U / m
   __shared__ float gz[kRows][D + 1];   // dS / m, then Z
   __shared__ float ms[kRows];
@@ -183,36 +183,49 @@ __global__ __launch_bounds__(256) void bwd_user(const uint16_t* __restrict__ Wv,
     gz[j][a] = m > 0.f ? dS[row0 * D + e] * (kScaleMax / m) : 0.f;
   }
   __syncthreads();
-  // Z[j][a] = sum_b Gm[j][b] Wv[a][b]: thread (jr, a) takes rows jr + RPI i
-  const int a = tid % D, jr = tid / D;
-  float z[PER];
+  // Z[j][a] = sum_b Gm[j][b] Wv[a][b] on bf16 MFMAs: wave w takes columns
+  // a = 32 w .. 32 w + 31 (D = 64: waves 0 and 1).  The B operand
+  // (8 consecutive b of row a of Wv) is a plain 16-byte load; Wv is exact in
+  // bf16 and each fp32 Gm value is split exactly into three bf16 terms, so
+  // the products keep fp32 accuracy with fp32 sums.
+  const int lane = tid & 63, wave = tid >> 6, col = lane & 31, g = lane >> 5;
+  float16v zacc = float16v{};
+  const bool zw = 32 * wave < D;   // uniform over the wave
+  if (zw) {
+    const bf16x8* wrow = reinterpret_cast<const bf16x8*>(Wv + (int64_t)(32 * wave + col) * D);
+    bf16x8 wb[D / 16];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) z[i] = 0.f;
-  // the thread's row of Wv, all of its loads in flight together
-  const u32x4* wrow = reinterpret_cast<const u32x4*>(Wv + (int64_t)a * D);
-  u32x4 wr[D / 8];
+    for (int ks = 0; ks < D / 16; ++ks) wb[ks] = wrow[2 * ks + g];
 #pragma unroll
-  for (int b8 = 0; b8 < D / 8; ++b8) wr[b8] = wrow[b8];
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int k0 = 16 * ks + 8 * g;
+      bf16x8 hi, mid, lo;
 #pragma unroll
-  for (int b8 = 0; b8 < D / 8; ++b8) {
-    const u32x4 w = wr[b8];
-    const uint32_t ww[4] = {w[0], w[1], w[2], w[3]};
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float wlo = __uint_as_float(ww[h] << 16), whi = __uint_as_float(ww[h] & 0xffff0000u);
-      const int b = 8 * b8 + 2 * h;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) z[i] = fmaf(gz[jr + RPI * i][b + 1], whi, fmaf(gz[jr + RPI * i][b], wlo, z[i]));
+      for (int e = 0; e < 8; ++e) {
+        const float x = gz[col][k0 + e];
+        const __bf16 h = (__bf16)x;
+        const float r1 = x - (float)h;
+        const __bf16 m1 = (__bf16)r1;
+        hi[e] = h;
+        mid[e] = m1;
+        lo[e] = (__bf16)(r1 - (float)m1);
+      }
+      zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, wb[ks], zacc, 0, 0, 0);
+      zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, wb[ks], zacc, 0, 0, 0);
+      zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, wb[ks], zacc, 0, 0, 0);
     }
   }
-  __syncthreads();
+  __syncthreads();   // every read of Gm is done before Z overwrites it
   float zm = 0.f;
   float* z32 = ws_f32(ws, L.off_bz32) + row0 * D;
+  if (zw) {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    gz[jr + RPI * i][a] = z[i];
-    z32[(int64_t)(jr + RPI * i) * D + a] = z[i];
-    zm = fmaxf(zm, fabsf(z[i]));
+    for (int r = 0; r < 16; ++r) {
+      const int j = acc_row(r, g), a = 32 * wave + col;
+      gz[j][a] = zacc[r];
+      z32[(int64_t)j * D + a] = zacc[r];
+      zm = fmaxf(zm, fabsf(zacc[r]));
+    }
   }
   red[tid] = zm;
   __syncthreads();
