@@ -64,8 +64,8 @@ TRAFFIC = {
     # 1.0702e9 fetched + 0.0565e9 written (40 x 100K tokens, k = 1024, d = 128)
     "pass2_accum": (1126671448, "106926115929e4c35f66bb44da9f6cb58f6424a9449823e6a4de3926fbb74eed",
                     ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
-    # 1.311e9 fetched + 2.068e9 written (same workload, --backward)
-    "bwd_dh": (3379065899, "55dfda71937f8875e165f3c5a753791da095f9262ae8f7bbce05e70f24ad799e",
+    # 1.314e9 fetched + 2.068e9 written (same workload, --backward)
+    "bwd_dh": (3382438784, "914d35d3139e031b2105be580f031a6e8e3e0a5a8e60901f605bef6be8979db7",
                ("sa_bwd.hip", "sa_layout.h", "sa_device.h")),
     # 1.866e8 fetched + 0.461e8 written (300 users x 300 candidates, --target-attention)
     "ta_attend": (232643200, "11b373b6d79b31a2e8df715ce2921d811169938d1f4e8e23ab76e504573584f6",

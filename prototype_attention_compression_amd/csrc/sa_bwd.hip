@@ -59,6 +59,7 @@ constexpr int kRows = 32;                         // prototypes per bwd_user wor
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kScaleMax = 16384.0f;             // 2^14
 constexpr int kSlotBatch = 4;                     // partial slots whose loads are in flight together
+constexpr int kERows = 8;                         // prototypes per E-reduction workgroup
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16f(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
@@ -650,12 +651,13 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_ereduce(const uint16_t* __restrict__ Wk,
                                                    const int32_t* __restrict__ tile_base, Layout L, void* ws,
                                                    float* __restrict__ dP) {
-  constexpr int PER = kRows * D / 256;
+  constexpr int PER = kERows * D / 256;
   constexpr int RPI = 256 / D;
   constexpr int WCH = D * D / 8 / 256;   // 16-byte chunks of Wk per thread
-  __shared__ float es[kRows][D + 1];
+  constexpr int SB = 16;                 // slots whose loads are in flight together
+  __shared__ float es[kERows][D + 1];
   __shared__ __attribute__((aligned(16))) uint16_t wk[D * D];
-  const int j0 = blockIdx.x * kRows, tid = threadIdx.x;
+  const int j0 = blockIdx.x * kERows, tid = threadIdx.x;
   {
     // Wk staged in LDS, all of its loads in flight together
     u32x4 w[WCH];
@@ -671,7 +673,7 @@ __global__ __launch_bounds__(256) void bwd_ereduce(const uint16_t* __restrict__ 
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   // the slots bwd_e wrote: group + u for every group whose tile range meets
   // user u's tiles, walked users in order, then groups in order, with the
-  // loads of kSlotBatch consecutive slots of that walk in flight together
+  // loads of SB consecutive slots of that walk in flight together
   const int32_t T = ws_i32(ws, L.off_hdr)[kHdrTiles];
   const int G = L.e_groups;
   const int32_t Tg = (T + 4 * G - 1) / (4 * G) * 4;
@@ -689,10 +691,10 @@ __global__ __launch_bounds__(256) void bwd_ereduce(const uint16_t* __restrict__ 
     return true;
   };
   for (;;) {
-    int sl[kSlotBatch];
+    int sl[SB];
     int n = 0;
 #pragma unroll
-    for (int q = 0; q < kSlotBatch; ++q) {
+    for (int q = 0; q < SB; ++q) {
       sl[q] = 0;
       if (n == q && seek()) {
         sl[q] = c++;
@@ -700,9 +702,9 @@ __global__ __launch_bounds__(256) void bwd_ereduce(const uint16_t* __restrict__ 
       }
     }
     if (n == 0) break;
-    float v[kSlotBatch][PER];
+    float v[SB][PER];
 #pragma unroll
-    for (int q = 0; q < kSlotBatch; ++q) {
+    for (int q = 0; q < SB; ++q) {
       if (q < n) {
         const float* base = ep + ((int64_t)sl[q] * L.k + j0) * D;
 #pragma unroll
@@ -710,7 +712,7 @@ __global__ __launch_bounds__(256) void bwd_ereduce(const uint16_t* __restrict__ 
       }
     }
 #pragma unroll
-    for (int q = 0; q < kSlotBatch; ++q)
+    for (int q = 0; q < SB; ++q)
       if (q < n)
 #pragma unroll
         for (int i = 0; i < PER; ++i) acc[i] += v[q][i];
@@ -900,10 +902,10 @@ hipError_t launch_bwd_params(const Layout& L, const void* P, const void* Wk, con
   const int32_t* tb = hptr<const int32_t>(ws, L.off_tile_base);
   // E and dP
   if (D == 128)
-    hipLaunchKernelGGL((bwd_ereduce<128>), dim3(L.k / kRows), dim3(256), 0, stream, (const uint16_t*)Wk, tb, L, ws,
+    hipLaunchKernelGGL((bwd_ereduce<128>), dim3(L.k / kERows), dim3(256), 0, stream, (const uint16_t*)Wk, tb, L, ws,
                        dP);
   else
-    hipLaunchKernelGGL((bwd_ereduce<64>), dim3(L.k / kRows), dim3(256), 0, stream, (const uint16_t*)Wk, tb, L, ws,
+    hipLaunchKernelGGL((bwd_ereduce<64>), dim3(L.k / kERows), dim3(256), 0, stream, (const uint16_t*)Wk, tb, L, ws,
                        dP);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   // dWk = E^T P / sqrt(d): k rows in as many chunks of a multiple of 32 rows
