@@ -89,12 +89,6 @@ typedef struct {
  */
 #define SA_FLAG_TWO_PASS 1
 #define SA_FLAG_ONE_PASS 2
-/* Backward only (sa_compress_backward): reuse the forward state the
- * workspace already holds instead of recomputing it -- meant for right
- * after an sa_compress of the same problem and inputs on the same
- * workspace.  Currently switched off: sa_compress_backward and
- * sa_backward_workspace_size return SA_E_UNSUPPORTED for it. */
-#define SA_FLAG_REUSE_FORWARD 4
 
 /*
  * Workspace size for `problem`.  Writes the byte count to *bytes.  Returns
@@ -106,12 +100,21 @@ typedef struct {
 sa_status sa_workspace_size(const sa_problem* problem, size_t* bytes);
 
 /*
+ * The same workspace size as a return value: sa_workspace_size's byte count
+ * for a problem sa_compress accepts, and 0 for one it rejects (including
+ * problem = NULL).  Pure host code.
+ */
+size_t sa_workspace_bytes(const sa_problem* problem);
+
+/*
  * Compress a ragged batch of R user histories into R sketches.
  *
  *   H           [N, d] row-major, dtype `problem->dtype`, 16-byte aligned.
  *               User u owns rows offsets[u] .. offsets[u+1]-1.  For SA_BF16,
- *               magnitudes of unmasked entries must be below 65504: they are
- *               widened exactly to fp16 MFMA operands, larger ones saturate.
+ *               magnitudes of unmasked entries must not exceed 65504: they are
+ *               widened exactly to fp16 MFMA operands; a larger, infinite or
+ *               NaN kept value raises SA_DEVICE_ERR_RANGE (that call's
+ *               outputs are invalid).
  *   offsets     [R+1] int64, 0 = offsets[0] <= offsets[1] <= ... <= offsets[R]
  *               = N.  Device memory, 8-byte aligned.  If the sequence breaks this contract
  *               the kernels treat every user as empty (S = 0, mass = 0) and
@@ -219,8 +222,7 @@ sa_status sa_compress_with_sbar(const sa_problem* problem,
  *
  * Built for bf16 inputs (problem->dtype = SA_BF16) with the same d and k as
  * sa_compress; SA_F32 or SA_FLAG_ONE_PASS give SA_E_UNSUPPORTED (the
- * backward needs the two-pass forward's state: it recomputes it, or with
- * SA_FLAG_REUSE_FORWARD takes it from the workspace).  Internally
+ * backward recomputes the two-pass forward's per-token state).  Internally
  * the products use fp16 MFMA operands (the token rows widened exactly, the
  * allocations, their gradients and dS / m scaled by powers of two into fp16
  * range) with fp32 sums.  dS must be finite.
@@ -287,8 +289,7 @@ sa_status sa_compress_backward_with_events(const sa_problem* problem,
  * being recomputed, which removes the forward's accumulation pass from the
  * backward (events[1] then marks the end of the per-token logsumexp pass).
  * The chain rule needs Sbar and m; the per-token allocations are still
- * recomputed.  Sbar and mass must be non-NULL when R > 0 and
- * SA_FLAG_REUSE_FORWARD must not be set (SA_E_INVALID).  If they do not come
+ * recomputed.  Sbar and mass must be non-NULL when R > 0 (SA_E_INVALID).  If they do not come
  * from the same inputs the gradients are those of a different forward; no
  * memory outside the stated shapes is read either way.  Same workspace
  * (sa_backward_workspace_size), outputs, errors and semantics otherwise.
@@ -335,8 +336,9 @@ sa_status sa_compress_backward_with_sbar(const sa_problem* problem,
  *                 device error flag as sa_compress's offsets; on a violation
  *                 out and lse are zero).
  *   S             [R, k, d] float32 sketches (sa_compress's output layout),
- *                 16-byte aligned; entries must be below 65504 in magnitude
- *                 (fp16 MFMA operands).
+ *                 16-byte aligned; entries must not exceed 65504 in magnitude
+ *                 (fp16 MFMA operands; a larger or non-finite entry, or such
+ *                 a query value, raises SA_DEVICE_ERR_RANGE).
  *   out           [C, d] float32, fully overwritten.
  *   lse           [C] float32 natural-log normaliser log sum_j exp(q . s_j /
  *                 sqrt(d)), or NULL.
@@ -358,17 +360,21 @@ sa_status sa_target_attention(const sa_problem* problem,
 
 /*
  * sa_target_attention with the sketches read through a row index: user u's
- * sketch is S[sketch_rows[u]] (sketch_rows: [R] int32 device, each in
- * [0, rows of S)), e.g. the slots of a sketch cache's slab (sa_cache_*), so
- * cached sketches are attended in place without a gather.  The caller
- * guarantees the indices are in range (they are not checked on the device).
- * sketch_rows = NULL is sa_target_attention.
+ * sketch is S[sketch_rows[u]], where S holds sketch_count sketches
+ * [sketch_count, k, d] and sketch_rows is [R] int32 device memory, e.g. the
+ * slots of a sketch cache's slab (sa_cache_*), so cached sketches are
+ * attended in place without a gather.  An index outside [0, sketch_count)
+ * reads nothing: that user's candidates get zero out and lse rows and the
+ * device error flag SA_DEVICE_ERR_SKETCH_ROW is raised.  sketch_rows = NULL
+ * with sketch_count = R is sa_target_attention.  sketch_count < 0 is
+ * SA_E_INVALID.
  */
 sa_status sa_target_attention_rows(const sa_problem* problem,
                                    const void* Q,
                                    const int64_t* cand_offsets,
                                    const float* S,
                                    const int32_t* sketch_rows,
+                                   int64_t sketch_count,
                                    float* out,
                                    float* lse,
                                    void* workspace,
@@ -399,8 +405,8 @@ sa_status sa_target_attention_rows(const sa_problem* problem,
  *   the least recently used entry that no request of this batch uses; later
  *   requests of the same user in the batch share that slot and count as
  *   hits.  A stale entry is recomputed in place (counted as a miss and as
- *   expired).  More distinct users in one batch than slots is SA_E_INVALID
- *   (and leaves the cache in an unspecified but consistent state).
+ *   expired).  More distinct users in one batch than slots is SA_E_INVALID,
+ *   checked before anything changes: the cache is left as it was.
  * sa_cache_fill: gathers the miss users' history rows from the caller's
  *   packed store (H_store [N_store, d] with host store_offsets [R_store+1],
  *   optional mask_store [N_store]; `store` describes it: num_users =
@@ -440,11 +446,21 @@ sa_status sa_cache_fill(sa_cache* cache, const sa_problem* store, const void* H_
 #define SA_DEVICE_ERR_OFFSETS 1   /* offsets broke their contract: all users empty */
 #define SA_DEVICE_ERR_EXCHANGE 2  /* one-pass: a bounded wait between workgroups
                                      expired; the sketches of that call are invalid */
+#define SA_DEVICE_ERR_RANGE 4     /* a kept bf16 history value (or, in target
+                                     attention, a candidate query or sketch value)
+                                     lies outside fp16's finite range: |x| > 65504,
+                                     an infinity or a NaN.  Such values become fp16
+                                     MFMA operands, so the outputs of that call are
+                                     invalid; masked tokens are not checked. */
+#define SA_DEVICE_ERR_SKETCH_ROW 8 /* sa_target_attention_rows: a sketch_rows index
+                                     outside [0, sketch_count); that user's outputs
+                                     are zero */
 
 /*
- * Synchronously read the device error flags that the last sa_compress on
- * `workspace` set (0 = none, else a combination of SA_DEVICE_ERR_*).  Waits
- * for `stream`.  Returns SA_E_HIP if the copy fails.
+ * Synchronously read the device error flags that the last call on
+ * `workspace` set (sa_compress and its variants, the backward, target
+ * attention; 0 = none, else a combination of SA_DEVICE_ERR_*).  Waits for
+ * `stream`.  Returns SA_E_HIP if the copy fails.
  */
 sa_status sa_read_device_error(const void* workspace, void* stream, int32_t* flag);
 

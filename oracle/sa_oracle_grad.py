@@ -7,9 +7,9 @@ code with the HIP library.
 Why gradients: the blog "100,000 videos in your pocket" ("How it works",
 item 1) notes that the compression is differentiable, so the gradients of
 the final ranking loss flow back through it and train the prototypes and
-projections; its "Why it matters" item 2 and "Takeaways" say SequenceO1
-trains the compressor on the ranking loss end to end instead of freezing an
-offline stage.  The pages give no formula for the backward pass; it is the
+projections; its "State of the art: the pattern behind the paper" item 2
+and "Takeaways" say SequenceO1 trains the compressor on the ranking loss end
+to end instead of freezing an offline stage.  The pages give no formula for the backward pass; it is the
 chain rule applied to the forward definition of ``sa_oracle`` (the same
 readings: K = H Wk, V = H Wv, logits P K^T / sqrt(d), softmax over
 prototypes per token, each sketch row the mass-weighted mean of the values,

@@ -7,13 +7,14 @@ from ._lib import (  # noqa: F401
     SA_BF16,
     SA_DEVICE_ERR_EXCHANGE,
     SA_DEVICE_ERR_OFFSETS,
+    SA_DEVICE_ERR_RANGE,
+    SA_DEVICE_ERR_SKETCH_ROW,
     SA_E_HIP,
     SA_E_INVALID,
     SA_E_UNSUPPORTED,
     SA_E_WORKSPACE,
     SA_F32,
     SA_FLAG_ONE_PASS,
-    SA_FLAG_REUSE_FORWARD,
     SA_FLAG_TWO_PASS,
     SA_OK,
     SaError,
@@ -35,6 +36,6 @@ __all__ = [
     "compress", "compress_backward", "backward_workspace_size", "target_attention",
     "target_attention_workspace_size", "load", "read_device_error", "status_string", "version", "workspace_size",
     "SaError", "SA_OK", "SA_E_INVALID", "SA_E_UNSUPPORTED", "SA_E_WORKSPACE", "SA_E_HIP",
-    "SA_BF16", "SA_F32", "SA_FLAG_ONE_PASS", "SA_FLAG_TWO_PASS", "SA_FLAG_REUSE_FORWARD", "SA_DEVICE_ERR_OFFSETS",
+    "SA_BF16", "SA_F32", "SA_FLAG_ONE_PASS", "SA_FLAG_TWO_PASS", "SA_DEVICE_ERR_OFFSETS", "SA_DEVICE_ERR_RANGE", "SA_DEVICE_ERR_SKETCH_ROW",
     "SA_DEVICE_ERR_EXCHANGE",
 ]

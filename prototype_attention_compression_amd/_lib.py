@@ -14,12 +14,12 @@ LIB_PATH = os.path.join(_PKG, "libsa.so")
 
 SA_OK, SA_E_INVALID, SA_E_UNSUPPORTED, SA_E_WORKSPACE, SA_E_HIP = range(5)
 SA_BF16, SA_F32 = 0, 1
-SA_FLAG_TWO_PASS, SA_FLAG_ONE_PASS, SA_FLAG_REUSE_FORWARD = 1, 2, 4
-SA_DEVICE_ERR_OFFSETS, SA_DEVICE_ERR_EXCHANGE = 1, 2
+SA_FLAG_TWO_PASS, SA_FLAG_ONE_PASS = 1, 2
+SA_DEVICE_ERR_OFFSETS, SA_DEVICE_ERR_EXCHANGE, SA_DEVICE_ERR_RANGE, SA_DEVICE_ERR_SKETCH_ROW = 1, 2, 4, 8
 _PATH_FLAGS = {None: 0, "auto": 0, "two": SA_FLAG_TWO_PASS, "one": SA_FLAG_ONE_PASS}
 
 # functions declared in include/sa.h
-EXPORTS = ("sa_workspace_size", "sa_compress", "sa_compress_with_events", "sa_compress_with_sbar",
+EXPORTS = ("sa_workspace_size", "sa_workspace_bytes", "sa_compress", "sa_compress_with_events", "sa_compress_with_sbar",
            "sa_backward_workspace_size", "sa_compress_backward", "sa_compress_backward_with_events",
            "sa_compress_backward_with_sbar",
            "sa_target_attention_workspace_size", "sa_target_attention", "sa_target_attention_rows",
@@ -77,6 +77,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     lib.sa_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
     lib.sa_workspace_size.restype = ctypes.c_int
+    lib.sa_workspace_bytes.argtypes = [P]
+    lib.sa_workspace_bytes.restype = sz
     lib.sa_compress.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sa_compress.restype = ctypes.c_int
     lib.sa_compress_with_events.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
@@ -97,7 +99,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sa_target_attention_workspace_size.restype = ctypes.c_int
     lib.sa_target_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sa_target_attention.restype = ctypes.c_int
-    lib.sa_target_attention_rows.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sa_target_attention_rows.argtypes = [P, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp, sz, vp]
     lib.sa_target_attention_rows.restype = ctypes.c_int
     i64p, i32p = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)
     lib.sa_cache_create.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_double, vp, vp,
@@ -290,15 +292,13 @@ def read_device_error(workspace) -> int:
 
 
 def compress_backward(H, offsets, Wk, Wv, P, dS, mask=None, workspace=None, events=None,
-                      reuse_forward: bool = False, sbar=None, mass=None):
+                      sbar=None, mass=None):
     """Gradients of a loss through the sketches, computed by libsa on the GPU.
 
     Inputs as for ``compress`` (bfloat16 only), plus dS [R, k, d] float32 =
     dLoss/dS.  Returns (dH [N, d], dP [k, d], dWk [d, d], dWv [d, d]), all
     float32; dP, dWk and dWv are summed over the users.  Runs on torch's
-    current stream.  ``reuse_forward`` (SA_FLAG_REUSE_FORWARD): ``workspace``
-    holds the two-pass forward of these same inputs (a ``compress`` call on
-    it just before), which the backward then does not recompute.  ``sbar``
+    current stream.  ``sbar``
     and ``mass`` (sa_compress_backward_with_sbar): the forward's Sbar
     [R, k, d] and masses [R, k] from ``compress(return_sbar=True)`` on the
     same inputs; the per-user sums are then not recomputed.
@@ -330,8 +330,6 @@ def compress_backward(H, offsets, Wk, Wv, P, dS, mask=None, workspace=None, even
     if (sbar is None) != (mass is None):
         raise ValueError("sbar and mass go together")
     if sbar is not None:
-        if reuse_forward:
-            raise ValueError("sbar/mass and reuse_forward are exclusive")
         if (sbar.dtype != torch.float32 or sbar.shape != (R, k, d) or mass.dtype != torch.float32
                 or mass.shape != (R, k)):
             raise ValueError("sbar must be float32 [R, k, d] and mass float32 [R, k]")
@@ -339,11 +337,9 @@ def compress_backward(H, offsets, Wk, Wv, P, dS, mask=None, workspace=None, even
             if not t.is_cuda or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous GPU tensor")
     dev = H.device
-    pb = problem(R, N, d, k, SA_BF16, SA_FLAG_REUSE_FORWARD if reuse_forward else 0)
+    pb = problem(R, N, d, k, SA_BF16)
     wbytes = backward_workspace_size(R, N, d, k, SA_BF16)
     if workspace is None or workspace.numel() * workspace.element_size() < wbytes:
-        if reuse_forward:
-            raise ValueError("reuse_forward needs the workspace the forward ran on")
         workspace = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
     dH = torch.empty((N, d), dtype=torch.float32, device=dev)
     dP = torch.empty((k, d), dtype=torch.float32, device=dev)
@@ -377,13 +373,16 @@ def target_attention_workspace_size(num_users: int, total_candidates: int, d: in
 
 
 def raw_target_attention(pb: SaProblem, Q, cand_offsets, S, out, lse, workspace, workspace_bytes: int,
-                         stream, sketch_rows=None) -> int:
-    """Direct call of sa_target_attention(_rows); returns the status."""
+                         stream, sketch_rows=None, sketch_count: int = 0) -> int:
+    """Direct call of sa_target_attention, or of sa_target_attention_rows when
+    ``sketch_rows`` is given (S then holds ``sketch_count`` sketches); returns
+    the status."""
     if sketch_rows is None:
         return int(load().sa_target_attention(ctypes.byref(pb), Q, cand_offsets, S, out, lse, workspace,
                                               ctypes.c_size_t(workspace_bytes), stream))
-    return int(load().sa_target_attention_rows(ctypes.byref(pb), Q, cand_offsets, S, sketch_rows, out, lse,
-                                               workspace, ctypes.c_size_t(workspace_bytes), stream))
+    return int(load().sa_target_attention_rows(ctypes.byref(pb), Q, cand_offsets, S, sketch_rows,
+                                               int(sketch_count), out, lse, workspace,
+                                               ctypes.c_size_t(workspace_bytes), stream))
 
 
 def target_attention(Q, cand_offsets, S, return_lse: bool = False, out=None, workspace=None, sketch_rows=None):
@@ -392,7 +391,9 @@ def target_attention(Q, cand_offsets, S, return_lse: bool = False, out=None, wor
     Q [C, d] bfloat16 candidate queries packed user by user, cand_offsets
     [R+1] int64, S [R, k, d] float32 sketches (as ``compress`` returns).
     With ``sketch_rows`` ([R] int32 GPU tensor), user u's sketch is
-    S[sketch_rows[u]] and S may hold any number of rows (e.g. a cache slab).
+    S[sketch_rows[u]] and S may hold any number of rows (e.g. a cache slab);
+    an index outside S gives that user zero outputs and raises
+    SA_DEVICE_ERR_SKETCH_ROW (``read_device_error(workspace)``).
     Returns out [C, d] float32 (and the natural-log normalisers [C] if
     ``return_lse``).  Runs on torch's current stream.
     """
@@ -428,7 +429,7 @@ def target_attention(Q, cand_offsets, S, return_lse: bool = False, out=None, wor
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     st = raw_target_attention(pb, _ptr(Q) if C > 0 else None, _ptr(cand_offsets), _ptr(S),
                               _ptr(o) if C > 0 else None, _ptr(lse) if C > 0 else None, _ptr(workspace), wbytes,
-                              stream, _ptr(sketch_rows))
+                              stream, _ptr(sketch_rows), S.shape[0])
     if st != SA_OK:
         raise SaError(st, "sa_target_attention")
     return (o, lse) if return_lse else o

@@ -35,17 +35,11 @@ sa_status check_problem(const sa_problem* p) {
   return SA_OK;
 }
 
-// The backward pass: bf16 inputs only; it always runs the two forward passes
+// The backward pass: bf16 inputs only; it always runs the two forward passes.
 sa_status check_problem_bwd(const sa_problem* p) {
-  if (p == nullptr) return SA_E_INVALID;
-  sa_problem q = *p;
-  q.flags &= ~SA_FLAG_REUSE_FORWARD;
-  sa_status st = check_problem(&q);
+  sa_status st = check_problem(p);
   if (st != SA_OK) return st;
   if (p->dtype != SA_BF16 || (p->flags & SA_FLAG_ONE_PASS)) return SA_E_UNSUPPORTED;
-  // Reusing the forward's state is switched off: the first GPU run that
-  // exercised it ended in a device fault whose cause has not been found.
-  if (p->flags & SA_FLAG_REUSE_FORWARD) return SA_E_UNSUPPORTED;
   return SA_OK;
 }
 
@@ -297,12 +291,11 @@ sa_status backward_impl(const sa_problem* problem, const void* H, const int64_t*
     if (workspace == nullptr || workspace_bytes < L.total) return SA_E_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % sa::kAlign != 0) return SA_E_INVALID;
     if (!mark(0)) return SA_E_HIP;
-    // forward passes 1 and 2: fp16 token rows, logsumexps, partial sums
-    // (already in the workspace when the caller asks to reuse them); pass 2
-    // is not needed when the caller hands in the forward's Sbar and masses
-    const bool reuse = (p.flags & SA_FLAG_REUSE_FORWARD) != 0;
-    if (!reuse && sa::launch_prep(L, P, Wk, offsets, workspace, s) != hipSuccess) return SA_E_HIP;
-    if (!reuse && p.total_tokens > 0) {
+    // forward passes 1 and 2: fp16 token rows, logsumexps, partial sums;
+    // pass 2 is not needed when the caller hands in the forward's Sbar and
+    // masses
+    if (sa::launch_prep(L, P, Wk, offsets, workspace, s) != hipSuccess) return SA_E_HIP;
+    if (p.total_tokens > 0) {
       const hipError_t e = sa::pass1q_ok(L) ? sa::launch_pass1q(L, H, offsets, token_mask, workspace, s)
                                             : sa::launch_pass1(L, H, offsets, token_mask, workspace, s);
       if (e != hipSuccess) return SA_E_HIP;
@@ -334,6 +327,11 @@ sa_status sa_workspace_size(const sa_problem* problem, size_t* bytes) {
   if (st != SA_OK) return st;
   *bytes = sa::make_layout(*problem).total;
   return SA_OK;
+}
+
+size_t sa_workspace_bytes(const sa_problem* problem) {
+  size_t bytes = 0;
+  return sa_workspace_size(problem, &bytes) == SA_OK ? bytes : 0;
 }
 
 sa_status sa_compress(const sa_problem* problem, const void* H, const int64_t* offsets, const uint8_t* token_mask,
@@ -401,7 +399,6 @@ sa_status sa_compress_backward_with_sbar(const sa_problem* problem, const void* 
                                          float* dWk, float* dWv, void* workspace, size_t workspace_bytes,
                                          void* stream, void* const* events) {
   if (problem == nullptr) return SA_E_INVALID;
-  if (problem->flags & SA_FLAG_REUSE_FORWARD) return SA_E_INVALID;
   if (problem->num_users > 0 && (Sbar == nullptr || mass == nullptr)) return SA_E_INVALID;
   return sa::backward_impl(problem, H, offsets, token_mask, Wk, Wv, P, Sbar, mass, dS, dH, dP, dWk, dWv, workspace,
                            workspace_bytes, stream, events);
@@ -417,26 +414,28 @@ sa_status sa_target_attention_workspace_size(const sa_problem* problem, size_t* 
 
 sa_status sa_target_attention(const sa_problem* problem, const void* Q, const int64_t* cand_offsets, const float* S,
                               float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  return sa_target_attention_rows(problem, Q, cand_offsets, S, nullptr, out, lse, workspace, workspace_bytes,
-                                  stream);
+  if (problem == nullptr) return SA_E_INVALID;
+  return sa_target_attention_rows(problem, Q, cand_offsets, S, nullptr, problem->num_users, out, lse, workspace,
+                                  workspace_bytes, stream);
 }
 
 sa_status sa_target_attention_rows(const sa_problem* problem, const void* Q, const int64_t* cand_offsets,
-                                   const float* S, const int32_t* sketch_rows, float* out, float* lse,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+                                   const float* S, const int32_t* sketch_rows, int64_t sketch_count, float* out,
+                                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   try {
     sa_status st = sa::check_problem_target(problem);
     if (st != SA_OK) return st;
     const sa_problem& p = *problem;
     if (p.num_users == 0) return SA_OK;
-    if (cand_offsets == nullptr || S == nullptr) return SA_E_INVALID;
+    if (cand_offsets == nullptr || S == nullptr || sketch_count < 0) return SA_E_INVALID;
     if (p.total_tokens > 0 && (Q == nullptr || out == nullptr)) return SA_E_INVALID;
     if (reinterpret_cast<uintptr_t>(S) % 16 != 0 || reinterpret_cast<uintptr_t>(Q) % 16 != 0) return SA_E_INVALID;
     const sa::Layout L = sa::make_layout_target(p);
     if (workspace == nullptr || workspace_bytes < L.total) return SA_E_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % sa::kAlign != 0) return SA_E_INVALID;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (sa::launch_target_attention(L, Q, cand_offsets, S, sketch_rows, workspace, out, lse, s) != hipSuccess)
+    if (sa::launch_target_attention(L, Q, cand_offsets, S, sketch_rows, sketch_count, workspace, out, lse, s) !=
+        hipSuccess)
       return SA_E_HIP;
     return SA_OK;
   } catch (...) {

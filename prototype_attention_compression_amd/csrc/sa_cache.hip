@@ -30,6 +30,7 @@
 #include <algorithm>
 #include <new>
 #include <unordered_map>
+#include <unordered_set>
 #include <vector>
 
 #include "sa.h"
@@ -175,6 +176,18 @@ sa_status sa_cache_lookup(sa_cache* c, const int64_t* users, int64_t n, double n
   if (n > 0 && (users == nullptr || slots == nullptr || miss_users == nullptr || miss_slots == nullptr))
     return SA_E_INVALID;
   try {
+    // Every distinct user of the batch holds one slot for the rest of the
+    // batch, so a slot can be found for each new user exactly when the batch
+    // has no more distinct users than slots.  Checked before anything
+    // changes: a refused batch leaves the cache as it was.
+    {
+      std::unordered_set<int64_t> distinct;
+      distinct.reserve((size_t)std::min<int64_t>(n, (int64_t)c->capacity + 1) * 2);
+      for (int64_t i = 0; i < n; ++i) {
+        distinct.insert(users[i]);
+        if ((int64_t)distinct.size() > c->capacity) return SA_E_INVALID;
+      }
+    }
     const int64_t batch = ++c->batch;
     sa_cache_stats st;
     memset(&st, 0, sizeof(st));
@@ -226,7 +239,7 @@ sa_status sa_cache_lookup(sa_cache* c, const int64_t* users, int64_t n, double n
             best_used = e.t_used;
           }
         }
-        if (best < 0) return SA_E_INVALID;   // more distinct users in the batch than slots
+        if (best < 0) return SA_E_INVALID;   // excluded by the distinct-user check above
         c->map.erase(c->slot_user[(size_t)best]);
         ++st.evictions;
         slot = best;

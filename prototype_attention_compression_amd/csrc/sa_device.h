@@ -190,6 +190,19 @@ __device__ __forceinline__ half8 bf16x8_to_f16x8(u32x4 v) {
   return out;
 }
 
+// Nonzero if one of 8 packed bf16 values (one 16-byte load) lies outside
+// fp16's finite range: |x| > 65504, an infinity or a NaN.  With the sign
+// cleared, bf16 magnitudes order like their bit patterns, and 0x477F (65280)
+// is the largest bf16 value not above 65504; adding 0x3880 to a cleared half
+// carries into its bit 15 exactly when the half exceeds 0x477F, and never
+// into the other half (0x7FFF + 0x3880 < 0x10000).
+__device__ __forceinline__ uint32_t bf16x8_range_bits(u32x4 v) {
+  uint32_t bad = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bad |= ((v[i] & 0x7FFF7FFFu) + 0x38803880u) & 0x80008000u;
+  return bad;
+}
+
 // Largest u with base[u] <= x, for a non-decreasing base[0..R] with base[0] = 0
 // and x < base[R].  Users with no tiles (base[u] == base[u+1]) are skipped.
 __device__ __forceinline__ int find_user(const int32_t* base, int R, int32_t x) {

@@ -53,7 +53,8 @@ hipError_t launch_bwd_params(const Layout& L, const void* P, const void* Wk, con
 hipError_t launch_schedule(const Layout& L, const int64_t* offsets, void* ws, hipStream_t stream);
 // sketch-branch target attention (schedule + attention kernel)
 hipError_t launch_target_attention(const Layout& L, const void* Q, const int64_t* cand_offsets, const float* S,
-                                   const int32_t* sketch_rows, void* ws, float* out, float* lse, hipStream_t stream);
+                                   const int32_t* sketch_rows, int64_t sketch_count, void* ws, float* out, float* lse,
+                                   hipStream_t stream);
 // zero fill (used when the batch has no users)
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 

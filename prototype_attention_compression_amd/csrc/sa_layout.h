@@ -46,6 +46,8 @@ constexpr int kOuterRows = 256;      // rows per chunk of the outer-product redu
 // Device error flags (workspace header word 0, bitwise or).
 constexpr int32_t kErrBadOffsets = 1;
 constexpr int32_t kErrExchange = 2;  // a bounded wait between workgroups expired
+constexpr int32_t kErrRange = 4;     // a kept bf16 input value outside fp16's finite range
+constexpr int32_t kErrSketchRow = 8; // a sketch row index outside the given sketch array
 
 struct Layout {
   // problem

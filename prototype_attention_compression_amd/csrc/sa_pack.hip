@@ -40,6 +40,7 @@ __global__ __launch_bounds__(256) void pack_rows(const uint16_t* __restrict__ H,
   const int32_t tb = min(T, ta + per_wg);
   const int tid = threadIdx.x;
   float nmax = 0.f;
+  uint32_t range_bad = 0u;   // kept values outside fp16's finite range
   if (ta < tb) {
     const int32_t* tile_base = ws_i32(ws, L.off_tile_base);
     _Float16* h16 = ws_f16(ws, L.off_h16);
@@ -64,6 +65,7 @@ __global__ __launch_bounds__(256) void pack_rows(const uint16_t* __restrict__ H,
           keep = (mask == nullptr) || (mask[tok] != 0);
           if (keep) raw = reinterpret_cast<const u32x4*>(H + tok * D)[c];
         }
+        range_bad |= bf16x8_range_bits(raw);
         const half8 hv = bf16x8_to_f16x8(raw);
         *reinterpret_cast<half8*>(h16 + ((int64_t)tile * kTile + row) * D + 8 * c) = hv;
         if (c == 0) valid[(int64_t)tile * kTile + row] = keep ? 1u : 0u;
@@ -81,6 +83,7 @@ __global__ __launch_bounds__(256) void pack_rows(const uint16_t* __restrict__ H,
       }
     }
   }
+  if (__ballot(range_bad != 0u) != 0ull && (tid & 63) == 0) atomicOr(hdr + kHdrErr, kErrRange);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) nmax = fmaxf(nmax, __shfl_xor(nmax, o));
   if ((tid & 63) == 0) red[tid >> 6] = nmax;

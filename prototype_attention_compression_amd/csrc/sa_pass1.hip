@@ -179,6 +179,7 @@ __global__ __launch_bounds__(256) void pass1_lse(const uint16_t* __restrict__ H,
   bool valid[2];
   int32_t tiles[2];
   bool need_exact = false;
+  uint32_t range_bad = 0u;   // kept values outside fp16's finite range
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
     const int32_t tile = tile0 + 2 * wave + tau;
@@ -194,7 +195,11 @@ __global__ __launch_bounds__(256) void pass1_lse(const uint16_t* __restrict__ H,
         if (valid[tau]) {
           const u32x4* src = reinterpret_cast<const u32x4*>(H + tok * D);
 #pragma unroll
-          for (int s = 0; s < C::S; ++s) hreg[tau][s] = bf16x8_to_f16x8(src[2 * s + g]);
+          for (int s = 0; s < C::S; ++s) {
+            const u32x4 raw = src[2 * s + g];
+            range_bad |= bf16x8_range_bits(raw);
+            hreg[tau][s] = bf16x8_to_f16x8(raw);
+          }
         }
       }
     }
@@ -210,6 +215,7 @@ __global__ __launch_bounds__(256) void pass1_lse(const uint16_t* __restrict__ H,
     if (valid[tau] && qmax * sqrtf(n2) >= 100.0f) need_exact = true;
   }
   need_exact = __syncthreads_or(need_exact);
+  if (__ballot(range_bad != 0u) != 0ull && lane == 0) atomicOr(ws_i32(ws, L.off_hdr) + kHdrErr, kErrRange);
 
   const char* q16 = reinterpret_cast<const char*>(ws_f16(ws, L.off_q16));
   float sum[2] = {0.f, 0.f};

@@ -13,8 +13,9 @@
 // Per 32-token tile:
 //   * conversion (all 512 threads, one 16-byte chunk each): the bf16 row
 //     chunk loaded two tiles earlier is widened to fp16 (exact for
-//     magnitudes in [2^-17, 65504]), written to LDS and to the fp16 row
-//     buffer pass 2 reads; masked tokens and padding rows are zero.  The row
+//     magnitudes in [2^-17, 65504]; a kept value beyond that range raises
+//     a device error bit), written to LDS and to the fp16 row buffer pass 2
+//     reads; masked tokens and padding rows are zero.  The row
 //     norms decide, per tile, whether any logit can reach |L| >= 100
 //     (Cauchy-Schwarz with the largest query norm): then the tile takes the
 //     exact form (running maximum, rescaled sums), else plain sums of 2^L;
@@ -114,19 +115,26 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   // whether the slot is live kept aside: no load sits behind a branch, so
   // the compiler's wait before the conversion two tiles later counts only
   // what was issued after it instead of draining the prefetches and stores.
+  // A slot that holds no token of the user reads the user's first row: a
+  // user with tiles has at least one token, whereas the first slot of a
+  // padding tile (tiles are rounded up to a multiple of kUserTileAlign) lies
+  // past the user's rows, and for the last user past the end of H.
   int lu = find_user(tile_base, L.R, ta);
   auto load = [&](int32_t tile, u32x4& raw, uint32_t& mb, bool& in) {
     const bool live = tile < tb;               // uniform
     const int32_t tl = live ? tile : tb - 1;   // a tile of this workgroup
     while (tl >= tile_base[lu + 1]) ++lu;      // uniform
-    const int64_t t0 = offsets[lu] + (int64_t)(tl - tile_base[lu]) * kTile;
-    const int64_t tok = t0 + crow;
+    const int64_t first = offsets[lu];
+    const int64_t tok = first + (int64_t)(tl - tile_base[lu]) * kTile + crow;
     in = live && conv && tok < offsets[lu + 1];
-    const int64_t tc = in ? tok : t0;          // t0 is a token of user lu
+    const int64_t tc = in ? tok : first;       // a token of user lu
     raw = reinterpret_cast<const u32x4*>(H + tc * D)[cch];
     if constexpr (MASKED) mb = mask[tc];
     else mb = 1u;
   };
+  // kept values outside fp16's finite range, raised as a device error bit
+  // once the tiles are done (no branch inside the loop)
+  uint32_t range_bad = 0u;
   // widen, store to LDS buffer b and to the fp16 rows; keep words and the
   // per-wave "some logit may reach 100" bit.  A dropped token's row becomes
   // zero here (whatever it held, NaN included).  Runs for every iteration,
@@ -135,6 +143,7 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   auto convert = [&](int32_t tile, int b, const u32x4& raw_in, uint32_t mb, bool in) {
     const bool keep = in && mb != 0u;
     const u32x4 raw = keep ? raw_in : u32x4{0u, 0u, 0u, 0u};
+    range_bad |= bf16x8_range_bits(raw);
     const half8 hv = bf16x8_to_f16x8(raw);
     float n2 = 0.f;
 #pragma unroll
@@ -313,6 +322,7 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   if (j < n) iteration(j, std::integral_constant<int, 1>{});
   lds_barrier();
   finalize(n - 1, (n - 1) % kBufs);
+  if (__ballot(range_bad != 0u) != 0ull && lane == 0) atomicOr(ws_i32(ws, L.off_hdr) + kHdrErr, kErrRange);
 }
 
 bool pass1q_ok(const Layout& L) {

@@ -43,7 +43,7 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void ta_attend(const uint16_t* __restrict__ Q,
                                                     const int64_t* __restrict__ cand_offsets,
                                                     const float* __restrict__ Sk,
-                                                    const int32_t* __restrict__ sketch_rows,
+                                                    const int32_t* __restrict__ sketch_rows, int64_t sketch_count,
                                                     const int32_t* __restrict__ tile_base, Layout L, void* ws,
                                                     float* __restrict__ out, float* __restrict__ lse_out) {
   constexpr int S = D / 16, DT = D / 32, PITCH = tile_pitch<D>(), BLK = kTile * PITCH;
@@ -80,19 +80,37 @@ __global__ __launch_bounds__(256, 2) void ta_attend(const uint16_t* __restrict__
   const int count = rem < 0 ? 0 : (rem < kTile ? (int)rem : kTile);
   const bool active = __builtin_amdgcn_readfirstlane(count) > 0;   // uniform over the wave
 
+  // the user's sketch: row u of Sk, or row sketch_rows[u] (e.g. a cache
+  // slot).  An index outside [0, sketch_count) reads nothing: the user's
+  // candidates get zero outputs and the device error flag is raised (the
+  // test is uniform over the workgroup: its 4 tiles belong to user u).
+  const int64_t srow = sketch_rows != nullptr ? (int64_t)sketch_rows[u] : (int64_t)u;
+  if (srow < 0 || srow >= sketch_count) {
+    for (int t = 0; t < count; ++t) out[(c0 + t) * D + lane] = 0.f;
+    if constexpr (D > 64)
+      for (int t = 0; t < count; ++t) out[(c0 + t) * D + 64 + lane] = 0.f;
+    if (lse_out != nullptr && lane < count) lse_out[c0 + lane] = 0.f;
+    if (tid == 0) atomicOr(ws_i32(ws, L.off_hdr) + kHdrErr, kErrSketchRow);
+    return;
+  }
+  const float* Su = Sk + srow * L.k * D;
+
+  // candidate queries and sketch values outside fp16's finite range (they
+  // become fp16 MFMA operands) raise a device error bit at the end
+  uint32_t range_bad = 0u;
   half8 qB[S];
   if (col < count) {
     const uint16_t* qrow = Q + (c0 + col) * D;
 #pragma unroll
-    for (int s = 0; s < S; ++s) qB[s] = bf16x8_to_f16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * g));
+    for (int s = 0; s < S; ++s) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * g);
+      range_bad |= bf16x8_range_bits(raw);
+      qB[s] = bf16x8_to_f16x8(raw);
+    }
   } else {
 #pragma unroll
     for (int s = 0; s < S; ++s) qB[s] = half8{};
   }
-
-  // the user's sketch: row u of Sk, or row sketch_rows[u] (e.g. a cache slot)
-  const int64_t srow = sketch_rows != nullptr ? (int64_t)sketch_rows[u] : (int64_t)u;
-  const float* Su = Sk + srow * L.k * D;
   const int NB = L.k / kTile;
   // two register sets: the global loads of block i + 2 are issued while
   // block i is computed, and block i + 1 (loaded an iteration earlier) goes
@@ -107,6 +125,8 @@ __global__ __launch_bounds__(256, 2) void ta_attend(const uint16_t* __restrict__
 #pragma unroll
     for (int k2 = 0; k2 < LPT; ++k2) {
       const int idx = tid + 256 * k2, row = idx / F4R, c4 = idx % F4R;
+      const float big = fmaxf(fmaxf(fabsf(pf[k2].x), fabsf(pf[k2].y)), fmaxf(fabsf(pf[k2].z), fabsf(pf[k2].w)));
+      range_bad |= !(big <= 65504.0f) ? 1u : 0u;   // NaN fails the test too
       const half2v lo = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(pf[k2].x, pf[k2].y));
       const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(pf[k2].z, pf[k2].w));
       uint2 w;
@@ -222,10 +242,12 @@ __global__ __launch_bounds__(256, 2) void ta_attend(const uint16_t* __restrict__
     }
   }
   if (lse_out != nullptr && g == 0 && col < count) lse_out[c0 + col] = (m + __log2f(l)) * 0.69314718055994531f;
+  if (__ballot(range_bad != 0u) != 0ull && lane == 0) atomicOr(ws_i32(ws, L.off_hdr) + kHdrErr, kErrRange);
 }
 
 hipError_t launch_target_attention(const Layout& L, const void* Q, const int64_t* cand_offsets, const float* S,
-                                   const int32_t* sketch_rows, void* ws, float* out, float* lse, hipStream_t stream) {
+                                   const int32_t* sketch_rows, int64_t sketch_count, void* ws, float* out, float* lse,
+                                   hipStream_t stream) {
   if (launch_schedule(L, cand_offsets, ws, stream) != hipSuccess) return hipErrorLaunchFailure;
   if (L.N == 0) return hipSuccess;
   // a multiple of 8 workgroups covering every quad of tiles (see ta_attend)
@@ -233,10 +255,10 @@ hipError_t launch_target_attention(const Layout& L, const void* Q, const int64_t
   const int32_t* tb = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(ws) + L.off_tile_base);
   if (L.d == 128)
     hipLaunchKernelGGL((ta_attend<128>), dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)Q, cand_offsets,
-                       S, sketch_rows, tb, L, ws, out, lse);
+                       S, sketch_rows, sketch_count, tb, L, ws, out, lse);
   else
     hipLaunchKernelGGL((ta_attend<64>), dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)Q, cand_offsets,
-                       S, sketch_rows, tb, L, ws, out, lse);
+                       S, sketch_rows, sketch_count, tb, L, ws, out, lse);
   return hipGetLastError();
 }
 

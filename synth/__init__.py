@@ -11,6 +11,7 @@ from .gen import (  # noqa: F401
     f32_to_bf16_bits,
     make_candidates,
     make_config,
+    make_hard_assignment_inputs,
     make_inputs,
     make_sketch_grad,
     make_sketches,

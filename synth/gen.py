@@ -42,6 +42,7 @@ __all__ = [
     "bf16_bits_to_f32",
     "f32_to_bf16_bits",
     "make_config",
+    "make_hard_assignment_inputs",
     "make_inputs",
     "make_candidates",
     "make_sketch_grad",
@@ -275,6 +276,76 @@ def make_config(name: str, **overrides) -> Inputs:
 
 def config_names() -> List[str]:
     return list(CONFIGS)
+
+
+def make_hard_assignment_inputs(lengths, d: int, k: int, seed: int, soft_frac: float = 0.2,
+                                name: str = "hard") -> Inputs:
+    """Inputs in the hard-assignment limit of the per-token softmax, with
+    prototypes that receive no mass although tokens are present.
+
+    Built so that the logit p_j . (h_t Wk) / sqrt(d) of every token is either
+    one of its one or two "winning" values, at least 800 above every other
+    logit of that token, or within about 0.1 of zero:
+
+    * Wk = identity, Wv ~ N(0, 1/d) (bf16);
+    * P: row j < d - 1 is alpha e_j with alpha = 64; row d - 1 is zero; rows
+      d .. 2d - 2 (when k allows) are -alpha e_(j - d); every further row is
+      zero.  The zero rows and the negated rows never win a token;
+    * token t (own stream per user): a "hard" token is beta_h e_c plus noise,
+      c uniform in [0, d - 2], with beta_h = 8 sqrt(d) * 128 / alpha rounded
+      to a bf16 value; a "soft" token (fraction ``soft_frac``) is
+      beta_s e_a + (beta_s + delta) e_b plus noise for two distinct a, b,
+      with beta_s about 0.78 beta_h and delta one bf16 step or zero, so its
+      two winning logits differ by a few units;
+    * noise: 0.01 N(0, 1) on every feature.
+
+    Everything is drawn in float32 and rounded to bf16 (RNE), as
+    ``make_inputs`` does.  Nothing here evaluates logits or allocations.
+    """
+    lens = np.asarray(list(lengths), dtype=np.int64)
+    offsets = np.zeros(lens.shape[0] + 1, dtype=np.int64)
+    np.cumsum(lens, out=offsets[1:])
+    N = int(offsets[-1])
+    ss = np.random.SeedSequence(seed)
+    rng = np.random.default_rng(ss.spawn(1)[0])
+    alpha = np.float32(64.0)
+    Wk32 = np.eye(d, dtype=np.float32)
+    Wv32 = rng.standard_normal((d, d), dtype=np.float32) * np.float32(1.0 / math.sqrt(d))
+    P32 = np.zeros((k, d), dtype=np.float32)
+    for j in range(min(k, d - 1)):
+        P32[j, j] = alpha
+    for j in range(d, min(k, 2 * d - 1)):
+        P32[j, j - d] = -alpha
+    def bf16_value(x, up=0):
+        bits = f32_to_bf16_bits(np.array([x], dtype=np.float32)) + np.uint16(up)
+        return float(bf16_bits_to_f32(bits)[0])
+
+    beta_h = bf16_value(8.0 * math.sqrt(d) * 128.0 / 64.0)
+    beta_s = bf16_value(0.78 * beta_h)
+    step = bf16_value(beta_s, up=1) - beta_s   # one bf16 step above beta_s
+    H32 = np.empty((N, d), dtype=np.float32)
+    user_ss = np.random.SeedSequence(seed).spawn(1 + lens.shape[0])[1:]
+    for u in range(lens.shape[0]):
+        lo, hi = int(offsets[u]), int(offsets[u + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        g = np.random.default_rng(user_ss[u])
+        H32[lo:hi] = np.float32(0.01) * g.standard_normal((n, d), dtype=np.float32)
+        soft = g.random(n) < soft_frac
+        c = g.integers(0, d - 1, size=n)
+        b = (c + 1 + g.integers(0, d - 2, size=n)) % (d - 1)     # != c
+        delta = np.where(g.random(n) < 0.5, 0.0, step).astype(np.float32)
+        rows = np.arange(lo, hi)
+        H32[rows[~soft], c[~soft]] += np.float32(beta_h)
+        H32[rows[soft], c[soft]] += np.float32(beta_s)
+        H32[rows[soft], b[soft]] += np.float32(beta_s) + delta[soft]
+    H, H_bits = _round_store(H32, "bf16")
+    Wk, Wk_bits = _round_store(Wk32, "bf16")
+    Wv, Wv_bits = _round_store(Wv32, "bf16")
+    P, P_bits = _round_store(P32, "bf16")
+    return Inputs(name=name, dtype="bf16", d=d, k=k, lengths=lens, offsets=offsets, H=H, Wk=Wk, Wv=Wv, P=P,
+                  mask=None, seed=seed, H_bits=H_bits, Wk_bits=Wk_bits, Wv_bits=Wv_bits, P_bits=P_bits)
 
 
 def make_sketch_grad(R: int, k: int, d: int, seed: int, scale: float = 1.0, users=None) -> np.ndarray:

@@ -152,18 +152,18 @@ def test_backward_argument_errors_before_launch():
     lib = _lib.load()
     vp = None
     assert lib.sa_compress_backward(None, *([vp] * 12), 0, vp) == sa.SA_E_INVALID
-    pb = _lib.problem(2, 100, 128, 256, 0)
+    pb = _lib.problem(2, 100, 128, 512, 0)
     for name in ("off", "H", "Wk", "Wv", "P", "dS", "dH", "dP", "dWk", "dWv"):
         assert _bcall(pb, **{name: None}) == sa.SA_E_INVALID, name
     assert _bcall(pb, ws=None) == sa.SA_E_WORKSPACE
-    need = _bws(2, 100, 128, 256, 0)[1]
+    need = _bws(2, 100, 128, 512, 0)[1]
     assert _bcall(pb, wsb=need - 1) == sa.SA_E_WORKSPACE
     assert _bcall(pb, ws=FAKE + 16, wsb=need) == sa.SA_E_INVALID
-    assert _bcall(_lib.problem(2, 100, 128, 256, sa.SA_F32)) == sa.SA_E_UNSUPPORTED
-    assert _bcall(_lib.problem(2, 100, 128, 256, 0, sa.SA_FLAG_ONE_PASS)) == sa.SA_E_UNSUPPORTED
+    assert _bcall(_lib.problem(2, 100, 128, 512, sa.SA_F32)) == sa.SA_E_UNSUPPORTED
+    assert _bcall(_lib.problem(2, 100, 128, 512, 0, sa.SA_FLAG_ONE_PASS)) == sa.SA_E_UNSUPPORTED
     # no tokens: H and dH may be NULL (the call would then launch, so only
     # the argument checks that come first are exercised here)
-    assert _bcall(_lib.problem(2, 0, 128, 256, 0), H=None, dH=None, ws=None) == sa.SA_E_WORKSPACE
+    assert _bcall(_lib.problem(2, 0, 128, 512, 0), H=None, dH=None, ws=None) == sa.SA_E_WORKSPACE
 
 
 def test_backward_binding_validates_before_library():
@@ -199,13 +199,32 @@ def test_target_attention_argument_errors_before_launch():
     assert call(pb, ws=None) == sa.SA_E_WORKSPACE
     assert call(pb, wsb=need - 1) == sa.SA_E_WORKSPACE
     assert call(_lib.problem(0, 0, 128, 1024, 0), Q=None, off=None, S=None, o=None, ws=None, wsb=0) == sa.SA_OK
+    # the row-indexed form: a negative sketch count is an argument error
+    rows = FAKE + 256
+    assert _lib.raw_target_attention(pb, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None, sketch_rows=rows,
+                                     sketch_count=-1) == sa.SA_E_INVALID
+    assert _lib.raw_target_attention(pb, FAKE, FAKE, FAKE, FAKE, None, None, 0, None, sketch_rows=rows,
+                                     sketch_count=7) == sa.SA_E_WORKSPACE
+    assert lib.sa_target_attention(None, *([None] * 6), 0, None) == sa.SA_E_INVALID
 
 
-def test_reuse_forward_flag_is_backward_only():
-    assert _ws(1, 10, 128, 1024, 0, flags=sa.SA_FLAG_REUSE_FORWARD)[0] == sa.SA_E_INVALID
-    # switched off (see the note on SA_FLAG_REUSE_FORWARD in include/sa.h)
-    assert _bws(1, 10, 128, 1024, 0, flags=sa.SA_FLAG_REUSE_FORWARD)[0] == sa.SA_E_UNSUPPORTED
-    assert _bws(1, 10, 128, 1024, 0, flags=sa.SA_FLAG_REUSE_FORWARD | sa.SA_FLAG_ONE_PASS)[0] == sa.SA_E_UNSUPPORTED
+def test_workspace_bytes_matches_workspace_size():
+    lib = _lib.load()
+    for R, N, d, k, dt in ((1, 100_000, 128, 1024, 0), (40, 4_000_000, 128, 1024, 0), (3, 77, 64, 320, 1),
+                           (0, 0, 128, 256, 0)):
+        pb = _lib.problem(R, N, d, k, dt)
+        assert lib.sa_workspace_bytes(ctypes.byref(pb)) == sa.workspace_size(R, N, d, k, dt)
+    assert lib.sa_workspace_bytes(None) == 0
+    bad = _lib.problem(1, 10, 96, 1024, 0)
+    assert lib.sa_workspace_bytes(ctypes.byref(bad)) == 0
+
+
+def test_unknown_flag_bits_are_invalid():
+    for bit in (4, 8, 1 << 30):
+        assert _ws(1, 10, 128, 1024, 0, flags=bit)[0] == sa.SA_E_INVALID
+        assert _bws(1, 10, 128, 1024, 0, flags=bit)[0] == sa.SA_E_INVALID
+
+
 
 
 # ---------------------------------------------------------------- forward state for the backward
@@ -226,7 +245,7 @@ def test_compress_with_sbar_argument_errors_before_launch():
 
 
 def test_backward_with_sbar_argument_errors_before_launch():
-    pb = _lib.problem(2, 100, 128, 256, 0)
+    pb = _lib.problem(2, 100, 128, 512, 0)
 
     def call(pb, Sbar=FAKE, mass=FAKE, ws=FAKE, wsb=1 << 40, **kw):
         a = dict(H=FAKE, off=FAKE, Wk=FAKE, Wv=FAKE, P=FAKE, dS=FAKE, dH=FAKE, dP=FAKE, dWk=FAKE, dWv=FAKE)
@@ -240,10 +259,10 @@ def test_backward_with_sbar_argument_errors_before_launch():
     for name in ("off", "H", "Wk", "Wv", "P", "dS", "dH", "dP", "dWk", "dWv"):
         assert call(pb, **{name: None}) == sa.SA_E_INVALID, name
     assert call(pb, ws=None) == sa.SA_E_WORKSPACE
-    need = _bws(2, 100, 128, 256, 0)[1]
+    need = _bws(2, 100, 128, 512, 0)[1]
     assert call(pb, wsb=need - 1) == sa.SA_E_WORKSPACE
-    assert call(_lib.problem(2, 100, 128, 256, 0, sa.SA_FLAG_REUSE_FORWARD)) == sa.SA_E_INVALID
-    assert call(_lib.problem(2, 100, 128, 256, sa.SA_F32)) == sa.SA_E_UNSUPPORTED
+    assert call(_lib.problem(2, 100, 128, 512, 0, 4)) == sa.SA_E_INVALID   # unknown flag bit
+    assert call(_lib.problem(2, 100, 128, 512, sa.SA_F32)) == sa.SA_E_UNSUPPORTED
     assert _lib.load().sa_compress_backward_with_sbar(None, *([None] * 14), 0, None, None) == sa.SA_E_INVALID
 
 
@@ -258,7 +277,7 @@ def test_sbar_binding_validates_before_library():
 def test_misaligned_inputs_rejected_before_launch():
     """H, Wk, Wv and P are read in 16-byte vectors and offsets as int64: a
     misaligned pointer is an argument error, caught on the host."""
-    pb = _lib.problem(2, 100, 128, 256, 0)
+    pb = _lib.problem(2, 100, 128, 512, 0)
     for name in ("H", "Wk", "Wv", "P"):
         assert _call(pb, **{name: FAKE + 2}) == sa.SA_E_INVALID, name
         assert _bcall(pb, **{name: FAKE + 8}) == sa.SA_E_INVALID, name

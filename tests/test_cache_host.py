@@ -147,3 +147,30 @@ def test_argument_errors():
     assert lib.sa_cache_fill_workspace_size(ctypes.byref(pb), 3, 100, ctypes.byref(out)) == sa.SA_OK
     assert out.value >= sa.workspace_size(3, 100, 128, 256)
     assert lib.sa_cache_fill_workspace_size(ctypes.byref(pb), -1, 100, ctypes.byref(out)) == sa.SA_E_INVALID
+
+
+def test_refused_batch_leaves_the_cache_unchanged():
+    """A batch with more distinct users than slots is refused before any
+    state changes: the lookups that follow give exactly what they give on a
+    cache that never saw the refused batch (slots, misses, statistics)."""
+    g = np.random.default_rng(9)
+    cap, ttl = 6, 5.0
+    a = sa.SketchCache(cap, 64, 64, ttl, FAKE_SLAB)
+    b = sa.SketchCache(cap, 64, 64, ttl, FAKE_SLAB)
+    now = 0.0
+    for step in range(40):
+        now += float(g.exponential(1.0))
+        users = g.integers(0, 12, size=int(g.integers(1, 9))).astype(np.int64)
+        if len(set(users.tolist())) > cap:
+            users = users[:cap]
+        if step % 5 == 2:
+            # some users already cached, then more distinct users than slots
+            refused = np.concatenate([users, np.arange(100, 100 + cap + 1)]).astype(np.int64)
+            with pytest.raises(sa.SaError):
+                a.lookup(refused, now)
+        ra, rb = a.lookup(users, now), b.lookup(users, now)
+        assert ra[0].tolist() == rb[0].tolist()
+        assert ra[1].tolist() == rb[1].tolist() and ra[2].tolist() == rb[2].tolist()
+        assert ra[3] == rb[3]
+    a.close()
+    b.close()
