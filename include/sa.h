@@ -180,6 +180,38 @@ sa_status sa_compress_with_events(const sa_problem* problem,
                                   void* const* events);
 
 /*
+ * For callers that cannot allocate device memory at call time (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * sa_compress without a workspace argument.  Its workspace is a static
+ * device array of SA_STATIC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends; the call itself allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).
+ *   - Problems whose sa_workspace_size exceeds SA_STATIC_SCRATCH_BYTES are
+ *     SA_E_WORKSPACE (64 MiB: e.g. one 100,000-token user at k = 1024,
+ *     d = 128, or any batch of up to about 30,000 tokens at k <= 1024).
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap
+ *     on one GPU (different streams, other threads) race and give undefined
+ *     results.  Serialise them, e.g. on one stream.
+ *   - device_error: optional [1] int32 device pointer; when non-NULL it
+ *     receives the call's device error flags (the SA_DEVICE_ERR_* bits that
+ *     sa_read_device_error reports for a workspace), stream-ordered.
+ * Arguments, results and errors otherwise as sa_compress.
+ */
+#define SA_STATIC_SCRATCH_BYTES (64u << 20)
+
+sa_status sa_compress_static(const sa_problem* problem,
+                             const void* H,
+                             const int64_t* offsets,
+                             const uint8_t* token_mask,
+                             const void* Wk,
+                             const void* Wv,
+                             const void* P,
+                             float* S,
+                             float* mass,
+                             int32_t* device_error,
+                             void* stream);
+
+/*
  * sa_compress_with_events that also writes the mass-normalised rows
  *     Sbar [R, k, d] float32,  Sbar_u[j] = (sum_t A[j,t] h_t) / m_j
  * (0 where m_j = 0), i.e. S_u = Sbar_u Wv before the value projection.  A

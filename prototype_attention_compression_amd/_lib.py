@@ -19,7 +19,7 @@ SA_DEVICE_ERR_OFFSETS, SA_DEVICE_ERR_EXCHANGE, SA_DEVICE_ERR_RANGE, SA_DEVICE_ER
 _PATH_FLAGS = {None: 0, "auto": 0, "two": SA_FLAG_TWO_PASS, "one": SA_FLAG_ONE_PASS}
 
 # functions declared in include/sa.h
-EXPORTS = ("sa_workspace_size", "sa_workspace_bytes", "sa_compress", "sa_compress_with_events", "sa_compress_with_sbar",
+EXPORTS = ("sa_workspace_size", "sa_workspace_bytes", "sa_compress_static", "sa_compress", "sa_compress_with_events", "sa_compress_with_sbar",
            "sa_backward_workspace_size", "sa_compress_backward", "sa_compress_backward_with_events",
            "sa_compress_backward_with_sbar",
            "sa_target_attention_workspace_size", "sa_target_attention", "sa_target_attention_rows",
@@ -27,6 +27,7 @@ EXPORTS = ("sa_workspace_size", "sa_workspace_bytes", "sa_compress", "sa_compres
            "sa_cache_fill",
            "sa_read_device_error", "sa_status_string", "sa_version")
 NUM_PHASE_EVENTS = 5
+STATIC_SCRATCH_BYTES = 64 << 20   # SA_STATIC_SCRATCH_BYTES
 NUM_BWD_PHASE_EVENTS = 6
 
 
@@ -81,6 +82,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sa_workspace_bytes.restype = sz
     lib.sa_compress.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sa_compress.restype = ctypes.c_int
+    lib.sa_compress_static.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.sa_compress_static.restype = ctypes.c_int
     lib.sa_compress_with_events.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.sa_compress_with_events.restype = ctypes.c_int
     lib.sa_compress_with_sbar.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
@@ -195,6 +198,13 @@ def raw_compress(pb: SaProblem, H, offsets, mask, Wk, Wv, P, S, mass, workspace,
     return int(load().sa_compress_with_events(ctypes.byref(pb), H, offsets, mask, Wk, Wv, P, S, mass,
                                               workspace, ctypes.c_size_t(workspace_bytes), stream,
                                               events))
+
+
+def raw_compress_static(pb: SaProblem, H, offsets, mask, Wk, Wv, P, S, mass, device_error, stream) -> int:
+    """Direct call of sa_compress_static (no workspace argument); returns the
+    status."""
+    return int(load().sa_compress_static(ctypes.byref(pb), H, offsets, mask, Wk, Wv, P, S, mass, device_error,
+                                         stream))
 
 
 def _ptr(t):

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "sa.h"
 #include "sa_launch.h"
@@ -316,10 +317,73 @@ sa_status backward_impl(const sa_problem* problem, const void* H, const int64_t*
   }
 }
 
+// ------------------------------------------------ allocation-free entry point
+// sa_compress_static's workspace: a file-scope device array, held by every
+// GPU the library runs on until the process ends.  In host code `scratch`
+// names a host-side stand-in, never device memory: its device address on a
+// GPU comes from hipGetSymbolAddress, taken once per device (with that
+// device current) and kept; kernels only ever receive that address.
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mutex;
+
+}  // namespace
+
+__device__ __align__(256) unsigned char scratch[SA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+// The current device's scratch address, or nullptr if it cannot be had.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+    if (reinterpret_cast<uintptr_t>(q) % kAlign != 0) return nullptr;
+    g_scratch_ptr[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
 }  // namespace
 }  // namespace sa
 
 extern "C" {
+
+sa_status sa_compress_static(const sa_problem* problem, const void* H, const int64_t* offsets,
+                             const uint8_t* token_mask, const void* Wk, const void* Wv, const void* P, float* S,
+                             float* mass, int32_t* device_error, void* stream) {
+  try {
+    sa_status st = sa::check_problem(problem);
+    if (st != SA_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (problem->num_users == 0) {
+      // nothing to compress; the error word of a no-op is 0
+      if (device_error != nullptr &&
+          sa::launch_fill_zero(reinterpret_cast<float*>(device_error), 1, s) != hipSuccess)
+        return SA_E_HIP;
+      return SA_OK;
+    }
+    if (sa::make_layout(*problem).total > (size_t)SA_STATIC_SCRATCH_BYTES) return SA_E_WORKSPACE;
+    void* ws = sa::scratch_address();
+    if (ws == nullptr) return SA_E_HIP;
+    st = sa::compress_impl(problem, H, offsets, token_mask, Wk, Wv, P, S, mass, nullptr, ws,
+                           (size_t)SA_STATIC_SCRATCH_BYTES, stream, nullptr);
+    if (st != SA_OK) return st;
+    if (device_error != nullptr &&
+        sa::launch_copy_error(sa::make_layout(*problem), ws, device_error, s) != hipSuccess)
+      return SA_E_HIP;
+    return SA_OK;
+  } catch (...) {
+    return SA_E_HIP;
+  }
+}
 
 sa_status sa_workspace_size(const sa_problem* problem, size_t* bytes) {
   if (bytes == nullptr) return SA_E_INVALID;

@@ -57,5 +57,7 @@ hipError_t launch_target_attention(const Layout& L, const void* Q, const int64_t
                                    hipStream_t stream);
 // zero fill (used when the batch has no users)
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+// dst[0] = the workspace's device error word
+hipError_t launch_copy_error(const Layout& L, const void* ws, int32_t* dst, hipStream_t stream);
 
 }  // namespace sa

@@ -166,6 +166,18 @@ __global__ __launch_bounds__(256) void clear_words(uint64_t* __restrict__ p, int
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0ull;
 }
 
+// dst[0] = the workspace's device error word (a kernel rather than a copy,
+// so that the sequence can be captured in a graph)
+__global__ __launch_bounds__(64) void copy_error_word(const int32_t* __restrict__ hdr, int32_t* __restrict__ dst) {
+  if (threadIdx.x == 0) dst[0] = hdr[kHdrErr];
+}
+
+hipError_t launch_copy_error(const Layout& L, const void* ws, int32_t* dst, hipStream_t stream) {
+  const int32_t* hdr = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + L.off_hdr);
+  hipLaunchKernelGGL(copy_error_word, dim3(1), dim3(64), 0, stream, hdr, dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_schedule(const Layout& L, const int64_t* offsets, void* ws, hipStream_t stream) {
   hipLaunchKernelGGL(prep_schedule, dim3(1), dim3(1024), 0, stream, offsets, L, ws);
   return hipGetLastError();
