@@ -73,6 +73,29 @@ TRAFFIC = {
 }
 
 
+# MFMA busy fraction of a kernel (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE / 8
+# x 1024 SIMDs) and the shader clock under that load (GRBM_GUI_ACTIVE / 8 over the
+# kernel's time), from rocprofv3 --pmc on the default workload; valid, like the
+# traffic figures, only for the kernel sources they were taken on (null after).
+COUNTERS = {
+    "pass2_accum": ({"mfma_busy": 0.59, "clock_mhz": 1900.0},
+                    "106926115929e4c35f66bb44da9f6cb58f6424a9449823e6a4de3926fbb74eed",
+                    ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
+}
+
+# The pages' own efficiency figures, context only: analytic FLOP ratios of the
+# cached-sketch path against direct target attention over the 100K history, with
+# no hardware stated (blog "100,000 videos in your pocket", "The numbers"; review
+# page, "Key claims under review").
+PAGES_CONTEXT = {
+    "training_flop_ratio": 49.9,
+    "training_setting": "R = 40 users per batch, cache-hit rate 0.5",
+    "serving_flop_ratio": 63.9,
+    "serving_setting": "R = 300 requests, cache-hit rate 0.6",
+    "note": "analytic FLOP ratios of the cache-hit path vs direct STCA at 100K; not measured, no hardware",
+}
+
+
 def sources_digest(names) -> str:
     import hashlib
 
@@ -82,6 +105,42 @@ def sources_digest(names) -> str:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def measured_counters(kernel: str):
+    """Stored counter figures of ``kernel``, or None once its sources changed."""
+    if kernel not in COUNTERS:
+        return None
+    vals, digest, names = COUNTERS[kernel]
+    return dict(vals) if sources_digest(names) == digest else None
+
+
+def executed_mfma_flop(lengths, k: int, d: int, path: str) -> float:
+    """MFMA FLOP the kernels execute for one step (not the algorithmic 4 N k d):
+    two passes recompute every logit (pass 1: 2 k d per tile-padded token; pass
+    2: 4 k d plus the -l step's 2 k 16), the one-pass kernel computes each once
+    (4 k d); the query preparation and the value projection add 2 k d^2 and
+    3 x 2 R k d^2 (three-term split)."""
+    lens = np.asarray(lengths, dtype=np.int64)
+    n_pad = float(((lens + 127) // 128 * 128).sum())
+    per_token = 4.0 * k * d if path == "one" else 2.0 * k * d + 4.0 * k * d + 2.0 * k * 16
+    return n_pad * per_token + 2.0 * k * d * d + 6.0 * len(lens) * k * d * d
+
+
+def oracle_chunk_one_thread(inp) -> dict:
+    """The fp64 oracle on one 8192-token chunk of the workload with one BLAS
+    thread (a per-core reference beside the multi-core baseline)."""
+    import threadpoolctl
+
+    from oracle import sketch_one
+
+    n = min(8192, int(inp.lengths[0]))
+    Hu = inp.H[:n]
+    with threadpoolctl.threadpool_limits(1):
+        t0 = time.perf_counter()
+        sketch_one(Hu, inp.Wk, inp.Wv, inp.P)
+        t = time.perf_counter() - t0
+    return {"tokens": n, "seconds": t, "tokens_per_s": n / t, "threads": 1}
 
 
 def measured_traffic(kernel: str):
@@ -700,9 +759,11 @@ def main(argv=None):
 
     phases = ["prep", "pass1_lse", "pass2_accum", "finalize"]
     phase_ms = {p: 0.0 for p in phases}
+    per_step = []
     for evs in step_events:
         for i, p in enumerate(phases):
             phase_ms[p] += hip.elapsed_ms(evs[i], evs[i + 1]) / args.steps
+        per_step.append(hip.elapsed_ms(evs[0], evs[-1]))
     for evs in step_events:
         for e in evs:
             hip.destroy(e)
@@ -712,6 +773,12 @@ def main(argv=None):
     tokens_per_s = n_valid / (ms_step * 1e-3)
     p2_s = phase_ms["pass2_accum"] * 1e-3
     p2_achieved = algo_flop / p2_s / 1e12 if p2_s > 0 else 0.0
+    path = "two" if args.path == "auto" else args.path
+    exec_flop = executed_mfma_flop(inp.lengths, k, d, path) if inp.dtype == "bf16" else None
+    two_pass_default = inp.name == DEFAULT_WORKLOAD and args.path != "one"
+    traffic = measured_traffic("pass2_accum") if two_pass_default else None
+    counters = measured_counters("pass2_accum") if two_pass_default else None
+    props = torch.cuda.get_device_properties(dev)
     roofline = {
         "kernel": "pass2_accum",
         "bound": "mfma",
@@ -720,9 +787,13 @@ def main(argv=None):
         "unit": "TFLOP/s",
         "frac": p2_achieved / PEAK_MFMA_F16_TFLOPS,
         # counters were taken on the default workload's two-pass kernels
-        "traffic": measured_traffic("pass2_accum") if inp.name == DEFAULT_WORKLOAD and args.path != "one" else None,
+        "traffic": traffic,
         "per_launch_flop": algo_flop,
         "avg_launch_ms": phase_ms["pass2_accum"],
+        # the whole step (every kernel) against the same peak
+        "step_frac": tflops / PEAK_MFMA_F16_TFLOPS,
+        "mfma_busy": None if counters is None else counters["mfma_busy"],
+        "hbm_gbps": None if traffic is None or p2_s <= 0 else traffic / p2_s / 1e9,
     }
     out = {
         "metric": METRIC,
@@ -741,14 +812,23 @@ def main(argv=None):
                    "input_dtype": inp.dtype, "parallelism": "single_gpu"},
         "tflops": tflops,
         "pct_peak": tflops / PEAK_MFMA_F16_TFLOPS,
+        "exec_tflops": None if exec_flop is None else exec_flop / (ms_step * 1e-3) / 1e12,
+        "step_ms": {"median": float(np.median(per_step)), "min": float(np.min(per_step)), "reps": len(per_step)},
         "phase_ms": phase_ms,
         "wall_s_timed": t_wall,
         "roofline": roofline,
+        "gpu": {"name": props.name, "cus": props.multi_processor_count,
+                "clock_max_mhz": getattr(props, "clock_rate", 0) / 1000.0 or None,
+                "clock_under_load_mhz": None if counters is None else counters["clock_mhz"],
+                "rocm": torch.version.hip},
+        "seed": int(inp.seed),
+        "pages_context": PAGES_CONTEXT,
     }
     if args.calibrate_copy:
         _calibration_copy(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, S.cpu().numpy(), args.cpu_budget)
+        out["cpu_baseline"]["one_thread_chunk"] = oracle_chunk_one_thread(inp)
     print(json.dumps(out), flush=True)
     return 0
 

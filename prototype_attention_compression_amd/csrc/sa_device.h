@@ -16,6 +16,12 @@ typedef float float2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Word 3 of a gfx9 buffer resource for raw (unformatted) 32-bit data.  With
+// stride 0 the hardware drops stores and returns zeros for loads at byte
+// offsets at or beyond the resource's record count.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 // D = A(32x16) * B(16x32) + C on the matrix cores, fp16 operands, fp32 sums.
 // Lane l holds row (l % 32) of A and column (l % 32) of B, 8 contraction

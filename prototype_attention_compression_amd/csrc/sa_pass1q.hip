@@ -78,6 +78,10 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   __shared__ float part[2][kTile][W];
   __shared__ __attribute__((aligned(16))) uint32_t exact_bits[kBufs][W];
   __shared__ uint32_t keep_words[kBufs][kTile];
+  // A word per lane for the stores of lanes whose value another lane
+  // already stores: the store address is a select, not a branch, and no two
+  // lanes of a store share an address (same-address LDS stores serialise).
+  __shared__ uint32_t spare[W * 64];
 
   const int32_t* hdr = ws_i32(ws, L.off_hdr);
   const int32_t T = hdr[kHdrTiles];
@@ -105,8 +109,10 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   _Float16* h16 = ws_f16(ws, L.off_h16);
   uint32_t* nl = reinterpret_cast<uint32_t*>(ws_i32(ws, L.off_nl));
 
-  // conversion role of this thread: chunk q of a tile (row q / CPR, chunk q % CPR)
-  const bool conv = tid < C::CHUNKS;
+  // conversion role of this thread: chunk q of a tile (row q / CPR, chunk q %
+  // CPR); at d = 128 every thread has one
+  constexpr bool kAllConvert = C::CHUNKS == W * 64;
+  const bool conv = kAllConvert || tid < C::CHUNKS;
   const int crow = tid / C::CPR, cch = tid % C::CPR;
   // Forward walk over the tiles being loaded (tile index increases).  The
   // user lookup reads only kernel arguments the kernel never writes, so it
@@ -135,11 +141,23 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   // kept values outside fp16's finite range, raised as a device error bit
   // once the tiles are done (no branch inside the loop)
   uint32_t range_bad = 0u;
+  // A buffer view of this workgroup's fp16 rows, tiles [ta, tb): the
+  // hardware's range check drops the stores of conversions past the last
+  // tile, so the row store needs no branch.
+  const __amdgpu_buffer_rsrc_t h16_rows = __builtin_amdgcn_make_buffer_rsrc(
+      h16 + (int64_t)ta * kTile * D, (short)0, n * kTile * D * 2, kBufferRsrcWord3);
+  // the same for the -l pairs of tiles [ta, tb)
+  const __amdgpu_buffer_rsrc_t nl_view =
+      __builtin_amdgcn_make_buffer_rsrc(nl + (int64_t)ta * kTile, (short)0, n * kTile * 4, kBufferRsrcWord3);
   // widen, store to LDS buffer b and to the fp16 rows; keep words and the
   // per-wave "some logit may reach 100" bit.  A dropped token's row becomes
   // zero here (whatever it held, NaN included).  Runs for every iteration,
-  // past the last tile too (into a buffer nobody reads, no global store), so
-  // that consuming the prefetched registers never sits behind a branch.
+  // past the last tile too (into a buffer nobody reads; the row store is
+  // dropped), so that consuming the prefetched registers never sits behind
+  // a branch.  The exact/fast decision needs a bound on each row's norm: CPR
+  // times the largest squared norm of the row's 8-value chunks bounds it, so
+  // no exchange between lanes is needed.  At d = 128 the body has no branch,
+  // which lets it run interleaved with the previous tile's MFMAs.
   auto convert = [&](int32_t tile, int b, const u32x4& raw_in, uint32_t mb, bool in) {
     const bool keep = in && mb != 0u;
     const u32x4 raw = keep ? raw_in : u32x4{0u, 0u, 0u, 0u};
@@ -147,20 +165,23 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
     const half8 hv = bf16x8_to_f16x8(raw);
     float n2 = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = (float)hv[e];
-      n2 = fmaf(v, v, n2);
+    for (int i = 0; i < 4; ++i) {
+      // (the element goes through a named scalar: hipcc lowers a bit cast
+      // taken directly from a vector element to a read of element 0)
+      const uint32_t w = raw[i];
+      const bf16x2 x = __builtin_bit_cast(bf16x2, w);
+      n2 = __builtin_amdgcn_fdot2_f32_bf16(x, x, n2, false);
     }
-#pragma unroll
-    for (int o = 1; o < C::CPR; o <<= 1) n2 += __shfl_xor(n2, o);
-    if (conv) {
+    if (conv) {   // uniform: true for every thread at d = 128
       *reinterpret_cast<half8*>(&rows[b][crow * C::PITCH + 16 * cch]) = hv;
-      if (tile < tb) *reinterpret_cast<half8*>(h16 + ((int64_t)tile * kTile + crow) * D + 8 * cch) = hv;
-      if (cch == 0) keep_words[b][crow] = keep ? 1u : 0u;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hv), h16_rows,
+                                             ((tile - ta) * kTile + crow) * (D * 2) + 16 * cch, 0, 0);
+      uint32_t* kw = cch == 0 ? &keep_words[b][crow] : &spare[tid];
+      *kw = keep ? 1u : 0u;
     }
-    const bool big = conv && keep && n2 >= lim2;
-    const uint64_t bal = __ballot(big);
-    if (lane == 0) exact_bits[b][wave] = bal != 0 ? 1u : 0u;
+    const bool big = conv && keep && n2 * (float)C::CPR >= lim2;
+    const uint32_t eb = __ballot(big) != 0ull ? 1u : 0u;   // uniform over the wave
+    *(lane == 0 ? &exact_bits[b][wave] : &spare[tid]) = eb;
   };
 
   // whether some wave flagged tile buffer b for the exact form
@@ -210,7 +231,10 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
     return log_add_exp2(hp.lo, hp.hi);
   };
 
-  auto compute = [&](int j, int b) {
+  // `mid` (the next tile's conversion) runs after the first block's MFMAs
+  // are issued, in the same basic block, so its VALU work fills the MFMA
+  // pipeline's gaps instead of a phase of its own
+  auto compute = [&](int j, int b, auto&& mid) {
     const bool exact = tile_exact(b);
     float wpart;
     if constexpr (NBW == 1) {
@@ -226,6 +250,7 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
 #pragma unroll
         for (int bl = 0; bl < NBW; ++bl) a[bl] = mfma32x32x16(qf[bl][s], h, a[bl]);
       }
+      mid();
       wpart = block_partials(exact, a);
     } else {
       // block-major MFMA chains over the tile's operands held in registers:
@@ -240,6 +265,7 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
           float16v a = float16v{};
 #pragma unroll
           for (int s = 0; s < C::S; ++s) a = mfma32x32x16(qf[bl][s], ha[s], a);
+          if (bl == 0) mid();
 #pragma unroll
           for (int r = 0; r < 16; r += 2) {
             p0 += __builtin_amdgcn_exp2f(a[r]);
@@ -255,21 +281,25 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
           float16v a = float16v{};
 #pragma unroll
           for (int s = 0; s < C::S; ++s) a = mfma32x32x16(qf[bl][s], ha[s], a);
+          if (bl == 0) mid();
           exact_block(a, m, p);
         }
         const HalfPair hp = lane_halves(m + log2f(p));
         wpart = log_add_exp2(hp.lo, hp.hi);
       }
     }
-    if (g == 0) part[j & 1][col][wave] = wpart;
+    // both lane halves hold the same value; the upper half's store is spare
+    float* pw = g == 0 ? &part[j & 1][col][wave] : reinterpret_cast<float*>(&spare[tid]);
+    *pw = wpart;
   };
 
   // -l pairs of tile j (buffer b) from its 8 partials: wave w, lanes 0..3,
   // tokens 4 w .. 4 w + 3
   auto finalize = [&](int j, int b) {
     constexpr int TPW = kTile / W;   // tokens per wave
-    if (lane >= TPW) return;
-    const int tok = wave * TPW + lane;
+    // every lane works (no branch): lanes with equal lane % TPW store the
+    // same value to the same word
+    const int tok = wave * TPW + (lane % TPW);
     const bool exact = tile_exact(b);
     const float* pp = part[j & 1][tok];
     float lse;
@@ -289,7 +319,10 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
     const _Float16 hi = (_Float16)nlv;
     const _Float16 lo = keep ? (_Float16)(nlv - (float)hi) : (_Float16)0.0f;
     const half2v pr = {hi, lo};
-    nl[(int64_t)(ta + j) * kTile + tok] = __builtin_bit_cast(uint32_t, pr);
+    // lanes past TPW computed duplicates: their byte offset lies past the
+    // view's end, so the hardware drops their stores
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pr), nl_view,
+                                          lane < TPW ? (j * kTile + tok) * 4 : 0x7FFFFFF0, 0, 0);
   };
 
   // prologue: tiles 0 and 1 loaded, tile 0 converted into buffer 0
@@ -301,17 +334,17 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   convert(ta, 0, raw[0], mb[0], in[0]);
   load(ta + 2, raw[0], mb[0], in[0]);
 
-  // iteration j: convert tile j + 1 (loaded two iterations ago) into buffer
-  // (j + 1) % 3, finalize tile j - 1, compute tile j, then load tile j + 3.  The wait for tile j + 1's registers counts vector memory
+  // iteration j: compute tile j with the conversion of tile j + 1 (loaded two
+  // iterations ago) into buffer (j + 1) % 3 interleaved, finalize tile j - 1,
+  // then load tile j + 3.  The wait for tile j + 1's registers counts vector memory
   // operations in issue order; with the newest load the last one issued
   // before it, that load stays in flight across the wait.
   auto iteration = [&](int j, auto oddc) {
     constexpr int R = decltype(oddc)::value;   // raw slot of tile j + 1
     lds_barrier();
     const int b = j % kBufs;
-    convert(ta + j + 1, (j + 1) % kBufs, raw[R], mb[R], in[R]);
+    compute(j, b, [&] { convert(ta + j + 1, (j + 1) % kBufs, raw[R], mb[R], in[R]); });
     if (j >= 1) finalize(j - 1, (j + kBufs - 1) % kBufs);
-    compute(j, b);
     load(ta + j + 3, raw[R], mb[R], in[R]);
   };
   int j = 0;
