@@ -28,6 +28,10 @@ fill (gather + one sa_compress + scatter) on a side stream.
 300 requests (300 candidates each) attend their cached sketches in place,
 timed with the misses' fill serial and overlapped on a side stream.
 
+``--data-probe`` runs the default workload's kernels on its seeded history
+and on an all-zero history (same shapes and instruction streams) and reports
+both pass times: a difference is the data dependence of the clock.
+
 ``--backward`` times one sa_compress_backward call per step instead (the
 gradients dH, dP, dWk, dWv for a seeded dS, forward recomputation included)
 on the same workload; its roofline object reports the token-major dH kernel
@@ -677,6 +681,115 @@ def bench_serving_pipeline(args, torch, dev, sa):
     return 0
 
 
+OTHER_CONFIGS = ("c1_fp32_n4096_d64_k64", "c2_n100k_d128_k1024", "c3_r40_ragged_d128_k1024",
+                 "c4_r120_lognormal_d128_k1024", "c5_r8_n100k_d128_k256", "c5_r8_n100k_d128_k512",
+                 "c5_r8_n100k_d128_k2048", "c5mask_r8_n100k_d128_k1024")
+
+
+def measure_config(name: str, torch, dev, sa, steps: int = 10, warmup: int = 3) -> dict:
+    """A short measurement of one named workload: clean timed steps, then the
+    same number with phase events for the pass-2 share."""
+    from synth import make_config
+
+    inp = make_config(name)
+    H, off, Wk, Wv, P, mask = _upload(inp, torch, dev)
+    R, N, d, k = inp.R, inp.N, inp.d, inp.k
+    dt = sa.SA_BF16 if inp.dtype == "bf16" else sa.SA_F32
+    ws = torch.empty(sa.workspace_size(R, N, d, k, dt), dtype=torch.uint8, device=dev)
+    S = torch.empty((R, k, d), dtype=torch.float32, device=dev)
+    m = torch.empty((R, k), dtype=torch.float32, device=dev)
+    hip = _Hip()
+    n_ev = sa._lib.NUM_PHASE_EVENTS
+    evs = [[hip.event() for _ in range(n_ev)] for _ in range(steps)]
+    arrs = [(ctypes.c_void_p * n_ev)(*e) for e in evs]
+
+    def step(events=None):
+        sa.compress(H, off, Wk, Wv, P, mask=mask, return_mass=True, out=S, mass_out=m, workspace=ws,
+                    events=events)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    for i in range(steps):
+        step(arrs[i])
+    torch.cuda.synchronize()
+    p2 = sum(hip.elapsed_ms(e[2], e[3]) for e in evs) / steps
+    p1 = sum(hip.elapsed_ms(e[1], e[2]) for e in evs) / steps
+    for e in evs:
+        for x in e:
+            hip.destroy(x)
+    n_valid = inp.valid_tokens()
+    algo = 4.0 * n_valid * k * d
+    out = {"users": R, "tokens": n_valid, "k": k, "d": d, "dtype": inp.dtype, "ms_per_step": ms,
+           "tokens_per_s": n_valid / (ms * 1e-3), "tflops": algo / (ms * 1e-3) / 1e12,
+           "pct_peak": algo / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS if inp.dtype == "bf16" else None,
+           "pass1_ms": p1, "pass2_ms": p2,
+           "pass2_frac": algo / (p2 * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS if inp.dtype == "bf16" else None}
+    del H, off, Wk, Wv, P, mask, ws, S, m
+    return out
+
+
+def bench_data_probe(args, torch, dev, sa):
+    """The headline workload twice through the same kernels: once on its
+    seeded history, once on an all-zero history (a valid input: every logit
+    is 0, every allocation 1/k, every sketch 0).  Same shapes, launches and
+    instruction streams; only the operand data differ.  A time that depends
+    on the data shows a clock set by power, not by issue rates."""
+    from synth import make_config
+
+    inp = make_config(DEFAULT_WORKLOAD)
+    H, off, Wk, Wv, P, mask = _upload(inp, torch, dev)
+    R, N, d, k = inp.R, inp.N, inp.d, inp.k
+    ws = torch.empty(sa.workspace_size(R, N, d, k), dtype=torch.uint8, device=dev)
+    S = torch.empty((R, k, d), dtype=torch.float32, device=dev)
+    m = torch.empty((R, k), dtype=torch.float32, device=dev)
+    hip = _Hip()
+    n_ev = sa._lib.NUM_PHASE_EVENTS
+    res = {}
+    for name, hist in (("seeded", H), ("zero", torch.zeros_like(H)), ("seeded_again", H)):
+        evs = [[hip.event() for _ in range(n_ev)] for _ in range(args.steps)]
+        arrs = [(ctypes.c_void_p * n_ev)(*e) for e in evs]
+        for _ in range(args.warmup):
+            sa.compress(hist, off, Wk, Wv, P, mask=mask, return_mass=True, out=S, mass_out=m, workspace=ws)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            sa.compress(hist, off, Wk, Wv, P, mask=mask, return_mass=True, out=S, mass_out=m, workspace=ws,
+                        events=arrs[i])
+        torch.cuda.synchronize()
+        ph = {"pass1_lse": 0.0, "pass2_accum": 0.0}
+        for e in evs:
+            ph["pass1_lse"] += hip.elapsed_ms(e[1], e[2]) / args.steps
+            ph["pass2_accum"] += hip.elapsed_ms(e[2], e[3]) / args.steps
+            for x in e:
+                hip.destroy(x)
+        res[name] = ph
+        if name == "zero":
+            assert not S.any(), "a zero history gives zero sketches"
+    algo = 4.0 * N * k * d
+    out = {
+        "metric": "pass times on seeded vs all-zero history (same kernels)",
+        "value": res["zero"]["pass2_accum"] / res["seeded"]["pass2_accum"],
+        "unit": "ratio (zero / seeded pass-2 time)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "higher_is_better": False,
+        "data": "synthetic",
+        "config": {"workload": DEFAULT_WORKLOAD, "users": R, "tokens": N, "k": k, "d": d},
+        "phase_ms": res,
+        "pass2_tflops": {n: algo / (v["pass2_accum"] * 1e-3) / 1e12 for n, v in res.items()},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -685,6 +798,8 @@ def main(argv=None):
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the short measurements of the other workloads")
     ap.add_argument("--path", choices=["auto", "one", "two"], default="auto",
                     help="kernel path: the library's choice, the one-pass or the two-pass kernels")
     ap.add_argument("--target-attention", action="store_true",
@@ -698,6 +813,8 @@ def main(argv=None):
     ap.add_argument("--with-sbar", action="store_true",
                     help="with --backward: hand the forward's Sbar and masses to the backward "
                          "(sa_compress_backward_with_sbar) instead of recomputing its sums")
+    ap.add_argument("--data-probe", action="store_true",
+                    help="time the headline workload on its seeded history and on an all-zero history")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device once (counter calibration)")
     args = ap.parse_args(argv)
@@ -722,6 +839,8 @@ def main(argv=None):
         return bench_cache(args, torch, dev, sa)
     if args.serving_pipeline:
         return bench_serving_pipeline(args, torch, dev, sa)
+    if args.data_probe:
+        return bench_data_probe(args, torch, dev, sa)
     inp = make_config(args.workload)
     if args.backward:
         return bench_backward(args, inp, torch, dev, sa)
@@ -745,17 +864,24 @@ def main(argv=None):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the timed steps carry no phase events (each event record costs a few
+    # microseconds between kernels, which shows at small workloads)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        step(ev_arrays[i])
+        step()
     stop.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
+    # then the same number of steps again with events at the phase
+    # boundaries, for the per-phase durations and the per-step spread
+    for i in range(args.steps):
+        step(ev_arrays[i])
+    torch.cuda.synchronize()
 
     phases = ["prep", "pass1_lse", "pass2_accum", "finalize"]
     phase_ms = {p: 0.0 for p in phases}
@@ -813,6 +939,7 @@ def main(argv=None):
         "tflops": tflops,
         "pct_peak": tflops / PEAK_MFMA_F16_TFLOPS,
         "exec_tflops": None if exec_flop is None else exec_flop / (ms_step * 1e-3) / 1e12,
+        # spread over the steps that carry phase events
         "step_ms": {"median": float(np.median(per_step)), "min": float(np.min(per_step)), "reps": len(per_step)},
         "phase_ms": phase_ms,
         "wall_s_timed": t_wall,
@@ -829,6 +956,15 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, S.cpu().numpy(), args.cpu_budget)
         out["cpu_baseline"]["one_thread_chunk"] = oracle_chunk_one_thread(inp)
+    if not args.no_other_configs and inp.name == DEFAULT_WORKLOAD:
+        # the other workloads of the pages, measured briefly in the same run
+        # (context beside the headline, not bench lines of their own)
+        del H, ws, S, m
+        torch.cuda.empty_cache()
+        out["other_configs"] = {}
+        for name in OTHER_CONFIGS:
+            out["other_configs"][name] = measure_config(name, torch, dev, sa)
+            torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
     return 0
 
