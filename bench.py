@@ -65,14 +65,17 @@ DEFAULT_WORKLOAD = "c3lit_r40_n100k_d128_k1024"
 # the figure is reported as null once they differ.
 COPY_CALIBRATION_BYTES = 1 << 30
 TRAFFIC = {
-    # 1.0702e9 fetched + 0.0565e9 written (40 x 100K tokens, k = 1024, d = 128)
-    "pass2_accum": (1126671448, "106926115929e4c35f66bb44da9f6cb58f6424a9449823e6a4de3926fbb74eed",
+    # 1.0264e9 fetched + 1.0410e9 written (40 x 100K tokens, k = 1024, d = 128)
+    "pass1_qres": (2067393335, "b3f654bba8e561a8ffc39fc91f885e847469bdaaa14d360d036d27b64b9ff6fb",
+                   ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
+    # 1.0827e9 fetched + 0.0565e9 written (same workload)
+    "pass2_accum": (1139212538, "e32abe5be091c6496e53fdd79298c75137006cad1966b01643fe0ec21395b6c0",
                     ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
-    # 1.314e9 fetched + 2.068e9 written (same workload, --backward)
-    "bwd_dh": (3382438784, "914d35d3139e031b2105be580f031a6e8e3e0a5a8e60901f605bef6be8979db7",
+    # 1.3119e9 fetched + 2.0680e9 written (same workload, --backward)
+    "bwd_dh": (3379912097, "330d012913985479c72517fbed527e8148ae56c82bd0234e815efd4f6f7fd350",
                ("sa_bwd.hip", "sa_layout.h", "sa_device.h")),
-    # 1.866e8 fetched + 0.461e8 written (300 users x 300 candidates, --target-attention)
-    "ta_attend": (232643200, "11b373b6d79b31a2e8df715ce2921d811169938d1f4e8e23ab76e504573584f6",
+    # 1.8648e8 fetched + 0.4608e8 written (300 users x 300 candidates, --target-attention)
+    "ta_attend": (232557499, "dde2a4eb66f782be60a870e733718eafb646e6eea17a678c05ab161aea159158",
                   ("sa_target.hip", "sa_layout.h", "sa_device.h")),
 }
 
@@ -82,8 +85,11 @@ TRAFFIC = {
 # kernel's time), from rocprofv3 --pmc on the default workload; valid, like the
 # traffic figures, only for the kernel sources they were taken on (null after).
 COUNTERS = {
-    "pass2_accum": ({"mfma_busy": 0.59, "clock_mhz": 1900.0},
-                    "106926115929e4c35f66bb44da9f6cb58f6424a9449823e6a4de3926fbb74eed",
+    "pass1_qres": ({"mfma_busy": 0.410, "clock_mhz": 1945.0},
+                   "b3f654bba8e561a8ffc39fc91f885e847469bdaaa14d360d036d27b64b9ff6fb",
+                   ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
+    "pass2_accum": ({"mfma_busy": 0.617, "clock_mhz": 1810.0},
+                    "e32abe5be091c6496e53fdd79298c75137006cad1966b01643fe0ec21395b6c0",
                     ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
 }
 
@@ -921,6 +927,25 @@ def main(argv=None):
         "mfma_busy": None if counters is None else counters["mfma_busy"],
         "hbm_gbps": None if traffic is None or p2_s <= 0 else traffic / p2_s / 1e9,
     }
+    # the second kernel of the step: pass 1's logit contraction (2 N k d
+    # algorithmic FLOP) and its H read + fp16 copy write
+    p1_s = phase_ms["pass1_lse"] * 1e-3
+    p1_flop = 2.0 * n_valid * k * d
+    p1_traffic = measured_traffic("pass1_qres") if two_pass_default else None
+    p1_counters = measured_counters("pass1_qres") if two_pass_default else None
+    if path == "two" and p1_s > 0:
+        roofline["pass1"] = {
+            "kernel": "pass1_qres",
+            "bound": "mfma",
+            "achieved": p1_flop / p1_s / 1e12,
+            "peak": PEAK_MFMA_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": p1_flop / p1_s / 1e12 / PEAK_MFMA_F16_TFLOPS,
+            "avg_launch_ms": phase_ms["pass1_lse"],
+            "traffic": p1_traffic,
+            "hbm_gbps": None if p1_traffic is None else p1_traffic / p1_s / 1e9,
+            "mfma_busy": None if p1_counters is None else p1_counters["mfma_busy"],
+        }
     out = {
         "metric": METRIC,
         "value": tokens_per_s,

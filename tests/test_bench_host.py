@@ -11,7 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
 
-@pytest.mark.parametrize("kernel", ["pass2_accum", "bwd_dh", "ta_attend"])
+@pytest.mark.parametrize("kernel", ["pass1_qres", "pass2_accum", "bwd_dh", "ta_attend"])
 def test_traffic_figures_match_current_sources(kernel):
     """Each stored HBM-traffic figure carries the sha256 of the sources it
     was measured on; a kernel edited since reports null traffic, so the
