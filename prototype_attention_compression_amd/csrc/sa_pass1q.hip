@@ -22,8 +22,8 @@
 //   * compute (each wave: its k/8 prototypes, NBW blocks of 32): 8 16-byte
 //     operand reads, NBW x 8 fp16 MFMAs (lane = token, so the sum over
 //     prototypes stays in the lane), exponentials and sums;
-//   * every wave turns 4 tokens of the previous tile from 8 partials into
-//     -l pairs.
+//   * the first four waves turn 8 tokens each of the previous tile from 8
+//     partials into -l pairs.
 // One barrier per tile; three LDS tile buffers (convert t+1 while computing
 // t); the global loads run two tiles ahead in registers.
 #include <hip/hip_runtime.h>
@@ -125,14 +125,25 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   // user with tiles has at least one token, whereas the first slot of a
   // padding tile (tiles are rounded up to a multiple of kUserTileAlign) lies
   // past the user's rows, and for the last user past the end of H.
+  // The current user's tile base and token range stay in registers and are
+  // read again only when the walk crosses into the next user (a workgroup's
+  // range meets a few users), so a load waits on no scalar memory read.
   int lu = find_user(tile_base, L.R, ta);
+  int32_t u_tile0 = tile_base[lu], u_tile1 = tile_base[lu + 1];
+  int64_t u_first = offsets[lu], u_end = offsets[lu + 1];
   auto load = [&](int32_t tile, u32x4& raw, uint32_t& mb, bool& in) {
     const bool live = tile < tb;               // uniform
     const int32_t tl = live ? tile : tb - 1;   // a tile of this workgroup
-    while (tl >= tile_base[lu + 1]) ++lu;      // uniform
-    const int64_t first = offsets[lu];
-    const int64_t tok = first + (int64_t)(tl - tile_base[lu]) * kTile + crow;
-    in = live && conv && tok < offsets[lu + 1];
+    if (tl >= u_tile1) {                       // uniform
+      do ++lu; while (tl >= tile_base[lu + 1]);
+      u_tile0 = tile_base[lu];
+      u_tile1 = tile_base[lu + 1];
+      u_first = offsets[lu];
+      u_end = offsets[lu + 1];
+    }
+    const int64_t first = u_first;
+    const int64_t tok = first + (int64_t)(tl - u_tile0) * kTile + crow;
+    in = live && conv && tok < u_end;
     const int64_t tc = in ? tok : first;       // a token of user lu
     raw = reinterpret_cast<const u32x4*>(H + tc * D)[cch];
     if constexpr (MASKED) mb = mask[tc];
@@ -235,6 +246,13 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   // are issued, in the same basic block, so its VALU work fills the MFMA
   // pipeline's gaps instead of a phase of its own
   auto compute = [&](int j, int b, auto&& mid) {
+    // the operand reads go out before the exact-mode bits are read, so the
+    // two LDS round trips overlap
+    half8 ha[C::S];
+    if constexpr (NBW > 1) {
+#pragma unroll
+      for (int s = 0; s < C::S; ++s) ha[s] = *reinterpret_cast<const half8*>(&rows[b][hbase + 32 * s]);
+    }
     const bool exact = tile_exact(b);
     float wpart;
     if constexpr (NBW == 1) {
@@ -255,9 +273,6 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
     } else {
       // block-major MFMA chains over the tile's operands held in registers:
       // the exponentials of block b run under the MFMAs of block b + 1
-      half8 ha[C::S];
-#pragma unroll
-      for (int s = 0; s < C::S; ++s) ha[s] = *reinterpret_cast<const half8*>(&rows[b][hbase + 32 * s]);
       if (!exact) {
         float p0 = 0.f, p1 = 0.f;
 #pragma unroll
@@ -291,16 +306,25 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
     // both lane halves hold the same value; the upper half's store is spare
     float* pw = g == 0 ? &part[j & 1][col][wave] : reinterpret_cast<float*>(&spare[tid]);
     *pw = wpart;
+    return exact;
   };
 
   // -l pairs of tile j (buffer b) from its 8 partials: wave w, lanes 0..3,
   // tokens 4 w .. 4 w + 3
-  auto finalize = [&](int j, int b) {
-    constexpr int TPW = kTile / W;   // tokens per wave
+  // Only the first W / 2 waves finalize (kTile / (W / 2) tokens each).
+  // Waves w and w + W / 2 share a SIMD, and the first of the pair, which the
+  // arbiter favours, finishes its MFMAs well before the second (measured: by
+  // about a third of a tile period); its finalize then fills that gap
+  // instead of lengthening the second wave's path to the next barrier.
+  auto finalize = [&](int j, int b, bool exact) {
+    constexpr int FW = W / 2;
+    constexpr int TPW = kTile / FW;   // tokens per finalizing wave
+    static_assert(TPW * FW == kTile && TPW <= 64, "tokens per wave");
+    if (wave >= FW) return;           // uniform
     // every lane works (no branch): lanes with equal lane % TPW store the
     // same value to the same word
     const int tok = wave * TPW + (lane % TPW);
-    const bool exact = tile_exact(b);
+    const bool keep = keep_words[b][tok] != 0u;
     const float* pp = part[j & 1][tok];
     float lse;
     if (!exact) {
@@ -313,7 +337,6 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
 #pragma unroll
       for (int w = 0; w < W; ++w) lse = log_add_exp2(lse, pp[w]);
     }
-    const bool keep = keep_words[b][tok] != 0u;
     // -l = 14 - lse as an fp16 pair (hi, lo) with hi + lo = -l to ~2^-16
     const float nlv = keep ? kAllocShift - lse : -60000.0f;
     const _Float16 hi = (_Float16)nlv;
@@ -339,12 +362,15 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   // then load tile j + 3.  The wait for tile j + 1's registers counts vector memory
   // operations in issue order; with the newest load the last one issued
   // before it, that load stays in flight across the wait.
+  // exact-mode decision of the previous tile, for its finalize
+  bool ex_prev = false;
   auto iteration = [&](int j, auto oddc) {
     constexpr int R = decltype(oddc)::value;   // raw slot of tile j + 1
     lds_barrier();
     const int b = j % kBufs;
-    compute(j, b, [&] { convert(ta + j + 1, (j + 1) % kBufs, raw[R], mb[R], in[R]); });
-    if (j >= 1) finalize(j - 1, (j + kBufs - 1) % kBufs);
+    const bool ex = compute(j, b, [&] { convert(ta + j + 1, (j + 1) % kBufs, raw[R], mb[R], in[R]); });
+    if (j >= 1) finalize(j - 1, (j + kBufs - 1) % kBufs, ex_prev);
+    ex_prev = ex;
     load(ta + j + 3, raw[R], mb[R], in[R]);
   };
   int j = 0;
@@ -354,7 +380,7 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   }
   if (j < n) iteration(j, std::integral_constant<int, 1>{});
   lds_barrier();
-  finalize(n - 1, (n - 1) % kBufs);
+  finalize(n - 1, (n - 1) % kBufs, ex_prev);
   if (__ballot(range_bad != 0u) != 0ull && lane == 0) atomicOr(ws_i32(ws, L.off_hdr) + kHdrErr, kErrRange);
 }
 
