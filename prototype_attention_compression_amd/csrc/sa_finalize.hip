@@ -25,6 +25,7 @@ namespace sa {
 namespace {
 constexpr int kSlotBatch = 4;   // partial slots whose loads are in flight together
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 }  // namespace
 
 template <typename T>
@@ -95,40 +96,47 @@ __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout
   const float* part_u = ws_f32(ws, L.off_part_u);
   const float* part_m = ws_f32(ws, L.off_part_m);
 
-  float acc[PER];
+  // thread tid owns the 16-byte pieces tid + 256 i (i < V4) of the 32-row
+  // block: elements 4 (tid + 256 i) .. + 3, one 16-byte load per piece
+  constexpr int V4 = PER / 4;
+  static_assert(V4 * 4 == PER, "whole pieces");
+  f32x4 acc[V4];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  for (int i = 0; i < V4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto slot_block = [&](int c) {
+    return reinterpret_cast<const f32x4*>(part_u + ((int64_t)c * L.k + j0) * D);
+  };
   if (pre) {
-    float v[kPreSplit][PER];
+    f32x4 v[kPreSplit][V4];
 #pragma unroll
     for (int q = 0; q < kPreSplit; ++q) {
-      const float* base = part_u + ((int64_t)sub_head(c0, n, q) * L.k + j0) * D;
+      const f32x4* base = slot_block(sub_head(c0, n, q));
 #pragma unroll
-      for (int i = 0; i < PER; ++i) v[q][i] = base[tid + 256 * i];
+      for (int i = 0; i < V4; ++i) v[q][i] = base[tid + 256 * i];
     }
 #pragma unroll
     for (int q = 0; q < kPreSplit; ++q)
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += v[q][i];
+      for (int i = 0; i < V4; ++i) acc[i] += v[q][i];
   } else {
     int c = c0;
     for (; c + kSlotBatch <= c1; c += kSlotBatch) {
-      float v[kSlotBatch][PER];
+      f32x4 v[kSlotBatch][V4];
 #pragma unroll
       for (int q = 0; q < kSlotBatch; ++q) {
-        const float* base = part_u + ((int64_t)(c + q) * L.k + j0) * D;
+        const f32x4* base = slot_block(c + q);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) v[q][i] = base[tid + 256 * i];
+        for (int i = 0; i < V4; ++i) v[q][i] = base[tid + 256 * i];
       }
 #pragma unroll
       for (int q = 0; q < kSlotBatch; ++q)
 #pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] += v[q][i];
+        for (int i = 0; i < V4; ++i) acc[i] += v[q][i];
     }
     for (; c < c1; ++c) {
-      const float* base = part_u + ((int64_t)c * L.k + j0) * D;
+      const f32x4* base = slot_block(c);
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
+      for (int i = 0; i < V4; ++i) acc[i] += base[tid + 256 * i];
     }
   }
   if (tid < kFinRows) {
@@ -142,12 +150,17 @@ __global__ __launch_bounds__(256) void finalize(const T* __restrict__ Wv, Layout
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = tid + 256 * i, j = e / D, a = e % D;
+  for (int i = 0; i < V4; ++i) {
+    const int e = 4 * (tid + 256 * i), j = e / D, a = e % D;   // one row per piece (D % 4 == 0)
     const float m = ms[j];
-    const float v = m > 0.f ? acc[i] / m : 0.f;
-    sh[j][a] = v;
-    if (Sbar != nullptr) Sbar[((int64_t)u * L.k + j0) * D + e] = v;   // the mass-normalised rows
+    f32x4 v;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[c] = m > 0.f ? acc[i][c] / m : 0.f;
+      sh[j][a + c] = v[c];
+    }
+    if (Sbar != nullptr)   // the mass-normalised rows
+      *reinterpret_cast<f32x4*>(Sbar + ((int64_t)u * L.k + j0) * D + e) = v;
   }
   __syncthreads();
   float* dst = S + ((int64_t)u * L.k + j0) * D;
@@ -217,35 +230,39 @@ __global__ __launch_bounds__(256) void presum_slots(Layout L, void* ws) {
   const int a = sub_head(c0, n, sidx), b = sub_head(c0, n, sidx + 1);
   float* part_u = ws_f32(ws, L.off_part_u);
   float* part_m = ws_f32(ws, L.off_part_m);
-  float acc[PER];
+  // 16-byte pieces tid + 256 i of the 32-row block, as in finalize
+  constexpr int V4 = PER / 4;
+  static_assert(V4 * 4 == PER, "whole pieces");
+  auto slot_block = [&](int c) { return reinterpret_cast<f32x4*>(part_u + ((int64_t)c * L.k + j0) * D); };
+  f32x4 acc[V4];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  for (int i = 0; i < V4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   int c = a;
   for (; c + kSlotBatch <= b; c += kSlotBatch) {
-    float v[kSlotBatch][PER];
+    f32x4 v[kSlotBatch][V4];
 #pragma unroll
     for (int q = 0; q < kSlotBatch; ++q) {
-      const float* base = part_u + ((int64_t)(c + q) * L.k + j0) * D;
+      const f32x4* base = slot_block(c + q);
 #pragma unroll
-      for (int i = 0; i < PER; ++i) v[q][i] = base[tid + 256 * i];
+      for (int i = 0; i < V4; ++i) v[q][i] = base[tid + 256 * i];
     }
 #pragma unroll
     for (int q = 0; q < kSlotBatch; ++q)
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += v[q][i];
+      for (int i = 0; i < V4; ++i) acc[i] += v[q][i];
   }
   for (; c < b; ++c) {
-    const float* base = part_u + ((int64_t)c * L.k + j0) * D;
+    const f32x4* base = slot_block(c);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += base[tid + 256 * i];
+    for (int i = 0; i < V4; ++i) acc[i] += base[tid + 256 * i];
   }
   float m = 0.f;
   if (tid < kFinRows)
     for (int cc = a; cc < b; ++cc) m += part_m[(int64_t)cc * L.k + j0 + tid];
   __syncthreads();   // every read of slot a is done before it is overwritten
-  float* dst = part_u + ((int64_t)a * L.k + j0) * D;
+  f32x4* dst = slot_block(a);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) dst[tid + 256 * i] = acc[i];
+  for (int i = 0; i < V4; ++i) dst[tid + 256 * i] = acc[i];
   if (tid < kFinRows) part_m[(int64_t)a * L.k + j0 + tid] = m;
 }
 
