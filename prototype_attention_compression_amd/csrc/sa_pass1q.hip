@@ -160,8 +160,14 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
     if constexpr (MASKED) mb = mask[tc];
     else mb = 1u;
   };
-  // kept values outside fp16's finite range, raised as a device error bit
-  // once the tiles are done (no branch inside the loop)
+  // Kept values outside fp16's finite range raise a device error bit once
+  // the tiles are done.  Inside the loop only the chunk's squared norm is
+  // tested (no branch): a kept value beyond 65504, or inf or NaN, makes it
+  // exceed 65504^2 or NaN.  A wave that saw such a chunk reads its chunks
+  // again after the loop and tests every value (a slow path that only
+  // such inputs take).
+  constexpr float kF16MaxSq = 65504.0f * 65504.0f;   // exact in fp32
+  uint64_t range_sus = 0ull;
   uint32_t range_bad = 0u;
   // A buffer view of this workgroup's fp16 rows, tiles [ta, tb): the
   // hardware's range check drops the stores of conversions past the last
@@ -183,7 +189,6 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   auto convert = [&](int32_t tile, int b, const u32x4& raw_in, uint32_t mb, bool in) {
     const bool keep = in && mb != 0u;
     const u32x4 raw = keep ? raw_in : u32x4{0u, 0u, 0u, 0u};
-    range_bad |= bf16x8_range_bits(raw);
     const half8 hv = bf16x8_to_f16x8(raw);
     float n2 = 0.f;
 #pragma unroll
@@ -201,6 +206,7 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
       uint32_t* kw = cch == 0 ? &keep_words[b][crow] : &spare[tid];
       *kw = keep ? 1u : 0u;
     }
+    range_sus |= __ballot(!(n2 <= kF16MaxSq));
     const bool big = conv && keep && n2 * (float)C::CPR >= lim2;
     const uint32_t eb = __ballot(big) != 0ull ? 1u : 0u;   // uniform over the wave
     *(lane == 0 ? &exact_bits[b][wave] : &spare[tid]) = eb;
@@ -400,6 +406,20 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   if (j < n) iteration(j, std::integral_constant<int, 1>{});
   lds_barrier();
   finalize(n - 1, (n - 1) % kBufs, ex_prev);
+  if (range_sus != 0ull) {   // uniform over the wave
+    lu = find_user(tile_base, L.R, ta);
+    u_tile0 = tile_base[lu];
+    u_tile1 = tile_base[lu + 1];
+    u_first = offsets[lu];
+    u_end = offsets[lu + 1];
+    for (int32_t t = ta; t < tb; ++t) {
+      u32x4 r;
+      uint32_t m;
+      bool i;
+      load(t, r, m, i);
+      if (i && m != 0u) range_bad |= bf16x8_range_bits(r);
+    }
+  }
   if (__ballot(range_bad != 0u) != 0ull && lane == 0) atomicOr(ws_i32(ws, L.off_hdr) + kHdrErr, kErrRange);
 }
 
