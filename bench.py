@@ -66,7 +66,7 @@ DEFAULT_WORKLOAD = "c3lit_r40_n100k_d128_k1024"
 COPY_CALIBRATION_BYTES = 1 << 30
 TRAFFIC = {
     # 1.0264e9 fetched + 1.0410e9 written (40 x 100K tokens, k = 1024, d = 128)
-    "pass1_qres": (2067386088, "da605645f56297645f0a5912bc37bc762aa9c20e345bfef1a5a13c72bfb0510b",
+    "pass1_qres": (2067380424, "fed9728c7e8e8f851b3620ac5960d025e9dcc093b83088c2a6db37f0d175820f",
                    ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
     # 1.0827e9 fetched + 0.0565e9 written (same workload)
     "pass2_accum": (1139212538, "e32abe5be091c6496e53fdd79298c75137006cad1966b01643fe0ec21395b6c0",
@@ -85,8 +85,8 @@ TRAFFIC = {
 # kernel's time), from rocprofv3 --pmc on the default workload; valid, like the
 # traffic figures, only for the kernel sources they were taken on (null after).
 COUNTERS = {
-    "pass1_qres": ({"mfma_busy": 0.527, "clock_mhz": 1766.0},
-                   "da605645f56297645f0a5912bc37bc762aa9c20e345bfef1a5a13c72bfb0510b",
+    "pass1_qres": ({"mfma_busy": 0.552, "clock_mhz": 1754.0},
+                   "fed9728c7e8e8f851b3620ac5960d025e9dcc093b83088c2a6db37f0d175820f",
                    ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
     "pass2_accum": ({"mfma_busy": 0.617, "clock_mhz": 1810.0},
                     "e32abe5be091c6496e53fdd79298c75137006cad1966b01643fe0ec21395b6c0",
