@@ -692,9 +692,16 @@ OTHER_CONFIGS = ("c1_fp32_n4096_d64_k64", "c2_n100k_d128_k1024", "c3_r40_ragged_
                  "c5_r8_n100k_d128_k2048", "c5mask_r8_n100k_d128_k1024")
 
 
-def measure_config(name: str, torch, dev, sa, steps: int = 10, warmup: int = 3) -> dict:
+INFINITY_CACHE_BYTES = 256 << 20   # MI355X's last-level (MALL) cache
+
+
+def measure_config(name: str, torch, dev, sa, steps: int = 10, warmup: int = 3, flush=None) -> dict:
     """A short measurement of one named workload: clean timed steps, then the
-    same number with phase events for the pass-2 share."""
+    same number with phase events for the pass-2 share.  Those steps run warm:
+    a history that fits the Infinity Cache stays there between steps.  When
+    it fits and ``flush`` (a device buffer of at least twice the cache) is
+    given, the steps are timed once more one by one, each after a write of
+    the whole buffer that evicts the cache: ``cold_ms`` (median, min)."""
     from synth import make_config
 
     inp = make_config(name)
@@ -728,6 +735,19 @@ def measure_config(name: str, torch, dev, sa, steps: int = 10, warmup: int = 3) 
     torch.cuda.synchronize()
     p2 = sum(hip.elapsed_ms(e[2], e[3]) for e in evs) / steps
     p1 = sum(hip.elapsed_ms(e[1], e[2]) for e in evs) / steps
+    h_bytes = H.numel() * H.element_size()
+    cold = None
+    if flush is not None and h_bytes < INFINITY_CACHE_BYTES:
+        times = []
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(steps):
+            flush.fill_(float(i))
+            c0.record()
+            step()
+            c1.record()
+            torch.cuda.synchronize()
+            times.append(c0.elapsed_time(c1))
+        cold = {"median": float(np.median(times)), "min": float(np.min(times)), "reps": steps}
     for e in evs:
         for x in e:
             hip.destroy(x)
@@ -737,7 +757,9 @@ def measure_config(name: str, torch, dev, sa, steps: int = 10, warmup: int = 3) 
            "tokens_per_s": n_valid / (ms * 1e-3), "tflops": algo / (ms * 1e-3) / 1e12,
            "pct_peak": algo / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS if inp.dtype == "bf16" else None,
            "pass1_ms": p1, "pass2_ms": p2,
-           "pass2_frac": algo / (p2 * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS if inp.dtype == "bf16" else None}
+           "pass2_frac": algo / (p2 * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS if inp.dtype == "bf16" else None,
+           "cache": "warm" if h_bytes < INFINITY_CACHE_BYTES else "history larger than the Infinity Cache",
+           "cold_ms": cold}
     del H, off, Wk, Wv, P, mask, ws, S, m
     return out
 
@@ -987,9 +1009,11 @@ def main(argv=None):
         del H, ws, S, m
         torch.cuda.empty_cache()
         out["other_configs"] = {}
+        flush = torch.empty(2 * INFINITY_CACHE_BYTES // 4, dtype=torch.float32, device=dev)
         for name in OTHER_CONFIGS:
-            out["other_configs"][name] = measure_config(name, torch, dev, sa)
+            out["other_configs"][name] = measure_config(name, torch, dev, sa, flush=flush)
             torch.cuda.empty_cache()
+        del flush
     print(json.dumps(out), flush=True)
     return 0
 
