@@ -125,7 +125,6 @@ Layout make_layout(const sa_problem& p, bool bwd = false) {
     L.o_chunks = (int32_t)((rows + kOuterRows - 1) / kOuterRows);
     L.off_bz32 = take(Rk * p.d * sizeof(float));
     L.off_bsbar = take(Rk * p.d * sizeof(float));
-    L.off_bc = take(Rk * sizeof(float));
     L.off_bzmax = take((size_t)p.num_users * (p.k / 32) * sizeof(float));
     L.off_bz16 = take(Rk * p.d * 2);
     L.off_bcz = take(Rk * sizeof(float));

@@ -22,9 +22,10 @@
 // kernels reuse the fp16 token rows and logsumexps of forward passes 1 and 2
 // and never form a k x n array:
 //   bwd_user   per (user, 32 prototypes): sums pass 2's partial slots into
-//              U and m, writes Sbar, Z (fp32), c and the block's largest |Z|;
+//              U and m, writes Sbar, Z (fp32) and the block's largest |Z|;
 //   bwd_zpack  per user scale zs (a power of two putting max |Z| in
-//              [2^13, 2^14)): Z zs in fp16 (MFMA operand), c zs;
+//              [2^13, 2^14)): Z zs in fp16 (MFMA operand) and c zs from
+//              that rounded row;
 //   bwd_dh     token-major: a wave owns a 32-token tile with its rows as the
 //              B operand in registers and walks every prototype block twice
 //              (queries and Z rows staged in LDS): sweep 1 sums delta_t and
@@ -103,8 +104,7 @@ __global__ __launch_bounds__(256) void bwd_user(const uint16_t* __restrict__ Wv,
                                                 const float* __restrict__ Sbar_in, const float* __restrict__ mass_in,
                                                 Layout L, void* ws, int presummed) {
   constexpr int PER = kRows * D / 256;
-  __shared__ float sb[kRows][D + 1];   // U / m
-  __shared__ float gz[kRows][D + 1];   // dS / m, then Z
+  __shared__ float gz[kRows][D + 1];   // dS / m
   __shared__ float ms[kRows];
   __shared__ float red[256];
   const int nrb = L.k / kRows;
@@ -179,7 +179,6 @@ __global__ __launch_bounds__(256) void bwd_user(const uint16_t* __restrict__ Wv,
     const int e = tid + 256 * i, j = e / D, a = e % D;
     const float m = ms[j];
     const float v = m > 0.f ? (Sbar_in == nullptr ? acc[i] / m : acc[i]) : 0.f;
-    sb[j][a] = v;
     sbar[e] = v;
     gz[j][a] = m > 0.f ? dS[row0 * D + e] * (kScaleMax / m) : 0.f;
   }
@@ -216,30 +215,18 @@ __global__ __launch_bounds__(256) void bwd_user(const uint16_t* __restrict__ Wv,
       zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, wb[ks], zacc, 0, 0, 0);
     }
   }
-  __syncthreads();   // every read of Gm is done before Z overwrites it
   float zm = 0.f;
   float* z32 = ws_f32(ws, L.off_bz32) + row0 * D;
   if (zw) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = acc_row(r, g), a = 32 * wave + col;
-      gz[j][a] = zacc[r];
       z32[(int64_t)j * D + a] = zacc[r];
       zm = fmaxf(zm, fabsf(zacc[r]));
     }
   }
   red[tid] = zm;
   __syncthreads();
-  // c_j = Z_j . Sbar_j: 8 threads per row
-  {
-    const int j = tid >> 3, part = tid & 7;
-    float s = 0.f;
-    for (int e = part; e < D; e += 8) s = fmaf(gz[j][e], sb[j][e], s);
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
-    if (part == 0) ws_f32(ws, L.off_bc)[row0 + j] = s;
-  }
   for (int off = 128; off > 0; off >>= 1) {
     if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
     __syncthreads();
@@ -266,10 +253,23 @@ __global__ __launch_bounds__(256) void bwd_zpack(Layout L, void* ws) {
   const float zs = pow2_scale(red[0], 14);
   const int64_t row0 = (int64_t)u * L.k + rb * kRows;
   const float* z32 = ws_f32(ws, L.off_bz32) + row0 * D;
+  const float* sbar = ws_f32(ws, L.off_bsbar) + row0 * D;
   _Float16* z16 = ws_f16(ws, L.off_bz16) + row0 * D;
 #pragma unroll
   for (int i = 0; i < PER; ++i) z16[tid + 256 * i] = (_Float16)(z32[tid + 256 * i] * zs);
-  if (tid < kRows) ws_f32(ws, L.off_bcz)[row0 + tid] = ws_f32(ws, L.off_bc)[row0 + tid] * zs;
+  // c_j zs = Zs_j . Sbar_j from the rounded fp16 row itself, so that
+  // Y - c zs = Zs_j . (h_t - Sbar_j) keeps its accuracy where h_t is close to
+  // Sbar_j (a user of one token: exactly zero), rather than the fp16 rounding
+  // of Zs_j . h_t (8 threads per row)
+  {
+    const int j = tid >> 3, part = tid & 7;
+    float s = 0.f;
+    for (int e = part; e < D; e += 8) s = fmaf((float)(_Float16)(z32[j * D + e] * zs), sbar[j * D + e], s);
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    if (part == 0) ws_f32(ws, L.off_bcz)[row0 + j] = s;
+  }
   if (rb == 0 && tid == 0) {
     ws_f32(ws, L.off_bzs)[u] = zs;
     ws_i32(ws, L.off_bbmax)[u] = 0;

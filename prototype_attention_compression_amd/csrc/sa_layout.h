@@ -87,7 +87,6 @@ struct Layout {
   int32_t o_chunks;        // row chunks of the outer-product reductions
   size_t off_bz32;         // [R, k, d] float   Z = (dS / m) Wv^T
   size_t off_bsbar;        // [R, k, d] float   U / m (the mass-normalised history rows)
-  size_t off_bc;           // [R, k] float      c_j = Z_j . (U_j / m_j)
   size_t off_bzmax;        // [R, k / 32] float largest |Z| of each 32-row block
   size_t off_bz16;         // [R, k, d] fp16    Z zs_u
   size_t off_bcz;          // [R, k] float      c zs_u

@@ -69,6 +69,30 @@ def test_backward_small_ragged(k, d):
     _check(inp, make_sketch_grad(inp.R, k, d, seed=5000 + k + d))
 
 
+def test_backward_one_token_users():
+    """A user of one token has the sketch row h Wv for every prototype,
+    whatever P and Wk, so it adds nothing to dP and dWk.  With many such users
+    beside one long user those two gradients must equal what the long user
+    gives alone, up to fp32 summation order (bar: mean_rel 1e-4, max_rel
+    1e-3).  This holds only if each row's mean term c_j = Zs_j . Sbar_j is
+    formed from the same fp16-rounded Z row as the per-token products
+    Zs_j . h_t: with c from the unrounded row, every one-token user adds the
+    fp16 rounding of Zs_j . h_t (about 5e-4 of it) where the exact value is 0."""
+    import dataclasses
+    lens = [1] * 24 + [1500] + [1] * 8
+    inp = make_inputs(lens, d=128, k=256, seed=4700, name="bwd_one_token")
+    dS = make_sketch_grad(inp.R, 256, 128, seed=5700)
+    dH, dP, dWk, _ = _check(inp, dS)
+    sl = inp.user_slice(24)
+    alone = dataclasses.replace(inp, name="bwd_one_token_alone", lengths=np.array([1500], dtype=np.int64),
+                                offsets=np.array([0, 1500], dtype=np.int64), H=inp.H[sl], H_bits=inp.H_bits[sl])
+    dH1, dP1, dWk1, _ = _run(upload(alone), np.ascontiguousarray(dS[24:25]))
+    for name, g, r in (("dP", dP, dP1), ("dWk", dWk, dWk1), ("dH", dH[sl], dH1)):
+        mx, mean = rel_errors(g, r)
+        print(f"   {name} batch vs alone: max_rel={mx:.3e} mean_rel={mean:.3e}", flush=True)
+        assert mx <= 1e-3 and mean <= 1e-4, (name, mx, mean)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_backward_largest_k(d):
     """k = 4096, the largest built: 128 prototype blocks per token sweep,

@@ -74,7 +74,6 @@ def layout(R, N, d, k, bwd):
         L["o_chunks"] = (max(Rk, k) + OUTER_ROWS - 1) // OUTER_ROWS
         take("bz32", Rk * d * 4, 4)
         take("bsbar", Rk * d * 4, 4)
-        take("bc", Rk * 4, 4)
         take("bzmax", R * (k // 32) * 4, 4)
         take("bz16", Rk * d * 2, 2)
         take("bcz", Rk * 4, 4)

@@ -86,6 +86,20 @@ def test_closed_form_one_prototype():
     np.testing.assert_allclose(dWv, np.outer(H.mean(axis=0), G[0]), rtol=1e-13, atol=1e-14)
 
 
+def test_closed_form_one_token():
+    # n = 1: A[j] = 1 for every prototype, m_j = 1, S_j = h Wv whatever P and
+    # Wk are, so dP = dWk = 0, dH = (sum_j G_j) Wv^T, dWv = h^T (sum_j G_j)
+    g = np.random.default_rng(7)
+    k, d = 5, 4
+    H, Wk, Wv = g.standard_normal((1, d)), g.standard_normal((d, d)), g.standard_normal((d, d))
+    P, G = g.standard_normal((k, d)), g.standard_normal((k, d))
+    dH, dP, dWk, dWv = sketch_one_grad(H, Wk, Wv, P, G)
+    np.testing.assert_allclose(dP, 0.0, atol=1e-14)
+    np.testing.assert_allclose(dWk, 0.0, atol=1e-14)
+    np.testing.assert_allclose(dH, G.sum(axis=0)[None, :] @ Wv.T, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dWv, np.outer(H[0], G.sum(axis=0)), rtol=1e-13, atol=1e-14)
+
+
 def test_closed_form_zero_key_projection():
     # Wk = 0: every logit is 0, A = 1/k, m_j = n/k, S_j = mean value row vbar.
     # Worked by hand from the definition:
