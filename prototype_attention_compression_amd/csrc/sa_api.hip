@@ -105,7 +105,7 @@ Layout make_layout(const sa_problem& p, bool bwd = false) {
   L.off_chunk_base = take(R1 * sizeof(int32_t));
   if (!f32) {
     L.off_q16 = take((size_t)p.k * p.d * 2);
-    L.off_qnorm = take((size_t)p.k * sizeof(float));
+    L.off_qpart = take((size_t)(p.k / 32) * sizeof(float));
     L.off_h16 = take((size_t)tiles_max * kTile * p.d * 2);
     L.off_nl = take((size_t)tiles_max * kTile * sizeof(uint32_t));
     if (L.groups > 0) L.off_xbuf = take((size_t)L.groups * kXSlots * kTile * (p.k / kFusedProtos) * sizeof(uint64_t));

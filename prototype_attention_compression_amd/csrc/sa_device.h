@@ -230,6 +230,17 @@ __device__ __forceinline__ _Float16* ws_f16(void* ws, size_t off) {
   return reinterpret_cast<_Float16*>(reinterpret_cast<char*>(ws) + off);
 }
 
+// The largest row norm of the fp16 queries: the maximum of the per-32-row
+// maxima the preparation writes (in every lane of the calling wave).
+__device__ __forceinline__ float query_norm_max(const Layout& L, void* ws) {
+  const float* qp = ws_f32(ws, L.off_qpart);
+  float m = 0.f;
+  for (int i = threadIdx.x & 63; i < L.k / 32; i += 64) m = fmaxf(m, qp[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  return m;
+}
+
 // Where a tile lives: user, first token (packed index) and valid row count.
 struct TileInfo {
   int user;

@@ -670,7 +670,7 @@ __global__ __launch_bounds__(kWaves * 64) void fused_accum(Layout L, void* ws) {
   if (ga >= gb) return;  // uniform over the group
   // |q_j . h_t| <= qmax hmax: below 100 no 2^L can overflow or leave the
   // normal range, and plain sums are exact enough
-  const float bound = __int_as_float(hdr[kHdrQmax]) * __int_as_float(hdr[kHdrHmax]);
+  const float bound = query_norm_max(L, ws) * __int_as_float(hdr[kHdrHmax]);
   if (bound < 100.0f)
     fused_body<D, P, false>(L, ws, lds, ctl, group, pb, ga, gb);
   else

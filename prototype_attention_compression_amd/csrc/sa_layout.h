@@ -66,11 +66,11 @@ struct Layout {
   int32_t parts_max;       // partial-sum slots: chunks_max (fp32), else max(groups, p2_groups) + R
   int32_t p2_groups;       // pass-2 groups (bf16): kP2WGs / n_pblocks
   // byte offsets into the workspace (all 256-aligned)
-  size_t off_hdr;          // [64] int32: error flag, qmax (float), totals
+  size_t off_hdr;          // [64] int32: error flag, totals
   size_t off_tile_base;    // [R+1] int32
   size_t off_chunk_base;   // [R+1] int32
   size_t off_q16;          // [k, d] fp16    queries
-  size_t off_qnorm;        // [k] float      |q_j| of the fp16 queries
+  size_t off_qpart;        // [k / 32] float largest |q_j| of each 32-row block of the fp16 queries
   size_t off_h16;          // [tiles_max, 32, d] fp16    token rows
   size_t off_nl;           // [tiles_max, 32] uint32 per token.  Two-pass: fp16 pairs
                            //   (-l_hi, -l_lo), l = lse_t - 14, (-60000, 0) if dropped.
@@ -101,7 +101,7 @@ struct Layout {
 
 // Header words.
 constexpr int kHdrErr = 0;
-constexpr int kHdrQmax = 1;      // float bits
+                                 // (word 1 unused)
 constexpr int kHdrTiles = 2;     // total tiles
 constexpr int kHdrChunks = 3;    // total chunks
 constexpr int kHdrHmax = 4;      // float bits: largest |h_t| of a kept token (one-pass)

@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256) void pass1_lse(const uint16_t* __restrict__ H,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, g = lane >> 5;
   const int32_t* tile_base = ws_i32(ws, L.off_tile_base);
-  const float qmax = __int_as_float(hdr[kHdrQmax]);
+  const float qmax = query_norm_max(L, ws);
 
   half8 hreg[2][C::S];
   bool valid[2];

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   const int32_t tb = min(T, ta + per);
   if (ta >= tb) return;  // uniform
   const int n = tb - ta;
-  const float qmax = __int_as_float(hdr[kHdrQmax]);
+  const float qmax = query_norm_max(L, ws);
   const float lim2 = 10000.0f / fmaxf(qmax * qmax, 1e-30f);   // |h|^2 >= lim2  <=>  qmax |h| >= 100
 
   const int tid = threadIdx.x, lane = tid & 63;

@@ -10,40 +10,91 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "sa_device.h"
 #include "sa_launch.h"
 
 namespace sa {
 
-template <typename T>
-__device__ __forceinline__ float load_in(const T* p, int64_t i);
-template <>
-__device__ __forceinline__ float load_in<uint16_t>(const uint16_t* p, int64_t i) {
-  return __uint_as_float(((uint32_t)p[i]) << 16);
-}
-template <>
-__device__ __forceinline__ float load_in<float>(const float* p, int64_t i) {
-  return p[i];
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Queries from bf16 inputs on bf16 MFMAs: P and Wk are exact in bf16, so the
+// products are exact in fp32 and the sums are fp32, the same arithmetic as an
+// fp32 dot product in another order.  The workgroup (4 waves) computes rows
+// r0 .. r0 + 32 RB - 1; wave w the 32 x 32 output block (row block w / CB,
+// column block w % CB).  Operands come straight from global memory: lane
+// (col, g) reads 8 consecutive elements of row col of P and of Wk (the
+// A operand's row m = col, the B operand's column n = col, K elements 8 g ..
+// 8 g + 7 of the step).  The rows go to fp16 (the MFMA operand type of the
+// passes); qpart receives each 32-row block's largest row norm of the fp16
+// values, which bounds every logit of a token by |h_t| times its maximum.
+template <int D>
+__device__ __forceinline__ void queries_bf16(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Wk,
+                                             const Layout& L, void* ws, int blk) {
+  constexpr int CB = D / 32;      // 32-column blocks
+  constexpr int RB = 4 / CB;      // 32-row blocks per workgroup
+  constexpr int ROWS = 32 * RB;
+  constexpr int TPR = 256 / ROWS; // threads per row in the norm sums
+  __shared__ float sq[ROWS][D + 1];
+  __shared__ float rn[ROWS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, g = lane >> 5;
+  const int rb = wave / CB, cb = wave % CB;
+  const int r0 = blk * ROWS + 32 * rb, c0 = 32 * cb;
+  const bf16x8* pa = reinterpret_cast<const bf16x8*>(P + (int64_t)(r0 + col) * D + 8 * g);
+  const bf16x8* wb = reinterpret_cast<const bf16x8*>(Wk + (int64_t)(c0 + col) * D + 8 * g);
+  bf16x8 a[D / 16], b[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    a[s] = pa[2 * s];
+    b[s] = wb[2 * s];
+  }
+  float16v acc = float16v{};
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b[s], acc, 0, 0, 0);
+  const float scale = 1.4426950408889634f / sqrtf((float)D);
+  _Float16* q16 = ws_f16(ws, L.off_q16);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = acc_row(r, g);
+    const _Float16 qh = (_Float16)(acc[r] * scale);
+    q16[(int64_t)(r0 + m) * D + c0 + col] = qh;
+    const float qf = (float)qh;
+    sq[32 * rb + m][c0 + col] = qf * qf;
+  }
+  __syncthreads();
+  {
+    const int row = tid / TPR, part = tid % TPR;
+    float s = 0.f;
+    for (int c = part; c < D; c += TPR) s += sq[row][c];
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) s += __shfl_xor(s, o);
+    if (part == 0) rn[row] = s;
+  }
+  __syncthreads();
+  if (tid < RB) {
+    float m = 0.f;
+    for (int r = 0; r < 32; ++r) m = fmaxf(m, rn[32 * tid + r]);
+    ws_f32(ws, L.off_qpart)[blk * RB + tid] = sqrtf(m);
+  }
 }
 
-// One workgroup of 256 threads computes 256 / D query rows.  Thread (j, c)
-// forms q[j][c] = sum_a P[j][a] * Wk[c][a], scaled.  The bf16 path stores the
-// rows in fp16 (the MFMA operand type) with their norms; the fp32 path stores
-// fp32 rows.
-template <int D, typename T>
-__global__ __launch_bounds__(256) void prep_queries(const T* __restrict__ P, const T* __restrict__ Wk,
-                                                    Layout L, void* ws) {
+// Queries from fp32 inputs: one workgroup of 256 threads computes 256 / D
+// rows; thread (j, c) forms q[j][c] = sum_a P[j][a] Wk[c][a], scaled, in
+// fp32 (the fp32 path's passes bound nothing by the query norms).
+template <int D>
+__device__ __forceinline__ void queries_f32(const float* __restrict__ P, const float* __restrict__ Wk,
+                                            const Layout& L, void* ws, int blk) {
   constexpr int PR = 256 / D;
   // Wk staged in LDS with all of its 16-byte loads in flight together (a
   // row-per-thread walk through global memory waited on each load); the
   // padded pitch keeps the row-per-thread LDS reads on distinct banks
-  constexpr int EPC = 16 / (int)sizeof(T);                 // elements per 16-byte chunk
-  constexpr int WCH = D * D / EPC / 256;                   // chunks per thread
-  constexpr int WP = D + (sizeof(T) == 2 ? 2 : 1);
-  static_assert(WCH * 256 * EPC == D * D, "whole chunks");
+  constexpr int WCH = D * D / 4 / 256;                     // 16-byte chunks per thread
+  constexpr int WP = D + 1;
+  static_assert(WCH * 256 * 4 == D * D, "whole chunks");
   __shared__ float prow[PR][D];
-  __shared__ float red[256];
-  __shared__ T wk[D * WP];
+  __shared__ float wk[D * WP];
   const int tid = threadIdx.x;
   {
     u32x4 w[WCH];
@@ -51,112 +102,111 @@ __global__ __launch_bounds__(256) void prep_queries(const T* __restrict__ P, con
     for (int i = 0; i < WCH; ++i) w[i] = reinterpret_cast<const u32x4*>(Wk)[tid + 256 * i];
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
-      const int q = tid + 256 * i, row = q / (D / EPC), e0 = EPC * (q % (D / EPC));
-      const T* v = reinterpret_cast<const T*>(&w[i]);
+      const int q = tid + 256 * i, row = q / (D / 4), e0 = 4 * (q % (D / 4));
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) wk[row * WP + e0 + e] = v[e];
+      for (int e = 0; e < 4; ++e) wk[row * WP + e0 + e] = __uint_as_float(w[i][e]);
     }
   }
   const int jl = tid / D, c = tid % D;
-  const int j = blockIdx.x * PR + jl;
-  prow[jl][c] = load_in<T>(P, (int64_t)j * D + c);
+  const int j = blk * PR + jl;
+  prow[jl][c] = P[(int64_t)j * D + c];
   __syncthreads();
   float acc = 0.f;
 #pragma unroll 8
-  for (int a = 0; a < D; ++a) acc = fmaf(prow[jl][a], load_in<T>(wk, c * WP + a), acc);
-  const float scale = 1.4426950408889634f / sqrtf((float)D);
-  const float q = acc * scale;
-  if (L.dtype == 1) {
-    ws_f32(ws, L.off_q32)[(int64_t)j * D + c] = q;
-    return;
+  for (int a = 0; a < D; ++a) acc = fmaf(prow[jl][a], wk[c * WP + a], acc);
+  ws_f32(ws, L.off_q32)[(int64_t)j * D + c] = acc * (1.4426950408889634f / sqrtf((float)D));
+}
+
+// The ragged schedule (one workgroup of 256 threads).  Checks 0 = offsets[0]
+// <= ... <= offsets[R] = N; on a violation every user is treated as empty and
+// the error flag is raised.  Writes tile_base / chunk_base (exclusive prefix
+// sums of tiles_u = ceil(n_u / 32) rounded up to a multiple of
+// kUserTileAlign, and of ceil(tiles_u / tiles_per_chunk)) and the totals.
+// Users go 256 at a time: a scan within each wave (lane shuffles), the four
+// wave totals through LDS, and a running carry.
+__device__ __forceinline__ void schedule(const int64_t* __restrict__ offsets, const Layout& L, void* ws) {
+  __shared__ int32_t wt[2][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = L.R;
+  const int CT = L.tiles_per_chunk;
+  int32_t* tile_base = ws_i32(ws, L.off_tile_base);
+  int32_t* chunk_base = ws_i32(ws, L.off_chunk_base);
+  int bad = 0;
+  int32_t carry_t = 0, carry_c = 0;
+  for (int u0 = 0; u0 < R; u0 += 256) {
+    const int u = u0 + tid;
+    int32_t t = 0;
+    if (u < R) {
+      const int64_t n = offsets[u + 1] - offsets[u];
+      if (n < 0) bad = 1;
+      else t = (int32_t)((n + kTile * kUserTileAlign - 1) / (kTile * kUserTileAlign)) * kUserTileAlign;
+    }
+    const int32_t c = (t + CT - 1) / CT;
+    int32_t st = t, sc = c;   // inclusive scans over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t xt = __shfl_up(st, o), xc = __shfl_up(sc, o);
+      if (lane >= o) {
+        st += xt;
+        sc += xc;
+      }
+    }
+    if (lane == 63) {
+      wt[0][wave] = st;
+      wt[1][wave] = sc;
+    }
+    __syncthreads();
+    int32_t bt = carry_t + st - t, bc = carry_c + sc - c;
+    for (int w = 0; w < wave; ++w) {
+      bt += wt[0][w];
+      bc += wt[1][w];
+    }
+    carry_t += wt[0][0] + wt[0][1] + wt[0][2] + wt[0][3];
+    carry_c += wt[1][0] + wt[1][1] + wt[1][2] + wt[1][3];
+    __syncthreads();   // every read of wt is done before the next users' totals
+    if (u < R) {
+      tile_base[u] = bt;
+      chunk_base[u] = bc;
+    }
   }
-  _Float16* q16 = ws_f16(ws, L.off_q16) + (int64_t)j * D;
-  const _Float16 qh = (_Float16)q;
-  q16[c] = qh;
-  const float qf = (float)qh;
-  red[tid] = qf * qf;
-  __syncthreads();
-  if (c == 0) {
-    float s = 0.f;
-    for (int a = 0; a < D; ++a) s += red[jl * D + a];
-    ws_f32(ws, L.off_qnorm)[j] = sqrtf(s);
+  if (tid == 0 && (offsets[0] != 0 || offsets[R] != L.N)) bad = 1;
+  bad = __syncthreads_or(bad);   // also orders the stores above before those below
+  if (bad) {
+    for (int u = tid; u < R; u += 256) {
+      tile_base[u] = 0;
+      chunk_base[u] = 0;
+    }
+    carry_t = 0;
+    carry_c = 0;
+  }
+  if (tid == 0) {
+    int32_t* hdr = ws_i32(ws, L.off_hdr);
+    tile_base[R] = carry_t;
+    chunk_base[R] = carry_c;
+    hdr[kHdrErr] = bad ? kErrBadOffsets : 0;
+    hdr[kHdrTiles] = carry_t;
+    hdr[kHdrChunks] = carry_c;
+    hdr[kHdrHmax] = 0;
   }
 }
 
-// Single workgroup.  Checks 0 = offsets[0] <= ... <= offsets[R] = N; on a
-// violation every user is treated as empty and the error flag is raised.
-// Writes tile_base / chunk_base (exclusive prefix sums of tiles_u = ceil(n_u /
-// 32) rounded up to a multiple of kUserTileAlign, and ceil(tiles_u /
-// tiles_per_chunk)), the totals, and the largest query norm.
-__global__ __launch_bounds__(1024) void prep_schedule(const int64_t* __restrict__ offsets, Layout L,
-                                                      void* ws) {
-  __shared__ int32_t sc_t[1024];
-  __shared__ int32_t sc_c[1024];
-  __shared__ float sq[1024];
-  const int tid = threadIdx.x;
-  const int R = L.R;
-  int bad = 0;
-  for (int u = tid; u < R; u += 1024)
-    if (offsets[u + 1] < offsets[u]) bad = 1;
-  if (tid == 0 && (offsets[0] != 0 || offsets[R] != L.N)) bad = 1;
-  bad = __syncthreads_or(bad);
+// Per-launch preparation in one launch: workgroups 0 .. nq - 1 compute the
+// queries, workgroup nq the schedule (the two are independent).
+template <int D, typename T>
+__global__ __launch_bounds__(256) void prep(const T* __restrict__ P, const T* __restrict__ Wk,
+                                            const int64_t* __restrict__ offsets, Layout L, void* ws, int nq) {
+  const int blk = blockIdx.x;
+  if (blk == nq) {
+    schedule(offsets, L, ws);
+    return;
+  }
+  if constexpr (std::is_same<T, uint16_t>::value) queries_bf16<D>(P, Wk, L, ws, blk);
+  else queries_f32<D>(P, Wk, L, ws, blk);
+}
 
-  const int seg = (R + 1023) / 1024;
-  const int u0 = min(R, tid * seg), u1 = min(R, u0 + seg);
-  const int CT = L.tiles_per_chunk;
-  int32_t nt = 0, nc = 0;
-  for (int u = u0; u < u1; ++u) {
-    int64_t n = bad ? 0 : offsets[u + 1] - offsets[u];
-    int32_t t = (int32_t)((n + kTile * kUserTileAlign - 1) / (kTile * kUserTileAlign)) * kUserTileAlign;
-    nt += t;
-    nc += (t + CT - 1) / CT;
-  }
-  sc_t[tid] = nt;
-  sc_c[tid] = nc;
-  __syncthreads();
-  // inclusive Hillis-Steele scan over the 1024 per-thread totals
-  for (int off = 1; off < 1024; off <<= 1) {
-    int32_t a = tid >= off ? sc_t[tid - off] : 0;
-    int32_t b = tid >= off ? sc_c[tid - off] : 0;
-    __syncthreads();
-    sc_t[tid] += a;
-    sc_c[tid] += b;
-    __syncthreads();
-  }
-  int32_t bt = sc_t[tid] - nt, bc = sc_c[tid] - nc;
-  int32_t* tile_base = ws_i32(ws, L.off_tile_base);
-  int32_t* chunk_base = ws_i32(ws, L.off_chunk_base);
-  for (int u = u0; u < u1; ++u) {
-    tile_base[u] = bt;
-    chunk_base[u] = bc;
-    int64_t n = bad ? 0 : offsets[u + 1] - offsets[u];
-    int32_t t = (int32_t)((n + kTile * kUserTileAlign - 1) / (kTile * kUserTileAlign)) * kUserTileAlign;
-    bt += t;
-    bc += (t + CT - 1) / CT;
-  }
-  int32_t* hdr = ws_i32(ws, L.off_hdr);
-  if (tid == 1023) {
-    tile_base[R] = sc_t[1023];
-    chunk_base[R] = sc_c[1023];
-    hdr[kHdrErr] = bad ? kErrBadOffsets : 0;
-    hdr[kHdrTiles] = sc_t[1023];
-    hdr[kHdrChunks] = sc_c[1023];
-    hdr[kHdrHmax] = 0;
-  }
-  if (L.dtype == 0) {
-    float m = 0.f;
-    const float* qn = ws_f32(ws, L.off_qnorm);
-    for (int j = tid; j < L.k; j += 1024) m = fmaxf(m, qn[j]);
-    sq[tid] = m;
-    __syncthreads();
-    for (int off = 512; off > 0; off >>= 1) {
-      if (tid < off) sq[tid] = fmaxf(sq[tid], sq[tid + off]);
-      __syncthreads();
-    }
-    if (tid == 0) hdr[kHdrQmax] = __float_as_int(sq[0]);
-  } else if (tid == 0) {
-    hdr[kHdrQmax] = 0;
-  }
+// The schedule alone (target attention's candidate tiles).
+__global__ __launch_bounds__(256) void prep_schedule(const int64_t* __restrict__ offsets, Layout L, void* ws) {
+  schedule(offsets, L, ws);
 }
 
 // Zero fill of the one-pass exchange ring (its tags must not match a tile of
@@ -179,31 +229,32 @@ hipError_t launch_copy_error(const Layout& L, const void* ws, int32_t* dst, hipS
 }
 
 hipError_t launch_schedule(const Layout& L, const int64_t* offsets, void* ws, hipStream_t stream) {
-  hipLaunchKernelGGL(prep_schedule, dim3(1), dim3(1024), 0, stream, offsets, L, ws);
+  hipLaunchKernelGGL(prep_schedule, dim3(1), dim3(256), 0, stream, offsets, L, ws);
   return hipGetLastError();
 }
 
 hipError_t launch_prep(const Layout& L, const void* P, const void* Wk, const int64_t* offsets, void* ws,
                        hipStream_t stream) {
-  const int PR = 256 / L.d;
-  dim3 gq(L.k / PR), bq(256);
+  // query workgroups: 32 (d = 128) or 64 (d = 64) rows each on MFMAs, 256 / d
+  // rows each in fp32; one more workgroup for the schedule
+  const int nq = L.dtype == 0 ? L.k / (L.d == 128 ? 32 : 64) : L.k / (256 / L.d);
+  const dim3 grid((unsigned)(nq + 1)), block(256);
   if (L.dtype == 0) {
     if (L.d == 128)
-      hipLaunchKernelGGL((prep_queries<128, uint16_t>), gq, bq, 0, stream, (const uint16_t*)P,
-                         (const uint16_t*)Wk, L, ws);
+      hipLaunchKernelGGL((prep<128, uint16_t>), grid, block, 0, stream, (const uint16_t*)P, (const uint16_t*)Wk,
+                         offsets, L, ws, nq);
     else
-      hipLaunchKernelGGL((prep_queries<64, uint16_t>), gq, bq, 0, stream, (const uint16_t*)P,
-                         (const uint16_t*)Wk, L, ws);
+      hipLaunchKernelGGL((prep<64, uint16_t>), grid, block, 0, stream, (const uint16_t*)P, (const uint16_t*)Wk,
+                         offsets, L, ws, nq);
   } else {
     if (L.d == 128)
-      hipLaunchKernelGGL((prep_queries<128, float>), gq, bq, 0, stream, (const float*)P, (const float*)Wk, L, ws);
+      hipLaunchKernelGGL((prep<128, float>), grid, block, 0, stream, (const float*)P, (const float*)Wk, offsets, L,
+                         ws, nq);
     else
-      hipLaunchKernelGGL((prep_queries<64, float>), gq, bq, 0, stream, (const float*)P, (const float*)Wk, L, ws);
+      hipLaunchKernelGGL((prep<64, float>), grid, block, 0, stream, (const float*)P, (const float*)Wk, offsets, L,
+                         ws, nq);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prep_schedule, dim3(1), dim3(1024), 0, stream, offsets, L, ws);
-  e = hipGetLastError();
   if (e != hipSuccess || !L.fused) return e;
   const int64_t words = (int64_t)L.groups * kXSlots * kTile * (L.k / kFusedProtos);
   hipLaunchKernelGGL(clear_words, dim3(64), dim3(256), 0, stream,

@@ -58,7 +58,7 @@ def layout(R, N, d, k, bwd):
     take("tile_base", (R + 1) * 4, 4)
     take("chunk_base", (R + 1) * 4, 4)
     take("q16", k * d * 2, 2)
-    take("qnorm", k * 4, 4)
+    take("qpart", (k // 32) * 4, 4)
     take("h16", L["tiles_max"] * TILE * d * 2, 2)
     take("nl", L["tiles_max"] * TILE * 4, 4)
     if L["groups"]:
