@@ -65,17 +65,17 @@ DEFAULT_WORKLOAD = "c3lit_r40_n100k_d128_k1024"
 # the figure is reported as null once they differ.
 COPY_CALIBRATION_BYTES = 1 << 30
 TRAFFIC = {
-    # 1.0264e9 fetched + 1.0410e9 written (40 x 100K tokens, k = 1024, d = 128)
-    "pass1_qres": (2067380424, "fed9728c7e8e8f851b3620ac5960d025e9dcc093b83088c2a6db37f0d175820f",
+    # 1.0265e9 fetched + 1.0410e9 written (40 x 100K tokens, k = 1024, d = 128)
+    "pass1_qres": (2067465011, "0b14292b442f37dd1325e30f44f719d99ac7efeb8fc0bb7187ad6d5196db771d",
                    ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
-    # 1.0827e9 fetched + 0.0565e9 written (same workload)
-    "pass2_accum": (1139212538, "e32abe5be091c6496e53fdd79298c75137006cad1966b01643fe0ec21395b6c0",
+    # 1.0552e9 fetched + 0.0565e9 written (same workload)
+    "pass2_accum": (1111685530, "4dee340760e4da8b2560b07fe6caa9f344ee5d14f6ef998196360ccf4d180372",
                     ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
-    # 1.3119e9 fetched + 2.0680e9 written (same workload, --backward)
-    "bwd_dh": (3379912097, "330d012913985479c72517fbed527e8148ae56c82bd0234e815efd4f6f7fd350",
+    # 1.3084e9 fetched + 2.0680e9 written (same workload, --backward)
+    "bwd_dh": (3376437248, "e6bde02432203cccb6948771d30a1bfdd87afbcc79a40b7cef0c706b9e6b4316",
                ("sa_bwd.hip", "sa_layout.h", "sa_device.h")),
-    # 1.8648e8 fetched + 0.4608e8 written (300 users x 300 candidates, --target-attention)
-    "ta_attend": (232557499, "dde2a4eb66f782be60a870e733718eafb646e6eea17a678c05ab161aea159158",
+    # 1.8668e8 fetched + 0.4608e8 written (300 users x 300 candidates, --target-attention)
+    "ta_attend": (232757862, "7df8952f9bb791989e794cd57a7512979ee00b2cbab3284f360ae66dc62f52d3",
                   ("sa_target.hip", "sa_layout.h", "sa_device.h")),
 }
 
@@ -85,11 +85,11 @@ TRAFFIC = {
 # kernel's time), from rocprofv3 --pmc on the default workload; valid, like the
 # traffic figures, only for the kernel sources they were taken on (null after).
 COUNTERS = {
-    "pass1_qres": ({"mfma_busy": 0.552, "clock_mhz": 1754.0},
-                   "fed9728c7e8e8f851b3620ac5960d025e9dcc093b83088c2a6db37f0d175820f",
+    "pass1_qres": ({"mfma_busy": 0.549, "clock_mhz": 1734.0},
+                   "0b14292b442f37dd1325e30f44f719d99ac7efeb8fc0bb7187ad6d5196db771d",
                    ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
-    "pass2_accum": ({"mfma_busy": 0.617, "clock_mhz": 1810.0},
-                    "e32abe5be091c6496e53fdd79298c75137006cad1966b01643fe0ec21395b6c0",
+    "pass2_accum": ({"mfma_busy": 0.611, "clock_mhz": 1791.0},
+                    "4dee340760e4da8b2560b07fe6caa9f344ee5d14f6ef998196360ccf4d180372",
                     ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
 }
 
