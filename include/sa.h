@@ -496,6 +496,24 @@ sa_status sa_cache_fill(sa_cache* cache, const sa_problem* store, const void* H_
  */
 sa_status sa_read_device_error(const void* workspace, void* stream, int32_t* flag);
 
+/*
+ * Measurement helper, not part of the compression path: how fast the matrix
+ * cores run on a given kind of operand data.  Queues one launch of a loop of
+ * fp16 32x32x16 MFMAs with no memory traffic: 512 workgroups of 4 waves (two
+ * waves per SIMD on 256 CUs), each wave `iters` x 8 MFMAs over four
+ * accumulator chains with its operands in registers.  `operands`: 0 all
+ * zeros, 1 one constant value, 2 uniform values in [-1, 1) that differ per
+ * lane and per instruction.  The launch does 2048 x iters x 8 x 32768 FLOP;
+ * timed with events on `stream`, it gives the MFMA rate on that data (the
+ * clock of a power-limited part depends on how many operand bits toggle).
+ * `sink` (device, SA_PROBE_SINK_FLOATS floats, caller-owned) receives one sum
+ * per thread so that the work is not optimised away.  SA_E_INVALID for a NULL
+ * sink, `operands` outside 0..2 or `iters` outside 1..1,000,000; SA_E_HIP if
+ * the launch fails.
+ */
+#define SA_PROBE_SINK_FLOATS 131072
+sa_status sa_probe_mfma(int32_t operands, int32_t iters, float* sink, void* stream);
+
 /* Static text for a status code.  Never NULL. */
 const char* sa_status_string(sa_status status);
 

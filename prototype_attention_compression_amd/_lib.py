@@ -25,7 +25,7 @@ EXPORTS = ("sa_workspace_size", "sa_workspace_bytes", "sa_compress_static", "sa_
            "sa_target_attention_workspace_size", "sa_target_attention", "sa_target_attention_rows",
            "sa_cache_create", "sa_cache_destroy", "sa_cache_lookup", "sa_cache_fill_workspace_size",
            "sa_cache_fill",
-           "sa_read_device_error", "sa_status_string", "sa_version")
+           "sa_read_device_error", "sa_probe_mfma", "sa_status_string", "sa_version")
 NUM_PHASE_EVENTS = 5
 STATIC_SCRATCH_BYTES = 64 << 20   # SA_STATIC_SCRATCH_BYTES
 NUM_BWD_PHASE_EVENTS = 6
@@ -119,6 +119,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sa_cache_fill.restype = ctypes.c_int
     lib.sa_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
     lib.sa_read_device_error.restype = ctypes.c_int
+    lib.sa_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp]
+    lib.sa_probe_mfma.restype = ctypes.c_int
     lib.sa_status_string.argtypes = [ctypes.c_int]
     lib.sa_status_string.restype = ctypes.c_char_p
     lib.sa_version.argtypes = []
@@ -287,6 +289,25 @@ def compress(H, offsets, Wk, Wv, P, mask=None, return_mass: bool = False,
     if st != SA_OK:
         raise SaError(st, "sa_compress")
     return (S, m) if return_mass else S
+
+
+PROBE_SINK_FLOATS = 131072   # SA_PROBE_SINK_FLOATS
+PROBE_WAVES = 2048
+
+
+def probe_mfma(operands: int, iters: int, sink, stream=None) -> float:
+    """Queue sa_probe_mfma on ``stream`` (default: the current stream) and
+    return the FLOP count of that launch.  ``sink``: a float32 device tensor
+    of PROBE_SINK_FLOATS elements."""
+    import torch
+
+    if sink.dtype != torch.float32 or sink.numel() < PROBE_SINK_FLOATS or not sink.is_cuda:
+        raise ValueError("sink: a float32 device tensor of PROBE_SINK_FLOATS elements")
+    s = stream if stream is not None else torch.cuda.current_stream(sink.device)
+    st = load().sa_probe_mfma(int(operands), int(iters), _ptr(sink), ctypes.c_void_p(s.cuda_stream))
+    if st != SA_OK:
+        raise SaError(st, "sa_probe_mfma")
+    return float(PROBE_WAVES) * iters * 8 * 32768
 
 
 def read_device_error(workspace) -> int:

@@ -283,3 +283,14 @@ def test_misaligned_inputs_rejected_before_launch():
         assert _bcall(pb, **{name: FAKE + 8}) == sa.SA_E_INVALID, name
     assert _call(pb, off=FAKE + 4) == sa.SA_E_INVALID
     assert _bcall(pb, off=FAKE + 4) == sa.SA_E_INVALID
+
+
+def test_probe_rejects_bad_arguments():
+    """sa_probe_mfma checks its arguments on the host before any launch."""
+    lib = _lib.load()
+    sink = ctypes.c_void_p(16)   # never dereferenced: every call below fails its checks
+    assert lib.sa_probe_mfma(2, 10, None, None) == sa.SA_E_INVALID
+    assert lib.sa_probe_mfma(3, 10, sink, None) == sa.SA_E_INVALID
+    assert lib.sa_probe_mfma(-1, 10, sink, None) == sa.SA_E_INVALID
+    assert lib.sa_probe_mfma(2, 0, sink, None) == sa.SA_E_INVALID
+    assert lib.sa_probe_mfma(2, 1000001, sink, None) == sa.SA_E_INVALID
