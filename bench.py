@@ -32,6 +32,10 @@ timed with the misses' fill serial and overlapped on a side stream.
 and on an all-zero history (same shapes and instruction streams) and reports
 both pass times: a difference is the data dependence of the clock.
 
+``--mfma-ceiling`` times sa_probe_mfma, a loop of fp16 32x32x16 MFMAs with no
+memory traffic, on zero, constant and random operands: the matrix cores'
+rate on random data is the practical ceiling the pass kernels are held to.
+
 ``--backward`` times one sa_compress_backward call per step instead (the
 gradients dH, dP, dWk, dWv for a seeded dS, forward recomputation included)
 on the same workload; its roofline object reports the token-major dH kernel
@@ -42,6 +46,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import json
+import math
 import os
 import sys
 import time
@@ -724,12 +729,22 @@ def measure_config(name: str, torch, dev, sa, steps: int = 10, warmup: int = 3, 
         step()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the clean timing window covers about 20 ms of work (at least `steps`
+    # steps), after as many warm-up steps again, so that the launch latency
+    # at its ends and the clock's transitions weigh little for small workloads
     a.record()
-    for _ in range(steps):
+    step()
+    b.record()
+    torch.cuda.synchronize()
+    clean = int(min(2000, max(steps, math.ceil(20.0 / max(a.elapsed_time(b), 1e-3)))))
+    for _ in range(clean):
+        step()
+    a.record()
+    for _ in range(clean):
         step()
     b.record()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+    ms = a.elapsed_time(b) / clean
     for i in range(steps):
         step(arrs[i])
     torch.cuda.synchronize()
@@ -753,7 +768,7 @@ def measure_config(name: str, torch, dev, sa, steps: int = 10, warmup: int = 3, 
             hip.destroy(x)
     n_valid = inp.valid_tokens()
     algo = 4.0 * n_valid * k * d
-    out = {"users": R, "tokens": n_valid, "k": k, "d": d, "dtype": inp.dtype, "ms_per_step": ms,
+    out = {"users": R, "tokens": n_valid, "k": k, "d": d, "dtype": inp.dtype, "ms_per_step": ms, "timed_steps": clean,
            "tokens_per_s": n_valid / (ms * 1e-3), "tflops": algo / (ms * 1e-3) / 1e12,
            "pct_peak": algo / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS if inp.dtype == "bf16" else None,
            "pass1_ms": p1, "pass2_ms": p2,
@@ -818,6 +833,48 @@ def bench_data_probe(args, torch, dev, sa):
     return 0
 
 
+def bench_mfma_ceiling(args, torch, dev, sa):
+    """The matrix cores' rate on zero, constant and random fp16 operands
+    (sa_probe_mfma: no memory traffic, two waves per SIMD, four independent
+    accumulator chains per wave), each kind warmed up and then timed over
+    ``--steps`` launches with events on the current stream.  The random kind
+    runs again at the end to show drift."""
+    sink = torch.empty(sa._lib.PROBE_SINK_FLOATS, dtype=torch.float32, device=dev)
+    iters = 4096
+    res = {}
+    for name, kind in (("random", 2), ("constant", 1), ("zeros", 0), ("random_again", 2)):
+        for _ in range(max(args.warmup, 20)):
+            sa._lib.probe_mfma(kind, iters, sink)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        flop = 0.0
+        for _ in range(args.steps):
+            flop += sa._lib.probe_mfma(kind, iters, sink)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        res[name] = {"tflops": flop / (ms * 1e-3) / 1e12, "ms_per_launch": ms / args.steps}
+        assert torch.isfinite(sink).all()
+    out = {
+        "metric": "fp16 MFMA rate (32x32x16, operands in registers, no memory traffic)",
+        "value": res["random"]["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": max(args.warmup, 20),
+        "higher_is_better": True,
+        "data": "synthetic",
+        "config": {"workload": "mfma_probe_2048_waves", "iters": iters, "mfma_per_iter": 8,
+                   "flop_per_launch": float(sa._lib.PROBE_WAVES) * iters * 8 * 32768},
+        "by_operands": res,
+        "peak": PEAK_MFMA_F16_TFLOPS,
+        "frac_random": res["random"]["tflops"] / PEAK_MFMA_F16_TFLOPS,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -846,6 +903,8 @@ def main(argv=None):
                          "(sa_compress_backward_with_sbar) instead of recomputing its sums")
     ap.add_argument("--data-probe", action="store_true",
                     help="time the headline workload on its seeded history and on an all-zero history")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="time a loop of fp16 MFMAs (no memory traffic) on zero, constant and random operands")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device once (counter calibration)")
     args = ap.parse_args(argv)
@@ -872,6 +931,8 @@ def main(argv=None):
         return bench_serving_pipeline(args, torch, dev, sa)
     if args.data_probe:
         return bench_data_probe(args, torch, dev, sa)
+    if args.mfma_ceiling:
+        return bench_mfma_ceiling(args, torch, dev, sa)
     inp = make_config(args.workload)
     if args.backward:
         return bench_backward(args, inp, torch, dev, sa)
