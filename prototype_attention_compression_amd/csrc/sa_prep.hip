@@ -122,9 +122,12 @@ __device__ __forceinline__ void queries_f32(const float* __restrict__ P, const f
 // the error flag is raised.  Writes tile_base / chunk_base (exclusive prefix
 // sums of tiles_u = ceil(n_u / 32) rounded up to a multiple of
 // kUserTileAlign, and of ceil(tiles_u / tiles_per_chunk)) and the totals.
-// Users go 256 at a time: a scan within each wave (lane shuffles), the four
-// wave totals through LDS, and a running carry.
+// Users go 2048 at a time, 8 consecutive ones per thread (their offsets are
+// loaded together): per-thread sums, a scan within each wave (lane shuffles),
+// the four wave totals through LDS, and a running carry.
 __device__ __forceinline__ void schedule(const int64_t* __restrict__ offsets, const Layout& L, void* ws) {
+  constexpr int UPT = 8;             // users per thread
+  constexpr int CHUNK = 256 * UPT;   // users per pass
   __shared__ int32_t wt[2][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = L.R;
@@ -133,20 +136,30 @@ __device__ __forceinline__ void schedule(const int64_t* __restrict__ offsets, co
   int32_t* chunk_base = ws_i32(ws, L.off_chunk_base);
   int bad = 0;
   int32_t carry_t = 0, carry_c = 0;
-  for (int u0 = 0; u0 < R; u0 += 256) {
-    const int u = u0 + tid;
-    int32_t t = 0;
-    if (u < R) {
-      const int64_t n = offsets[u + 1] - offsets[u];
-      if (n < 0) bad = 1;
-      else t = (int32_t)((n + kTile * kUserTileAlign - 1) / (kTile * kUserTileAlign)) * kUserTileAlign;
-    }
-    const int32_t c = (t + CT - 1) / CT;
-    int32_t st = t, sc = c;   // inclusive scans over the wave
+  for (int u0 = 0; u0 < R; u0 += CHUNK) {
+    const int ub = u0 + UPT * tid;   // this thread's users ub .. ub + UPT - 1
+    int64_t o[UPT + 1];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int32_t xt = __shfl_up(st, o), xc = __shfl_up(sc, o);
-      if (lane >= o) {
+    for (int i = 0; i <= UPT; ++i) o[i] = ub + i <= R ? offsets[ub + i] : 0;
+    int32_t t[UPT], c[UPT];
+    int32_t st = 0, sc = 0;
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      t[i] = 0;
+      if (ub + i < R) {
+        const int64_t n = o[i + 1] - o[i];
+        if (n < 0) bad = 1;
+        else t[i] = (int32_t)((n + kTile * kUserTileAlign - 1) / (kTile * kUserTileAlign)) * kUserTileAlign;
+      }
+      c[i] = (t[i] + CT - 1) / CT;
+      st += t[i];
+      sc += c[i];
+    }
+    const int32_t own_t = st, own_c = sc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {   // inclusive scans over the wave
+      const int32_t xt = __shfl_up(st, off), xc = __shfl_up(sc, off);
+      if (lane >= off) {
         st += xt;
         sc += xc;
       }
@@ -156,7 +169,7 @@ __device__ __forceinline__ void schedule(const int64_t* __restrict__ offsets, co
       wt[1][wave] = sc;
     }
     __syncthreads();
-    int32_t bt = carry_t + st - t, bc = carry_c + sc - c;
+    int32_t bt = carry_t + st - own_t, bc = carry_c + sc - own_c;
     for (int w = 0; w < wave; ++w) {
       bt += wt[0][w];
       bc += wt[1][w];
@@ -164,9 +177,14 @@ __device__ __forceinline__ void schedule(const int64_t* __restrict__ offsets, co
     carry_t += wt[0][0] + wt[0][1] + wt[0][2] + wt[0][3];
     carry_c += wt[1][0] + wt[1][1] + wt[1][2] + wt[1][3];
     __syncthreads();   // every read of wt is done before the next users' totals
-    if (u < R) {
-      tile_base[u] = bt;
-      chunk_base[u] = bc;
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      if (ub + i < R) {
+        tile_base[ub + i] = bt;
+        chunk_base[ub + i] = bc;
+      }
+      bt += t[i];
+      bc += c[i];
     }
   }
   if (tid == 0 && (offsets[0] != 0 || offsets[R] != L.N)) bad = 1;

@@ -74,6 +74,20 @@ def test_parity_many_short_users(k, d):
     _check(inp, path="two")
 
 
+@pytest.mark.parametrize("R", [2047, 2048, 2049, 6000])
+def test_parity_thousands_of_users(R):
+    """The schedule takes users 2048 at a time (8 per thread, a running carry
+    between the passes): user counts on both sides of a pass boundary and
+    several passes, short ragged users (a fifth of them empty), every
+    sketch and mass compared with the oracle."""
+    from synth import make_inputs
+    rng = np.random.default_rng(2400 + R)
+    lens = rng.integers(0, 48, size=R)
+    lens[rng.random(R) < 0.2] = 0
+    inp = make_inputs(lens.tolist(), d=64, k=64, seed=3400 + R, name=f"users{R}")
+    _check(inp, path="two")
+
+
 def _sample(inp, n_random=2, seed=0):
     lens = inp.lengths
     pick = {int(np.argmin(lens)), int(np.argmax(lens))}
