@@ -76,8 +76,8 @@ TRAFFIC = {
     # 1.0552e9 fetched + 0.0565e9 written (same workload)
     "pass2_accum": (1111685530, "4dee340760e4da8b2560b07fe6caa9f344ee5d14f6ef998196360ccf4d180372",
                     ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
-    # 1.3084e9 fetched + 2.0680e9 written (same workload, --backward)
-    "bwd_dh": (3376437248, "e6bde02432203cccb6948771d30a1bfdd87afbcc79a40b7cef0c706b9e6b4316",
+    # 1.3085e9 fetched + 2.0680e9 written (same workload, --backward)
+    "bwd_dh": (3376518208, "257c1bb93248425554e5f103ba9aef2c7aaf80e3e02a5791ce633ddd40fa2c91",
                ("sa_bwd.hip", "sa_layout.h", "sa_device.h")),
     # 1.8668e8 fetched + 0.4608e8 written (300 users x 300 candidates, --target-attention)
     "ta_attend": (232757862, "7df8952f9bb791989e794cd57a7512979ee00b2cbab3284f360ae66dc62f52d3",

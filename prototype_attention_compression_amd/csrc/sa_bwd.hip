@@ -62,6 +62,8 @@ constexpr float kScaleMax = 16384.0f;             // 2^14
 constexpr int kSlotBatch = 4;                     // partial slots whose loads are in flight together
 constexpr int kERows = 8;                         // prototypes per E-reduction workgroup
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16f(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
 
@@ -236,7 +238,6 @@ __global__ __launch_bounds__(256) void bwd_user(const uint16_t* __restrict__ Wv,
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_zpack(Layout L, void* ws) {
-  constexpr int PER = kRows * D / 256;
   __shared__ float red[256];
   const int nrb = L.k / kRows;
   const int u = blockIdx.x / nrb, rb = blockIdx.x % nrb;
@@ -252,24 +253,36 @@ __global__ __launch_bounds__(256) void bwd_zpack(Layout L, void* ws) {
   }
   const float zs = pow2_scale(red[0], 14);
   const int64_t row0 = (int64_t)u * L.k + rb * kRows;
-  const float* z32 = ws_f32(ws, L.off_bz32) + row0 * D;
-  const float* sbar = ws_f32(ws, L.off_bsbar) + row0 * D;
-  _Float16* z16 = ws_f16(ws, L.off_bz16) + row0 * D;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) z16[tid + 256 * i] = (_Float16)(z32[tid + 256 * i] * zs);
-  // c_j zs = Zs_j . Sbar_j from the rounded fp16 row itself, so that
+  // 8 threads per row, each with 16-byte pieces part + 8 m of it: Z zs in
+  // fp16, and c_j zs = Zs_j . Sbar_j from that rounded row itself, so that
   // Y - c zs = Zs_j . (h_t - Sbar_j) keeps its accuracy where h_t is close to
   // Sbar_j (a user of one token: exactly zero), rather than the fp16 rounding
-  // of Zs_j . h_t (8 threads per row)
-  {
-    const int j = tid >> 3, part = tid & 7;
-    float s = 0.f;
-    for (int e = part; e < D; e += 8) s = fmaf((float)(_Float16)(z32[j * D + e] * zs), sbar[j * D + e], s);
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
-    if (part == 0) ws_f32(ws, L.off_bcz)[row0 + j] = s;
+  // of Zs_j . h_t
+  const int j = tid >> 3, part = tid & 7;
+  const f32x4* zr = reinterpret_cast<const f32x4*>(ws_f32(ws, L.off_bz32) + (row0 + j) * D);
+  const f32x4* sr = reinterpret_cast<const f32x4*>(ws_f32(ws, L.off_bsbar) + (row0 + j) * D);
+  half4v* zo = reinterpret_cast<half4v*>(ws_f16(ws, L.off_bz16) + (row0 + j) * D);
+  f32x4 zv[D / 32], sv[D / 32];
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) {
+    zv[m] = zr[part + 8 * m];
+    sv[m] = sr[part + 8 * m];
   }
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) {
+    half4v h;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      h[c] = (_Float16)(zv[m][c] * zs);
+      s = fmaf((float)h[c], sv[m][c], s);
+    }
+    zo[part + 8 * m] = h;
+  }
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);
+  if (part == 0) ws_f32(ws, L.off_bcz)[row0 + j] = s;
   if (rb == 0 && tid == 0) {
     ws_f32(ws, L.off_bzs)[u] = zs;
     ws_i32(ws, L.off_bbmax)[u] = 0;
