@@ -107,7 +107,8 @@ Layout make_layout(const sa_problem& p, bool bwd = false) {
     L.off_q16 = take((size_t)p.k * p.d * 2);
     L.off_qpart = take((size_t)(p.k / 32) * sizeof(float));
     L.off_h16 = take((size_t)tiles_max * kTile * p.d * 2);
-    L.off_nl = take((size_t)tiles_max * kTile * sizeof(uint32_t));
+    // + 16 bytes: the pairs past the last tile that pass 2's -l pieces read
+    L.off_nl = take((size_t)tiles_max * kTile * sizeof(uint32_t) + 16);
     if (L.groups > 0) L.off_xbuf = take((size_t)L.groups * kXSlots * kTile * (p.k / kFusedProtos) * sizeof(uint64_t));
   } else {
     L.off_q32 = take((size_t)p.k * p.d * sizeof(float));

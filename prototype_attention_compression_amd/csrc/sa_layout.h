@@ -72,7 +72,7 @@ struct Layout {
   size_t off_q16;          // [k, d] fp16    queries
   size_t off_qpart;        // [k / 32] float largest |q_j| of each 32-row block of the fp16 queries
   size_t off_h16;          // [tiles_max, 32, d] fp16    token rows
-  size_t off_nl;           // [tiles_max, 32] uint32 per token.  Two-pass: fp16 pairs
+  size_t off_nl;           // [tiles_max, 32] uint32 per token (+ 4 words).  Two-pass: fp16 pairs
                            //   (-l_hi, -l_lo), l = lse_t - 14, (-60000, 0) if dropped.
                            //   One-pass: 1 if the token takes part, else 0.
   size_t off_xbuf;         // [groups, kXSlots, 32, n_pblocks] uint64 exchange words

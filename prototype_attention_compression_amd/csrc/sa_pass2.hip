@@ -29,7 +29,8 @@
 //
 // Data movement: token rows reach LDS with direct global->LDS loads (16 B per
 // lane), 4 tiles (128 tokens) per stage, four stage buffers, loads two stages
-// ahead.  A row occupies 2d + 16 bytes (the last 16 are never read and never
+// ahead; the -l pairs arrive as a 16-byte piece per token (its pair first), so
+// the feature step's operand is one LDS read.  A row occupies 2d + 16 bytes (the last 16 are never read and never
 // loaded); GEMM1's operand row m holds token tau(m), which puts the 4 tokens
 // of one transposing read 4 rows apart.  Then the 16-byte GEMM1 reads and the
 // transposing 8-byte reads both touch 64 distinct banks per pass (gfx950
@@ -79,8 +80,10 @@ struct P2 {
   static constexpr int PITCH = tile_pitch<D>();      // LDS bytes per token row
   static_assert(PITCH == SLOTS * 16, "padded row");
   static constexpr int TILE_BYTES = kTile * PITCH;   // one tile of token rows
-  static constexpr int NL_OFF = kStageTiles * TILE_BYTES;   // (-l_hi, -l_lo) pairs of the stage
-  static constexpr int STAGE_BYTES = NL_OFF + kStageTiles * kTile * 4;
+  // a 16-byte piece per token of the stage: its (-l_hi, -l_lo) pair, then the
+  // next three tokens' pairs (multiplied by zeros in the feature step)
+  static constexpr int NL_OFF = kStageTiles * TILE_BYTES;
+  static constexpr int STAGE_BYTES = NL_OFF + kStageTiles * kTile * 16;
   static constexpr int LOADS = kStageTiles * kTile * SLOTS / 64;   // 1-KB direct loads per stage
   static_assert(LOADS * 64 == kStageTiles * kTile * SLOTS, "whole loads per stage");
   static_assert(STAGE_BYTES % 256 == 0, "load alignment");
@@ -136,8 +139,11 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
 #pragma unroll
     for (int s = 0; s < C::S; ++s)
       qf[b][s] = *reinterpret_cast<const half8*>(q16 + (int64_t)(p0 + 32 * b + col) * D + 16 * s + 8 * g);
-  const half8 qfeat = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)0.0f, (_Float16)0.0f,
-                       (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
+  // (1, 1) at the pair's K positions of the lower lane half, zeros elsewhere
+  // (the upper half's K positions meet the same piece again)
+  const _Float16 one = g == 0 ? (_Float16)1.0f : (_Float16)0.0f;
+  const half8 qfeat = {one, one, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f,
+                       (_Float16)0.0f};
 
   const char* h16 = reinterpret_cast<const char*>(ws_f16(ws, L.off_h16));
   const char* nlg = reinterpret_cast<const char*>(ws_i32(ws, L.off_nl));
@@ -151,8 +157,11 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   // stage).  A lane's source offsets inside the stage's tiles are the same
   // for every stage, so they are computed once (~0 marks a padding slot).
   constexpr int KMAX = (C::LOADS + WAVES - 1) / WAVES;
-  constexpr int LMAX = KMAX + 1;
-  constexpr int LMIN = C::LOADS / WAVES + 1;
+  // -l pieces: 4-byte direct loads of 16 tokens' pieces each, NLL per wave
+  constexpr int NLL = kStageTiles * kTile * 4 / 64 / WAVES;
+  static_assert(NLL * 64 * WAVES == kStageTiles * kTile * 4, "whole -l loads");
+  constexpr int LMAX = KMAX + NLL;
+  constexpr int LMIN = C::LOADS / WAVES + NLL;
   const bool big = (C::LOADS % WAVES == 0) || (wave < C::LOADS % WAVES);
   uint32_t src_off[KMAX];
 #pragma unroll
@@ -176,11 +185,15 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
         __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(base + 1024 * i), 16, 0, 0);
       }
     }
-    constexpr int NL_LANES = kStageTiles * kTile * 4 / 16 / WAVES;   // 16-B pieces per wave
-    static_assert(NL_LANES * 16 * WAVES == kStageTiles * kTile * 4, "whole -l slices");
-    if (lane < NL_LANES) {
-      const char* src = nlg + tile0 * (kTile * 4) + (wave * NL_LANES + lane) * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(base + C::NL_OFF + wave * NL_LANES * 16), 16, 0, 0);
+    // the -l pieces: 4-byte direct loads; lane l of load i fills word l % 4
+    // of token 16 i' + l / 4's piece (i' = NLL wave + i) with the pair of
+    // token 16 i' + l / 4 + l % 4 (past the batch's last tile the pairs are
+    // zeros the preparation wrote)
+#pragma unroll
+    for (int i = 0; i < NLL; ++i) {
+      const int tk = 16 * (NLL * wave + i);
+      const char* src = nlg + (tile0 * kTile + tk + (lane >> 2) + (lane & 3)) * 4;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(base + C::NL_OFF + tk * 16), 4, 0, 0);
     }
   };
   // wait until only this wave's loads of the `later` stages after the
@@ -249,19 +262,18 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
     }
   };
   // GEMM1 operands of tile t: row of token tau(col), chunk 2 s + g; -l pair
-  auto read_a = [&](int t, half8 (&ha)[C::S], uint32_t& nlp) {
+  auto read_a = [&](int t, half8 (&ha)[C::S], half8& nlp) {
     const char* base = tile_lds(t);
     const char* rows = base + (t % kStageTiles) * C::TILE_BYTES + ha_base;
 #pragma unroll
     for (int s = 0; s < C::S; ++s) ha[s] = *reinterpret_cast<const half8*>(rows + 32 * s);
-    nlp = reinterpret_cast<const uint32_t*>(base + C::NL_OFF)[(t % kStageTiles) * kTile + tcol];
+    nlp = *reinterpret_cast<const half8*>(base + C::NL_OFF + ((t % kStageTiles) * kTile + tcol) * 16);
   };
   // GEMM1: C[tok, proto] = h_tok . q_proto - l_tok (the feature step adds
   // -l), split after its first K step
-  auto gemm1_head = [&](const half8 (&ha)[C::S], uint32_t nlp, float16v (&Cm)[NB]) {
-    const u32x4 fv = {g == 0 ? nlp : 0u, 0u, 0u, 0u};
+  auto gemm1_head = [&](const half8 (&ha)[C::S], const half8& nlp, float16v (&Cm)[NB]) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) Cm[b] = mfma32x32x16(__builtin_bit_cast(half8, fv), qfeat, float16v{});
+    for (int b = 0; b < NB; ++b) Cm[b] = mfma32x32x16(nlp, qfeat, float16v{});
 #pragma unroll
     for (int b = 0; b < NB; ++b) Cm[b] = mfma32x32x16(ha[0], qf[b][0], Cm[b]);
   };
@@ -303,7 +315,7 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   float16v C0[NB], C1[NB];
   half8 ap0[NB][2], ap1[NB][2];
   half8 ha[C::S], hb[2][C::DT];
-  uint32_t nlp;
+  half8 nlp;
   // Period t runs GEMM2 of tile t-2 interleaved with the exponentials of
   // tile t-1, then GEMM1 of tile t+1, so every MFMA result is consumed a
   // whole period after its chain was issued (issue is in order per wave,

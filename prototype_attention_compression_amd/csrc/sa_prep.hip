@@ -199,6 +199,15 @@ __device__ __forceinline__ void schedule(const int64_t* __restrict__ offsets, co
   }
   if (tid == 0) {
     int32_t* hdr = ws_i32(ws, L.off_hdr);
+    if (L.dtype == 0) {
+      // zero pairs after the last tile: pass 2 reads each token's -l pair
+      // together with the next three tokens' (multiplied by zeros there)
+      uint32_t* nl = reinterpret_cast<uint32_t*>(ws_i32(ws, L.off_nl)) + (int64_t)carry_t * kTile;
+      nl[0] = 0u;
+      nl[1] = 0u;
+      nl[2] = 0u;
+      nl[3] = 0u;
+    }
     tile_base[R] = carry_t;
     chunk_base[R] = carry_c;
     hdr[kHdrErr] = bad ? kErrBadOffsets : 0;

@@ -60,7 +60,7 @@ def layout(R, N, d, k, bwd):
     take("q16", k * d * 2, 2)
     take("qpart", (k // 32) * 4, 4)
     take("h16", L["tiles_max"] * TILE * d * 2, 2)
-    take("nl", L["tiles_max"] * TILE * 4, 4)
+    take("nl", L["tiles_max"] * TILE * 4 + 16, 4)
     if L["groups"]:
         take("xbuf", L["groups"] * XSLOTS * TILE * (k // FUSED_PROTOS) * 8, 8)
     take("part_u", parts * k * d * 4, 4)
@@ -190,6 +190,11 @@ def replay(lengths, d, k, backward=True):
     for g, uu, t0, te in segs:
         check((te - t0) % 4 == 0, "segments hold whole 4-tile stages")
         check(te <= T, "stage reads inside the tiles")
+        # -l pieces: token i's pair and the next three, 4 bytes each; past the
+        # last tile only the 4 zeroed words that follow the pairs
+        last = (te * TILE - 1) + 3
+        check(last <= T * TILE + 3, "-l piece reads end at most 4 words past the last tile")
+        check(last < S["nl"], "-l piece reads inside the workspace")
         check(g + uu < L["parts_max"], "pass-2 slot inside part_u")
     covered = sum(te - t0 for _, _, t0, te in segs)
     check(covered == T, "the segments cover every tile once")
