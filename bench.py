@@ -71,16 +71,16 @@ DEFAULT_WORKLOAD = "c3lit_r40_n100k_d128_k1024"
 COPY_CALIBRATION_BYTES = 1 << 30
 TRAFFIC = {
     # 1.0265e9 fetched + 1.0410e9 written (40 x 100K tokens, k = 1024, d = 128)
-    "pass1_qres": (2067465011, "0b14292b442f37dd1325e30f44f719d99ac7efeb8fc0bb7187ad6d5196db771d",
+    "pass1_qres": (2067464875, "7f3a056a8f79862006574bdc917b5c9f9468a8a087ada0a29272b7a007a9316c",
                    ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
-    # 1.0552e9 fetched + 0.0565e9 written (same workload)
-    "pass2_accum": (1111685530, "4dee340760e4da8b2560b07fe6caa9f344ee5d14f6ef998196360ccf4d180372",
+    # 1.0532e9 fetched + 0.0576e9 written (same workload)
+    "pass2_accum": (1110797717, "6b8eabc687e2868029d44ae5b8e15eedb4648ad46cbbec6d000d86e99231703b",
                     ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
-    # 1.3085e9 fetched + 2.0680e9 written (same workload, --backward)
-    "bwd_dh": (3376518208, "257c1bb93248425554e5f103ba9aef2c7aaf80e3e02a5791ce633ddd40fa2c91",
+    # 1.3054e9 fetched + 2.0680e9 written (same workload, --backward)
+    "bwd_dh": (3373457792, "bfe35bc42bbde3f58ae5717d78516043a2e8228ab748fe1c2c14a0c0557c92a3",
                ("sa_bwd.hip", "sa_layout.h", "sa_device.h")),
-    # 1.8668e8 fetched + 0.4608e8 written (300 users x 300 candidates, --target-attention)
-    "ta_attend": (232757862, "7df8952f9bb791989e794cd57a7512979ee00b2cbab3284f360ae66dc62f52d3",
+    # 1.8658e8 fetched + 0.4608e8 written (300 users x 300 candidates, --target-attention)
+    "ta_attend": (232664576, "0548404c496254a1c5d76c624f28efa6c6f2ab732b4f0bcb7099f0c11a681c03",
                   ("sa_target.hip", "sa_layout.h", "sa_device.h")),
 }
 
@@ -90,11 +90,11 @@ TRAFFIC = {
 # kernel's time), from rocprofv3 --pmc on the default workload; valid, like the
 # traffic figures, only for the kernel sources they were taken on (null after).
 COUNTERS = {
-    "pass1_qres": ({"mfma_busy": 0.549, "clock_mhz": 1734.0},
-                   "0b14292b442f37dd1325e30f44f719d99ac7efeb8fc0bb7187ad6d5196db771d",
+    "pass1_qres": ({"mfma_busy": 0.551, "clock_mhz": 1701.0},
+                   "7f3a056a8f79862006574bdc917b5c9f9468a8a087ada0a29272b7a007a9316c",
                    ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
-    "pass2_accum": ({"mfma_busy": 0.611, "clock_mhz": 1791.0},
-                    "4dee340760e4da8b2560b07fe6caa9f344ee5d14f6ef998196360ccf4d180372",
+    "pass2_accum": ({"mfma_busy": 0.641, "clock_mhz": 1718.0},
+                    "6b8eabc687e2868029d44ae5b8e15eedb4648ad46cbbec6d000d86e99231703b",
                     ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
 }
 
