@@ -49,10 +49,15 @@ struct Q1 {
   static constexpr int CHUNKS = kTile * CPR;       // 16-B chunks per tile (<= 512)
 };
 
+// log2 of x >= 2^-126 (no denormal inputs): the hardware instruction alone.
+// Every logarithm here is of a sum that holds a term of at least 2^-100 (the
+// fast form: every logit above -100) or of exactly 1 (the max-shifted form).
+__device__ __forceinline__ float log2_normal(float x) { return __builtin_amdgcn_logf(x); }
+
 __device__ __forceinline__ float log_add_exp2(float a, float b) {
   const float m = fmaxf(a, b);
   if (m == -INFINITY) return -INFINITY;
-  return m + log2f(__builtin_amdgcn_exp2f(a - m) + __builtin_amdgcn_exp2f(b - m));
+  return m + log2_normal(__builtin_amdgcn_exp2f(a - m) + __builtin_amdgcn_exp2f(b - m));
 }
 
 // Issue priority of the calling wave (0..3; the instruction takes a
@@ -87,7 +92,9 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   __shared__ __attribute__((aligned(1024))) char rows[kBufs][C::TILE_BYTES];
   static_assert(W % 4 == 0 && kTile % W == 0, "wave count");
   __shared__ float part[2][kTile][W];
-  __shared__ __attribute__((aligned(16))) uint32_t exact_bits[kBufs][W];
+  // one byte per wave: "a logit of this wave's chunks may reach 100"
+  static_assert(W == 4 || W == 8, "exact bytes read as one word");
+  __shared__ __attribute__((aligned(8))) uint8_t exact_bytes[kBufs][W];
   __shared__ uint32_t keep_words[kBufs][kTile];
   // A word per lane for the stores of lanes whose value another lane
   // already stores: the store address is a select, not a branch, and no two
@@ -209,18 +216,13 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
     range_sus |= __ballot(!(n2 <= kF16MaxSq));
     const bool big = conv && keep && n2 * (float)C::CPR >= lim2;
     const uint32_t eb = __ballot(big) != 0ull ? 1u : 0u;   // uniform over the wave
-    *(lane == 0 ? &exact_bits[b][wave] : &spare[tid]) = eb;
+    *(lane == 0 ? &exact_bytes[b][wave] : reinterpret_cast<uint8_t*>(&spare[tid])) = (uint8_t)eb;
   };
 
   // whether some wave flagged tile buffer b for the exact form
   auto tile_exact = [&](int b) {
-    uint32_t any = 0u;
-#pragma unroll
-    for (int w = 0; w < W; w += 4) {
-      const u32x4 e = *reinterpret_cast<const u32x4*>(&exact_bits[b][w]);
-      any |= e[0] | e[1] | e[2] | e[3];
-    }
-    return any != 0u;
+    if constexpr (W == 8) return *reinterpret_cast<const uint64_t*>(&exact_bytes[b][0]) != 0ull;
+    else return *reinterpret_cast<const uint32_t*>(&exact_bytes[b][0]) != 0u;
   };
 
   // partial of tile j (buffer b) into LDS slot j % 2
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
     float m = -INFINITY, p = 0.f;
 #pragma unroll
     for (int bl = 0; bl < NBW; ++bl) exact_block(a[bl], m, p);
-    const HalfPair hp = lane_halves(m + log2f(p));
+    const HalfPair hp = lane_halves(m + log2_normal(p));
     return log_add_exp2(hp.lo, hp.hi);
   };
 
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
           if (bl == 0) mid();
           exact_block(a, m, p);
         }
-        const HalfPair hp = lane_halves(m + log2f(p));
+        const HalfPair hp = lane_halves(m + log2_normal(p));
         wpart = log_add_exp2(hp.lo, hp.hi);
       }
     }
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < W; ++w) s += pp[w];
-      lse = log2f(s);
+      lse = log2_normal(s);
     } else {
       lse = -INFINITY;
 #pragma unroll
