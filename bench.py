@@ -71,7 +71,7 @@ DEFAULT_WORKLOAD = "c3lit_r40_n100k_d128_k1024"
 COPY_CALIBRATION_BYTES = 1 << 30
 TRAFFIC = {
     # 1.0265e9 fetched + 1.0410e9 written (40 x 100K tokens, k = 1024, d = 128)
-    "pass1_qres": (2067464875, "7f3a056a8f79862006574bdc917b5c9f9468a8a087ada0a29272b7a007a9316c",
+    "pass1_qres": (2067430955, "e8a1c4ab0f8ef702be4191b997d2b7c62de7c0aa65aa4003a7411f96f7188932",
                    ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
     # 1.0532e9 fetched + 0.0576e9 written (same workload)
     "pass2_accum": (1110797717, "6b8eabc687e2868029d44ae5b8e15eedb4648ad46cbbec6d000d86e99231703b",
@@ -90,8 +90,8 @@ TRAFFIC = {
 # kernel's time), from rocprofv3 --pmc on the default workload; valid, like the
 # traffic figures, only for the kernel sources they were taken on (null after).
 COUNTERS = {
-    "pass1_qres": ({"mfma_busy": 0.551, "clock_mhz": 1701.0},
-                   "7f3a056a8f79862006574bdc917b5c9f9468a8a087ada0a29272b7a007a9316c",
+    "pass1_qres": ({"mfma_busy": 0.567, "clock_mhz": 1709.0},
+                   "e8a1c4ab0f8ef702be4191b997d2b7c62de7c0aa65aa4003a7411f96f7188932",
                    ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
     "pass2_accum": ({"mfma_busy": 0.641, "clock_mhz": 1718.0},
                     "6b8eabc687e2868029d44ae5b8e15eedb4648ad46cbbec6d000d86e99231703b",
