@@ -336,8 +336,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
   half8 hB[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) hB[s] = *reinterpret_cast<const half8*>(hrow + 16 * s + 8 * g);
-  const float negl = negl_of(reinterpret_cast<const uint32_t*>(ws_i32(ws, L.off_nl))[(int64_t)tile * kTile + col]);
-  const bool keep = negl > -30000.f;
+  const uint32_t nlw = reinterpret_cast<const uint32_t*>(ws_i32(ws, L.off_nl))[(int64_t)tile * kTile + col];
+  const bool keep = negl_of(nlw) > -30000.f;
+  // Feature step of the logits: the token supplies (-l_hi, -l_lo, -14) (the
+  // lower lane half's K positions), the prototype (1, 1, 1), so the logit
+  // accumulators start at -lse_t and the allocations are 2^accumulator
+  const half2v nlp = __builtin_bit_cast(half2v, nlw);
+  const _Float16 z0 = (_Float16)0.0f;
+  const half8 hfeat = g == 0 ? half8{nlp[0], nlp[1], (_Float16)(-kAllocShift), z0, z0, z0, z0, z0}
+                             : half8{z0, z0, z0, z0, z0, z0, z0, z0};
+  const half8 qones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, z0, z0, z0, z0, z0};
 
   const int NB = L.k / kTile;
   // Staging of the 2 NB block steps (block i % NB of sweep i / NB): two
@@ -395,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
 
   // C = q . h and Y = Zs . h of the staged block (A operands read in halves)
   auto gemms = [&](const char* qb, float16v& Lc, float16v& Yc) {
-    Lc = float16v{};
+    Lc = mfma32x32x16(qones, hfeat, float16v{});
     Yc = float16v{};
 #pragma unroll
     for (int s0 = 0; s0 < S; s0 += 4) {
@@ -426,7 +434,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
       const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float A = __builtin_amdgcn_exp2f(Lc[4 * v + e] + negl);
+        const float A = __builtin_amdgcn_exp2f(Lc[4 * v + e]);
         const float yc = Yc[4 * v + e] - cv[e];
         dsum = fmaf(A, yc, dsum);
         bmx = fmaxf(bmx, fabsf(yc));
@@ -471,7 +479,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * v + e;
-        const float A = __builtin_amdgcn_exp2f(Lc[r] + negl);
+        const float A = __builtin_amdgcn_exp2f(Lc[r]);
         const float dl = A * (Yc[r] - cv[e] - delta);
         al[r >> 3][r & 7] = (_Float16)(dl * sl);
         ad[r >> 3][r & 7] = (_Float16)(A * sg);
@@ -524,7 +532,10 @@ __global__ __launch_bounds__(W * 64, W == 8 ? 1 : 2) void bwd_e(const int32_t* _
   constexpr int NT = W * 64;
   constexpr int LPT = kTile * CPR / NT;
   static_assert(LPT * NT == kTile * CPR, "whole loads");
-  constexpr int STAGE = TB + 2 * kTile * 4;
+  // the tile's rows, then per token the logits' feature piece
+  // {-l_hi, -l_lo, -14, 0 ...} (16 bytes), then delta_t zs (floats)
+  constexpr int FEAT = TB, DLT = TB + kTile * 16;
+  constexpr int STAGE = DLT + kTile * 4;
   __shared__ __attribute__((aligned(16))) char lds[2][STAGE];
   const int P = L.e_pblocks, G = L.e_groups;
   const int x = blockIdx.x, xcd = x & 7, slotw = x >> 3;
@@ -570,14 +581,20 @@ __global__ __launch_bounds__(W * 64, W == 8 ? 1 : 2) void bwd_e(const int32_t* _
       *reinterpret_cast<u32x4*>(base + row * PITCH + 16 * ch) = pr[k2];
     }
     if (tid < kTile) {
-      float* pv = reinterpret_cast<float*>(base + TB);
-      pv[acc_pos(tid)] = negl_of(pn);
-      pv[kTile + acc_pos(tid)] = pd;
+      // -14 in fp16 is 0xCB00
+      reinterpret_cast<u32x4*>(base + FEAT)[tid] = u32x4{pn, 0x0000CB00u, 0u, 0u};
+      reinterpret_cast<float*>(base + DLT)[acc_pos(tid)] = pd;
     }
   };
   const int abase = tau(col) * PITCH + 16 * g;
   const int i16 = lane & 15, gh = (lane >> 4) & 1;
   const int tr_base = (4 * (i16 >> 2) + 2 * g) * PITCH + 32 * gh + 8 * (i16 & 3);
+  // feature step of the logits: the token's piece (A operand, lane's token
+  // tau(col)) against (1, 1, 1) at the lower lane half's K positions, so the
+  // logit accumulators start at -lse_t (the upper half meets zeros)
+  const int fbase = FEAT + tau(col) * 16;
+  const _Float16 f1 = g == 0 ? (_Float16)1.0f : (_Float16)0.0f, f0 = (_Float16)0.0f;
+  const half8 qones = {f1, f1, f1, f0, f0, f0, f0, f0};
 
   int u = find_user(tile_base, L.R, s0);
   int32_t ub = tile_base[u + 1];
@@ -618,7 +635,8 @@ __global__ __launch_bounds__(W * 64, W == 8 ? 1 : 2) void bwd_e(const int32_t* _
       load_user();
     }
     const char* hb_ = lds[buf];
-    float16v Lc = float16v{}, Yc = float16v{};
+    float16v Lc = mfma32x32x16(*reinterpret_cast<const half8*>(hb_ + fbase), qones, float16v{});
+    float16v Yc = float16v{};
 #pragma unroll
     for (int s0h = 0; s0h < S; s0h += 4) {
       half8 ha[4];
@@ -630,17 +648,16 @@ __global__ __launch_bounds__(W * 64, W == 8 ? 1 : 2) void bwd_e(const int32_t* _
         Yc = mfma32x32x16(ha[s], zf[s0h + s], Yc);
       }
     }
-    const float4* pv = reinterpret_cast<const float4*>(hb_ + TB);
+    const float4* pv = reinterpret_cast<const float4*>(hb_ + DLT);
     half8 al[2];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float4 a4 = pv[4 * g + v], d4 = pv[8 + 4 * g + v];
-      const float nl[4] = {a4.x, a4.y, a4.z, a4.w};
+      const float4 d4 = pv[4 * g + v];
       const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * v + e;
-        const float A = __builtin_amdgcn_exp2f(Lc[r] + nl[e]);
+        const float A = __builtin_amdgcn_exp2f(Lc[r]);
         al[r >> 3][r & 7] = (_Float16)(A * (Yc[r] - cz - dd[e]) * su);
       }
     }
