@@ -76,8 +76,8 @@ TRAFFIC = {
     # 1.0532e9 fetched + 0.0576e9 written (same workload)
     "pass2_accum": (1110797717, "6b8eabc687e2868029d44ae5b8e15eedb4648ad46cbbec6d000d86e99231703b",
                     ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
-    # 1.3054e9 fetched + 2.0680e9 written (same workload, --backward)
-    "bwd_dh": (3373457792, "bfe35bc42bbde3f58ae5717d78516043a2e8228ab748fe1c2c14a0c0557c92a3",
+    # 1.3217e9 fetched + 2.0680e9 written (same workload, --backward)
+    "bwd_dh": (3389674568, "8aad78851833ae8185cc217cc9c5c510c3d5f5a5eebcdd45f2d2691648b29101",
                ("sa_bwd.hip", "sa_layout.h", "sa_device.h")),
     # 1.8658e8 fetched + 0.4608e8 written (300 users x 300 candidates, --target-attention)
     "ta_attend": (232664576, "0548404c496254a1c5d76c624f28efa6c6f2ab732b4f0bcb7099f0c11a681c03",
