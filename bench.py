@@ -70,17 +70,17 @@ DEFAULT_WORKLOAD = "c3lit_r40_n100k_d128_k1024"
 # the figure is reported as null once they differ.
 COPY_CALIBRATION_BYTES = 1 << 30
 TRAFFIC = {
-    # 1.0265e9 fetched + 1.0410e9 written (40 x 100K tokens, k = 1024, d = 128)
-    "pass1_qres": (2067430955, "e8a1c4ab0f8ef702be4191b997d2b7c62de7c0aa65aa4003a7411f96f7188932",
+    # 1.0263e9 fetched + 1.0410e9 written (40 x 100K tokens, k = 1024, d = 128)
+    "pass1_qres": (2067275674, "00b0cc45171c4ef4fc91998b4c712d03b0b83ec6753a2979ddb123ce213c3346",
                    ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
-    # 1.0532e9 fetched + 0.0576e9 written (same workload)
-    "pass2_accum": (1110797717, "6b8eabc687e2868029d44ae5b8e15eedb4648ad46cbbec6d000d86e99231703b",
+    # 1.0536e9 fetched + 0.0576e9 written (same workload)
+    "pass2_accum": (1111137089, "a32b5f381fe45e84b75521f015712631b65c414d1ef1eca63a684dda45eab8ff",
                     ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
-    # 1.3217e9 fetched + 2.0680e9 written (same workload, --backward)
-    "bwd_dh": (3389674568, "8aad78851833ae8185cc217cc9c5c510c3d5f5a5eebcdd45f2d2691648b29101",
+    # 1.3106e9 fetched + 2.0680e9 written (same workload, --backward)
+    "bwd_dh": (3378584226, "c9c3a06f4c752851e62eea7d41f59db5388e1b6d1d7f2f4c739bc8796604d04d",
                ("sa_bwd.hip", "sa_layout.h", "sa_device.h")),
     # 1.8658e8 fetched + 0.4608e8 written (300 users x 300 candidates, --target-attention)
-    "ta_attend": (232664576, "0548404c496254a1c5d76c624f28efa6c6f2ab732b4f0bcb7099f0c11a681c03",
+    "ta_attend": (232547216, "7fe0b40aabfc73acab82beed9163ae42dd37fdd3dc7c16f5d114279d1cae1736",
                   ("sa_target.hip", "sa_layout.h", "sa_device.h")),
 }
 
@@ -90,11 +90,11 @@ TRAFFIC = {
 # kernel's time), from rocprofv3 --pmc on the default workload; valid, like the
 # traffic figures, only for the kernel sources they were taken on (null after).
 COUNTERS = {
-    "pass1_qres": ({"mfma_busy": 0.567, "clock_mhz": 1709.0},
-                   "e8a1c4ab0f8ef702be4191b997d2b7c62de7c0aa65aa4003a7411f96f7188932",
+    "pass1_qres": ({"mfma_busy": 0.572, "clock_mhz": 1810.0},
+                   "00b0cc45171c4ef4fc91998b4c712d03b0b83ec6753a2979ddb123ce213c3346",
                    ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
-    "pass2_accum": ({"mfma_busy": 0.641, "clock_mhz": 1718.0},
-                    "6b8eabc687e2868029d44ae5b8e15eedb4648ad46cbbec6d000d86e99231703b",
+    "pass2_accum": ({"mfma_busy": 0.635, "clock_mhz": 1807.0},
+                    "a32b5f381fe45e84b75521f015712631b65c414d1ef1eca63a684dda45eab8ff",
                     ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
 }
 

@@ -106,6 +106,7 @@ Layout make_layout(const sa_problem& p, bool bwd = false) {
   if (!f32) {
     L.off_q16 = take((size_t)p.k * p.d * 2);
     L.off_qpart = take((size_t)(p.k / 32) * sizeof(float));
+    L.off_zrow = take(256);
     L.off_h16 = take((size_t)tiles_max * kTile * p.d * 2);
     // + 16 bytes: the pairs past the last tile that pass 2's -l pieces read
     L.off_nl = take((size_t)tiles_max * kTile * sizeof(uint32_t) + 16);

@@ -71,6 +71,7 @@ struct Layout {
   size_t off_chunk_base;   // [R+1] int32
   size_t off_q16;          // [k, d] fp16    queries
   size_t off_qpart;        // [k / 32] float largest |q_j| of each 32-row block of the fp16 queries
+  size_t off_zrow;         // [128] uint16 zeros: the row pass 1 loads for a tile slot without a token
   size_t off_h16;          // [tiles_max, 32, d] fp16    token rows
   size_t off_nl;           // [tiles_max, 32] uint32 per token (+ 4 words).  Two-pass: fp16 pairs
                            //   (-l_hi, -l_lo), l = lse_t - 14, (-60000, 0) if dropped.

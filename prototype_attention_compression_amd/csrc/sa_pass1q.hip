@@ -15,7 +15,8 @@
 //     chunk loaded two tiles earlier is widened to fp16 (exact for
 //     magnitudes in [2^-17, 65504]; a kept value beyond that range raises
 //     a device error bit), written to LDS and to the fp16 row buffer pass 2
-//     reads; masked tokens and padding rows are zero.  The row
+//     reads; masked tokens and padding rows are zero (a padding slot loads
+//     the workspace's zero row, a masked token's chunk is cleared).  The row
 //     norms decide, per tile, whether any logit can reach |L| >= 100
 //     (Cauchy-Schwarz with the largest query norm): then the tile takes the
 //     exact form (running maximum, rescaled sums), else plain sums of 2^L;
@@ -95,7 +96,9 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   // one byte per wave: "a logit of this wave's chunks may reach 100"
   static_assert(W == 4 || W == 8, "exact bytes read as one word");
   __shared__ __attribute__((aligned(8))) uint8_t exact_bytes[kBufs][W];
-  __shared__ uint32_t keep_words[kBufs][kTile];
+  // masked batches: whether each token of the tile is kept (unmasked ones
+  // use the tile's token count, a scalar)
+  __shared__ uint32_t keep_words[MASKED ? kBufs : 1][kTile];
   // A word per lane for the stores of lanes whose value another lane
   // already stores: the store address is a select, not a branch, and no two
   // lanes of a store share an address (same-address LDS stores serialise).
@@ -110,6 +113,7 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   const int n = tb - ta;
   const float qmax = query_norm_max(L, ws);
   const float lim2 = 10000.0f / fmaxf(qmax * qmax, 1e-30f);   // |h|^2 >= lim2  <=>  qmax |h| >= 100
+  const float lim2c = lim2 / (float)C::CPR;   // the same against a chunk's squared norm (CPR: power of two)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches on it
@@ -126,6 +130,7 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
 
   _Float16* h16 = ws_f16(ws, L.off_h16);
   uint32_t* nl = reinterpret_cast<uint32_t*>(ws_i32(ws, L.off_nl));
+  const uint16_t* zrow = reinterpret_cast<const uint16_t*>(ws_i32(ws, L.off_zrow));
 
   // conversion role of this thread: chunk q of a tile (row q / CPR, chunk q %
   // CPR); at d = 128 every thread has one
@@ -139,17 +144,27 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   // whether the slot is live kept aside: no load sits behind a branch, so
   // the compiler's wait before the conversion two tiles later counts only
   // what was issued after it instead of draining the prefetches and stores.
-  // A slot that holds no token of the user reads the user's first row: a
-  // user with tiles has at least one token, whereas the first slot of a
-  // padding tile (tiles are rounded up to a multiple of kUserTileAlign) lies
-  // past the user's rows, and for the last user past the end of H.
+  // A slot that holds no token (a padding slot: tiles are rounded up to a
+  // multiple of kUserTileAlign, so it may lie past the end of H) reads the
+  // workspace's zero row, and its mask byte (masked batches) from the user's
+  // first token: a user with tiles has at least one.  `cnt` is the tile's
+  // token count (scalar; 0 past the workgroup's range).
   // The current user's tile base and token range stay in registers and are
   // read again only when the walk crosses into the next user (a workgroup's
   // range meets a few users), so a load waits on no scalar memory read.
   int lu = find_user(tile_base, L.R, ta);
   int32_t u_tile0 = tile_base[lu], u_tile1 = tile_base[lu + 1];
   int64_t u_first = offsets[lu], u_end = offsets[lu + 1];
-  auto load = [&](int32_t tile, u32x4& raw, uint32_t& mb, bool& in) {
+  // the user's tiles that hold tokens, and the token count of the last one
+  // (32-bit scalar arithmetic per tile)
+  auto user_tiles = [&](int32_t& nt, int32_t& last) {
+    const int64_t n_u = u_end - u_first;
+    nt = (int32_t)((n_u + kTile - 1) / kTile);
+    last = (int32_t)(n_u - (int64_t)(nt - 1) * kTile);
+  };
+  int32_t u_nt, u_last;
+  user_tiles(u_nt, u_last);
+  auto load = [&](int32_t tile, u32x4& raw, uint32_t& mb, bool& in, int32_t& cnt) {
     const bool live = tile < tb;               // uniform
     const int32_t tl = live ? tile : tb - 1;   // a tile of this workgroup
     if (tl >= u_tile1) {                       // uniform
@@ -158,13 +173,16 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
       u_tile1 = tile_base[lu + 1];
       u_first = offsets[lu];
       u_end = offsets[lu + 1];
+      user_tiles(u_nt, u_last);
     }
     const int64_t first = u_first;
-    const int64_t tok = first + (int64_t)(tl - u_tile0) * kTile + crow;
+    const int32_t trel = tl - u_tile0;
+    cnt = !live ? 0 : (trel < u_nt - 1 ? kTile : (trel == u_nt - 1 ? u_last : 0));
+    const int64_t tok = first + (int64_t)trel * kTile + crow;
     in = live && conv && tok < u_end;
-    const int64_t tc = in ? tok : first;       // a token of user lu
-    raw = reinterpret_cast<const u32x4*>(H + tc * D)[cch];
-    if constexpr (MASKED) mb = mask[tc];
+    const uint16_t* row = in ? H + tok * D : zrow;
+    raw = reinterpret_cast<const u32x4*>(row)[cch];
+    if constexpr (MASKED) mb = mask[in ? tok : first];
     else mb = 1u;
   };
   // Kept values outside fp16's finite range raise a device error bit once
@@ -184,9 +202,9 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   // the same for the -l pairs of tiles [ta, tb)
   const __amdgpu_buffer_rsrc_t nl_view =
       __builtin_amdgcn_make_buffer_rsrc(nl + (int64_t)ta * kTile, (short)0, n * kTile * 4, kBufferRsrcWord3);
-  // widen, store to LDS buffer b and to the fp16 rows; keep words and the
-  // per-wave "some logit may reach 100" bit.  A dropped token's row becomes
-  // zero here (whatever it held, NaN included).  Runs for every iteration,
+  // widen, store to LDS buffer b and to the fp16 rows; keep words (masked
+  // batches) and the per-wave "some logit may reach 100" bit.  A masked
+  // token's row becomes zero here (whatever it held, NaN included).  Runs for every iteration,
   // past the last tile too (into a buffer nobody reads; the row store is
   // dropped), so that consuming the prefetched registers never sits behind
   // a branch.  The exact/fast decision needs a bound on each row's norm: CPR
@@ -194,8 +212,9 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   // no exchange between lanes is needed.  At d = 128 the body has no branch,
   // which lets it run interleaved with the previous tile's MFMAs.
   auto convert = [&](int32_t tile, int b, const u32x4& raw_in, uint32_t mb, bool in) {
-    const bool keep = in && mb != 0u;
-    const u32x4 raw = keep ? raw_in : u32x4{0u, 0u, 0u, 0u};
+    // unmasked: a slot without a token already holds the zero row
+    const bool keep = MASKED ? in && mb != 0u : true;
+    const u32x4 raw = !MASKED || keep ? raw_in : u32x4{0u, 0u, 0u, 0u};
     const half8 hv = bf16x8_to_f16x8(raw);
     float n2 = 0.f;
 #pragma unroll
@@ -210,11 +229,13 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
       *reinterpret_cast<half8*>(&rows[b][crow * C::PITCH + 16 * cch]) = hv;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hv), h16_rows,
                                              ((tile - ta) * kTile + crow) * (D * 2) + 16 * cch, 0, 0);
-      uint32_t* kw = cch == 0 ? &keep_words[b][crow] : &spare[tid];
-      *kw = keep ? 1u : 0u;
+      if constexpr (MASKED) {
+        uint32_t* kw = cch == 0 ? &keep_words[b][crow] : &spare[tid];
+        *kw = keep ? 1u : 0u;
+      }
     }
     range_sus |= __ballot(!(n2 <= kF16MaxSq));
-    const bool big = conv && keep && n2 * (float)C::CPR >= lim2;
+    const bool big = conv && keep && n2 >= lim2c;
     const uint32_t eb = __ballot(big) != 0ull ? 1u : 0u;   // uniform over the wave
     *(lane == 0 ? &exact_bytes[b][wave] : reinterpret_cast<uint8_t*>(&spare[tid])) = (uint8_t)eb;
   };
@@ -335,15 +356,14 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
     return exact;
   };
 
-  // -l pairs of tile j (buffer b) from its 8 partials: wave w, lanes 0..3,
-  // tokens 4 w .. 4 w + 3
-  // Only the first W / 2 waves finalize (kTile / (W / 2) tokens each).
+  // -l pairs of tile j (buffer b) from its W partials.  Only the first
+  // W / 2 waves finalize, TPW = kTile / (W / 2) tokens each.
   // Waves w and w + W / 2 share a SIMD, and the first of the pair, which the
   // arbiter favours at equal priority, finishes its MFMAs before the second;
   // its finalize then partly fills that gap instead of lengthening the
   // second wave's path to the next barrier (measured faster than a finalize
   // spread over all waves).
-  auto finalize = [&](int j, int b, bool exact) {
+  auto finalize = [&](int j, int b, bool exact, int32_t cnt) {
     constexpr int FW = W / 2;
     constexpr int TPW = kTile / FW;   // tokens per finalizing wave
     static_assert(TPW * FW == kTile && TPW <= 64, "tokens per wave");
@@ -351,7 +371,9 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
     // every lane works (no branch): lanes with equal lane % TPW store the
     // same value to the same word
     const int tok = wave * TPW + (lane % TPW);
-    const bool keep = keep_words[b][tok] != 0u;
+    bool keep;
+    if constexpr (MASKED) keep = keep_words[b][tok] != 0u;
+    else keep = tok < cnt;
     const float* pp = part[j & 1][tok];
     float lse;
     if (!exact) {
@@ -379,10 +401,13 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   u32x4 raw[2];
   uint32_t mb[2];
   bool in[2];
-  load(ta, raw[0], mb[0], in[0]);
-  load(ta + 1, raw[1], mb[1], in[1]);
+  int32_t cnt[2];
+  load(ta, raw[0], mb[0], in[0], cnt[0]);
+  load(ta + 1, raw[1], mb[1], in[1], cnt[1]);
   convert(ta, 0, raw[0], mb[0], in[0]);
-  load(ta + 2, raw[0], mb[0], in[0]);
+  // token counts of the tiles being finalized and computed
+  int32_t cnt_fin = 0, cnt_cmp = cnt[0];
+  load(ta + 2, raw[0], mb[0], in[0], cnt[0]);
 
   // iteration j: compute tile j with the conversion of tile j + 1 (loaded two
   // iterations ago) into buffer (j + 1) % 3 interleaved, finalize tile j - 1,
@@ -396,9 +421,11 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
     lds_barrier();
     const int b = j % kBufs;
     const bool ex = compute(j, b, [&] { convert(ta + j + 1, (j + 1) % kBufs, raw[R], mb[R], in[R]); });
-    if (j >= 1) finalize(j - 1, (j + kBufs - 1) % kBufs, ex_prev);
+    if (j >= 1) finalize(j - 1, (j + kBufs - 1) % kBufs, ex_prev, cnt_fin);
     ex_prev = ex;
-    load(ta + j + 3, raw[R], mb[R], in[R]);
+    cnt_fin = cnt_cmp;
+    cnt_cmp = cnt[R];
+    load(ta + j + 3, raw[R], mb[R], in[R], cnt[R]);
   };
   int j = 0;
   for (; j + 1 < n; j += 2) {
@@ -407,18 +434,20 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
   }
   if (j < n) iteration(j, std::integral_constant<int, 1>{});
   lds_barrier();
-  finalize(n - 1, (n - 1) % kBufs, ex_prev);
+  finalize(n - 1, (n - 1) % kBufs, ex_prev, cnt_fin);
   if (range_sus != 0ull) {   // uniform over the wave
     lu = find_user(tile_base, L.R, ta);
     u_tile0 = tile_base[lu];
     u_tile1 = tile_base[lu + 1];
     u_first = offsets[lu];
     u_end = offsets[lu + 1];
+    user_tiles(u_nt, u_last);
     for (int32_t t = ta; t < tb; ++t) {
       u32x4 r;
       uint32_t m;
       bool i;
-      load(t, r, m, i);
+      int32_t c;
+      load(t, r, m, i, c);
       if (i && m != 0u) range_bad |= bf16x8_range_bits(r);
     }
   }

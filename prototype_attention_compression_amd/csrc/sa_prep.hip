@@ -133,6 +133,8 @@ __device__ __forceinline__ void schedule(const int64_t* __restrict__ offsets, co
   const int R = L.R;
   const int CT = L.tiles_per_chunk;
   int32_t* tile_base = ws_i32(ws, L.off_tile_base);
+  // the zero row that pass 1 reads for tile slots holding no token
+  if (L.dtype == 0 && tid < 64) ws_i32(ws, L.off_zrow)[tid] = 0;
   int32_t* chunk_base = ws_i32(ws, L.off_chunk_base);
   int bad = 0;
   int32_t carry_t = 0, carry_c = 0;

@@ -59,6 +59,7 @@ def layout(R, N, d, k, bwd):
     take("chunk_base", (R + 1) * 4, 4)
     take("q16", k * d * 2, 2)
     take("qpart", (k // 32) * 4, 4)
+    take("zrow", 256, 4)
     take("h16", L["tiles_max"] * TILE * d * 2, 2)
     take("nl", L["tiles_max"] * TILE * 4 + 16, 4)
     if L["groups"]:
@@ -177,11 +178,23 @@ def replay(lengths, d, k, backward=True):
     check(offsets[u + 1] > first, "a user with tiles has a token")
     tok = first[:, None] + (t - tile_base[u])[:, None] * TILE + np.arange(TILE)[None, :]
     live = tok < offsets[u + 1][:, None]
+    # slots with a token read their row of H; the others the workspace's zero
+    # row (masked batches: their mask byte from the user's first token)
+    check((tok[live] >= 0) & (tok[live] < N), "pass 1 row loads inside H")
+    check(tok[live] * d + (CPR - 1) * 8 + 7 < N * d, "pass 1 chunk loads inside H")
+    check((CPR - 1) * 8 + 7 < S["zrow"] * 2, "pass 1 zero-row chunk loads inside the zero row")
     tc = np.where(live, tok, first[:, None])
-    check((tc >= 0) & (tc < N), "pass 1 row loads inside H")
-    check(tc * d + (CPR - 1) * 8 + 7 < N * d, "pass 1 chunk loads inside H")
+    check((tc >= 0) & (tc < N), "pass 1 mask byte loads inside the mask")
     check((t[:, None] * TILE + np.arange(TILE)) * d + d - 1 < S["h16"], "fp16 rows inside the workspace")
     check(t * TILE + TILE - 1 < S["nl"], "-l pairs inside the workspace")
+    # the tile's token count from 32-bit tile arithmetic (user's tile count and
+    # last-tile count) equals the count of live slots
+    n_u = offsets[u + 1] - first
+    nt = (n_u + TILE - 1) // TILE
+    last = n_u - (nt - 1) * TILE
+    trel = t - tile_base[u]
+    cnt = np.where(trel < nt - 1, TILE, np.where(trel == nt - 1, last, 0))
+    check(np.array_equal(cnt, live.sum(axis=1)), "pass 1 tile token counts")
 
     # ---- pass 2: groups, segments, slots and stage reads
     P, G = L["n_pblocks"], L["p2_groups"]
