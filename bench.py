@@ -76,8 +76,8 @@ TRAFFIC = {
     # 1.0536e9 fetched + 0.0576e9 written (same workload)
     "pass2_accum": (1111137089, "a32b5f381fe45e84b75521f015712631b65c414d1ef1eca63a684dda45eab8ff",
                     ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
-    # 1.3106e9 fetched + 2.0680e9 written (same workload, --backward)
-    "bwd_dh": (3378584226, "c9c3a06f4c752851e62eea7d41f59db5388e1b6d1d7f2f4c739bc8796604d04d",
+    # 1.3163e9 fetched + 2.0680e9 written (same workload, --backward)
+    "bwd_dh": (3384286289, "ea506718fbdb3929200410ceb488213ff1c3e8044723a6ea56600202deaf832d",
                ("sa_bwd.hip", "sa_layout.h", "sa_device.h")),
     # 1.8658e8 fetched + 0.4608e8 written (300 users x 300 candidates, --target-attention)
     "ta_attend": (232547216, "7fe0b40aabfc73acab82beed9163ae42dd37fdd3dc7c16f5d114279d1cae1736",

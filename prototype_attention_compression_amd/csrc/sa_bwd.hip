@@ -84,6 +84,13 @@ __device__ __forceinline__ float operand_scale(float b) {
   return b > 0.f ? fminf(kScaleMax, pow2_scale(b, 14)) : kScaleMax;
 }
 
+// log2 of such a scale (a normal power of two, 2^-100 .. 2^14), as an fp16
+// value (exact): a feature step that adds it to the logits makes the
+// exponentials come out already scaled
+__device__ __forceinline__ _Float16 scale_log2(float s) {
+  return (_Float16)(float)((int)((__float_as_uint(s) >> 23) & 0xFFu) - 127);
+}
+
 // Position of token i of a tile among the 16 accumulator registers of lane
 // half g (GEMM rows read from LDS row tau(m)): i = tau(acc_row(r, g)).
 __device__ __forceinline__ int acc_pos(int i) {
@@ -338,14 +345,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
   for (int s = 0; s < S; ++s) hB[s] = *reinterpret_cast<const half8*>(hrow + 16 * s + 8 * g);
   const uint32_t nlw = reinterpret_cast<const uint32_t*>(ws_i32(ws, L.off_nl))[(int64_t)tile * kTile + col];
   const bool keep = negl_of(nlw) > -30000.f;
-  // Feature step of the logits: the token supplies (-l_hi, -l_lo, -14) (the
-  // lower lane half's K positions), the prototype (1, 1, 1), so the logit
-  // accumulators start at -lse_t and the allocations are 2^accumulator
+  // Feature step of the logits: the token supplies (-l_hi, -l_lo, -14, e)
+  // (the lower lane half's K positions), the prototype (1, 1, 1, 1), so the
+  // logit accumulators start at e - lse_t and the allocations are
+  // 2^accumulator = 2^e A; e = 0 in sweep 1, log2 of the token's operand
+  // scale in sweep 2
   const half2v nlp = __builtin_bit_cast(half2v, nlw);
   const _Float16 z0 = (_Float16)0.0f;
   const half8 hfeat = g == 0 ? half8{nlp[0], nlp[1], (_Float16)(-kAllocShift), z0, z0, z0, z0, z0}
                              : half8{z0, z0, z0, z0, z0, z0, z0, z0};
-  const half8 qones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, z0, z0, z0, z0, z0};
+  const half8 qones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, z0, z0, z0, z0};
 
   const int NB = L.k / kTile;
   // Staging of the 2 NB block steps (block i % NB of sweep i / NB): two
@@ -402,8 +411,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
   for (int dt = 0; dt < DT; ++dt) dHc[dt] = float16v{};
 
   // C = q . h and Y = Zs . h of the staged block (A operands read in halves)
-  auto gemms = [&](const char* qb, float16v& Lc, float16v& Yc) {
-    Lc = mfma32x32x16(qones, hfeat, float16v{});
+  auto gemms = [&](const char* qb, float16v& Lc, float16v& Yc, const half8& feat) {
+    Lc = mfma32x32x16(qones, feat, float16v{});
     Yc = float16v{};
 #pragma unroll
     for (int s0 = 0; s0 < S; s0 += 4) {
@@ -426,7 +435,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
   // sweep 1: delta_t and the bound b_t
   auto sweep1 = [&](const char* qb) {
     float16v Lc, Yc;
-    gemms(qb, Lc, Yc);
+    gemms(qb, Lc, Yc, hfeat);
     const float4* cp = reinterpret_cast<const float4*>(qb + 2 * BLK) + 4 * g;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -454,7 +463,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
   if (!keep) bmx = 0.f;
   const float delta = dsum;
   const float sg = operand_scale(bmx);
-  const float sl = sg * kLn2;
+  // sweep 2's feature operand: the allocations come out as sg A
+  half8 hfeat2 = hfeat;
+  if (g == 0) hfeat2[3] = scale_log2(sg);
   if (g == 0) {
     sinv[wave][col] = 1.0f / (sg * zs);
     ws_f32(ws, L.off_bdelta)[(int64_t)tile * kTile + col] = delta;
@@ -466,10 +477,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
     if (lane == 0 && wm > 0.f)
       atomicMax(reinterpret_cast<unsigned int*>(ws_i32(ws, L.off_bbmax)) + u, __float_as_uint(wm));
   }
-  // sweep 2: dh += (sl dL)^T q + (sg A)^T Zs
+  // sweep 2: dh += (sg ln2 dL)^T q + (sg A)^T Zs
   auto sweep2 = [&](const char* qb) {
     float16v Lc, Yc;
-    gemms(qb, Lc, Yc);
+    gemms(qb, Lc, Yc, hfeat2);
     const float4* cp = reinterpret_cast<const float4*>(qb + 2 * BLK) + 4 * g;
     half8 al[2], ad[2];
 #pragma unroll
@@ -479,10 +490,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dh(const int64_t* __restrict__ off
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * v + e;
-        const float A = __builtin_amdgcn_exp2f(Lc[r]);
+        const float A = __builtin_amdgcn_exp2f(Lc[r]);   // sg A
         const float dl = A * (Yc[r] - cv[e] - delta);
-        al[r >> 3][r & 7] = (_Float16)(dl * sl);
-        ad[r >> 3][r & 7] = (_Float16)(A * sg);
+        al[r >> 3][r & 7] = (_Float16)(dl * kLn2);
+        ad[r >> 3][r & 7] = (_Float16)A;
       }
     }
 #pragma unroll
@@ -533,7 +544,7 @@ __global__ __launch_bounds__(W * 64, W == 8 ? 1 : 2) void bwd_e(const int32_t* _
   constexpr int LPT = kTile * CPR / NT;
   static_assert(LPT * NT == kTile * CPR, "whole loads");
   // the tile's rows, then per token the logits' feature piece
-  // {-l_hi, -l_lo, -14, 0 ...} (16 bytes), then delta_t zs (floats)
+  // {-l_hi, -l_lo, -14, 1, 0 ...} (16 bytes), then delta_t zs (floats)
   constexpr int FEAT = TB, DLT = TB + kTile * 16;
   constexpr int STAGE = DLT + kTile * 4;
   __shared__ __attribute__((aligned(16))) char lds[2][STAGE];
@@ -581,8 +592,8 @@ __global__ __launch_bounds__(W * 64, W == 8 ? 1 : 2) void bwd_e(const int32_t* _
       *reinterpret_cast<u32x4*>(base + row * PITCH + 16 * ch) = pr[k2];
     }
     if (tid < kTile) {
-      // -14 in fp16 is 0xCB00
-      reinterpret_cast<u32x4*>(base + FEAT)[tid] = u32x4{pn, 0x0000CB00u, 0u, 0u};
+      // -14 and 1 in fp16 are 0xCB00 and 0x3C00
+      reinterpret_cast<u32x4*>(base + FEAT)[tid] = u32x4{pn, 0x3C00CB00u, 0u, 0u};
       reinterpret_cast<float*>(base + DLT)[acc_pos(tid)] = pd;
     }
   };
@@ -590,11 +601,12 @@ __global__ __launch_bounds__(W * 64, W == 8 ? 1 : 2) void bwd_e(const int32_t* _
   const int i16 = lane & 15, gh = (lane >> 4) & 1;
   const int tr_base = (4 * (i16 >> 2) + 2 * g) * PITCH + 32 * gh + 8 * (i16 & 3);
   // feature step of the logits: the token's piece (A operand, lane's token
-  // tau(col)) against (1, 1, 1) at the lower lane half's K positions, so the
-  // logit accumulators start at -lse_t (the upper half meets zeros)
+  // tau(col)) against (1, 1, 1, log2 su) at the lower lane half's K
+  // positions, so the logit accumulators start at log2 su - lse_t and the
+  // exponentials come out as su A (the upper half meets zeros)
   const int fbase = FEAT + tau(col) * 16;
   const _Float16 f1 = g == 0 ? (_Float16)1.0f : (_Float16)0.0f, f0 = (_Float16)0.0f;
-  const half8 qones = {f1, f1, f1, f0, f0, f0, f0, f0};
+  half8 qones = {f1, f1, f1, f0, f0, f0, f0, f0};
 
   int u = find_user(tile_base, L.R, s0);
   int32_t ub = tile_base[u + 1];
@@ -606,6 +618,7 @@ __global__ __launch_bounds__(W * 64, W == 8 ? 1 : 2) void bwd_e(const int32_t* _
     cz = ws_f32(ws, L.off_bcz)[(int64_t)u * L.k + p0 + col];
     const float bm = __uint_as_float(reinterpret_cast<const uint32_t*>(ws_i32(ws, L.off_bbmax))[u]);
     su = operand_scale(bm);
+    qones[3] = g == 0 ? scale_log2(su) : f0;
     back = 1.0f / (su * ws_f32(ws, L.off_bzs)[u]);
   };
   float16v Ea[DT];
@@ -657,8 +670,8 @@ __global__ __launch_bounds__(W * 64, W == 8 ? 1 : 2) void bwd_e(const int32_t* _
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * v + e;
-        const float A = __builtin_amdgcn_exp2f(Lc[r]);
-        al[r >> 3][r & 7] = (_Float16)(A * (Yc[r] - cz - dd[e]) * su);
+        const float A = __builtin_amdgcn_exp2f(Lc[r]);   // su A
+        al[r >> 3][r & 7] = (_Float16)(A * (Yc[r] - cz - dd[e]));
       }
     }
 #pragma unroll
