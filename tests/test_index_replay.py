@@ -48,10 +48,12 @@ def layout(R, N, d, k, bwd):
     L["parts_max"] = parts
     off = 0
     sizes = {}
+    offs = {}
 
     def take(name, nbytes, elem):
         nonlocal off
         sizes[name] = nbytes // elem
+        offs[name] = off
         off = _align(off + nbytes)
 
     take("hdr", 256, 4)
@@ -86,6 +88,7 @@ def layout(R, N, d, k, bwd):
         take("bopart", L["o_chunks"] * d * d * 4, 4)
     L["total"] = off
     L["size"] = sizes
+    L["off"] = offs   # byte offsets
     return L
 
 
