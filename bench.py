@@ -71,7 +71,7 @@ DEFAULT_WORKLOAD = "c3lit_r40_n100k_d128_k1024"
 COPY_CALIBRATION_BYTES = 1 << 30
 TRAFFIC = {
     # 1.0263e9 fetched + 1.0410e9 written (40 x 100K tokens, k = 1024, d = 128)
-    "pass1_qres": (2067275674, "00b0cc45171c4ef4fc91998b4c712d03b0b83ec6753a2979ddb123ce213c3346",
+    "pass1_qres": (2067296585, "cef297ec68d3429cb9ae1a8bf88d374a992be6d9f2e827b7fbc4dba3503423a2",
                    ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
     # 1.0536e9 fetched + 0.0576e9 written (same workload)
     "pass2_accum": (1111137089, "a32b5f381fe45e84b75521f015712631b65c414d1ef1eca63a684dda45eab8ff",
@@ -90,8 +90,8 @@ TRAFFIC = {
 # kernel's time), from rocprofv3 --pmc on the default workload; valid, like the
 # traffic figures, only for the kernel sources they were taken on (null after).
 COUNTERS = {
-    "pass1_qres": ({"mfma_busy": 0.572, "clock_mhz": 1810.0},
-                   "00b0cc45171c4ef4fc91998b4c712d03b0b83ec6753a2979ddb123ce213c3346",
+    "pass1_qres": ({"mfma_busy": 0.590, "clock_mhz": 1735.0},
+                   "cef297ec68d3429cb9ae1a8bf88d374a992be6d9f2e827b7fbc4dba3503423a2",
                    ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
     "pass2_accum": ({"mfma_busy": 0.635, "clock_mhz": 1807.0},
                     "a32b5f381fe45e84b75521f015712631b65c414d1ef1eca63a684dda45eab8ff",

@@ -318,15 +318,25 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
       // both stay busy until the tile's end instead of the older wave
       // finishing first and the other running alone (measured: the two
       // waves' compute ends 0.2 instead of 1.5 thousand cycles apart).
+      // Block 0's MFMAs and the conversion come before the branch on the
+      // tile's form: with the conversion inside both branches the compiler
+      // hoists it above them, ahead of the first MFMA.
+      wave_priority(NBW - 1);
+      float16v a0 = float16v{};
+#pragma unroll
+      for (int s = 0; s < C::S; ++s) a0 = mfma32x32x16(qf[0][s], ha[s], a0);
+      mid();
       if (!exact) {
         float p0 = 0.f, p1 = 0.f;
 #pragma unroll
         for (int bl = 0; bl < NBW; ++bl) {
-          wave_priority(NBW - 1 - bl);
-          float16v a = float16v{};
+          float16v a = a0;
+          if (bl > 0) {
+            wave_priority(NBW - 1 - bl);
+            a = float16v{};
 #pragma unroll
-          for (int s = 0; s < C::S; ++s) a = mfma32x32x16(qf[bl][s], ha[s], a);
-          if (bl == 0) mid();
+            for (int s = 0; s < C::S; ++s) a = mfma32x32x16(qf[bl][s], ha[s], a);
+          }
 #pragma unroll
           for (int r = 0; r < 16; r += 2) {
             p0 += __builtin_amdgcn_exp2f(a[r]);
@@ -339,11 +349,13 @@ __global__ __launch_bounds__(W * 64, NBW == 1 ? 4 : 2) void pass1_qres(const uin
         float m = -INFINITY, p = 0.f;
 #pragma unroll
         for (int bl = 0; bl < NBW; ++bl) {
-          wave_priority(NBW - 1 - bl);
-          float16v a = float16v{};
+          float16v a = a0;
+          if (bl > 0) {
+            wave_priority(NBW - 1 - bl);
+            a = float16v{};
 #pragma unroll
-          for (int s = 0; s < C::S; ++s) a = mfma32x32x16(qf[bl][s], ha[s], a);
-          if (bl == 0) mid();
+            for (int s = 0; s < C::S; ++s) a = mfma32x32x16(qf[bl][s], ha[s], a);
+          }
           exact_block(a, m, p);
         }
         const HalfPair hp = lane_halves(m + log2_normal(p));
