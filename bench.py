@@ -73,8 +73,8 @@ TRAFFIC = {
     # 1.0263e9 fetched + 1.0410e9 written (40 x 100K tokens, k = 1024, d = 128)
     "pass1_qres": (2067296585, "cef297ec68d3429cb9ae1a8bf88d374a992be6d9f2e827b7fbc4dba3503423a2",
                    ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
-    # 1.0536e9 fetched + 0.0576e9 written (same workload)
-    "pass2_accum": (1111137089, "a32b5f381fe45e84b75521f015712631b65c414d1ef1eca63a684dda45eab8ff",
+    # 1.0508e9 fetched + 0.0597e9 written (same workload)
+    "pass2_accum": (1110476800, "2665c3bdef7508bcdfa688c5baa2451edda846c365be005d8835317ad3fd5fef",
                     ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
     # 1.3163e9 fetched + 2.0680e9 written (same workload, --backward)
     "bwd_dh": (3384286289, "ea506718fbdb3929200410ceb488213ff1c3e8044723a6ea56600202deaf832d",
@@ -93,8 +93,8 @@ COUNTERS = {
     "pass1_qres": ({"mfma_busy": 0.590, "clock_mhz": 1735.0},
                    "cef297ec68d3429cb9ae1a8bf88d374a992be6d9f2e827b7fbc4dba3503423a2",
                    ("sa_pass1q.hip", "sa_layout.h", "sa_device.h")),
-    "pass2_accum": ({"mfma_busy": 0.635, "clock_mhz": 1807.0},
-                    "a32b5f381fe45e84b75521f015712631b65c414d1ef1eca63a684dda45eab8ff",
+    "pass2_accum": ({"mfma_busy": 0.654, "clock_mhz": 1761.0},
+                    "2665c3bdef7508bcdfa688c5baa2451edda846c365be005d8835317ad3fd5fef",
                     ("sa_pass2.hip", "sa_layout.h", "sa_device.h")),
 }
 

@@ -288,7 +288,7 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
     tile_tr_reads<D>(lds_addr(tile_lds(t) + (t % kStageTiles) * C::TILE_BYTES) + tr_base, hb);
   };
   // allocations 2^C (= 2^14 A) in fp16 for accumulator elements 2 i, 2 i + 1
-  // (i = 0..7), and the masses of the rounded values
+  // (i = 0..7)
   auto expo2 = [&](const float16v (&Cm)[NB], half8 (&ap)[NB][2], int i) {
     const int kk = i >> 2, e = 2 * (i & 3);
 #pragma unroll
@@ -298,9 +298,21 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
       // keep the conversion (and its exponentials) here, between this
       // period's MFMAs, instead of next to the MFMA that consumes it
       asm volatile("" ::"v"(h));
-      msum[b] = __builtin_amdgcn_fdot2(h, ones, msum[b], false);
       ap[b][kk][e] = h[0];
       ap[b][kk][e + 1] = h[1];
+    }
+  };
+  // the masses of one tile's rounded allocations, pair i in the conversion's
+  // order.  They are summed as one block at the start of the next period,
+  // ahead of its MFMAs: one dot2 per GEMM2 step beside the exponentials made
+  // pass 2 4.5% slower, and the block 1.5-2% faster than the compiler's own
+  // placement (the same sums in the same order).
+  auto mass_pair = [&](const half8 (&ap)[NB][2], int i) {
+    const int kk = i >> 2, e = 2 * (i & 3);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const half2v h = {ap[b][kk][e], ap[b][kk][e + 1]};
+      msum[b] = __builtin_amdgcn_fdot2(h, ones, msum[b], false);
     }
   };
   // GEMM2 step m (m = 0 .. 2 DT - 1): U[proto, c] += sum_tok A'[proto, tok] h_tok[c]
@@ -316,8 +328,8 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
   half8 ap0[NB][2], ap1[NB][2];
   half8 ha[C::S], hb[2][C::DT];
   half8 nlp;
-  // Period t runs GEMM2 of tile t-2 interleaved with the exponentials of
-  // tile t-1, then GEMM1 of tile t+1, so every MFMA result is consumed a
+  // Period t sums the masses of tile t-2, runs GEMM2 of tile t-2 interleaved
+  // with the exponentials of tile t-1, then GEMM1 of tile t+1, so every MFMA result is consumed a
   // whole period after its chain was issued (issue is in order per wave,
   // and both waves of a SIMD would otherwise stall on the same chain).
   // Registers: C(t-1) and C(t+1) share a set (GEMM1 of t+1 starts after the
@@ -335,6 +347,11 @@ __global__ __launch_bounds__(WAVES * 64) void pass2_accum(Layout L, void* ws) {
     constexpr bool MORE = decltype(morec)::value, RB = decltype(rbc)::value;
     if constexpr (MORE) boundary(t + 1);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (G2) {   // masses of tile t-2 (its allocations came in period t-1)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mass_pair(app, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int m = 0; m < M2; ++m) {
       if constexpr (G2) mma2(hb, app, m);
