@@ -1,7 +1,7 @@
 // sa_f32.hip — Sketch Attention for float32 inputs (fp32 arithmetic on the
 // vector ALUs), the same two passes as the bf16 path:
-//   pass 1: lse_t = log2 sum_j 2^(q_j . h_t) per token, exact two-sweep form
-//           (maximum, then the shifted sum);
+//   pass 1: lse_t = log2 sum_j 2^(q_j . h_t) per token, in one sweep with a
+//           running maximum (the sum rescaled whenever the maximum grows);
 //   pass 2: per (chunk, 64-prototype block) A[j,t] = 2^(q_j . h_t - lse_t),
 //           U[j,:] += A[j,t] h_t and m_j += A[j,t].
 // The softmax runs over prototypes for each token (SequenceO1 blog "How it
@@ -15,43 +15,113 @@
 
 namespace sa {
 
-// One thread per token slot (tile * 32 + row).
+// Pass 1: four threads per token slot (tile * 32 + row), 64 slots (two
+// tiles) per workgroup.  Thread (slot sl = tid / 4, part = tid % 4) takes the
+// prototypes j = 4 i + part.  The queries pass through LDS 64 rows at a time,
+// each row padded by 16 bytes so that the four rows a wave reads at once sit
+// in different banks (the 16 lanes of a part read the same address: a
+// broadcast).  Each thread keeps a running maximum m and the sum of 2^(x - m)
+// over its prototypes (one sweep: the sum is rescaled when the maximum
+// grows); the four partial pairs of a token are combined by lane shuffles.
+// Every thread takes part in the staging barriers; slots past the batch's
+// last tile compute on zeros and write nothing.
 template <int D>
 __global__ __launch_bounds__(256) void pass1_f32(const float* __restrict__ H, const int64_t* __restrict__ offsets,
                                                  const uint8_t* __restrict__ mask, Layout L, void* ws) {
+  constexpr int QP = D + 4;   // padded query row (floats)
+  __shared__ __attribute__((aligned(16))) float qs[64 * QP];
   const int32_t* hdr = ws_i32(ws, L.off_hdr);
-  const int64_t slot = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int tid = threadIdx.x, part = tid & 3;
+  const int64_t slot = (int64_t)blockIdx.x * 64 + (tid >> 2);
+  const int32_t T = hdr[kHdrTiles];
   const int32_t tile = (int32_t)(slot / kTile);
   const int row = (int)(slot % kTile);
-  if (tile >= hdr[kHdrTiles]) return;
-  const TileInfo ti = tile_info(ws_i32(ws, L.off_tile_base), offsets, L.R, tile);
-  float* lse = ws_f32(ws, L.off_lse32);
-  bool valid = row < ti.count;
-  const int64_t tok = ti.tok0 + row;
-  if (valid && mask != nullptr) valid = mask[tok] != 0;
-  if (!valid) {
-    lse[slot] = INFINITY;
-    return;
+  bool valid = false;
+  int64_t tok = 0;
+  if (tile < T) {
+    const TileInfo ti = tile_info(ws_i32(ws, L.off_tile_base), offsets, L.R, tile);
+    valid = row < ti.count;
+    tok = ti.tok0 + row;
+    if (valid && mask != nullptr) valid = mask[tok] != 0;
   }
   float h[D];
+  if (valid) {   // one branch around the row's loads
 #pragma unroll
-  for (int a = 0; a < D; ++a) h[a] = H[tok * D + a];
+    for (int a = 0; a < D; a += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(H + tok * D + a);
+      h[a] = v.x;
+      h[a + 1] = v.y;
+      h[a + 2] = v.z;
+      h[a + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < D; ++a) h[a] = 0.f;
+  }
   const float* q = ws_f32(ws, L.off_q32);
-  float mx = -INFINITY;
-  for (int j = 0; j < L.k; ++j) {
-    float s = 0.f;
+  float m = -INFINITY, sum = 0.f;
+  auto update = [&](float x) {
+    const float mn = fmaxf(m, x);
+    sum = sum * exp2f(m - mn) + exp2f(x - mn);
+    m = mn;
+  };
+  constexpr int SL = 64 * (D / 4) / 256;   // 16-byte staging loads per thread and chunk
+  for (int j0 = 0; j0 < L.k; j0 += 64) {
+    // the chunk's loads issued together, then written (a vector type: an
+    // array of the float4 struct would stay in scratch memory)
+    u32x4 st[SL];
 #pragma unroll
-    for (int a = 0; a < D; ++a) s = fmaf(q[(int64_t)j * D + a], h[a], s);
-    mx = fmaxf(mx, s);
-  }
-  float sum = 0.f;
-  for (int j = 0; j < L.k; ++j) {
-    float s = 0.f;
+    for (int k2 = 0; k2 < SL; ++k2) {
+      const int e = tid + 256 * k2, r = e / (D / 4), c = e % (D / 4);
+      st[k2] = *reinterpret_cast<const u32x4*>(q + (int64_t)(j0 + r) * D + 4 * c);
+    }
+    __syncthreads();   // every read of the previous chunk is done
 #pragma unroll
-    for (int a = 0; a < D; ++a) s = fmaf(q[(int64_t)j * D + a], h[a], s);
-    sum += exp2f(s - mx);
+    for (int k2 = 0; k2 < SL; ++k2) {
+      const int e = tid + 256 * k2, r = e / (D / 4), c = e % (D / 4);
+      *reinterpret_cast<u32x4*>(qs + r * QP + 4 * c) = st[k2];
+    }
+    __syncthreads();
+    // two prototypes at a time, each dot product in two partial sums (four
+    // independent FMA chains)
+    for (int i = 0; i < 16; i += 2) {
+      const float* q0 = qs + (4 * i + part) * QP;
+      const float* q1 = q0 + 4 * QP;
+      float x0a = 0.f, x0b = 0.f, x1a = 0.f, x1b = 0.f;
+#pragma unroll
+      for (int a = 0; a < D; a += 8) {
+        const float4 u0 = *reinterpret_cast<const float4*>(q0 + a), v0 = *reinterpret_cast<const float4*>(q0 + a + 4);
+        const float4 u1 = *reinterpret_cast<const float4*>(q1 + a), v1 = *reinterpret_cast<const float4*>(q1 + a + 4);
+        x0a = fmaf(u0.x, h[a], x0a);
+        x0b = fmaf(v0.x, h[a + 4], x0b);
+        x1a = fmaf(u1.x, h[a], x1a);
+        x1b = fmaf(v1.x, h[a + 4], x1b);
+        x0a = fmaf(u0.y, h[a + 1], x0a);
+        x0b = fmaf(v0.y, h[a + 5], x0b);
+        x1a = fmaf(u1.y, h[a + 1], x1a);
+        x1b = fmaf(v1.y, h[a + 5], x1b);
+        x0a = fmaf(u0.z, h[a + 2], x0a);
+        x0b = fmaf(v0.z, h[a + 6], x0b);
+        x1a = fmaf(u1.z, h[a + 2], x1a);
+        x1b = fmaf(v1.z, h[a + 6], x1b);
+        x0a = fmaf(u0.w, h[a + 3], x0a);
+        x0b = fmaf(v0.w, h[a + 7], x0b);
+        x1a = fmaf(u1.w, h[a + 3], x1a);
+        x1b = fmaf(v1.w, h[a + 7], x1b);
+      }
+      update(x0a + x0b);
+      update(x1a + x1b);
+    }
   }
-  lse[slot] = mx + log2f(sum);
+  // the four parts of a token are lanes 4 sl .. 4 sl + 3 of one wave
+#pragma unroll
+  for (int off = 1; off < 4; off <<= 1) {
+    const float mo = __shfl_xor(m, off), so = __shfl_xor(sum, off);
+    const float mn = fmaxf(m, mo);
+    sum = sum * exp2f(m - mn) + so * exp2f(mo - mn);
+    m = mn;
+  }
+  if (part == 0 && tile < T) ws_f32(ws, L.off_lse32)[slot] = valid ? m + log2f(sum) : INFINITY;
 }
 
 // Workgroup = (chunk, block of 64 prototypes), 256 threads.  Per tile: thread
@@ -61,7 +131,8 @@ template <int D>
 __global__ __launch_bounds__(256) void pass2_f32(const float* __restrict__ H, const int64_t* __restrict__ offsets,
                                                  const uint8_t* __restrict__ mask, Layout L, void* ws) {
   constexpr int DQ = D / 4;
-  __shared__ float hs[kTile][D + 1];
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) float hs[kTile][D + 4];   // rows 16-byte aligned: vector reads
   __shared__ float as[64][kTile + 1];
   __shared__ float ls[kTile];
   const int32_t* hdr = ws_i32(ws, L.off_hdr);
@@ -88,32 +159,70 @@ __global__ __launch_bounds__(256) void pass2_f32(const float* __restrict__ H, co
   for (int c = 0; c < DQ; ++c) U[c] = 0.f;
   float m = 0.f;
   const int64_t u_lo = offsets[u], u_hi = offsets[u + 1];
-  for (int it = 0; it < nt; ++it) {
-    const int32_t tile = t0 + it;
+  // A tile's rows as 16-byte pieces, NV per thread, loaded together from
+  // addresses clamped to the user's rows (a user with tiles has a token) and
+  // zeroed past its end or where masked; the next tile's loads are issued
+  // before the current tile's arithmetic.
+  constexpr int NV = kTile * D / 4 / 256;
+  static_assert(NV * 256 * 4 == kTile * D, "whole pieces");
+  u32x4 rv[NV];
+  uint8_t mk[NV];      // the mask bytes of the pieces' tokens (1 without a mask)
+  uint32_t inb = 0;    // bit k2: piece k2's token lies inside the user's rows
+  float lv = 0.f;
+  auto load_tile = [&](int it) {
     const int64_t tok0 = u_lo + (int64_t)(ci * CT + it) * kTile;
-    for (int e = tid; e < kTile * D; e += 256) {
-      const int r = e / D, a = e % D;
-      const int64_t tok = tok0 + r;
-      bool ok = tok < u_hi;
-      if (ok && mask != nullptr) ok = mask[tok] != 0;
-      hs[r][a] = ok ? H[tok * D + a] : 0.f;
+    inb = 0;
+#pragma unroll
+    for (int k2 = 0; k2 < NV; ++k2) {
+      const int e = tid + 256 * k2, r = e / (D / 4), c4 = e % (D / 4);
+      const int64_t tok = tok0 + r, tc = tok < u_hi ? tok : u_hi - 1;
+      rv[k2] = *reinterpret_cast<const u32x4*>(H + tc * D + 4 * c4);
+      mk[k2] = mask != nullptr ? mask[tc] : (uint8_t)1;
+      inb |= (tok < u_hi ? 1u : 0u) << k2;
     }
-    if (tid < kTile) ls[tid] = lse[(int64_t)tile * kTile + tid];
+    if (tid < kTile) lv = lse[(int64_t)(t0 + it) * kTile + tid];
+  };
+  if (nt > 0) load_tile(0);
+  for (int it = 0; it < nt; ++it) {
+#pragma unroll
+    for (int k2 = 0; k2 < NV; ++k2) {
+      const int e = tid + 256 * k2, r = e / (D / 4), c4 = e % (D / 4);
+      const bool ok = ((inb >> k2) & 1u) != 0 && mk[k2] != 0;
+      *reinterpret_cast<u32x4*>(&hs[r][4 * c4]) = ok ? rv[k2] : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tid < kTile) ls[tid] = lv;
     __syncthreads();
+    if (it + 1 < nt) load_tile(it + 1);
+    // the logits of prototype j for tokens 8 grp .. 8 grp + 7: eight
+    // independent chains, rows read 16 bytes at a time (one address per wave)
+    float sx[8];
 #pragma unroll
-    for (int r8 = 0; r8 < 8; ++r8) {
-      const int r = grp * 8 + r8;
-      float s = 0.f;
+    for (int r8 = 0; r8 < 8; ++r8) sx[r8] = 0.f;
 #pragma unroll
-      for (int a = 0; a < D; ++a) s = fmaf(qv[a], hs[r][a], s);
-      as[j][r] = exp2f(s - ls[r]);
+    for (int a = 0; a < D; a += 4) {
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8) {
+        const f32x4 h4 = *reinterpret_cast<const f32x4*>(&hs[grp * 8 + r8][a]);
+        sx[r8] = fmaf(qv[a], h4.x, sx[r8]);
+        sx[r8] = fmaf(qv[a + 1], h4.y, sx[r8]);
+        sx[r8] = fmaf(qv[a + 2], h4.z, sx[r8]);
+        sx[r8] = fmaf(qv[a + 3], h4.w, sx[r8]);
+      }
     }
+#pragma unroll
+    for (int r8 = 0; r8 < 8; ++r8) as[j][grp * 8 + r8] = exp2f(sx[r8] - ls[grp * 8 + r8]);
     __syncthreads();
     for (int r = 0; r < kTile; ++r) {
       const float a = as[j][r];
       m += a;
 #pragma unroll
-      for (int c = 0; c < DQ; ++c) U[c] = fmaf(a, hs[r][grp * DQ + c], U[c]);
+      for (int c = 0; c < DQ; c += 4) {
+        const f32x4 h4 = *reinterpret_cast<const f32x4*>(&hs[r][grp * DQ + c]);
+        U[c] = fmaf(a, h4.x, U[c]);
+        U[c + 1] = fmaf(a, h4.y, U[c + 1]);
+        U[c + 2] = fmaf(a, h4.z, U[c + 2]);
+        U[c + 3] = fmaf(a, h4.w, U[c + 3]);
+      }
     }
     __syncthreads();
   }
@@ -125,7 +234,7 @@ __global__ __launch_bounds__(256) void pass2_f32(const float* __restrict__ H, co
 
 hipError_t launch_f32(const Layout& L, const void* H, const int64_t* offsets, const uint8_t* mask, void* ws,
                       hipStream_t stream) {
-  const int64_t g1 = ((int64_t)L.tiles_max * kTile + 255) / 256;
+  const int64_t g1 = ((int64_t)L.tiles_max * kTile + 63) / 64;
   if (g1 == 0) return hipSuccess;
   if (L.d == 128)
     hipLaunchKernelGGL(pass1_f32<128>, dim3((unsigned)g1), dim3(256), 0, stream, (const float*)H, offsets, mask, L, ws);
