@@ -309,3 +309,86 @@ def test_old_pass1_clamp_read_past_h():
     tok = t0[:, None] + np.arange(TILE)[None, :]
     tc = np.where(tok < offsets[u + 1][:, None], tok, first[:, None])
     assert int(tc.max()) == N - 1
+
+
+# ------------------------------------------------------------- fp32 path
+def replay_f32(lengths, d, k, masked=False):
+    """The fp32 kernels' indices (pass1_f32: four threads per token slot, 64
+    slots per workgroup, queries staged 64 rows at a time; pass2_f32: one
+    workgroup per (chunk, 64-prototype block), rows loaded from addresses
+    clamped to the user's rows) against their buffers: H and the mask [N],
+    the fp32 queries [k, d], lse32 [tiles_max * 32] and the chunk partials."""
+    offsets, tile_base, T = schedule(lengths)
+    R, N = len(lengths), int(offsets[-1])
+    span = TILE * ALIGN_T
+    tiles_max = (N + (span - 1) * R) // span * ALIGN_T
+    check(T <= tiles_max, "tiles within tiles_max")
+    n_lse = tiles_max * TILE
+    # pass1_f32: grid ceil(tiles_max * 32 / 64) workgroups of 256 threads
+    g1 = (tiles_max * TILE + 63) // 64
+    tid = np.arange(256)
+    part = tid & 3
+    for b in range(g1):
+        slot = b * 64 + (tid >> 2)
+        tile = slot // TILE
+        row = slot % TILE
+        live = tile < T
+        if not live.any():
+            continue
+        u = user_of(tile_base, tile[live])
+        tok0 = offsets[u] + (tile[live] - tile_base[u]) * TILE
+        count = np.minimum(TILE, offsets[u + 1] - tok0)
+        valid = row[live] < count
+        tok = (tok0 + row[live])[valid]
+        check((tok >= 0) & (tok < N), "pass1_f32: H row / mask byte in range")
+        check(tok * d + d <= N * d, "pass1_f32: H row end in range")
+        writes = slot[live & (part == 0)]
+        check(writes < n_lse, "pass1_f32: lse32 index in range")
+    for j0 in range(0, k, 64):
+        e = np.arange(64 * (d // 4))
+        r = e // (d // 4)
+        check((j0 + r) * d + 4 * (e % (d // 4)) + 4 <= k * d, "pass1_f32: query staging in range")
+    # pass2_f32: chunks of CT tiles per user, k / 64 prototype blocks
+    nblk = k // 64
+    want = (tiles_max * nblk + 255) // 256
+    ct = min(max(want, 4), 64)
+    CT = (ct + ALIGN_T - 1) // ALIGN_T * ALIGN_T
+    chunks_max = (tiles_max + (CT - 1) * R) // CT
+    tiles_u = np.diff(tile_base)
+    chunks_u = (tiles_u + CT - 1) // CT
+    check(chunks_u.sum() <= chunks_max, "pass2_f32: chunks within chunks_max")
+    nv = TILE * d // 4 // 256
+    for u in range(R):
+        lo, hi = int(offsets[u]), int(offsets[u + 1])
+        for ci in range(int(chunks_u[u])):
+            nt = min(CT, int(tiles_u[u]) - ci * CT)
+            check(nt > 0 and hi > lo, "pass2_f32: a chunk's user has a token")
+            for it in range(nt):
+                tok0 = lo + (ci * CT + it) * TILE
+                e = tid[:, None] + 256 * np.arange(nv)[None, :]
+                tok = tok0 + e // (d // 4)
+                tc = np.minimum(tok, hi - 1)
+                check((tc >= lo) & (tc < N), "pass2_f32: clamped row in the user's rows")
+                check(tc * d + 4 * (e % (d // 4)) + 4 <= N * d, "pass2_f32: row piece in range")
+                lse_idx = (int(tile_base[u]) + ci * CT + it) * TILE + np.arange(TILE)
+                check(lse_idx < n_lse, "pass2_f32: lse32 read in range")
+
+
+@pytest.mark.parametrize("lengths,d,k", [
+    ([4096], 64, 64),                      # C1
+    ([700, 0, 2049, 33], 128, 192),
+    ([1, 0, 0, 31, 32, 33, 129], 64, 128),
+    ([0, 0, 5], 128, 64),
+    ([100000], 128, 1024),
+])
+def test_replay_f32_in_bounds(lengths, d, k):
+    replay_f32(lengths, d, k)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_replay_f32_random_ragged(seed):
+    rng = np.random.default_rng(100 + seed)
+    R = int(rng.integers(1, 120))
+    lens = rng.integers(0, 2500, size=R)
+    lens[rng.random(R) < 0.15] = 0
+    replay_f32(lens.tolist(), int(rng.choice([64, 128])), int(rng.choice([64, 128, 192, 256, 1024])))
