@@ -124,19 +124,23 @@ __global__ __launch_bounds__(256) void pass1_f32(const float* __restrict__ H, co
   if (part == 0 && tile < T) ws_f32(ws, L.off_lse32)[slot] = valid ? m + log2f(sum) : INFINITY;
 }
 
-// Workgroup = (chunk, block of 64 prototypes), 256 threads.  Per tile: thread
-// (j = tid % 64, grp = tid / 64) computes the allocations of prototype j for
-// tokens 8*grp .. 8*grp+7, then accumulates U[j, grp*D/4 .. +D/4).
+// Workgroup = (chunk, block of 16 prototypes), 256 threads.  Per tile: thread
+// (j = tid % 16, grp = tid / 16) computes the allocations of prototype j for
+// tokens 2*grp and 2*grp+1, then accumulates U[j, grp*D/16 .. +D/16).  Small
+// blocks give small batches (one user of a few thousand tokens) enough
+// workgroups: the per-thread chains are short, and latency, not arithmetic,
+// sets their time.
 template <int D>
 __global__ __launch_bounds__(256) void pass2_f32(const float* __restrict__ H, const int64_t* __restrict__ offsets,
                                                  const uint8_t* __restrict__ mask, Layout L, void* ws) {
-  constexpr int DQ = D / 4;
+  constexpr int PB = 16, NG = 256 / PB, TPG = kTile / NG;   // prototypes, groups, tokens per group
+  constexpr int DQ = D / NG;
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(16))) float hs[kTile][D + 4];   // rows 16-byte aligned: vector reads
-  __shared__ float as[64][kTile + 1];
+  __shared__ float as[PB][kTile + 1];
   __shared__ float ls[kTile];
   const int32_t* hdr = ws_i32(ws, L.off_hdr);
-  const int nblk = L.k / 64;
+  const int nblk = L.k / PB;
   const int chunk = blockIdx.x / nblk, pb = blockIdx.x % nblk;
   if (chunk >= hdr[kHdrChunks]) return;
   const int32_t* tile_base = ws_i32(ws, L.off_tile_base);
@@ -147,8 +151,8 @@ __global__ __launch_bounds__(256) void pass2_f32(const float* __restrict__ H, co
   const int tiles_u = tile_base[u + 1] - tile_base[u];
   const int32_t t0 = tile_base[u] + ci * CT;
   const int nt = min(CT, tiles_u - ci * CT);
-  const int tid = threadIdx.x, j = tid & 63, grp = tid >> 6;
-  const int p = pb * 64 + j;
+  const int tid = threadIdx.x, j = tid % PB, grp = tid / PB;
+  const int p = pb * PB + j;
   const float* q32 = ws_f32(ws, L.off_q32);
   const float* lse = ws_f32(ws, L.off_lse32);
   float qv[D];
@@ -193,24 +197,31 @@ __global__ __launch_bounds__(256) void pass2_f32(const float* __restrict__ H, co
     if (tid < kTile) ls[tid] = lv;
     __syncthreads();
     if (it + 1 < nt) load_tile(it + 1);
-    // the logits of prototype j for tokens 8 grp .. 8 grp + 7: eight
-    // independent chains, rows read 16 bytes at a time (one address per wave)
-    float sx[8];
+    // the logits of prototype j for tokens TPG grp ..: TPG chains of two
+    // partial sums each, rows read 16 bytes at a time (a wave's four groups
+    // read four rows, in distinct banks)
+    float sx[TPG][2];
 #pragma unroll
-    for (int r8 = 0; r8 < 8; ++r8) sx[r8] = 0.f;
+    for (int r = 0; r < TPG; ++r) sx[r][0] = sx[r][1] = 0.f;
 #pragma unroll
-    for (int a = 0; a < D; a += 4) {
+    for (int a = 0; a < D; a += 8) {
 #pragma unroll
-      for (int r8 = 0; r8 < 8; ++r8) {
-        const f32x4 h4 = *reinterpret_cast<const f32x4*>(&hs[grp * 8 + r8][a]);
-        sx[r8] = fmaf(qv[a], h4.x, sx[r8]);
-        sx[r8] = fmaf(qv[a + 1], h4.y, sx[r8]);
-        sx[r8] = fmaf(qv[a + 2], h4.z, sx[r8]);
-        sx[r8] = fmaf(qv[a + 3], h4.w, sx[r8]);
+      for (int r = 0; r < TPG; ++r) {
+        const f32x4 h4 = *reinterpret_cast<const f32x4*>(&hs[grp * TPG + r][a]);
+        const f32x4 g4 = *reinterpret_cast<const f32x4*>(&hs[grp * TPG + r][a + 4]);
+        sx[r][0] = fmaf(qv[a], h4.x, sx[r][0]);
+        sx[r][1] = fmaf(qv[a + 4], g4.x, sx[r][1]);
+        sx[r][0] = fmaf(qv[a + 1], h4.y, sx[r][0]);
+        sx[r][1] = fmaf(qv[a + 5], g4.y, sx[r][1]);
+        sx[r][0] = fmaf(qv[a + 2], h4.z, sx[r][0]);
+        sx[r][1] = fmaf(qv[a + 6], g4.z, sx[r][1]);
+        sx[r][0] = fmaf(qv[a + 3], h4.w, sx[r][0]);
+        sx[r][1] = fmaf(qv[a + 7], g4.w, sx[r][1]);
       }
     }
 #pragma unroll
-    for (int r8 = 0; r8 < 8; ++r8) as[j][grp * 8 + r8] = exp2f(sx[r8] - ls[grp * 8 + r8]);
+    for (int r = 0; r < TPG; ++r)
+      as[j][grp * TPG + r] = exp2f(sx[r][0] + sx[r][1] - ls[grp * TPG + r]);
     __syncthreads();
     for (int r = 0; r < kTile; ++r) {
       const float a = as[j][r];
@@ -242,7 +253,7 @@ hipError_t launch_f32(const Layout& L, const void* H, const int64_t* offsets, co
     hipLaunchKernelGGL(pass1_f32<64>, dim3((unsigned)g1), dim3(256), 0, stream, (const float*)H, offsets, mask, L, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t g2 = (int64_t)L.chunks_max * (L.k / 64);
+  const int64_t g2 = (int64_t)L.chunks_max * (L.k / 16);
   if (g2 == 0) return hipSuccess;
   if (L.d == 128)
     hipLaunchKernelGGL(pass2_f32<128>, dim3((unsigned)g2), dim3(256), 0, stream, (const float*)H, offsets, mask, L, ws);
