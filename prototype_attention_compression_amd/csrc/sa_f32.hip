@@ -15,14 +15,14 @@
 
 namespace sa {
 
-// Pass 1: four threads per token slot (tile * 32 + row), 64 slots (two
-// tiles) per workgroup.  Thread (slot sl = tid / 4, part = tid % 4) takes the
-// prototypes j = 4 i + part.  The queries pass through LDS 64 rows at a time,
-// each row padded by 16 bytes so that the four rows a wave reads at once sit
+// Pass 1: eight threads per token slot (tile * 32 + row), 32 slots (one
+// tile) per workgroup.  Thread (slot sl = tid / 8, part = tid % 8) takes the
+// prototypes j = 8 i + part.  The queries pass through LDS 64 rows at a time,
+// each row padded by 16 bytes so that the eight rows a wave reads at once sit
 // in different banks (the 16 lanes of a part read the same address: a
 // broadcast).  Each thread keeps a running maximum m and the sum of 2^(x - m)
 // over its prototypes (one sweep: the sum is rescaled when the maximum
-// grows); the four partial pairs of a token are combined by lane shuffles.
+// grows); the eight partial pairs of a token are combined by lane shuffles.
 // Every thread takes part in the staging barriers; slots past the batch's
 // last tile compute on zeros and write nothing.
 template <int D>
@@ -31,8 +31,9 @@ __global__ __launch_bounds__(256) void pass1_f32(const float* __restrict__ H, co
   constexpr int QP = D + 4;   // padded query row (floats)
   __shared__ __attribute__((aligned(16))) float qs[64 * QP];
   const int32_t* hdr = ws_i32(ws, L.off_hdr);
-  const int tid = threadIdx.x, part = tid & 3;
-  const int64_t slot = (int64_t)blockIdx.x * 64 + (tid >> 2);
+  constexpr int TPT = 8;   // threads per token
+  const int tid = threadIdx.x, part = tid % TPT;
+  const int64_t slot = (int64_t)blockIdx.x * (256 / TPT) + tid / TPT;
   const int32_t T = hdr[kHdrTiles];
   const int32_t tile = (int32_t)(slot / kTile);
   const int row = (int)(slot % kTile);
@@ -84,9 +85,9 @@ __global__ __launch_bounds__(256) void pass1_f32(const float* __restrict__ H, co
     __syncthreads();
     // two prototypes at a time, each dot product in two partial sums (four
     // independent FMA chains)
-    for (int i = 0; i < 16; i += 2) {
-      const float* q0 = qs + (4 * i + part) * QP;
-      const float* q1 = q0 + 4 * QP;
+    for (int i = 0; i < 64 / TPT; i += 2) {
+      const float* q0 = qs + (TPT * i + part) * QP;
+      const float* q1 = q0 + TPT * QP;
       float x0a = 0.f, x0b = 0.f, x1a = 0.f, x1b = 0.f;
 #pragma unroll
       for (int a = 0; a < D; a += 8) {
@@ -113,9 +114,9 @@ __global__ __launch_bounds__(256) void pass1_f32(const float* __restrict__ H, co
       update(x1a + x1b);
     }
   }
-  // the four parts of a token are lanes 4 sl .. 4 sl + 3 of one wave
+  // the parts of a token are lanes TPT sl .. TPT sl + TPT - 1 of one wave
 #pragma unroll
-  for (int off = 1; off < 4; off <<= 1) {
+  for (int off = 1; off < TPT; off <<= 1) {
     const float mo = __shfl_xor(m, off), so = __shfl_xor(sum, off);
     const float mn = fmaxf(m, mo);
     sum = sum * exp2f(m - mn) + so * exp2f(mo - mn);
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(256) void pass2_f32(const float* __restrict__ H, co
 
 hipError_t launch_f32(const Layout& L, const void* H, const int64_t* offsets, const uint8_t* mask, void* ws,
                       hipStream_t stream) {
-  const int64_t g1 = ((int64_t)L.tiles_max * kTile + 63) / 64;
+  const int64_t g1 = ((int64_t)L.tiles_max * kTile + 31) / 32;
   if (g1 == 0) return hipSuccess;
   if (L.d == 128)
     hipLaunchKernelGGL(pass1_f32<128>, dim3((unsigned)g1), dim3(256), 0, stream, (const float*)H, offsets, mask, L, ws);

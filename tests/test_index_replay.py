@@ -313,7 +313,7 @@ def test_old_pass1_clamp_read_past_h():
 
 # ------------------------------------------------------------- fp32 path
 def replay_f32(lengths, d, k, masked=False):
-    """The fp32 kernels' indices (pass1_f32: four threads per token slot, 64
+    """The fp32 kernels' indices (pass1_f32: eight threads per token slot, 32
     slots per workgroup, queries staged 64 rows at a time; pass2_f32: one
     workgroup per (chunk, 64-prototype block), rows loaded from addresses
     clamped to the user's rows) against their buffers: H and the mask [N],
@@ -324,12 +324,12 @@ def replay_f32(lengths, d, k, masked=False):
     tiles_max = (N + (span - 1) * R) // span * ALIGN_T
     check(T <= tiles_max, "tiles within tiles_max")
     n_lse = tiles_max * TILE
-    # pass1_f32: grid ceil(tiles_max * 32 / 64) workgroups of 256 threads
-    g1 = (tiles_max * TILE + 63) // 64
+    # pass1_f32: grid ceil(tiles_max * 32 / 32) workgroups of 256 threads
+    g1 = (tiles_max * TILE + 31) // 32
     tid = np.arange(256)
-    part = tid & 3
+    part = tid % 8
     for b in range(g1):
-        slot = b * 64 + (tid >> 2)
+        slot = b * 32 + tid // 8
         tile = slot // TILE
         row = slot % TILE
         live = tile < T
